@@ -1,0 +1,162 @@
+"""Seeded synthetic workloads for latent-KV decode attention.
+
+Recipe (one numpy PCG64 stream per tensor, spawned from the workload seed in
+the fixed order lens, ckv, krope, q_nope, q_rope, w_uk, w_uv):
+
+* C_KV rows ~ N(0, 1), then divided by their own root-mean-square (unit RMS
+  rows, as a latent that has passed an RMS norm) unless the workload uses
+  fan-in scaling;
+* K_RoPE rows ~ N(0, 1). The cache stores them already rotated; a rotation of
+  an isotropic Gaussian is again isotropic Gaussian, so drawing them directly
+  gives the same distribution as rotating fresh draws;
+* q_nope, q_rope ~ N(0, 1); W_UK, W_UV ~ N(0, w_std^2);
+* "fan_in" workloads scale every tensor by 1/sqrt(its last width) instead
+  (C_KV, K_RoPE, q) and the weights by 1/sqrt(d_c);
+* bf16 workloads round every tensor to bf16 (round to nearest even) here, so
+  the oracle and the GPU see identical values.
+
+Nothing here computes a step of the decode path.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+
+def round_bf16(x):
+    """Round float32 values to the nearest bf16 (ties to even); returns
+    float32 holding bf16-representable values. Inputs must be finite."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    b = (b + (((b >> 16) & 1) + 0x7FFF)) & 0xFFFF0000
+    return b.view(np.float32)
+
+
+def bf16_bits(x):
+    """bf16 bit patterns (uint16) of bf16-representable float32 values."""
+    return (np.ascontiguousarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    heads: int
+    d_c: int
+    d_r: int
+    d_n: int
+    d_v: int
+    n: int                      # branch count (1 = MLA)
+    cache_len: int              # uniform length, or the upper end for ragged
+    dtype: str = "bf16"         # "bf16" or "fp32"
+    ragged_min: Optional[int] = None   # lengths ~ U{ragged_min..cache_len}
+    alpha_q: float = 1.0
+    alpha_kv: float = 1.0
+    theta: float = 10000.0
+    init: str = "rms"           # "rms" (unit-RMS latent rows, N(0,1) q) or "fan_in"
+    w_std: Optional[float] = None  # default 1/sqrt(d_c)
+    seed: int = 0
+
+    @property
+    def tau(self):
+        return 1.0 / math.sqrt(self.d_n + self.d_r)
+
+    @property
+    def row(self):
+        return self.d_c + self.d_r
+
+    def replace(self, **kw):
+        return dataclasses.replace(self, **kw)
+
+
+def _mlra4_scales():
+    # d = 7168 model width, d_c = 512, d_c' = 128 (four branches)
+    return math.sqrt(7168 / 128), math.sqrt(7168 / 512)
+
+
+_AQ4, _AKV4 = _mlra4_scales()
+
+DSV3 = dict(heads=128, d_c=512, d_r=64, d_n=128, d_v=128)
+
+WORKLOADS = {
+    # tiny fp32 MLA, fan-in scaled, positions 0..255
+    "tiny_mla_fp32": Workload("tiny_mla_fp32", 1, 4, 64, 16, 32, 32, 1, 256,
+                              dtype="fp32", init="fan_in", seed=1001),
+    # MLA at the DeepSeek-V3 attention shape, B=16, L=4096
+    "mla_b16_l4k": Workload("mla_b16_l4k", 16, n=1, cache_len=4096, seed=1002, **DSV3),
+    # MLRA-4 headline: B=16, L=32768
+    "mlra4_b16_l32k": Workload("mlra4_b16_l32k", 16, n=4, cache_len=32768,
+                               alpha_q=_AQ4, alpha_kv=_AKV4, seed=1003, **DSV3),
+    # MLA at the headline shape
+    "mla_b16_l32k": Workload("mla_b16_l32k", 16, n=1, cache_len=32768, seed=1003, **DSV3),
+    # long context, B=2, L=131072
+    "mla_b2_l128k": Workload("mla_b2_l128k", 2, n=1, cache_len=131072, seed=1004, **DSV3),
+    "mlra4_b2_l128k": Workload("mlra4_b2_l128k", 2, n=4, cache_len=131072,
+                               alpha_q=_AQ4, alpha_kv=_AKV4, seed=1004, **DSV3),
+    # one MLRA-4 branch (one tensor-parallel shard): latent 128 + rope 64,
+    # B=64, ragged lengths U{1024..65536}
+    "shard_b64_ragged": Workload("shard_b64_ragged", 64, 128, 128, 64, 128, 128, 1,
+                                 65536, ragged_min=1024, alpha_q=_AQ4, alpha_kv=_AKV4,
+                                 w_std=1.0 / math.sqrt(512), seed=1005),
+}
+
+
+def ragged_lens(rng, batch, lo, hi):
+    return rng.integers(lo, hi + 1, size=batch).astype(np.int32)
+
+
+def make_inputs(w: Workload, seed: Optional[int] = None, lens=None, max_len=None,
+                parts=("ckv", "krope", "q_nope", "q_rope", "w_uk", "w_uv")):
+    """Draw the inputs of workload ``w``.
+
+    Returns a dict of float32 arrays (bf16-representable for bf16 workloads):
+    ckv [B, L_max, d_c], krope [B, L_max, d_r], q_nope [B, H, d_n],
+    q_rope [B, H, d_r], w_uk [H, d_c, d_n], w_uv [H, d_c, d_v], plus
+    lens [B] int32. ``lens`` / ``max_len`` override the workload's lengths.
+    ``parts`` limits which tensors are drawn (the others are skipped but the
+    per-tensor streams stay the same).
+    """
+    ss = np.random.SeedSequence(w.seed if seed is None else seed)
+    g = [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(7)]
+    B, H = w.batch, w.heads
+    if lens is None:
+        if w.ragged_min is not None:
+            lens = ragged_lens(g[0], B, w.ragged_min, w.cache_len)
+        else:
+            lens = np.full(B, w.cache_len, dtype=np.int32)
+    lens = np.asarray(lens, dtype=np.int32)
+    if max_len is None:
+        max_len = int(max(int(lens.max()) if lens.size else 0, 1))
+    fan = w.init == "fan_in"
+    rnd = round_bf16 if w.dtype == "bf16" else (lambda a: np.asarray(a, np.float32))
+    w_std = w.w_std if w.w_std is not None else 1.0 / math.sqrt(w.d_c)
+    out = {"lens": lens}
+
+    if "ckv" in parts:
+        c = g[1].standard_normal((B, max_len, w.d_c), dtype=np.float32)
+        if fan:
+            c *= np.float32(1.0 / math.sqrt(w.d_c))
+        else:
+            ms = np.mean(np.square(c, dtype=np.float32), axis=-1, keepdims=True, dtype=np.float32)
+            c /= np.sqrt(ms + np.float32(1e-6))
+        out["ckv"] = rnd(c)
+        del c
+    if "krope" in parts:
+        k = g[2].standard_normal((B, max_len, w.d_r), dtype=np.float32)
+        if fan:
+            k *= np.float32(1.0 / math.sqrt(w.d_r))
+        out["krope"] = rnd(k)
+    if "q_nope" in parts:
+        q = g[3].standard_normal((B, H, w.d_n), dtype=np.float32)
+        out["q_nope"] = rnd(q / math.sqrt(w.d_n) if fan else q)
+    if "q_rope" in parts:
+        q = g[4].standard_normal((B, H, w.d_r), dtype=np.float32)
+        out["q_rope"] = rnd(q / math.sqrt(w.d_r) if fan else q)
+    if "w_uk" in parts:
+        out["w_uk"] = rnd(g[5].standard_normal((H, w.d_c, w.d_n), dtype=np.float32) * np.float32(w_std))
+    if "w_uv" in parts:
+        out["w_uv"] = rnd(g[6].standard_normal((H, w.d_c, w.d_v), dtype=np.float32) * np.float32(w_std))
+    return out
