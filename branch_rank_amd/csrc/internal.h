@@ -1,0 +1,72 @@
+// Internal declarations shared by the host API and the kernel translation
+// units. Not part of the public C ABI (include/mlra.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlra {
+
+// Split-KV plan. All cached tokens of the batch form one stream (sequence b
+// occupies [prefix[b], prefix[b+1])). The stream is cut into n_items equal
+// work items of `chunk` tokens; item k covers [k*chunk, (k+1)*chunk) and may
+// span several sequences, one segment per sequence. The segment of item k in
+// sequence b writes its softmax partials to slot k + b, which is unique
+// because a later sequence never starts in an earlier item.
+struct PlanHeader {
+  int32_t chunk;
+  int32_t n_items;
+  int32_t total;
+  int32_t pad;
+};
+
+// Partial softmax state per slot: m and l as [slot][n][H] fp32 (m in log2
+// units, i.e. max of score*log2(e)), acc as [slot][d_c][H] fp32 (unnormalised).
+struct Workspace {
+  PlanHeader* hdr;
+  int32_t* prefix;  // [B + 1]
+  float* m;         // [slots][n][H]
+  float* l;         // [slots][n][H]
+  float* acc;       // [slots][d_c][H]
+  void* q_abs;      // [B][H][d_c + d_r] (mlra_decode only)
+  float* latent;    // [B][H][d_c]       (mlra_decode only)
+};
+
+struct Geom {
+  int B, H, dc, dr, dn, dv, n;
+  int max_len;
+  int64_t ckv_bs, ckv_ts, kr_bs, kr_ts;  // element strides
+};
+
+constexpr int kMinChunk = 64;      // smallest automatic work item, tokens
+constexpr int kMaxAutoItems = 512; // upper bound on automatic work items
+
+// ---- launchers (return the launch status) ----
+hipError_t launch_plan(const int32_t* lens, int B, int max_len, int target_items,
+                       int forced_chunk, const Workspace& ws, hipStream_t s);
+
+template <typename T>
+hipError_t launch_absorb_q_generic(const Geom& g, const T* q_nope, const T* q_rope,
+                                   const int32_t* q_pos, const int32_t* lens, const T* w_uk,
+                                   T* q_abs, float tau, float alpha_q, float theta,
+                                   hipStream_t s);
+
+template <typename T>
+hipError_t launch_decode_generic(const Geom& g, const T* q_abs, const T* ckv, const T* krope,
+                                 const Workspace& ws, int grid_items, hipStream_t s);
+
+hipError_t launch_combine(const Geom& g, const Workspace& ws, float* latent_out, hipStream_t s);
+
+template <typename T, typename TO>
+hipError_t launch_out_proj_generic(const Geom& g, const float* latent, const T* w_uv, TO* out,
+                                   float alpha_kv, hipStream_t s);
+
+// Fast bf16 MFMA decode. Returns hipErrorNotSupported when the shape has no
+// specialisation (the caller then uses the generic kernel).
+bool decode_mfma_supported(const Geom& g);
+int decode_mfma_items_per_cu(const Geom& g);
+hipError_t launch_decode_mfma(const Geom& g, const void* q_abs, const void* ckv,
+                              const void* krope, const Workspace& ws, int grid_items,
+                              hipStream_t s);
+
+}  // namespace mlra

@@ -1,0 +1,430 @@
+// Host side of the C ABI declared in include/mlra.h: argument validation,
+// workspace layout, kernel selection and launches on the caller's stream.
+// Nothing here allocates device memory or synchronises.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/mlra.h"
+#include "internal.h"
+
+using namespace mlra;
+
+namespace {
+
+thread_local std::string g_detail;
+thread_local hipEvent_t g_ev_before = nullptr;
+thread_local hipEvent_t g_ev_after = nullptr;
+
+mlra_status_t fail(mlra_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_detail = buf;
+  return st;
+}
+
+mlra_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(MLRA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elt_size(mlra_dtype_t t) { return t == MLRA_BF16 ? 2 : 4; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Limits of the kernels (see the launchers).
+constexpr int kMaxLatent = 1024, kMaxRope = 256, kMaxNope = 512, kMaxBranches = 8;
+constexpr int kMaxHeadBranch = 1024;  // num_heads * num_branches
+
+mlra_status_t check_cfg(const mlra_config_t* c) {
+  if (!c) return fail(MLRA_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->num_heads < 1 || c->d_latent < 1 || c->d_rope < 0 || c->d_nope < 1 || c->d_v < 1)
+    return fail(MLRA_ERR_INVALID_ARG, "sizes must be positive (d_rope >= 0)");
+  if (c->d_rope % 2) return fail(MLRA_ERR_INVALID_ARG, "d_rope must be even");
+  if (c->num_branches < 1 || c->d_latent % c->num_branches)
+    return fail(MLRA_ERR_INVALID_ARG, "d_latent (%d) must be a multiple of num_branches (%d)",
+                c->d_latent, c->num_branches);
+  if (c->dtype != MLRA_BF16 && c->dtype != MLRA_FP32)
+    return fail(MLRA_ERR_INVALID_ARG, "unknown dtype %d", (int)c->dtype);
+  if (!(c->rope_theta > 0.f)) return fail(MLRA_ERR_INVALID_ARG, "rope_theta must be > 0");
+  if (!std::isfinite(c->alpha_q) || !std::isfinite(c->alpha_kv) || !std::isfinite(c->sm_scale))
+    return fail(MLRA_ERR_INVALID_ARG, "scales must be finite");
+  if (c->kv_chunk < 0) return fail(MLRA_ERR_INVALID_ARG, "kv_chunk must be >= 0");
+  if (c->d_latent > kMaxLatent || c->d_rope > kMaxRope || c->d_nope > kMaxNope ||
+      c->num_branches > kMaxBranches || c->num_heads * c->num_branches > kMaxHeadBranch ||
+      c->d_v > 4096)
+    return fail(MLRA_ERR_UNSUPPORTED,
+                "sizes beyond the supported range (d_latent<=%d, d_rope<=%d, d_nope<=%d, "
+                "branches<=%d, heads*branches<=%d, d_v<=4096)",
+                kMaxLatent, kMaxRope, kMaxNope, kMaxBranches, kMaxHeadBranch);
+  return MLRA_OK;
+}
+
+float tau_of(const mlra_config_t* c) {
+  return c->sm_scale > 0.f ? c->sm_scale : 1.0f / std::sqrt((float)(c->d_nope + c->d_rope));
+}
+
+mlra_status_t check_batch(int32_t batch, int32_t max_len) {
+  if (batch < 0 || batch > 65535) return fail(MLRA_ERR_INVALID_ARG, "batch must be in [0, 65535]");
+  if (max_len < 0) return fail(MLRA_ERR_INVALID_ARG, "max_len must be >= 0");
+  if ((int64_t)batch * max_len > 0x7fffffffLL)
+    return fail(MLRA_ERR_UNSUPPORTED, "batch * max_len must stay below 2^31 tokens");
+  return MLRA_OK;
+}
+
+int64_t items_max(const mlra_config_t* c, int32_t batch, int32_t max_len) {
+  const int64_t tokens = (int64_t)batch * max_len;
+  if (tokens == 0) return 0;
+  if (c->kv_chunk > 0) return (tokens + c->kv_chunk - 1) / c->kv_chunk;
+  const int64_t by_min = (tokens + kMinChunk - 1) / kMinChunk;
+  return by_min < kMaxAutoItems ? by_min : kMaxAutoItems;
+}
+
+struct Layout {
+  size_t hdr, prefix, m, l, acc, q_abs, latent, total;
+  int64_t slots;
+};
+
+Layout layout(const mlra_config_t* c, int32_t batch, int32_t max_len) {
+  Layout L;
+  const size_t H = c->num_heads, n = c->num_branches, dc = c->d_latent, dr = c->d_rope;
+  L.slots = items_max(c, batch, max_len) + batch;
+  size_t off = 0;
+  L.hdr = off;    off = round_up(off + sizeof(PlanHeader), 256);
+  L.prefix = off; off = round_up(off + 4 * (size_t)(batch + 1), 256);
+  L.m = off;      off = round_up(off + 4 * (size_t)L.slots * n * H, 256);
+  L.l = off;      off = round_up(off + 4 * (size_t)L.slots * n * H, 256);
+  L.acc = off;    off = round_up(off + 4 * (size_t)L.slots * dc * H, 256);
+  L.q_abs = off;  off = round_up(off + elt_size(c->dtype) * (size_t)batch * H * (dc + dr), 256);
+  L.latent = off; off = round_up(off + 4 * (size_t)batch * H * dc, 256);
+  L.total = off;
+  return L;
+}
+
+Workspace carve(const Layout& L, void* base) {
+  char* p = static_cast<char*>(base);
+  Workspace w;
+  w.hdr = reinterpret_cast<PlanHeader*>(p + L.hdr);
+  w.prefix = reinterpret_cast<int32_t*>(p + L.prefix);
+  w.m = reinterpret_cast<float*>(p + L.m);
+  w.l = reinterpret_cast<float*>(p + L.l);
+  w.acc = reinterpret_cast<float*>(p + L.acc);
+  w.q_abs = p + L.q_abs;
+  w.latent = reinterpret_cast<float*>(p + L.latent);
+  return w;
+}
+
+// ---- per-device properties, filled once per device ----
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+int g_cu_count[kMaxDevices];
+
+mlra_status_t current_device(int* dev, int* cus) {
+  int count = 0;
+  hipError_t e = hipGetDeviceCount(&count);
+  if (e != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return fail(MLRA_ERR_NO_DEVICE, "no HIP device available (%s)",
+                e == hipSuccess ? "count is 0" : hipGetErrorString(e));
+  }
+  e = hipGetDevice(dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (*dev < 0 || *dev >= kMaxDevices) return fail(MLRA_ERR_UNSUPPORTED, "device id too large");
+  hipError_t ae = hipSuccess;
+  std::call_once(g_dev_once[*dev], [&] {
+    int v = 0;
+    ae = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, *dev);
+    g_cu_count[*dev] = v > 0 ? v : 1;
+  });
+  if (ae != hipSuccess) return hip_fail(ae, "hipDeviceGetAttribute");
+  *cus = g_cu_count[*dev];
+  return MLRA_OK;
+}
+
+enum class DecodePath { Auto, Generic, Mfma };
+
+DecodePath path_override() {
+  static DecodePath p = [] {
+    const char* s = std::getenv("MLRA_DECODE_PATH");
+    if (s && !std::strcmp(s, "generic")) return DecodePath::Generic;
+    if (s && !std::strcmp(s, "mfma")) return DecodePath::Mfma;
+    return DecodePath::Auto;
+  }();
+  return p;
+}
+
+Geom make_geom(const mlra_config_t* c, int32_t batch, const mlra_cache_t* cache) {
+  Geom g;
+  g.B = batch;
+  g.H = c->num_heads;
+  g.dc = c->d_latent;
+  g.dr = c->d_rope;
+  g.dn = c->d_nope;
+  g.dv = c->d_v;
+  g.n = c->num_branches;
+  g.max_len = cache ? cache->max_len : 0;
+  g.ckv_bs = cache ? cache->ckv_batch_stride : 0;
+  g.ckv_ts = cache ? cache->ckv_token_stride : 0;
+  g.kr_bs = cache ? cache->krope_batch_stride : 0;
+  g.kr_ts = cache ? cache->krope_token_stride : 0;
+  return g;
+}
+
+mlra_status_t check_cache(const mlra_config_t* c, const mlra_cache_t* k, int32_t batch) {
+  if (!k) return fail(MLRA_ERR_INVALID_ARG, "cache is NULL");
+  mlra_status_t st = check_batch(batch, k->max_len);
+  if (st != MLRA_OK) return st;
+  if (batch == 0) return MLRA_OK;
+  if (!k->cache_lens) return fail(MLRA_ERR_INVALID_ARG, "cache_lens is NULL");
+  if (k->max_len == 0) return MLRA_OK;
+  if (!k->ckv || (c->d_rope > 0 && !k->krope))
+    return fail(MLRA_ERR_INVALID_ARG, "cache pointers are NULL");
+  if (!aligned16(k->ckv) || (c->d_rope > 0 && !aligned16(k->krope)))
+    return fail(MLRA_ERR_INVALID_ARG, "cache base pointers must be 16-byte aligned");
+  const int64_t e = (int64_t)elt_size(c->dtype);
+  if (k->ckv_token_stride < 1 || k->ckv_batch_stride < 0 ||
+      (c->d_rope > 0 && (k->krope_token_stride < 1 || k->krope_batch_stride < 0)))
+    return fail(MLRA_ERR_INVALID_ARG, "cache strides: token stride >= 1, batch stride >= 0");
+  if ((k->ckv_token_stride * e) % 16 || (k->ckv_batch_stride * e) % 16 ||
+      (c->d_rope > 0 && ((k->krope_token_stride * e) % 16 || (k->krope_batch_stride * e) % 16)))
+    return fail(MLRA_ERR_INVALID_ARG, "cache strides must be multiples of 16 bytes");
+  return MLRA_OK;
+}
+
+mlra_status_t check_ptr(const void* p, const char* name) {
+  if (!p) return fail(MLRA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(MLRA_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
+  return MLRA_OK;
+}
+
+#define TRY(x)                          \
+  do {                                  \
+    mlra_status_t st_ = (x);            \
+    if (st_ != MLRA_OK) return st_;     \
+  } while (0)
+
+#define TRY_HIP(x, what)                       \
+  do {                                         \
+    hipError_t e_ = (x);                       \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+// ---- launches (arguments already validated) ----
+
+mlra_status_t run_absorb(const mlra_config_t* c, const Geom& g, const void* q_nope,
+                         const void* q_rope, const int32_t* q_pos, const int32_t* lens,
+                         const void* w_uk, void* q_abs, hipStream_t s) {
+  const float tau = tau_of(c);
+  hipError_t e;
+  if (c->dtype == MLRA_BF16)
+    e = launch_absorb_q_generic<__bf16>(g, (const __bf16*)q_nope, (const __bf16*)q_rope, q_pos,
+                                        lens, (const __bf16*)w_uk, (__bf16*)q_abs, tau,
+                                        c->alpha_q, c->rope_theta, s);
+  else
+    e = launch_absorb_q_generic<float>(g, (const float*)q_nope, (const float*)q_rope, q_pos, lens,
+                                       (const float*)w_uk, (float*)q_abs, tau, c->alpha_q,
+                                       c->rope_theta, s);
+  TRY_HIP(e, "absorb_q launch");
+  return MLRA_OK;
+}
+
+mlra_status_t run_decode(const mlra_config_t* c, const Geom& g, int cus, const void* q_abs,
+                         const mlra_cache_t* k, const Workspace& ws, const Layout& L,
+                         float* latent_out, hipStream_t s) {
+  const int64_t imax = L.slots - g.B;
+  bool fast = c->dtype == MLRA_BF16 && decode_mfma_supported(g);
+  const DecodePath over = path_override();
+  if (over == DecodePath::Generic) fast = false;
+  if (over == DecodePath::Mfma && !fast)
+    return fail(MLRA_ERR_UNSUPPORTED, "MLRA_DECODE_PATH=mfma but no MFMA kernel for this shape");
+  int target;
+  if (fast) {
+    target = cus * decode_mfma_items_per_cu(g);
+  } else {
+    target = cus * 4 / g.H;
+    if (target < 1) target = 1;
+  }
+  if (target > kMaxAutoItems) target = kMaxAutoItems;
+  if (target > imax && imax > 0) target = (int)imax;
+  TRY_HIP(launch_plan(k->cache_lens, g.B, g.max_len, target > 0 ? target : 1, c->kv_chunk, ws, s),
+          "plan launch");
+  if (imax > 0) {
+    if (g_ev_before) TRY_HIP(hipEventRecord(g_ev_before, s), "hipEventRecord");
+    hipError_t e;
+    if (fast)
+      e = launch_decode_mfma(g, q_abs, k->ckv, k->krope, ws, (int)imax, s);
+    else if (c->dtype == MLRA_BF16)
+      e = launch_decode_generic<__bf16>(g, (const __bf16*)q_abs, (const __bf16*)k->ckv,
+                                        (const __bf16*)k->krope, ws, (int)imax, s);
+    else
+      e = launch_decode_generic<float>(g, (const float*)q_abs, (const float*)k->ckv,
+                                       (const float*)k->krope, ws, (int)imax, s);
+    TRY_HIP(e, "decode launch");
+    if (g_ev_after) TRY_HIP(hipEventRecord(g_ev_after, s), "hipEventRecord");
+  }
+  TRY_HIP(launch_combine(g, ws, latent_out, s), "combine launch");
+  return MLRA_OK;
+}
+
+mlra_status_t run_out_proj(const mlra_config_t* c, const Geom& g, const float* latent,
+                           const void* w_uv, void* out, mlra_dtype_t od, hipStream_t s) {
+  hipError_t e;
+  if (c->dtype == MLRA_BF16) {
+    if (od == MLRA_BF16)
+      e = launch_out_proj_generic<__bf16, __bf16>(g, latent, (const __bf16*)w_uv, (__bf16*)out,
+                                                  c->alpha_kv, s);
+    else
+      e = launch_out_proj_generic<__bf16, float>(g, latent, (const __bf16*)w_uv, (float*)out,
+                                                 c->alpha_kv, s);
+  } else {
+    if (od == MLRA_BF16)
+      e = launch_out_proj_generic<float, __bf16>(g, latent, (const float*)w_uv, (__bf16*)out,
+                                                 c->alpha_kv, s);
+    else
+      e = launch_out_proj_generic<float, float>(g, latent, (const float*)w_uv, (float*)out,
+                                                c->alpha_kv, s);
+  }
+  TRY_HIP(e, "out_proj launch");
+  return MLRA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mlra_status_string(mlra_status_t s) {
+  switch (s) {
+    case MLRA_OK: return "MLRA_OK";
+    case MLRA_ERR_INVALID_ARG: return "MLRA_ERR_INVALID_ARG";
+    case MLRA_ERR_UNSUPPORTED: return "MLRA_ERR_UNSUPPORTED";
+    case MLRA_ERR_WORKSPACE: return "MLRA_ERR_WORKSPACE";
+    case MLRA_ERR_NO_DEVICE: return "MLRA_ERR_NO_DEVICE";
+    case MLRA_ERR_HIP: return "MLRA_ERR_HIP";
+  }
+  return "MLRA_ERR_UNKNOWN";
+}
+
+const char* mlra_last_error_detail(void) { return g_detail.c_str(); }
+
+mlra_status_t mlra_set_kernel_timing(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr))
+    return fail(MLRA_ERR_INVALID_ARG, "give both events or neither");
+  g_ev_before = static_cast<hipEvent_t>(before);
+  g_ev_after = static_cast<hipEvent_t>(after);
+  return MLRA_OK;
+}
+
+mlra_status_t mlra_workspace_size(const mlra_config_t* cfg, int32_t batch, int32_t max_len,
+                                  size_t* bytes) {
+  g_detail.clear();
+  TRY(check_cfg(cfg));
+  TRY(check_batch(batch, max_len));
+  if (!bytes) return fail(MLRA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = layout(cfg, batch, max_len).total;
+  return MLRA_OK;
+}
+
+mlra_status_t mla_absorb_q(const mlra_config_t* cfg, int32_t batch, const void* q_nope,
+                           const void* q_rope, const int32_t* q_pos, const int32_t* cache_lens,
+                           const void* w_uk, void* q_abs, void* stream) {
+  g_detail.clear();
+  TRY(check_cfg(cfg));
+  TRY(check_batch(batch, 0));
+  if (batch == 0) return MLRA_OK;
+  TRY(check_ptr(q_nope, "q_nope"));
+  if (cfg->d_rope > 0) TRY(check_ptr(q_rope, "q_rope"));
+  TRY(check_ptr(w_uk, "w_uk"));
+  TRY(check_ptr(q_abs, "q_abs"));
+  if (!q_pos && !cache_lens) return fail(MLRA_ERR_INVALID_ARG, "need q_pos or cache_lens");
+  int dev, cus;
+  TRY(current_device(&dev, &cus));
+  Geom g = make_geom(cfg, batch, nullptr);
+  g.max_len = 0x7fffffff;  // cache_lens - 1 is used as given (clamped below by 0)
+  return run_absorb(cfg, g, q_nope, q_rope, q_pos, cache_lens, w_uk, q_abs,
+                    static_cast<hipStream_t>(stream));
+}
+
+mlra_status_t mla_decode_attn(const mlra_config_t* cfg, int32_t batch, const void* q_abs,
+                              const mlra_cache_t* cache, void* workspace, size_t ws_bytes,
+                              float* latent_out, void* stream) {
+  g_detail.clear();
+  TRY(check_cfg(cfg));
+  TRY(check_cache(cfg, cache, batch));
+  if (batch == 0) return MLRA_OK;
+  TRY(check_ptr(q_abs, "q_abs"));
+  TRY(check_ptr(latent_out, "latent_out"));
+  const Layout L = layout(cfg, batch, cache->max_len);
+  if (!workspace || ws_bytes < L.total)
+    return fail(MLRA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", L.total, ws_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(MLRA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  int dev, cus;
+  TRY(current_device(&dev, &cus));
+  const Geom g = make_geom(cfg, batch, cache);
+  return run_decode(cfg, g, cus, q_abs, cache, carve(L, workspace), L, latent_out,
+                    static_cast<hipStream_t>(stream));
+}
+
+mlra_status_t mla_out_proj(const mlra_config_t* cfg, int32_t batch, const float* latent_out,
+                           const void* w_uv, void* out, mlra_dtype_t out_dtype, void* stream) {
+  g_detail.clear();
+  TRY(check_cfg(cfg));
+  TRY(check_batch(batch, 0));
+  if (out_dtype != MLRA_BF16 && out_dtype != MLRA_FP32)
+    return fail(MLRA_ERR_INVALID_ARG, "unknown out_dtype");
+  if (batch == 0) return MLRA_OK;
+  TRY(check_ptr(latent_out, "latent_out"));
+  TRY(check_ptr(w_uv, "w_uv"));
+  TRY(check_ptr(out, "out"));
+  int dev, cus;
+  TRY(current_device(&dev, &cus));
+  return run_out_proj(cfg, make_geom(cfg, batch, nullptr), latent_out, w_uv, out, out_dtype,
+                      static_cast<hipStream_t>(stream));
+}
+
+mlra_status_t mlra_decode(const mlra_config_t* cfg_in, int32_t num_branches, int32_t batch,
+                          const void* q_nope, const void* q_rope, const int32_t* q_pos,
+                          const void* w_uk, const void* w_uv, const mlra_cache_t* cache,
+                          void* workspace, size_t ws_bytes, void* out, mlra_dtype_t out_dtype,
+                          void* stream) {
+  g_detail.clear();
+  if (!cfg_in) return fail(MLRA_ERR_INVALID_ARG, "cfg is NULL");
+  mlra_config_t cfg = *cfg_in;
+  cfg.num_branches = num_branches;
+  TRY(check_cfg(&cfg));
+  TRY(check_cache(&cfg, cache, batch));
+  if (out_dtype != MLRA_BF16 && out_dtype != MLRA_FP32)
+    return fail(MLRA_ERR_INVALID_ARG, "unknown out_dtype");
+  if (batch == 0) return MLRA_OK;
+  TRY(check_ptr(q_nope, "q_nope"));
+  if (cfg.d_rope > 0) TRY(check_ptr(q_rope, "q_rope"));
+  TRY(check_ptr(w_uk, "w_uk"));
+  TRY(check_ptr(w_uv, "w_uv"));
+  TRY(check_ptr(out, "out"));
+  const Layout L = layout(&cfg, batch, cache->max_len);
+  if (!workspace || ws_bytes < L.total)
+    return fail(MLRA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", L.total, ws_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(MLRA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  int dev, cus;
+  TRY(current_device(&dev, &cus));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const Geom g = make_geom(&cfg, batch, cache);
+  const Workspace ws = carve(L, workspace);
+  TRY(run_absorb(&cfg, g, q_nope, q_rope, q_pos, cache->cache_lens, w_uk, ws.q_abs, s));
+  TRY(run_decode(&cfg, g, cus, ws.q_abs, cache, ws, L, ws.latent, s));
+  return run_out_proj(&cfg, g, ws.latent, w_uv, out, out_dtype, s);
+}
+
+}  // extern "C"

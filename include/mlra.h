@@ -1,0 +1,161 @@
+/*
+ * mlra.h - one decode step of attention over a compressed latent KV cache,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Methods (pages cited by title and section):
+ *   MLA  - multi-head latent attention with weight absorption: the cache holds
+ *          one latent row c_t (width d_c) and one RoPE key row k^R_t (width
+ *          d_r) per token, shared by all heads ("ML Revisit: Attention",
+ *          section Multi-Head Latent Attention; "vllbc02MLA", 苏神思路).
+ *   MLRA-n - the multi-branch variant: branch j attends over its own latent
+ *          slice [j*d_c/n, (j+1)*d_c/n) plus the shared RoPE key, runs its own
+ *          softmax, and the branch outputs are summed ("Multi-Head Low-Rank
+ *          Attention", 核心方法 and 方法步骤详情). MLA is n = 1.
+ *
+ * Per sequence b with cache length L_b and head h the library computes
+ *   q_abs  = [alpha_q * tau * W_UK[h] q^N  ||  tau * RoPE(q^R, p_b)]
+ *   s_j,t  = q_abs[S_j] . c_t[S_j] + q_abs[rope] . k^R_t          (t < L_b)
+ *   o~_j   = sum_t softmax_t(s_j) c_t[S_j]
+ *   o      = alpha_kv * W_UV[h]^T concat_j(o~_j)
+ * with p_b = L_b - 1 unless a query position is given. L_b = 0 gives o = 0.
+ * RoPE rotates consecutive pairs (2i, 2i+1) by p * theta^(-2i/d_r).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers to dense row-major arrays unless
+ *     stated; the caller owns them. The library never allocates device memory
+ *     and never synchronises: each call only enqueues kernels on `stream`
+ *     (a hipStream_t; NULL = the legacy default stream) and results are valid
+ *     once that stream's work has completed.
+ *   - Host-side validation runs before any launch. On any error nothing is
+ *     launched and outputs are left untouched. Errors are reported as status
+ *     codes; mlra_last_error_detail() gives text for the calling thread.
+ *   - cache_lens values outside [0, max_len] are clamped on the device.
+ *   - dtype: MLRA_BF16 means q_nope, q_rope, W_UK, W_UV, the cache and q_abs
+ *     are bf16 (accumulation in fp32); MLRA_FP32 means all of them are fp32.
+ *     latent_out is always fp32.
+ *   - Calls are thread-safe and stateless apart from per-thread error text,
+ *     per-thread timing events (mlra_set_kernel_timing) and a per-device
+ *     table of device properties filled on first use.
+ */
+#ifndef MLRA_H_
+#define MLRA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MLRA_API __attribute__((visibility("default")))
+#else
+#define MLRA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLRA_OK = 0,
+  MLRA_ERR_INVALID_ARG = 1,  /* null pointer, bad size, misaligned pointer or stride */
+  MLRA_ERR_UNSUPPORTED = 2,  /* valid but unsupported combination of sizes/dtypes */
+  MLRA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than mlra_workspace_size */
+  MLRA_ERR_NO_DEVICE = 4,    /* no usable HIP device */
+  MLRA_ERR_HIP = 5           /* a HIP runtime call or kernel launch failed */
+} mlra_status_t;
+
+typedef enum { MLRA_BF16 = 0, MLRA_FP32 = 1 } mlra_dtype_t;
+
+typedef struct {
+  int32_t num_heads;     /* H >= 1 */
+  int32_t d_latent;      /* d_c, total latent width (all branches) */
+  int32_t d_rope;        /* d_r, even */
+  int32_t d_nope;        /* d_n */
+  int32_t d_v;           /* value width per head */
+  int32_t num_branches;  /* n >= 1, d_latent % n == 0; 1 = MLA */
+  float sm_scale;        /* tau; <= 0 selects 1/sqrt(d_nope + d_rope) */
+  float alpha_q;         /* multiplies the NoPE score term of every branch */
+  float alpha_kv;        /* multiplies the summed branch output */
+  float rope_theta;      /* RoPE base, e.g. 10000 */
+  mlra_dtype_t dtype;
+  int32_t kv_chunk;      /* tokens per split-KV work item; 0 = chosen by the library */
+} mlra_config_t;
+
+/* Strided view of the latent cache. Element strides (not bytes). Row t of
+ * sequence b is ckv + b*ckv_batch_stride + t*ckv_token_stride (d_latent
+ * contiguous elements) and krope + b*krope_batch_stride + t*krope_token_stride
+ * (d_rope contiguous elements, stored already rotated at position t). One
+ * interleaved buffer of [c_t || k^R_t] rows, two separate buffers, or a branch
+ * shard all fit this view. */
+typedef struct {
+  const void* ckv;
+  const void* krope;
+  int64_t ckv_batch_stride, ckv_token_stride;
+  int64_t krope_batch_stride, krope_token_stride;
+  const int32_t* cache_lens;  /* device [B] */
+  int32_t max_len;            /* rows allocated per sequence */
+} mlra_cache_t;
+
+/* Bytes of workspace that mla_decode_attn and mlra_decode need for this
+ * configuration, batch size and max_len. Host-only; launches nothing. */
+MLRA_API mlra_status_t mlra_workspace_size(const mlra_config_t* cfg, int32_t batch, int32_t max_len,
+                                  size_t* bytes);
+
+/* Step 1, query-side absorption ("Multi-Head Low-Rank Attention", 方法步骤详情
+ * step 1; "ML Revisit: Attention", Multi-Head Latent Attention: W_UK moves
+ * into the query; RoPE on the query part only, "从MHA到MLA" 3.2).
+ *   q_nope [B][H][d_nope], q_rope [B][H][d_rope] (unrotated), dtype cfg->dtype
+ *   q_pos  [B] int32 query positions, or NULL to use cache_lens[b] - 1
+ *   cache_lens [B] int32 (read only when q_pos is NULL)
+ *   w_uk   [H][d_latent][d_nope]
+ *   q_abs  out [B][H][d_latent + d_rope], dtype cfg->dtype
+ * All branches are covered at once: branch j's absorbed query is the slice
+ * S_j of q_abs. */
+MLRA_API mlra_status_t mla_absorb_q(const mlra_config_t* cfg, int32_t batch, const void* q_nope,
+                           const void* q_rope, const int32_t* q_pos, const int32_t* cache_lens,
+                           const void* w_uk, void* q_abs, void* stream);
+
+/* Step 2, MQA-style decode over [C_KV || K_RoPE] in latent space, one online
+ * softmax per branch, split over the token axis and merged
+ * ("Multi-Head Low-Rank Attention", 方法步骤详情 step 2; "vllbc02MLA",
+ * 苏神思路: decoding works like MQA).
+ *   q_abs      [B][H][d_latent + d_rope] from mla_absorb_q
+ *   cache      strided cache view (16-byte aligned bases and strides for bf16)
+ *   workspace  device buffer of at least mlra_workspace_size() bytes
+ *   latent_out out [B][H][d_latent] fp32 = concat_j o~_j (branch-normalised) */
+MLRA_API mlra_status_t mla_decode_attn(const mlra_config_t* cfg, int32_t batch, const void* q_abs,
+                              const mlra_cache_t* cache, void* workspace, size_t ws_bytes,
+                              float* latent_out, void* stream);
+
+/* Step 3, output up-projection and branch sum ("Multi-Head Low-Rank
+ * Attention", 方法步骤详情 step 3 and the sum over branches in 核心方法):
+ *   out[b][h] = alpha_kv * W_UV[h]^T latent_out[b][h]
+ *   latent_out [B][H][d_latent] fp32, w_uv [H][d_latent][d_v] (cfg->dtype),
+ *   out [B][H][d_v] in out_dtype. */
+MLRA_API mlra_status_t mla_out_proj(const mlra_config_t* cfg, int32_t batch, const float* latent_out,
+                           const void* w_uv, void* out, mlra_dtype_t out_dtype, void* stream);
+
+/* The whole decode step (steps 1-3) for MLRA with `num_branches` branches
+ * (overrides cfg->num_branches; 1 = MLA). Intermediates live in the workspace.
+ * Arguments as for the three calls above. */
+MLRA_API mlra_status_t mlra_decode(const mlra_config_t* cfg, int32_t num_branches, int32_t batch,
+                          const void* q_nope, const void* q_rope, const int32_t* q_pos,
+                          const void* w_uk, const void* w_uv, const mlra_cache_t* cache,
+                          void* workspace, size_t ws_bytes, void* out, mlra_dtype_t out_dtype,
+                          void* stream);
+
+/* Instrumentation: when both are non-NULL hipEvent_t handles, every later call
+ * made on this thread records `before` immediately before and `after`
+ * immediately after the split-KV decode kernel, on the call's stream. Pass
+ * NULL, NULL to stop. */
+MLRA_API mlra_status_t mlra_set_kernel_timing(void* before, void* after);
+
+/* Static text for a status code. */
+MLRA_API const char* mlra_status_string(mlra_status_t status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+MLRA_API const char* mlra_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLRA_H_ */

