@@ -1,13 +1,411 @@
-// bf16 MFMA split-KV latent decode for gfx950 (placeholder: no shape is
-// specialised yet, so the host falls back to the portable kernel).
+// bf16 MFMA split-KV latent decode for gfx950 (MI355X).
+//
+// What it computes ("Multi-Head Low-Rank Attention", 方法步骤详情 step 2 and
+// 核心方法; "vllbc02MLA", 苏神思路): for one work item (a token range of one
+// or more sequences, see PlanHeader) and a group of heads, the MQA-style
+// attention of the absorbed query q_abs[h] = [q~ || rho] over the latent rows
+// [c_t || k^R_t], one online softmax per branch j over the branch's latent
+// slice plus the shared RoPE key, accumulating acc_j[h] = sum_t p_t c_t[S_j].
+// It writes the unnormalised partial state (m, l, acc) that the combine merges.
+//
+// Mapping onto CDNA4:
+//  * A workgroup owns one work item and 16*NW heads (16 per wave); when that
+//    is less than all heads, the workgroups of one item's head groups are
+//    placed on the same XCD back to back so that the second read of every KV
+//    tile hits that XCD's L2.
+//  * KV tiles (32 tokens) stream HBM -> LDS with global_load_lds_dwordx4 (no
+//    VGPR staging) through an NS-stage ring shared by all waves; vmcnt waits
+//    are placed by hand because the compiler does not order LDS-DMA against
+//    ds_read.
+//  * QK: S^T[t][h] = sum_d K[t][d] Q[h][d] on v_mfma_f32_16x16x32_bf16 with 16
+//    tokens as M and the wave's 16 heads as N; Q^T stays in VGPRs for the
+//    whole segment. The RoPE part is computed once per tile and shared by all
+//    branches.
+//  * The S^T accumulators (lane = head, 4 token rows per M block) are exactly
+//    the B operand of PV, O^T[c][h] = sum_t V^T[c][t] P^T[t][h] with the 32
+//    tile tokens as K, so P never moves between lanes. V^T is read from the
+//    same row-major LDS tile with ds_read_b64_tr_b16. O^T keeps lane = head,
+//    so a softmax rescale is one multiplier per lane.
+//  * Lazy rescaling: the running max m only moves when a tile's max exceeds it
+//    by more than 2^8 in log2 units; p <= 256 stays exact enough in fp32 and
+//    bf16, and (m, l, acc) stay consistent.
+//  * LDS rows are XOR-swizzled in 16-byte chunks so that the QK reads (16 rows
+//    x 1 chunk per 16 lanes) and the transposed PV reads (4 rows x 2 chunks per
+//    16 lanes) are free of bank conflicts.
+
 #include "internal.h"
 
 namespace mlra {
+namespace {
 
-bool decode_mfma_supported(const Geom&) { return false; }
-int decode_mfma_items_per_cu(const Geom&) { return 1; }
-hipError_t launch_decode_mfma(const Geom&, const void*, const void*, const void*,
-                              const Workspace&, int, hipStream_t) {
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kT = 32;   // tokens per tile
+constexpr int kDR = 64;  // RoPE width
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescale = 8.f;  // log2 headroom before the running max moves
+
+struct Params {
+  const __bf16* q_abs;
+  const __bf16* ckv;
+  const __bf16* krope;
+  int64_t ckv_bs, ckv_ts, kr_bs, kr_ts;
+  const PlanHeader* hdr;
+  const int32_t* prefix;
+  float* m;
+  float* l;
+  float* acc;
+  int B;
+};
+
+// s_waitcnt vmcnt(N), leaving lgkmcnt/expcnt alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Latent-row swizzle: bijective on t mod 16 (QK reads of 16 rows) and, for the
+// four rows 4a..4a+3, spreads rows over chunk bits 1-2 (transposed PV reads).
+__device__ __forceinline__ int swz(int t) {
+  return ((t & 3) << 1) | ((t >> 2) & 1) | (((t >> 3) & 1) << 3);
+}
+// RoPE-row swizzle (128-byte rows): 16 rows of one chunk hit distinct banks.
+__device__ __forceinline__ int swz_r(int t) { return (t >> 1) & 7; }
+
+__device__ __forceinline__ int find_seq(const int32_t* prefix, int B, int pos) {
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= pos) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+template <int DC, int NB, int NW>
+struct Cfg {
+  static constexpr int CPR = DC / 8;             // 16-byte chunks per latent row
+  static constexpr int RPI = 64 / CPR;           // latent rows per 1 KB DMA instruction
+  static constexpr int NL = kT / RPI;            // latent DMA instructions per tile
+  static constexpr int NR = kT * kDR * 2 / 1024; // rope DMA instructions per tile
+  static constexpr int NI = NL + NR;
+  static constexpr int PER_HI = (NI + NW - 1) / NW;  // per wave (waves < NI % NW)
+  static constexpr int PER_LO = NI / NW;             // per wave (the others)
+  static constexpr int LAT_BYTES = kT * DC * 2;
+  static constexpr int STAGE = LAT_BYTES + kT * kDR * 2;
+  static constexpr int KS = DC / 32;             // latent k-steps (K = 32)
+  static constexpr int KPB = KS / NB;            // latent k-steps per branch
+  static constexpr int MB = DC / 16;             // PV output row blocks
+  static constexpr int MPB = MB / NB;            // PV row blocks per branch
+  static constexpr int HWG = 16 * NW;            // heads per workgroup
+  static_assert(CPR >= 16 && 64 % CPR == 0, "latent width must be 128, 256 or 512");
+  static_assert(KPB >= 1 && MPB >= 1, "branch slice must be >= 32 columns");
+};
+
+template <int DC, int NB, int NW>
+__device__ __forceinline__ void issue_tile(char LDS_AS* stage, const __bf16* cseq,
+                                           const __bf16* kseq, int64_t cts, int64_t kts,
+                                           int tstart, int tend, int wave, int lane) {
+  using C = Cfg<DC, NB, NW>;
+#pragma unroll
+  for (int u = 0; u < C::PER_HI; ++u) {
+    const int q = wave + NW * u;
+    if (q < C::NL) {
+      const int t = q * C::RPI + lane / C::CPR;
+      const int lc = (lane % C::CPR) ^ swz(t);
+      const int row = min(tstart + t, tend - 1);
+      const __bf16* src = cseq + (int64_t)row * cts + lc * 8;
+      __builtin_amdgcn_global_load_lds((const void*)src, (void LDS_AS*)(stage + q * 1024), 16, 0,
+                                       0);
+    } else if (q < C::NI) {
+      const int r = q - C::NL;
+      const int t = r * 8 + lane / 8;
+      const int lc = (lane % 8) ^ swz_r(t);
+      const int row = min(tstart + t, tend - 1);
+      const __bf16* src = kseq + (int64_t)row * kts + lc * 8;
+      __builtin_amdgcn_global_load_lds((const void*)src,
+                                       (void LDS_AS*)(stage + C::LAT_BYTES + r * 1024), 16, 0, 0);
+    }
+  }
+}
+
+// Wait until at most `ahead` tiles of this wave's DMA are still in flight.
+template <int PER, int NS>
+__device__ __forceinline__ void wait_tiles_per(int ahead) {
+  if constexpr (NS >= 4) {
+    if (ahead >= 2) { wait_vm<2 * PER>(); return; }
+  }
+  if constexpr (NS >= 3) {
+    if (ahead >= 1) { wait_vm<PER>(); return; }
+  }
+  wait_vm<0>();
+}
+template <int DC, int NB, int NW, int NS>
+__device__ __forceinline__ void wait_tiles(int ahead, int wave) {
+  using C = Cfg<DC, NB, NW>;
+  if constexpr (C::PER_HI == C::PER_LO) {
+    wait_tiles_per<C::PER_HI, NS>(ahead);
+  } else {
+    if (wave < C::NI % NW) wait_tiles_per<C::PER_HI, NS>(ahead);
+    else wait_tiles_per<C::PER_LO, NS>(ahead);
+  }
+}
+
+template <int DC, int NB, int NW, int NS, int HSPLIT>
+__global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(Params p) {
+  using C = Cfg<DC, NB, NW>;
+  constexpr int H = C::HWG * HSPLIT;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[NS * C::STAGE];
+  char LDS_AS* smem = (char LDS_AS*)smem_raw;
+
+  // workgroup -> (item, head group); the head groups of one item share an XCD
+  int k, hg;
+  if constexpr (HSPLIT == 1) {
+    k = blockIdx.x;
+    hg = 0;
+  } else {
+    const int i = blockIdx.x, x = i & 7, j = i >> 3;
+    k = (j / HSPLIT) * 8 + x;
+    hg = j % HSPLIT;
+  }
+  const PlanHeader hd = *p.hdr;
+  if (k >= hd.n_items) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, kg = lane >> 4;
+  const int head = hg * C::HWG + wave * 16 + l16;
+
+  // lane constants for the LDS reads (see the swizzle notes)
+  const int qk_x = kg ^ swz(l16);                    // QK latent: chunk 4ks+kg
+  const int rp_x = swz_r(l16);                       // QK rope
+  const int pv_r = l16 >> 2, pv_q = l16 & 3;         // PV: row r of 4, column quad q
+  const int pv_y = (pv_q >> 1) ^ (2 * pv_r + (kg & 1) + 8 * (kg >> 1));
+  const int pv_row_lo = (4 * kg + pv_r) * DC * 2 + 8 * (pv_q & 1);
+  const int pv_row_hi = pv_row_lo + 16 * DC * 2;
+
+  int start = k * hd.chunk;
+  const int end = min(start + hd.chunk, hd.total);
+  int b = find_seq(p.prefix, p.B, start);
+
+  while (start < end) {
+    while (p.prefix[b + 1] <= start) ++b;
+    const int seg_end = min(end, p.prefix[b + 1]);
+    const int t0 = start - p.prefix[b], t1 = seg_end - p.prefix[b];
+    const int ntiles = (t1 - t0 + kT - 1) / kT;
+    const __bf16* cseq = p.ckv + (int64_t)b * p.ckv_bs;
+    const __bf16* kseq = p.krope + (int64_t)b * p.kr_bs;
+
+    // earlier stores and loads of this wave done; all waves left the
+    // previous segment's LDS tiles
+    wait_vm<0>();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+
+    // Q^T as the B operand: lane (head, kg) holds q[head][32 ks + 8 kg .. +8]
+    bf16x8 q[C::KS + 2];
+    {
+      const __bf16* qrow = p.q_abs + ((int64_t)b * H + head) * (DC + kDR) + 8 * kg;
+#pragma unroll
+      for (int ks = 0; ks < C::KS + 2; ++ks) q[ks] = *(const bf16x8*)(qrow + 32 * ks);
+    }
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < ntiles)
+        issue_tile<DC, NB, NW>(smem + s * C::STAGE, cseq, kseq, p.ckv_ts, p.kr_ts, t0 + s * kT,
+                               t1, wave, lane);
+
+    f32x4 o[C::MB];
+#pragma unroll
+    for (int i = 0; i < C::MB; ++i) o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    float m_run[NB], l_run[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) { m_run[j] = -INFINITY; l_run[j] = 0.f; }
+
+    for (int it = 0; it < ntiles; ++it) {
+      const int ahead = min(NS - 2, ntiles - 1 - it);
+      wait_tiles<DC, NB, NW, NS>(ahead, wave);
+      __builtin_amdgcn_s_barrier();
+      if (it + NS - 1 < ntiles)
+        issue_tile<DC, NB, NW>(smem + ((it + NS - 1) % NS) * C::STAGE, cseq, kseq, p.ckv_ts,
+                               p.kr_ts, t0 + (it + NS - 1) * kT, t1, wave, lane);
+      const char LDS_AS* st = smem + (it % NS) * C::STAGE;
+      const int valid = min(kT, t1 - (t0 + it * kT));
+
+      // RoPE part of the scores, shared by every branch: two 16-token blocks
+      f32x4 R[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        R[mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        const char LDS_AS* rrow = st + C::LAT_BYTES + (16 * mb + l16) * kDR * 2;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 a = *(const bf16x8 LDS_AS*)(rrow + 16 * ((4 * ks + kg) ^ rp_x));
+          R[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, q[C::KS + ks], R[mb], 0, 0, 0);
+        }
+      }
+
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        f32x4 S[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          S[mb] = R[mb];
+          const char LDS_AS* crow = st + (16 * mb + l16) * DC * 2;
+#pragma unroll
+          for (int ks = j * C::KPB; ks < (j + 1) * C::KPB; ++ks) {
+            const bf16x8 a =
+                *(const bf16x8 LDS_AS*)(crow + 256 * (ks >> 2) + 16 * ((4 * (ks & 3)) ^ qk_x));
+            S[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, q[ks], S[mb], 0, 0, 0);
+          }
+        }
+        if (valid < kT) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (16 * mb + 4 * kg + e >= valid) S[mb][e] = -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
+                         fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mt = mx * kLog2e;
+        const bool need = mt > m_run[j] + kRescale;
+        if (__any(need)) {
+          const float mn = need ? mt : m_run[j];
+          const float f = need ? __builtin_amdgcn_exp2f(m_run[j] - mn) : 1.f;
+          l_run[j] *= f;
+#pragma unroll
+          for (int mb = j * C::MPB; mb < (j + 1) * C::MPB; ++mb) o[mb] *= f;
+          m_run[j] = mn;
+        }
+        bf16x8 P;
+        float ps = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pe =
+                __builtin_amdgcn_exp2f(__builtin_fmaf(S[mb][e], kLog2e, -m_run[j]));
+            ps += pe;
+            P[4 * mb + e] = (__bf16)pe;
+          }
+        l_run[j] += ps;
+#pragma unroll
+        for (int mb = j * C::MPB; mb < (j + 1) * C::MPB; ++mb) {
+          const int coff = 256 * (mb >> 3) + 16 * ((2 * (mb & 7)) ^ pv_y);
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (i16x4 LDS_AS*)(st + pv_row_lo + coff));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (i16x4 LDS_AS*)(st + pv_row_hi + coff));
+          const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), P, o[mb],
+                                                          0, 0, 0);
+        }
+      }
+    }
+
+    // partial state of this segment (slot-uniform base, compile-time offsets)
+    const int slot = k + b;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      float lt = l_run[j] + __shfl_xor(l_run[j], 16);
+      lt += __shfl_xor(lt, 32);
+      if (kg == 0) {
+        p.m[((int64_t)slot * NB + j) * H + head] = m_run[j];
+        p.l[((int64_t)slot * NB + j) * H + head] = lt;
+      }
+    }
+    float* accs = p.acc + (int64_t)slot * DC * H;
+    const int lane_off = 4 * kg * H + head;
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) accs[(16 * mb + e) * H + lane_off] = o[mb][e];
+    start = seg_end;
+    ++b;
+  }
+}
+
+template <int DC, int NB, int NW, int HSPLIT>
+hipError_t launch_t(const Geom& g, const void* q_abs, const void* ckv, const void* krope,
+                    const Workspace& ws, int items, hipStream_t s) {
+  using C = Cfg<DC, NB, NW>;
+  // as many stages as LDS holds (<= 4) and the 6-bit vmcnt can track
+  constexpr int NS_LDS = (160 * 1024) / C::STAGE;
+  constexpr int NS_VM = 2 * C::PER_HI < 64 ? 4 : 3;
+  constexpr int NS = NS_LDS < NS_VM ? NS_LDS : NS_VM;
+  static_assert(NS >= 2, "tile does not fit LDS");
+  Params p;
+  p.q_abs = (const __bf16*)q_abs;
+  p.ckv = (const __bf16*)ckv;
+  p.krope = (const __bf16*)krope;
+  p.ckv_bs = g.ckv_bs;
+  p.ckv_ts = g.ckv_ts;
+  p.kr_bs = g.kr_bs;
+  p.kr_ts = g.kr_ts;
+  p.hdr = ws.hdr;
+  p.prefix = ws.prefix;
+  p.m = ws.m;
+  p.l = ws.l;
+  p.acc = ws.acc;
+  p.B = g.B;
+  int grid = items;
+  if (HSPLIT > 1) grid = ((items + 7) / 8) * 8 * HSPLIT;  // whole XCD rounds
+  hipLaunchKernelGGL((decode_mfma_kernel<DC, NB, NW, NS, HSPLIT>), dim3(grid), dim3(64 * NW), 0,
+                     s, p);
+  return hipGetLastError();
+}
+
+// heads -> (waves per workgroup, head groups per item)
+template <int DC, int NB>
+hipError_t launch_h(const Geom& g, const void* q, const void* c, const void* k,
+                    const Workspace& ws, int items, hipStream_t s) {
+  switch (g.H) {
+    case 32: return launch_t<DC, NB, 2, 1>(g, q, c, k, ws, items, s);
+    case 64: return launch_t<DC, NB, 4, 1>(g, q, c, k, ws, items, s);
+    case 128: return launch_t<DC, NB, 4, 2>(g, q, c, k, ws, items, s);
+  }
+  return hipErrorNotSupported;
+}
+
+template <int DC>
+hipError_t launch_nb(const Geom& g, const void* q, const void* c, const void* k,
+                     const Workspace& ws, int items, hipStream_t s) {
+  switch (g.n) {
+    case 1: return launch_h<DC, 1>(g, q, c, k, ws, items, s);
+    case 2: return launch_h<DC, 2>(g, q, c, k, ws, items, s);
+    case 4: return launch_h<DC, 4>(g, q, c, k, ws, items, s);
+  }
+  return hipErrorNotSupported;
+}
+
+}  // namespace
+
+bool decode_mfma_supported(const Geom& g) {
+  if (g.dr != kDR) return false;
+  if (g.H != 32 && g.H != 64 && g.H != 128) return false;
+  if (g.dc != 128 && g.dc != 256 && g.dc != 512) return false;
+  if (g.n != 1 && g.n != 2 && g.n != 4) return false;
+  if (g.dc / g.n < 32) return false;
+  return true;
+}
+
+// Workgroups per work item (head groups); one workgroup runs per CU.
+int decode_mfma_wgs_per_item(const Geom& g) { return g.H == 128 ? 2 : 1; }
+
+hipError_t launch_decode_mfma(const Geom& g, const void* q_abs, const void* ckv,
+                              const void* krope, const Workspace& ws, int items,
+                              hipStream_t s) {
+  switch (g.dc) {
+    case 128: return launch_nb<128>(g, q_abs, ckv, krope, ws, items, s);
+    case 256: return launch_nb<256>(g, q_abs, ckv, krope, ws, items, s);
+    case 512: return launch_nb<512>(g, q_abs, ckv, krope, ws, items, s);
+  }
   return hipErrorNotSupported;
 }
 

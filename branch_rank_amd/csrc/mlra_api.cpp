@@ -250,7 +250,7 @@ mlra_status_t run_decode(const mlra_config_t* c, const Geom& g, int cus, const v
     return fail(MLRA_ERR_UNSUPPORTED, "MLRA_DECODE_PATH=mfma but no MFMA kernel for this shape");
   int target;
   if (fast) {
-    target = cus * decode_mfma_items_per_cu(g);
+    target = cus / decode_mfma_wgs_per_item(g);
   } else {
     target = cus * 4 / g.H;
     if (target < 1) target = 1;
