@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of latent-KV attention (MLA / MLRA-n) on one MI355X.
+
+One step = one full `mlra_decode` call (absorb_q -> plan -> split-KV decode ->
+combine -> out_proj) for one layer over a batch of sequences whose caches are
+already resident in HBM. The default workload is MLRA-4 at the DeepSeek-V3
+attention shape, B=16, L=32768 (bf16 cache). Cache copies rotate between
+steps so that no step is served from the 256 MB Infinity Cache.
+
+Prints ONE JSON line: tokens/s (value), KV-cache GB/s, the roofline of the
+split-KV decode kernel (timed live with HIP events recorded around that
+kernel on its stream) and the float64 oracle timed on the host cores.
+
+  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload NAME]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attn tokens/s and KV-cache GB/s (% HBM peak) at B=16, L=32K, 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "latent_decode_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "branch_rank_amd", "csrc", "decode_mfma.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mlra4_b16_l32k")
+    ap.add_argument("--also", default="mla_b16_l32k",
+                    help="comma-separated extra workloads reported beside (empty: none)")
+    ap.add_argument("--cache-bytes-min", type=float, default=2.0,
+                    help="GiB of rotating cache copies (>= 8x the Infinity Cache)")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe-copy", action="store_true",
+                    help="only run a 1 GiB device copy (scale factor for HBM counters)")
+    return ap.parse_args()
+
+
+def kernel_flops_bytes(w, lens):
+    """Algorithmic work of the split-KV decode kernel: every cached element is
+    read once (the branches share the RoPE key and partition the latent), and
+    per token each head does 2*(d_c + d_r) flop for the scores and 2*d_c for
+    the value accumulation."""
+    tokens = int(sum(int(x) for x in lens))
+    row = w.d_c + w.d_r
+    esz = 2 if w.dtype == "bf16" else 4
+    return tokens * row * esz, tokens * w.heads * 2 * (row + w.d_c), tokens
+
+
+def traffic_for(workload):
+    """HBM bytes per decode launch from the committed counter summary, if it
+    was taken on the current kernel source and this workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        if t.get("kernel_sha256") != sha or t.get("workload") != workload:
+            return None
+        return int(t["hbm_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def run_workload(name, steps, warmup, cache_gib, torch, br, synth):
+    w = synth.WORKLOADS[name]
+    inp = synth.make_inputs(w, parts=("q_nope", "q_rope", "w_uk", "w_uv"))
+    lens = inp["lens"]
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = {k: torch.from_numpy(inp[k]).cuda().to(dt) for k in ("q_nope", "q_rope", "w_uk", "w_uv")}
+    kv_bytes, flops, tokens = kernel_flops_bytes(w, lens)
+    copies = max(2, min(16, math.ceil(cache_gib * 2**30 / max(kv_bytes, 1))))
+    log(f"[bench] {name}: B={w.batch} tokens={tokens} cache={kv_bytes / 1e6:.1f} MB x {copies} copies")
+    lens_dev = torch.from_numpy(lens).cuda()
+    cfg = br.make_config(w.heads, w.d_c, w.d_r, w.d_n, w.d_v, n=w.n, sm_scale=w.tau,
+                         alpha_q=w.alpha_q, alpha_kv=w.alpha_kv, theta=w.theta, dtype=w.dtype)
+    views, bufs = [], []
+    for i in range(copies):
+        buf, _ = synth.make_cache_device(w, seed=w.seed + 7919 * (i + 1), lens=lens)
+        bufs.append(buf)
+        views.append(br.cache_view(buf[..., :w.d_c], buf[..., w.d_c:], lens_dev, cfg))
+    ws = br.alloc_workspace(cfg, w.batch, bufs[0].shape[1])
+    out = torch.empty(w.batch, w.heads, w.d_v, dtype=torch.float32, device="cuda")
+
+    def step(i):
+        br.mlra_decode(cfg, w.n, dev["q_nope"], dev["q_rope"], dev["w_uk"], dev["w_uv"],
+                       views[i % copies], ws, out)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g0.record()
+    for i in range(steps):
+        br.set_kernel_timing(*kev[i])
+        step(i)
+    g1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    br.set_kernel_timing(None, None)
+    ms_step = (t1 - t0) * 1e3 / steps
+    gpu_ms_step = g0.elapsed_time(g1) / steps
+    k_ms = sum(a.elapsed_time(b) for a, b in kev) / steps
+    assert torch.isfinite(out).all().item(), "non-finite output"
+    del bufs, views
+    return dict(w=w, lens=lens, kv_bytes=kv_bytes, flops=flops, tokens=tokens, copies=copies,
+                ms_step=ms_step, gpu_ms_step=gpu_ms_step, kernel_ms=k_ms)
+
+
+def cpu_baseline(w, seconds):
+    """The float64 oracle (unabsorbed definition) on host cores, one sequence
+    at a time of the same workload recipe until `seconds` have elapsed."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max((d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"), default=1)
+    except Exception:  # noqa: BLE001
+        cores = len(os.sched_getaffinity(0))
+    done, spent = 0, 0.0
+    L = None
+    while spent < seconds and done < w.batch:
+        one = w.replace(batch=1)
+        inp = synth.make_inputs(one, seed=w.seed + 104729 * (done + 1))
+        L = int(inp["lens"][0])
+        t0 = time.perf_counter()
+        oracle.mlra_decode_ref(inp["q_nope"], inp["q_rope"], inp["w_uk"], inp["w_uv"], inp["ckv"],
+                               inp["krope"], inp["lens"], w.n, tau=w.tau, alpha_q=w.alpha_q,
+                               alpha_kv=w.alpha_kv, theta=w.theta)
+        spent += time.perf_counter() - t0
+        done += 1
+        log(f"[bench] oracle: {done} sequence(s) in {spent:.1f} s")
+    return {"value": done / spent, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {w.batch} sequences (L={L}, all {w.heads} heads, {w.n} branch(es)), "
+                      f"float64 unabsorbed oracle, {spent:.1f} s"}
+
+
+def probe_copy(torch):
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "copy", "bytes_read": n, "bytes_written": n, "launches": 3}))
+
+
+def main():
+    a = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {a.gpus}, WORLD_SIZE {world}); "
+              "this decode path has no multi-GPU leg.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import branch_rank_amd as br
+    import synth
+    br.lib()  # fails loudly when the HIP library is missing
+    if a.probe_copy:
+        probe_copy(torch)
+        return
+    main_r = run_workload(a.workload, a.steps, a.warmup, a.cache_bytes_min, torch, br, synth)
+    extras = {}
+    for name in [x for x in a.also.split(",") if x and x != a.workload]:
+        r = run_workload(name, a.steps, a.warmup, a.cache_bytes_min, torch, br, synth)
+        extras[name] = {
+            "tokens_per_s": r["w"].batch / (r["ms_step"] / 1e3),
+            "ms_per_step": r["ms_step"],
+            "decode_kernel_us": r["kernel_ms"] * 1e3,
+            "kv_cache_gbs_kernel": r["kv_bytes"] / (r["kernel_ms"] / 1e3) / 1e9,
+            "kv_cache_gbs_step": r["kv_bytes"] / (r["ms_step"] / 1e3) / 1e9,
+        }
+    w = main_r["w"]
+    ms = main_r["ms_step"]
+    k_s = main_r["kernel_ms"] / 1e3
+    kv_gbs_kernel = main_r["kv_bytes"] / k_s / 1e9
+    kv_gbs_step = main_r["kv_bytes"] / (ms / 1e3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": w.batch / (ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; unit-RMS bf16 latent rows, N(0,1) K_RoPE, random-init W_UK/W_UV)",
+        "config": {"workload": w.name, "batch": w.batch, "cache_len": w.cache_len,
+                   "heads": w.heads, "d_c": w.d_c, "d_r": w.d_r, "d_nope": w.d_n, "d_v": w.d_v,
+                   "branches": w.n, "alpha_q": round(w.alpha_q, 6),
+                   "alpha_kv": round(w.alpha_kv, 6), "cache_copies": main_r["copies"],
+                   "parallelism": "none (1 GPU)"},
+        "kv_cache_gbs": kv_gbs_step,
+        "kv_cache_frac_hbm_peak": kv_gbs_step / HBM_PEAK_GBS,
+        "gpu_ms_per_step": main_r["gpu_ms_step"],
+        "decode_kernel_us": main_r["kernel_ms"] * 1e3,
+        "decode_kernel_kv_gbs": kv_gbs_kernel,
+        "decode_kernel_mfma_tflops": main_r["flops"] / k_s / 1e12,
+        "decode_kernel_mfma_frac": main_r["flops"] / k_s / 1e12 / BF16_PEAK_TFLOPS,
+        "roofline": {"bound": "hbm", "achieved": kv_gbs_kernel, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": kv_gbs_kernel / HBM_PEAK_GBS,
+                     "traffic": traffic_for(w.name)},
+        "also": extras,
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -9,6 +9,7 @@ from .inputs import (  # noqa: F401
     Workload,
     WORKLOADS,
     make_inputs,
+    make_cache_device,
     round_bf16,
     bf16_bits,
     ragged_lens,

@@ -160,3 +160,36 @@ def make_inputs(w: Workload, seed: Optional[int] = None, lens=None, max_len=None
     if "w_uv" in parts:
         out["w_uv"] = rnd(g[6].standard_normal((H, w.d_c, w.d_v), dtype=np.float32) * np.float32(w_std))
     return out
+
+
+def make_cache_device(w: Workload, seed: int, lens=None, device="cuda"):
+    """The cache of workload ``w`` drawn on the device with torch (same recipe
+    as ``make_inputs``: unit-RMS latent rows, N(0,1) K_RoPE rows, rounded to
+    the workload dtype), as one interleaved buffer [B, L_max, d_c + d_r].
+
+    For benchmark copies of large caches, where drawing on the host would
+    take longer than the measurement. Values differ from ``make_inputs``
+    (another generator); the distribution is the same.
+    """
+    import torch
+
+    B = w.batch
+    if lens is None:
+        lens = make_inputs(w, seed=seed, parts=())["lens"]
+    Lmax = int(max(int(np.max(lens)) if len(lens) else 0, 1))
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    buf = torch.empty(B, Lmax, w.d_c + w.d_r, dtype=dt, device=device)
+    for b in range(B):  # one sequence at a time keeps the fp32 scratch small
+        c = torch.randn(Lmax, w.d_c, generator=g, device=device, dtype=torch.float32)
+        if w.init == "fan_in":
+            c *= 1.0 / math.sqrt(w.d_c)
+        else:
+            c /= torch.sqrt(torch.mean(c * c, dim=-1, keepdim=True) + 1e-6)
+        buf[b, :, :w.d_c] = c.to(dt)
+        k = torch.randn(Lmax, w.d_r, generator=g, device=device, dtype=torch.float32)
+        if w.init == "fan_in":
+            k *= 1.0 / math.sqrt(w.d_r)
+        buf[b, :, w.d_c:] = k.to(dt)
+    return buf, np.asarray(lens, np.int32)
