@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmlra.so")
 
-SOURCES = ["mlra_api.cpp", "kernels_generic.hip", "decode_mfma.hip"]
+SOURCES = ["mlra_api.cpp", "kernels_generic.hip", "decode_mfma.hip", "proj_mfma.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -53,7 +53,8 @@ struct Params {
   const __bf16* q_abs;
   const __bf16* ckv;
   const __bf16* krope;
-  int64_t ckv_bs, ckv_ts, kr_bs, kr_ts;
+  int64_t ckv_bs, kr_bs;
+  int ckv_ts, kr_ts;  // token strides in elements (host checks the byte ranges fit 31 bits)
   const PlanHeader* hdr;
   const int32_t* prefix;
   float* m;
@@ -107,11 +108,38 @@ struct Cfg {
   static_assert(KPB >= 1 && MPB >= 1, "branch slice must be >= 32 columns");
 };
 
+// Raw buffer descriptor (gfx9 layout: base, stride 0, byte range, word 3)
+// over one sequence's rows [0, rows).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 seq_rsrc(const __bf16* base, int rows, int ts) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;  // wave-uniform values, made explicit for the SGPR operands
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
+  r.z = __builtin_amdgcn_readfirstlane(rows * ts * 2);
+  r.w = 0x00020000;
+  return r;
+}
+
+// One LDS-DMA instruction: 16 bytes per lane from rsrc + voff into LDS at
+// lds_base + 16 * lane. Issued from asm so that the compiler does not add
+// its own (conservative) vmcnt waits before later LDS reads; every wait for
+// this data is placed by hand (wait_tiles). No output registers.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_base, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+
 template <int DC, int NB, int NW>
-__device__ __forceinline__ void issue_tile(char LDS_AS* stage, const __bf16* cseq,
-                                           const __bf16* kseq, int64_t cts, int64_t kts,
-                                           int tstart, int tend, int wave, int lane) {
+__device__ __forceinline__ void issue_tile(char LDS_AS* stage, i32x4 crs, i32x4 krs, int cts,
+                                           int kts, int tstart, int tend, int wave, int lane) {
   using C = Cfg<DC, NB, NW>;
+  const uint32_t sbase = (uint32_t)(uintptr_t)stage;
 #pragma unroll
   for (int u = 0; u < C::PER_HI; ++u) {
     const int q = wave + NW * u;
@@ -119,17 +147,13 @@ __device__ __forceinline__ void issue_tile(char LDS_AS* stage, const __bf16* cse
       const int t = q * C::RPI + lane / C::CPR;
       const int lc = (lane % C::CPR) ^ swz(t);
       const int row = min(tstart + t, tend - 1);
-      const __bf16* src = cseq + (int64_t)row * cts + lc * 8;
-      __builtin_amdgcn_global_load_lds((const void*)src, (void LDS_AS*)(stage + q * 1024), 16, 0,
-                                       0);
+      dma16(crs, sbase + q * 1024, row * cts * 2 + lc * 16);
     } else if (q < C::NI) {
       const int r = q - C::NL;
       const int t = r * 8 + lane / 8;
       const int lc = (lane % 8) ^ swz_r(t);
       const int row = min(tstart + t, tend - 1);
-      const __bf16* src = kseq + (int64_t)row * kts + lc * 8;
-      __builtin_amdgcn_global_load_lds((const void*)src,
-                                       (void LDS_AS*)(stage + C::LAT_BYTES + r * 1024), 16, 0, 0);
+      dma16(krs, sbase + C::LAT_BYTES + r * 1024, row * kts * 2 + lc * 16);
     }
   }
 }
@@ -156,10 +180,29 @@ __device__ __forceinline__ void wait_tiles(int ahead, int wave) {
   }
 }
 
+// Static schedule of one tile for one wave: group 0 is the RoPE part of the
+// scores; then, per branch, QG groups of QK MFMAs (the last one followed by
+// the branch softmax) and PG groups of PV MFMAs. Each group uses at most 8
+// A-fragments read from LDS; the fragments of group g+1 are read while group
+// g computes.
+template <int DC, int NB>
+struct Sched {
+  static constexpr int KS = DC / 32, KPB = KS / NB, MB = DC / 16, MPB = MB / NB;
+  static constexpr int QG = (KPB + 3) / 4;   // QK groups per branch
+  static constexpr int QGK = KPB / QG;       // k-steps per QK group (2 M blocks each)
+  static constexpr int PG = (MPB + 7) / 8;   // PV groups per branch
+  static constexpr int PGM = MPB / PG;       // output blocks per PV group
+  static constexpr int GPB = QG + PG;
+  static constexpr int NG = 1 + NB * GPB;
+  static_assert(QG * QGK == KPB && PG * PGM == MPB && 2 * QGK <= 8 && PGM <= 8, "schedule");
+};
+
 template <int DC, int NB, int NW, int NS, int HSPLIT>
 __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(Params p) {
   using C = Cfg<DC, NB, NW>;
+  using SC = Sched<DC, NB>;
   constexpr int H = C::HWG * HSPLIT;
+  static_assert(NW * 16 * (DC + 4) * 4 <= NS * C::STAGE, "epilogue transpose must fit the stages");
   __shared__ __attribute__((aligned(1024))) char smem_raw[NS * C::STAGE];
   char LDS_AS* smem = (char LDS_AS*)smem_raw;
 
@@ -196,8 +239,8 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(Params p) {
     const int seg_end = min(end, p.prefix[b + 1]);
     const int t0 = start - p.prefix[b], t1 = seg_end - p.prefix[b];
     const int ntiles = (t1 - t0 + kT - 1) / kT;
-    const __bf16* cseq = p.ckv + (int64_t)b * p.ckv_bs;
-    const __bf16* kseq = p.krope + (int64_t)b * p.kr_bs;
+    const i32x4 crs = seq_rsrc(p.ckv + (int64_t)b * p.ckv_bs, t1, p.ckv_ts);
+    const i32x4 krs = seq_rsrc(p.krope + (int64_t)b * p.kr_bs, t1, p.kr_ts);
 
     // earlier stores and loads of this wave done; all waves left the
     // previous segment's LDS tiles
@@ -212,10 +255,13 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(Params p) {
 #pragma unroll
       for (int ks = 0; ks < C::KS + 2; ++ks) q[ks] = *(const bf16x8*)(qrow + 32 * ks);
     }
+    // Q complete before any DMA is in flight: the compiler then needs no vmcnt
+    // wait for Q inside the tile loop (such a wait would also drain the DMA)
+    wait_vm<0>();
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
       if (s < ntiles)
-        issue_tile<DC, NB, NW>(smem + s * C::STAGE, cseq, kseq, p.ckv_ts, p.kr_ts, t0 + s * kT,
+        issue_tile<DC, NB, NW>(smem + s * C::STAGE, crs, krs, p.ckv_ts, p.kr_ts, t0 + s * kT,
                                t1, wave, lane);
 
     f32x4 o[C::MB];
@@ -229,87 +275,132 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(Params p) {
       const int ahead = min(NS - 2, ntiles - 1 - it);
       wait_tiles<DC, NB, NW, NS>(ahead, wave);
       __builtin_amdgcn_s_barrier();
-      if (it + NS - 1 < ntiles)
-        issue_tile<DC, NB, NW>(smem + ((it + NS - 1) % NS) * C::STAGE, cseq, kseq, p.ckv_ts,
-                               p.kr_ts, t0 + (it + NS - 1) * kT, t1, wave, lane);
       const char LDS_AS* st = smem + (it % NS) * C::STAGE;
       const int valid = min(kT, t1 - (t0 + it * kT));
 
-      // RoPE part of the scores, shared by every branch: two 16-token blocks
-      f32x4 R[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        R[mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        const char LDS_AS* rrow = st + C::LAT_BYTES + (16 * mb + l16) * kDR * 2;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 a = *(const bf16x8 LDS_AS*)(rrow + 16 * ((4 * ks + kg) ^ rp_x));
-          R[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, q[C::KS + ks], R[mb], 0, 0, 0);
-        }
-      }
-
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        f32x4 S[2];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          S[mb] = R[mb];
-          const char LDS_AS* crow = st + (16 * mb + l16) * DC * 2;
-#pragma unroll
-          for (int ks = j * C::KPB; ks < (j + 1) * C::KPB; ++ks) {
-            const bf16x8 a =
-                *(const bf16x8 LDS_AS*)(crow + 256 * (ks >> 2) + 16 * ((4 * (ks & 3)) ^ qk_x));
-            S[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, q[ks], S[mb], 0, 0, 0);
-          }
-        }
-        if (valid < kT) {
+      // ---- fragment loads of one group into F[0..7]
+      auto load = [&](int gid, bf16x8* F) {
+        if (gid == 0) {
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (16 * mb + 4 * kg + e >= valid) S[mb][e] = -INFINITY;
+            for (int ks = 0; ks < 2; ++ks)
+              F[2 * mb + ks] = *(const bf16x8 LDS_AS*)(st + C::LAT_BYTES +
+                                                       (16 * mb + l16) * kDR * 2 +
+                                                       16 * ((4 * ks + kg) ^ rp_x));
+          return;
         }
-        float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
-                         fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mt = mx * kLog2e;
-        const bool need = mt > m_run[j] + kRescale;
-        if (__any(need)) {
-          const float mn = need ? mt : m_run[j];
-          const float f = need ? __builtin_amdgcn_exp2f(m_run[j] - mn) : 1.f;
-          l_run[j] *= f;
+        const int g = gid - 1, j = g / SC::GPB, r = g % SC::GPB;
+        if (r < SC::QG) {
 #pragma unroll
-          for (int mb = j * C::MPB; mb < (j + 1) * C::MPB; ++mb) o[mb] *= f;
-          m_run[j] = mn;
-        }
-        bf16x8 P;
-        float ps = 0.f;
+          for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+            for (int kk = 0; kk < SC::QGK; ++kk) {
+              const int ks = j * SC::KPB + r * SC::QGK + kk;
+              F[mb * SC::QGK + kk] = *(const bf16x8 LDS_AS*)(st + (16 * mb + l16) * DC * 2 +
+                                                            256 * (ks >> 2) +
+                                                            16 * ((4 * (ks & 3)) ^ qk_x));
+            }
+        } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float pe =
-                __builtin_amdgcn_exp2f(__builtin_fmaf(S[mb][e], kLog2e, -m_run[j]));
-            ps += pe;
-            P[4 * mb + e] = (__bf16)pe;
+          for (int i = 0; i < SC::PGM; ++i) {
+            const int mb = j * SC::MPB + (r - SC::QG) * SC::PGM + i;
+            const int coff = 256 * (mb >> 3) + 16 * ((2 * (mb & 7)) ^ pv_y);
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (i16x4 LDS_AS*)(st + pv_row_lo + coff));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (i16x4 LDS_AS*)(st + pv_row_hi + coff));
+            const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            F[i] = __builtin_bit_cast(bf16x8, v);
           }
-        l_run[j] += ps;
-#pragma unroll
-        for (int mb = j * C::MPB; mb < (j + 1) * C::MPB; ++mb) {
-          const int coff = 256 * (mb >> 3) + 16 * ((2 * (mb & 7)) ^ pv_y);
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (i16x4 LDS_AS*)(st + pv_row_lo + coff));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (i16x4 LDS_AS*)(st + pv_row_hi + coff));
-          const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), P, o[mb],
-                                                          0, 0, 0);
         }
+      };
+
+      f32x4 R[2], S[2];
+      bf16x8 P;
+      // ---- MFMAs of one group (and the branch softmax after its last QK group)
+      auto compute = [&](int gid, const bf16x8* F) {
+        if (gid == 0) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            R[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(F[2 * mb], q[C::KS], (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            R[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(F[2 * mb + 1], q[C::KS + 1], R[mb], 0, 0, 0);
+          }
+          return;
+        }
+        const int g = gid - 1, j = g / SC::GPB, r = g % SC::GPB;
+        if (r < SC::QG) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            if (r == 0) S[mb] = R[mb];
+#pragma unroll
+            for (int kk = 0; kk < SC::QGK; ++kk) {
+              const int ks = j * SC::KPB + r * SC::QGK + kk;
+              S[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(F[mb * SC::QGK + kk], q[ks], S[mb],
+                                                              0, 0, 0);
+            }
+          }
+          if (r == SC::QG - 1) {
+            // softmax of branch j over this tile's 32 tokens
+            if (valid < kT) {
+#pragma unroll
+              for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  if (16 * mb + 4 * kg + e >= valid) S[mb][e] = -INFINITY;
+            }
+            float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
+                             fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mt = mx * kLog2e;
+            const bool need = mt > m_run[j] + kRescale;
+            if (__any(need)) {
+              const float mn = need ? mt : m_run[j];
+              const float f = need ? __builtin_amdgcn_exp2f(m_run[j] - mn) : 1.f;
+              l_run[j] *= f;
+#pragma unroll
+              for (int mb = j * C::MPB; mb < (j + 1) * C::MPB; ++mb) o[mb] *= f;
+              m_run[j] = mn;
+            }
+            float ps = 0.f;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float pe =
+                    __builtin_amdgcn_exp2f(__builtin_fmaf(S[mb][e], kLog2e, -m_run[j]));
+                ps += pe;
+                P[4 * mb + e] = (__bf16)pe;
+              }
+            l_run[j] += ps;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < SC::PGM; ++i) {
+            const int mb = j * SC::MPB + (r - SC::QG) * SC::PGM + i;
+            o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(F[i], P, o[mb], 0, 0, 0);
+          }
+        }
+      };
+
+      bf16x8 F[2][8];
+      load(0, F[0]);
+      // the DMA for a later tile overlaps the first fragment reads
+      if (it + NS - 1 < ntiles)
+        issue_tile<DC, NB, NW>(smem + ((it + NS - 1) % NS) * C::STAGE, crs, krs, p.ckv_ts,
+                               p.kr_ts, t0 + (it + NS - 1) * kT, t1, wave, lane);
+#pragma unroll
+      for (int gid = 0; gid < SC::NG; ++gid) {
+        if (gid + 1 < SC::NG) load(gid + 1, F[(gid + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(gid, F[gid & 1]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
-    // partial state of this segment (slot-uniform base, compile-time offsets)
+    // partial state of this segment: m, l as [slot][n][H]; acc as
+    // [slot][H][d_c] (one contiguous row per head) through an LDS transpose
     const int slot = k + b;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
@@ -320,12 +411,23 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(Params p) {
         p.l[((int64_t)slot * NB + j) * H + head] = lt;
       }
     }
-    float* accs = p.acc + (int64_t)slot * DC * H;
-    const int lane_off = 4 * kg * H + head;
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();  // every wave is done with the tile stages
+    {
+      constexpr int RS = DC + 4;   // padded row (floats): conflict-free transposed writes
+      float LDS_AS* tb = (float LDS_AS*)smem + wave * 16 * RS;
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
+      for (int mb = 0; mb < C::MB; ++mb)
+        *(f32x4 LDS_AS*)(tb + l16 * RS + 16 * mb + 4 * kg) = o[mb];
+      wait_lgkm0();
+      float* rows = p.acc + ((int64_t)slot * H + hg * C::HWG + wave * 16) * DC;
+      constexpr int CH = DC / 4;   // 16-byte chunks per head row
 #pragma unroll
-      for (int e = 0; e < 4; ++e) accs[(16 * mb + e) * H + lane_off] = o[mb][e];
+      for (int i = 0; i < 16 * CH / 64; ++i) {
+        const int qi = lane + 64 * i, hh = qi / CH, c4 = qi % CH;
+        *(f32x4*)(rows + hh * DC + 4 * c4) = *(const f32x4 LDS_AS*)(tb + hh * RS + 4 * c4);
+      }
+    }
     start = seg_end;
     ++b;
   }
@@ -345,9 +447,9 @@ hipError_t launch_t(const Geom& g, const void* q_abs, const void* ckv, const voi
   p.ckv = (const __bf16*)ckv;
   p.krope = (const __bf16*)krope;
   p.ckv_bs = g.ckv_bs;
-  p.ckv_ts = g.ckv_ts;
+  p.ckv_ts = (int)g.ckv_ts;
   p.kr_bs = g.kr_bs;
-  p.kr_ts = g.kr_ts;
+  p.kr_ts = (int)g.kr_ts;
   p.hdr = ws.hdr;
   p.prefix = ws.prefix;
   p.m = ws.m;

@@ -69,4 +69,21 @@ hipError_t launch_decode_mfma(const Geom& g, const void* q_abs, const void* ckv,
                               const void* krope, const Workspace& ws, int grid_items,
                               hipStream_t s);
 
+// bf16 MFMA projections and the merge for the MFMA decode's partial layout
+// ([slot][H][d_c] acc), see proj_mfma.hip.
+bool proj_mfma_supported(const Geom& g);   // out projection / fused merge
+bool absorb_mfma_supported(const Geom& g);
+hipError_t launch_absorb_q_mfma(const Geom& g, const __bf16* q_nope, const __bf16* q_rope,
+                                const int32_t* q_pos, const int32_t* lens, const __bf16* w_uk,
+                                __bf16* q_abs, float tau, float alpha_q, float theta,
+                                hipStream_t s);
+hipError_t launch_combine_hc(const Geom& g, const Workspace& ws, float* latent_out,
+                             hipStream_t s);
+template <typename TO>
+hipError_t launch_combine_out(const Geom& g, const Workspace& ws, const __bf16* w_uv, TO* out,
+                              float alpha_kv, hipStream_t s);
+template <typename TO>
+hipError_t launch_out_proj_mfma(const Geom& g, const float* latent, const __bf16* w_uv, TO* out,
+                                float alpha_kv, hipStream_t s);
+
 }  // namespace mlra

@@ -227,7 +227,11 @@ mlra_status_t run_absorb(const mlra_config_t* c, const Geom& g, const void* q_no
                          const void* w_uk, void* q_abs, hipStream_t s) {
   const float tau = tau_of(c);
   hipError_t e;
-  if (c->dtype == MLRA_BF16)
+  if (c->dtype == MLRA_BF16 && absorb_mfma_supported(g))
+    e = launch_absorb_q_mfma(g, (const __bf16*)q_nope, (const __bf16*)q_rope, q_pos, lens,
+                             (const __bf16*)w_uk, (__bf16*)q_abs, tau, c->alpha_q, c->rope_theta,
+                             s);
+  else if (c->dtype == MLRA_BF16)
     e = launch_absorb_q_generic<__bf16>(g, (const __bf16*)q_nope, (const __bf16*)q_rope, q_pos,
                                         lens, (const __bf16*)w_uk, (__bf16*)q_abs, tau,
                                         c->alpha_q, c->rope_theta, s);
@@ -239,11 +243,16 @@ mlra_status_t run_absorb(const mlra_config_t* c, const Geom& g, const void* q_no
   return MLRA_OK;
 }
 
+// Plan + split-KV decode into the workspace partials. *fast tells which
+// decode ran: the MFMA kernel (partial acc as [slot][H][d_c]) or the portable
+// one ([slot][d_c][H]); the merge must match.
 mlra_status_t run_decode(const mlra_config_t* c, const Geom& g, int cus, const void* q_abs,
-                         const mlra_cache_t* k, const Workspace& ws, const Layout& L,
-                         float* latent_out, hipStream_t s) {
+                         const mlra_cache_t* k, const Workspace& ws, const Layout& L, bool* fast_out,
+                         hipStream_t s) {
   const int64_t imax = L.slots - g.B;
-  bool fast = c->dtype == MLRA_BF16 && decode_mfma_supported(g);
+  bool fast = c->dtype == MLRA_BF16 && decode_mfma_supported(g) &&
+              (int64_t)k->max_len * k->ckv_token_stride * 2 < 0x7fffffffLL &&
+              (int64_t)k->max_len * k->krope_token_stride * 2 < 0x7fffffffLL;
   const DecodePath over = path_override();
   if (over == DecodePath::Generic) fast = false;
   if (over == DecodePath::Mfma && !fast)
@@ -253,12 +262,11 @@ mlra_status_t run_decode(const mlra_config_t* c, const Geom& g, int cus, const v
     target = cus / decode_mfma_wgs_per_item(g);
   } else {
     target = cus * 4 / g.H;
-    if (target < 1) target = 1;
   }
+  if (target < 1) target = 1;
   if (target > kMaxAutoItems) target = kMaxAutoItems;
   if (target > imax && imax > 0) target = (int)imax;
-  TRY_HIP(launch_plan(k->cache_lens, g.B, g.max_len, target > 0 ? target : 1, c->kv_chunk, ws, s),
-          "plan launch");
+  TRY_HIP(launch_plan(k->cache_lens, g.B, g.max_len, target, c->kv_chunk, ws, s), "plan launch");
   if (imax > 0) {
     if (g_ev_before) TRY_HIP(hipEventRecord(g_ev_before, s), "hipEventRecord");
     hipError_t e;
@@ -273,14 +281,26 @@ mlra_status_t run_decode(const mlra_config_t* c, const Geom& g, int cus, const v
     TRY_HIP(e, "decode launch");
     if (g_ev_after) TRY_HIP(hipEventRecord(g_ev_after, s), "hipEventRecord");
   }
-  TRY_HIP(launch_combine(g, ws, latent_out, s), "combine launch");
+  *fast_out = fast;
+  return MLRA_OK;
+}
+
+mlra_status_t run_merge(const Geom& g, const Workspace& ws, bool fast, float* latent_out,
+                        hipStream_t s) {
+  TRY_HIP(fast ? launch_combine_hc(g, ws, latent_out, s) : launch_combine(g, ws, latent_out, s),
+          "combine launch");
   return MLRA_OK;
 }
 
 mlra_status_t run_out_proj(const mlra_config_t* c, const Geom& g, const float* latent,
                            const void* w_uv, void* out, mlra_dtype_t od, hipStream_t s) {
   hipError_t e;
-  if (c->dtype == MLRA_BF16) {
+  if (c->dtype == MLRA_BF16 && proj_mfma_supported(g)) {
+    if (od == MLRA_BF16)
+      e = launch_out_proj_mfma<__bf16>(g, latent, (const __bf16*)w_uv, (__bf16*)out, c->alpha_kv, s);
+    else
+      e = launch_out_proj_mfma<float>(g, latent, (const __bf16*)w_uv, (float*)out, c->alpha_kv, s);
+  } else if (c->dtype == MLRA_BF16) {
     if (od == MLRA_BF16)
       e = launch_out_proj_generic<__bf16, __bf16>(g, latent, (const __bf16*)w_uv, (__bf16*)out,
                                                   c->alpha_kv, s);
@@ -372,8 +392,11 @@ mlra_status_t mla_decode_attn(const mlra_config_t* cfg, int32_t batch, const voi
   int dev, cus;
   TRY(current_device(&dev, &cus));
   const Geom g = make_geom(cfg, batch, cache);
-  return run_decode(cfg, g, cus, q_abs, cache, carve(L, workspace), L, latent_out,
-                    static_cast<hipStream_t>(stream));
+  const Workspace ws = carve(L, workspace);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  bool fast = false;
+  TRY(run_decode(cfg, g, cus, q_abs, cache, ws, L, &fast, s));
+  return run_merge(g, ws, fast, latent_out, s);
 }
 
 mlra_status_t mla_out_proj(const mlra_config_t* cfg, int32_t batch, const float* latent_out,
@@ -423,7 +446,18 @@ mlra_status_t mlra_decode(const mlra_config_t* cfg_in, int32_t num_branches, int
   const Geom g = make_geom(&cfg, batch, cache);
   const Workspace ws = carve(L, workspace);
   TRY(run_absorb(&cfg, g, q_nope, q_rope, q_pos, cache->cache_lens, w_uk, ws.q_abs, s));
-  TRY(run_decode(&cfg, g, cus, ws.q_abs, cache, ws, L, ws.latent, s));
+  bool fast = false;
+  TRY(run_decode(&cfg, g, cus, ws.q_abs, cache, ws, L, &fast, s));
+  if (fast && proj_mfma_supported(g)) {  // merge fused into the output projection
+    hipError_t e = out_dtype == MLRA_BF16
+                       ? launch_combine_out<__bf16>(g, ws, (const __bf16*)w_uv, (__bf16*)out,
+                                                    cfg.alpha_kv, s)
+                       : launch_combine_out<float>(g, ws, (const __bf16*)w_uv, (float*)out,
+                                                   cfg.alpha_kv, s);
+    TRY_HIP(e, "combine_out launch");
+    return MLRA_OK;
+  }
+  TRY(run_merge(g, ws, fast, ws.latent, s));
   return run_out_proj(&cfg, g, ws.latent, w_uv, out, out_dtype, s);
 }
 

@@ -1,0 +1,335 @@
+// bf16 MFMA kernels around the split-KV decode on gfx950:
+//
+//  * absorb_q_mfma - query-side absorption, q~[b][h] = alpha_q tau W_UK[h] q^N[b][h]
+//    ("Multi-Head Low-Rank Attention", 方法步骤详情 step 1), one small GEMM per
+//    head (M = sequences, N = d_c, K = d_n) on v_mfma_f32_16x16x32_bf16, plus
+//    the RoPE rotation of the query's rotary part in double precision.
+//  * combine_out   - merge of the split-KV partials per branch (online-softmax
+//    rescaling) fused with the output up-projection and branch sum
+//    o[b][h] = alpha_kv W_UV[h]^T concat_j o~_j (方法步骤详情 step 3, 核心方法).
+//    The merged fp32 latent is split into bf16 hi + lo parts so that the MFMA
+//    product keeps fp32 accuracy; W_UV[h] is staged in LDS once and read
+//    transposed with ds_read_b64_tr_b16. With FROM_PARTIALS = false the same
+//    kernel is the plain output projection of a given latent_out.
+//  * combine_hc    - the merge alone, writing latent_out [B][H][d_c] fp32.
+//
+// Partials come from decode_mfma_kernel: m, l as [slot][n][H] (m in log2
+// units), acc as [slot][H][d_c]; sequence b's slots are k + b for the work
+// items k that overlap it (see PlanHeader).
+
+#include <math.h>
+
+#include "internal.h"
+
+namespace mlra {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
+#define LDS_AS __attribute__((address_space(3)))
+
+__device__ __forceinline__ int clamp_len(int v, int max_len) {
+  return v < 0 ? 0 : (v > max_len ? max_len : v);
+}
+
+// ------------------------------------------------------------- absorb_q ----
+
+// grid (H, ceil(B / (16 MBLK)), 2 halves of d_c); 4 waves
+template <int KSN, int MBLK>
+__global__ __launch_bounds__(256) void absorb_q_mfma(Geom g, const __bf16* __restrict__ q_nope,
+                                                     const __bf16* __restrict__ q_rope,
+                                                     const int32_t* __restrict__ q_pos,
+                                                     const int32_t* __restrict__ lens,
+                                                     const __bf16* __restrict__ w_uk,
+                                                     __bf16* __restrict__ q_abs, float scale,
+                                                     float tau, float theta) {
+  const int h = blockIdx.x, b0 = blockIdx.y * 16 * MBLK, half = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, kg = lane >> 4;
+  const int row = g.dc + g.dr;
+  const int dn = KSN * 32;
+  // A = q^N rows of this block's sequences: lane (b = l16, kg)
+  bf16x8 A[MBLK][KSN];
+#pragma unroll
+  for (int m = 0; m < MBLK; ++m) {
+    const int b = b0 + 16 * m + l16;
+#pragma unroll
+    for (int ks = 0; ks < KSN; ++ks) {
+      if (b < g.B)
+        A[m][ks] = *(const bf16x8*)(q_nope + ((size_t)b * g.H + h) * dn + 32 * ks + 8 * kg);
+      else
+        A[m][ks] = (bf16x8){};
+    }
+  }
+  // N blocks of 16 latent columns: this half's blocks, spread over the 4 waves
+  const int nblk = g.dc / 16, per_half = nblk / 2;
+  const __bf16* w = w_uk + (size_t)h * g.dc * dn;
+  for (int nb = half * per_half + wave; nb < (half + 1) * per_half; nb += 4) {
+    const int c = 16 * nb + l16;
+    bf16x8 Bf[KSN];
+#pragma unroll
+    for (int ks = 0; ks < KSN; ++ks) Bf[ks] = *(const bf16x8*)(w + (size_t)c * dn + 32 * ks + 8 * kg);
+#pragma unroll
+    for (int m = 0; m < MBLK; ++m) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KSN; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[m][ks], Bf[ks], acc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int b = b0 + 16 * m + 4 * kg + i;
+        if (b < g.B) q_abs[((size_t)b * g.H + h) * row + c] = (__bf16)(scale * acc[i]);
+      }
+    }
+  }
+  // RoPE on the query's rotary part (angle in double precision): half 0 only
+  if (half == 0) {
+    const int hp = g.dr / 2;
+    for (int i = threadIdx.x; i < 16 * MBLK * hp; i += 256) {
+      const int b = b0 + i / hp, k = i % hp;
+      if (b >= g.B) continue;
+      const int p = q_pos ? q_pos[b] : clamp_len(lens[b], g.max_len) - 1;
+      const double omega = pow((double)theta, -2.0 * (double)k / (double)g.dr);
+      double sn, cs;
+      sincos((double)p * omega, &sn, &cs);
+      const size_t qi = ((size_t)b * g.H + h) * g.dr + 2 * k;
+      const double x0 = (float)q_rope[qi], x1 = (float)q_rope[qi + 1];
+      __bf16* o = q_abs + ((size_t)b * g.H + h) * row + g.dc + 2 * k;
+      o[0] = (__bf16)(float)(tau * (x0 * cs - x1 * sn));
+      o[1] = (__bf16)(float)(tau * (x0 * sn + x1 * cs));
+    }
+  }
+}
+
+// -------------------------------------------------------- merge helpers ----
+
+// Merge weights of sequence b, head h, branch j over its slots: writes
+// M (max, log2 units) and 1/L where L = sum_k 2^(m_k - M) l_k.
+__device__ __forceinline__ void branch_norm(const Workspace& ws, int H, int NB, int b, int h,
+                                            int j, int kf, int kl, float& M, float& Linv) {
+  float mx = -INFINITY;
+  for (int k = kf; k <= kl; ++k) mx = fmaxf(mx, ws.m[((size_t)(k + b) * NB + j) * H + h]);
+  float L = 0.f;
+  for (int k = kf; k <= kl; ++k) {
+    const size_t i = ((size_t)(k + b) * NB + j) * H + h;
+    L += exp2f(ws.m[i] - mx) * ws.l[i];
+  }
+  M = mx;
+  Linv = 1.f / L;
+}
+
+// Four consecutive latent columns c0..c0+3 (one branch) of sequence b, head h.
+__device__ __forceinline__ f32x4 merged4(const Workspace& ws, const PlanHeader& hd, int H,
+                                         int DC, int NB, int b, int h, int c0) {
+  const int p0 = ws.prefix[b], p1 = ws.prefix[b + 1];
+  f32x4 r = {0.f, 0.f, 0.f, 0.f};
+  if (p1 <= p0) return r;
+  const int kf = p0 / hd.chunk, kl = (p1 - 1) / hd.chunk;
+  const int j = c0 / (DC / NB);
+  float M, Linv;
+  branch_norm(ws, H, NB, b, h, j, kf, kl, M, Linv);
+  for (int k = kf; k <= kl; ++k) {
+    const float w = exp2f(ws.m[((size_t)(k + b) * NB + j) * H + h] - M) * Linv;
+    const f32x4 a = *(const f32x4*)(ws.acc + ((size_t)(k + b) * H + h) * DC + c0);
+    r += w * a;
+  }
+  return r;
+}
+
+// ----------------------------------------------------------- combine_hc ----
+
+// grid (B, H); DC/4 threads: latent_out[b][h][:] from the partials
+__global__ __launch_bounds__(128) void combine_hc(Geom g, Workspace ws,
+                                                  float* __restrict__ latent_out) {
+  const int b = blockIdx.x, h = blockIdx.y;
+  const PlanHeader hd = *ws.hdr;
+  for (int c4 = threadIdx.x; c4 < g.dc / 4; c4 += blockDim.x) {
+    const f32x4 r = merged4(ws, hd, g.H, g.dc, g.n, b, h, 4 * c4);
+    *(f32x4*)(latent_out + ((size_t)b * g.H + h) * g.dc + 4 * c4) = r;
+  }
+}
+
+// ---------------------------------------------------------- combine_out ----
+
+// W_UV rows of one v-half staged in LDS: 64 bf16 (128 B) per latent column,
+// padded to 160 B so that the transposed reads (4 rows x 32 B per 16 lanes)
+// hit distinct banks. Latent rows (bf16 hi and lo) padded by 16 B.
+constexpr int kDVH = 64;            // output columns per workgroup
+constexpr int kWRow = 160;          // bytes per staged W_UV row
+template <int DC>
+struct OutLds {
+  static constexpr int LROW = (DC + 8) * 2;                 // bytes per latent row
+  static constexpr int W_BYTES = DC * kWRow;
+  static constexpr int L_BYTES = 16 * LROW;
+  static constexpr int TOTAL = W_BYTES + 2 * L_BYTES;
+};
+
+// grid H * 2 (the two v-halves of a head share an XCD); 4 waves, wave w owns
+// output columns [16 w, 16 w + 16) of its half.
+template <int DC, bool FROM_PARTIALS, typename TO>
+__global__ __launch_bounds__(256) void combine_out(Geom g, Workspace ws,
+                                                   const float* __restrict__ latent_in,
+                                                   const __bf16* __restrict__ w_uv,
+                                                   TO* __restrict__ out, float alpha_kv) {
+  using LD = OutLds<DC>;
+  __shared__ __attribute__((aligned(16))) char smem_raw[LD::TOTAL];
+  char LDS_AS* smem = (char LDS_AS*)smem_raw;
+  char LDS_AS* wl = smem;
+  char LDS_AS* lhi = smem + LD::W_BYTES;
+  char LDS_AS* llo = lhi + LD::L_BYTES;
+  const int i = blockIdx.x, x = i & 7, jj = i >> 3;
+  const int h = (jj >> 1) * 8 + x, vh = jj & 1;
+  if (h >= g.H) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, kg = lane >> 4;
+  PlanHeader hd;
+  if (FROM_PARTIALS) hd = *ws.hdr;
+
+  // stage W_UV[h][:, 64 vh .. 64 vh + 64)
+  {
+    const __bf16* w = w_uv + (size_t)h * DC * g.dv + kDVH * vh;
+    for (int q = tid; q < DC * 8; q += 256) {
+      const int c = q >> 3, ch = q & 7;
+      *(bf16x8 LDS_AS*)(wl + c * kWRow + 16 * ch) = *(const bf16x8*)(w + (size_t)c * g.dv + 8 * ch);
+    }
+  }
+  // per-lane offsets of the transposed W reads (rows 4 r + {0..3}, column quad q)
+  const int r4 = l16 >> 2, q4 = l16 & 3;
+  const int wcol = 2 * (16 * wave + 4 * q4);
+
+  for (int b0 = 0; b0 < g.B; b0 += 16) {
+    __syncthreads();  // W staged / previous block's latent consumed
+    // latent rows of sequences b0..b0+15 as bf16 hi + lo
+    for (int q = tid; q < 16 * (DC / 4); q += 256) {
+      const int bb = q / (DC / 4), c4 = q % (DC / 4), b = b0 + bb;
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (b < g.B) {
+        if (FROM_PARTIALS)
+          v = merged4(ws, hd, g.H, DC, g.n, b, h, 4 * c4);
+        else
+          v = *(const f32x4*)(latent_in + ((size_t)b * g.H + h) * DC + 4 * c4);
+      }
+      __bf16 hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = (__bf16)v[e];
+        lo[e] = (__bf16)(v[e] - (float)hi[e]);
+      }
+      __bf16 LDS_AS* ph = (__bf16 LDS_AS*)(lhi + bb * LD::LROW) + 4 * c4;
+      __bf16 LDS_AS* pl = (__bf16 LDS_AS*)(llo + bb * LD::LROW) + 4 * c4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { ph[e] = hi[e]; pl[e] = lo[e]; }
+    }
+    __syncthreads();
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int ks = 0; ks < DC / 32; ++ks) {
+      const int aoff = l16 * LD::LROW + 2 * (32 * ks + 8 * kg);
+      const bf16x8 ah = *(const bf16x8 LDS_AS*)(lhi + aoff);
+      const bf16x8 al = *(const bf16x8 LDS_AS*)(llo + aoff);
+      const int wr = (32 * ks + 8 * kg + r4) * kWRow + wcol;
+      const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(wl + wr));
+      const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(wl + wr + 4 * kWRow));
+      const i16x8 wv = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      const bf16x8 wb = __builtin_bit_cast(bf16x8, wv);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wb, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wb, acc, 0, 0, 0);
+    }
+    // D[b][v]: lane (v = 16 wave + l16 of this half, rows b0 + 4 kg + i)
+    const int v = kDVH * vh + 16 * wave + l16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int b = b0 + 4 * kg + e;
+      if (b < g.B) out[((size_t)b * g.H + h) * g.dv + v] = (TO)(alpha_kv * acc[e]);
+    }
+  }
+}
+
+template <int DC, bool FP, typename TO>
+hipError_t launch_out_t(const Geom& g, const Workspace& ws, const float* lat, const __bf16* w_uv,
+                        TO* out, float alpha_kv, hipStream_t s) {
+  const int grid = ((g.H + 7) / 8) * 8 * 2;
+  hipLaunchKernelGGL((combine_out<DC, FP, TO>), dim3(grid), dim3(256), 0, s, g, ws, lat, w_uv,
+                     out, alpha_kv);
+  return hipGetLastError();
+}
+
+template <bool FP, typename TO>
+hipError_t launch_out_dc(const Geom& g, const Workspace& ws, const float* lat,
+                         const __bf16* w_uv, TO* out, float alpha_kv, hipStream_t s) {
+  switch (g.dc) {
+    case 128: return launch_out_t<128, FP, TO>(g, ws, lat, w_uv, out, alpha_kv, s);
+    case 256: return launch_out_t<256, FP, TO>(g, ws, lat, w_uv, out, alpha_kv, s);
+    case 512: return launch_out_t<512, FP, TO>(g, ws, lat, w_uv, out, alpha_kv, s);
+  }
+  return hipErrorNotSupported;
+}
+
+template <int KSN>
+hipError_t launch_absorb_k(const Geom& g, const __bf16* qn, const __bf16* qr, const int32_t* qp,
+                           const int32_t* lens, const __bf16* w, __bf16* qa, float scale,
+                           float tau, float theta, hipStream_t s) {
+  if (g.B > 32) {
+    hipLaunchKernelGGL((absorb_q_mfma<KSN, 4>), dim3(g.H, (g.B + 63) / 64, 2), dim3(256), 0, s,
+                       g, qn, qr, qp, lens, w, qa, scale, tau, theta);
+  } else {
+    hipLaunchKernelGGL((absorb_q_mfma<KSN, 1>), dim3(g.H, (g.B + 15) / 16, 2), dim3(256), 0, s,
+                       g, qn, qr, qp, lens, w, qa, scale, tau, theta);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool proj_mfma_supported(const Geom& g) {
+  return (g.dc == 128 || g.dc == 256 || g.dc == 512) && g.dv == 2 * kDVH;
+}
+
+bool absorb_mfma_supported(const Geom& g) {
+  return g.dc % 32 == 0 && (g.dn == 64 || g.dn == 128 || g.dn == 256);
+}
+
+hipError_t launch_absorb_q_mfma(const Geom& g, const __bf16* q_nope, const __bf16* q_rope,
+                                const int32_t* q_pos, const int32_t* lens, const __bf16* w_uk,
+                                __bf16* q_abs, float tau, float alpha_q, float theta,
+                                hipStream_t s) {
+  const float scale = alpha_q * tau;
+  switch (g.dn) {
+    case 64: return launch_absorb_k<2>(g, q_nope, q_rope, q_pos, lens, w_uk, q_abs, scale, tau, theta, s);
+    case 128: return launch_absorb_k<4>(g, q_nope, q_rope, q_pos, lens, w_uk, q_abs, scale, tau, theta, s);
+    case 256: return launch_absorb_k<8>(g, q_nope, q_rope, q_pos, lens, w_uk, q_abs, scale, tau, theta, s);
+  }
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_combine_hc(const Geom& g, const Workspace& ws, float* latent_out,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(combine_hc, dim3(g.B, g.H), dim3(128), 0, s, g, ws, latent_out);
+  return hipGetLastError();
+}
+
+template <typename TO>
+hipError_t launch_combine_out(const Geom& g, const Workspace& ws, const __bf16* w_uv, TO* out,
+                              float alpha_kv, hipStream_t s) {
+  return launch_out_dc<true, TO>(g, ws, nullptr, w_uv, out, alpha_kv, s);
+}
+
+template <typename TO>
+hipError_t launch_out_proj_mfma(const Geom& g, const float* latent, const __bf16* w_uv, TO* out,
+                                float alpha_kv, hipStream_t s) {
+  Workspace none{};
+  return launch_out_dc<false, TO>(g, none, latent, w_uv, out, alpha_kv, s);
+}
+
+template hipError_t launch_combine_out<float>(const Geom&, const Workspace&, const __bf16*,
+                                              float*, float, hipStream_t);
+template hipError_t launch_combine_out<__bf16>(const Geom&, const Workspace&, const __bf16*,
+                                               __bf16*, float, hipStream_t);
+template hipError_t launch_out_proj_mfma<float>(const Geom&, const float*, const __bf16*, float*,
+                                                float, hipStream_t);
+template hipError_t launch_out_proj_mfma<__bf16>(const Geom&, const float*, const __bf16*,
+                                                 __bf16*, float, hipStream_t);
+
+}  // namespace mlra

@@ -165,3 +165,19 @@ def test_shard_b64_ragged_sampled():
     err = row_rel_err(got[seqs], absorbed_oracle(w, inp, seqs))
     say(f"  rel err {err:.2e}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("batch", [16, 64, 3])
+def test_out_proj_step_bf16(batch):
+    # output projection alone on the oracle's fp32 latent: the fp32 latent is
+    # split into bf16 hi + lo for the MFMA, so the result is fp32-accurate
+    w = WORKLOADS["mlra4_b16_l32k"].replace(batch=batch)
+    inp = make_inputs(w, lens=np.full(batch, 8, np.int32), max_len=8)
+    rng = np.random.default_rng(5)
+    lo = rng.standard_normal((batch, w.heads, w.d_c))
+    d = Dev(w, inp)
+    got = host(d.out_proj(config_for(w), torch.from_numpy(lo.astype(np.float32)).cuda()))
+    ref = oracle.out_proj_ref(lo.astype(np.float32).astype(np.float64), inp["w_uv"], w.alpha_kv)
+    err = row_rel_err(got, ref)
+    say(f"out_proj bf16 B={batch}: rel err {err:.2e}")
+    assert err <= 1e-4
