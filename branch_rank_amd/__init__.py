@@ -14,7 +14,8 @@ import math
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmlra.so")
+# MLRA_LIB points at another build of the same library (kernel tuning)
+LIB_PATH = os.environ.get("MLRA_LIB") or os.path.join(_HERE, "libmlra.so")
 
 MLRA_OK, MLRA_ERR_INVALID_ARG, MLRA_ERR_UNSUPPORTED, MLRA_ERR_WORKSPACE, \
     MLRA_ERR_NO_DEVICE, MLRA_ERR_HIP = range(6)

@@ -26,9 +26,10 @@
 //    tile tokens as K, so P never moves between lanes. V^T is read from the
 //    same row-major LDS tile with ds_read_b64_tr_b16. O^T keeps lane = head,
 //    so a softmax rescale is one multiplier per lane.
-//  * Lazy rescaling: the running max m only moves when a tile's max exceeds it
-//    by more than 2^8 in log2 units; p <= 256 stays exact enough in fp32 and
-//    bf16, and (m, l, acc) stay consistent.
+//  * Lazy rescaling: the segment's first tile sets the reference max m; it only
+//    moves (rescaling l and O in registers) when a tile's max exceeds it by
+//    more than 16 in log2 units, so p <= 2^16, which fp32 and bf16 hold with
+//    their usual relative precision. (m, l, acc) stay consistent.
 //  * LDS rows are XOR-swizzled in 16-byte chunks so that the QK reads (16 rows
 //    x 1 chunk per 16 lanes) and the transposed PV reads (4 rows x 2 chunks per
 //    16 lanes) are free of bank conflicts.
@@ -47,7 +48,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
 constexpr int kT = 32;   // tokens per tile
 constexpr int kDR = 64;  // RoPE width
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescale = 8.f;  // log2 headroom before the running max moves
+constexpr float kRescale = 16.f;  // log2 headroom before the running max moves
 
 struct Params {
   const __bf16* q_abs;
@@ -71,10 +72,16 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// Latent-row swizzle: bijective on t mod 16 (QK reads of 16 rows) and, for the
-// four rows 4a..4a+3, spreads rows over chunk bits 1-2 (transposed PV reads).
+// Latent-row swizzle (16-byte chunk index XOR per row). Measured on gfx950
+// (rocprofv3 SQ_LDS_BANK_CONFLICT on the two read patterns): for rows of
+// >= 512 bytes, chunk ^ 2*(t & 15) makes both the QK reads (16 rows x one
+// chunk per 16 lanes, ds_read_b128) and the transposed PV reads (4 rows x
+// 32 bytes per 16 lanes, ds_read_b64_tr_b16) conflict-free. 256-byte rows
+// (d_c = 128) keep a 4-bit swizzle.
+template <int DC>
 __device__ __forceinline__ int swz(int t) {
-  return ((t & 3) << 1) | ((t >> 2) & 1) | (((t >> 3) & 1) << 3);
+  if constexpr (DC >= 256) return 2 * (t & 15);
+  else return ((t & 3) << 1) | ((t >> 2) & 1) | (((t >> 3) & 1) << 3);
 }
 // RoPE-row swizzle (128-byte rows): 16 rows of one chunk hit distinct banks.
 __device__ __forceinline__ int swz_r(int t) { return (t >> 1) & 7; }
@@ -104,6 +111,7 @@ struct Cfg {
   static constexpr int MB = DC / 16;             // PV output row blocks
   static constexpr int MPB = MB / NB;            // PV row blocks per branch
   static constexpr int HWG = 16 * NW;            // heads per workgroup
+  static constexpr bool PRE_VOFF = PER_HI <= 9;  // DMA lane offsets held in VGPRs
   static_assert(CPR >= 16 && 64 % CPR == 0, "latent width must be 128, 256 or 512");
   static_assert(KPB >= 1 && MPB >= 1, "branch slice must be >= 32 columns");
 };
@@ -121,39 +129,66 @@ __device__ __forceinline__ i32x4 seq_rsrc(const __bf16* base, int rows, int ts) 
   return r;
 }
 
-// One LDS-DMA instruction: 16 bytes per lane from rsrc + voff into LDS at
-// lds_base + 16 * lane. Issued from asm so that the compiler does not add
-// its own (conservative) vmcnt waits before later LDS reads; every wait for
-// this data is placed by hand (wait_tiles). No output registers.
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_base, uint32_t voff) {
+// One LDS-DMA instruction: 16 bytes per lane from rsrc + voff + soff into
+// LDS at lds_base + 16 * lane. Issued from asm so that the compiler does not
+// add its own (conservative) vmcnt waits before later LDS reads; every wait
+// for this data is placed by hand (wait_tiles). No output registers.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_base, uint32_t voff,
+                                      uint32_t soff) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
       :
-      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(rsrc)
+      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(rsrc),
+        "s"(__builtin_amdgcn_readfirstlane(soff))
       : "memory");
 }
 
+// Row t and logical chunk of the u-th DMA instruction of this wave.
 template <int DC, int NB, int NW>
+__device__ __forceinline__ void dma_lane(int u, int wave, int lane, bool& rope, int& t, int& lc) {
+  using C = Cfg<DC, NB, NW>;
+  const int q = wave + NW * u;
+  rope = q >= C::NL;
+  if (!rope) {
+    t = q * C::RPI + lane / C::CPR;
+    lc = (lane % C::CPR) ^ swz<DC>(t);
+  } else {
+    t = (q - C::NL) * 8 + lane / 8;
+    lc = (lane % 8) ^ swz_r(t);
+  }
+}
+
+// DMA of one tile. Full tiles: per-lane offsets precomputed (voff), the tile
+// offset in soffset. The tail tile clamps rows to the segment (tend - 1).
+template <int DC, int NB, int NW, bool TAIL>
 __device__ __forceinline__ void issue_tile(char LDS_AS* stage, i32x4 crs, i32x4 krs, int cts,
-                                           int kts, int tstart, int tend, int wave, int lane) {
+                                           int kts, int tstart, int tend, int wave, int lane,
+                                           const uint32_t* voff) {
   using C = Cfg<DC, NB, NW>;
   const uint32_t sbase = (uint32_t)(uintptr_t)stage;
 #pragma unroll
   for (int u = 0; u < C::PER_HI; ++u) {
     const int q = wave + NW * u;
-    if (q < C::NL) {
-      const int t = q * C::RPI + lane / C::CPR;
-      const int lc = (lane % C::CPR) ^ swz(t);
+    if (q >= C::NI) continue;
+    const bool rope = q >= C::NL;
+    const uint32_t ldsb = rope ? sbase + C::LAT_BYTES + (q - C::NL) * 1024 : sbase + q * 1024;
+    const i32x4 rs = rope ? krs : crs;
+    const int ts = rope ? kts : cts;
+    if constexpr (!TAIL && C::PRE_VOFF) {
+      dma16(rs, ldsb, voff[u], (uint32_t)(tstart * ts * 2));
+    } else if constexpr (!TAIL) {
+      bool r_;
+      int t, lc;
+      dma_lane<DC, NB, NW>(u, wave, lane, r_, t, lc);
+      dma16(rs, ldsb, (uint32_t)(t * ts * 2 + lc * 16), (uint32_t)(tstart * ts * 2));
+    } else {
+      bool r_;
+      int t, lc;
+      dma_lane<DC, NB, NW>(u, wave, lane, r_, t, lc);
       const int row = min(tstart + t, tend - 1);
-      dma16(crs, sbase + q * 1024, row * cts * 2 + lc * 16);
-    } else if (q < C::NI) {
-      const int r = q - C::NL;
-      const int t = r * 8 + lane / 8;
-      const int lc = (lane % 8) ^ swz_r(t);
-      const int row = min(tstart + t, tend - 1);
-      dma16(krs, sbase + C::LAT_BYTES + r * 1024, row * kts * 2 + lc * 16);
+      dma16(rs, ldsb, (uint32_t)(row * ts * 2 + lc * 16), 0u);
     }
   }
 }
@@ -197,12 +232,43 @@ struct Sched {
   static_assert(QG * QGK == KPB && PG * PGM == MPB && 2 * QGK <= 8 && PGM <= 8, "schedule");
 };
 
+// Reductions over the four lanes that hold one head (l16 + 16 kg) with the
+// gfx950 lane swaps (VALU, no LDS): permlane16_swap(x, x) gives, per lane,
+// x of this lane and of lane ^ 16; permlane32_swap likewise for lane ^ 32.
+// The lane swaps are issued from asm with both registers as in/out
+// operands: this compiler's permlane*_swap builtins return the first result
+// for both halves of the pair. s_nop 1 on either side covers the VALU ->
+// permlane and permlane -> VALU operand hazards.
+__device__ __forceinline__ void swap16(float x, float& lo, float& hi) {
+  float y = x;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+  lo = x;
+  hi = y;
+}
+__device__ __forceinline__ void swap32(float x, float& lo, float& hi) {
+  float y = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+  lo = x;
+  hi = y;
+}
+__device__ __forceinline__ float max4(float x) {
+  float a, b;
+  swap16(x, a, b);
+  swap32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum4(float x) {
+  float a, b;
+  swap16(x, a, b);
+  swap32(a + b, a, b);
+  return a + b;
+}
+
 template <int DC, int NB, int NW, int NS, int HSPLIT>
 __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(Params p) {
   using C = Cfg<DC, NB, NW>;
   using SC = Sched<DC, NB>;
   constexpr int H = C::HWG * HSPLIT;
-  static_assert(NW * 16 * (DC + 4) * 4 <= NS * C::STAGE, "epilogue transpose must fit the stages");
   __shared__ __attribute__((aligned(1024))) char smem_raw[NS * C::STAGE];
   char LDS_AS* smem = (char LDS_AS*)smem_raw;
 
@@ -218,15 +284,26 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(Params p) {
   }
   const PlanHeader hd = *p.hdr;
   if (k >= hd.n_items) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l16 = lane & 15, kg = lane >> 4;
   const int head = hg * C::HWG + wave * 16 + l16;
 
-  // lane constants for the LDS reads (see the swizzle notes)
-  const int qk_x = kg ^ swz(l16);                    // QK latent: chunk 4ks+kg
-  const int rp_x = swz_r(l16);                       // QK rope
-  const int pv_r = l16 >> 2, pv_q = l16 & 3;         // PV: row r of 4, column quad q
-  const int pv_y = (pv_q >> 1) ^ (2 * pv_r + (kg & 1) + 8 * (kg >> 1));
+  // per-lane DMA offsets of full tiles (fixed for the whole kernel; kept in
+  // registers only when few)
+  uint32_t voff[C::PRE_VOFF ? C::PER_HI : 1];
+#pragma unroll
+  for (int u = 0; u < (C::PRE_VOFF ? C::PER_HI : 0); ++u) {
+    bool rope;
+    int t, lc;
+    dma_lane<DC, NB, NW>(u, wave, lane, rope, t, lc);
+    voff[u] = (uint32_t)(t * (rope ? p.kr_ts : p.ckv_ts) * 2 + lc * 16);
+  }
+  // lane constants of the LDS reads (see the swizzle)
+  const int qk_y = kg ^ swz<DC>(l16);
+  const int rp_x = swz_r(l16);
+  const int pv_r = l16 >> 2, pv_q = l16 & 3;
+  const int pv_w = (pv_q >> 1) ^ swz<DC>(4 * kg + pv_r);
   const int pv_row_lo = (4 * kg + pv_r) * DC * 2 + 8 * (pv_q & 1);
   const int pv_row_hi = pv_row_lo + 16 * DC * 2;
 
@@ -241,6 +318,8 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(Params p) {
     const int ntiles = (t1 - t0 + kT - 1) / kT;
     const i32x4 crs = seq_rsrc(p.ckv + (int64_t)b * p.ckv_bs, t1, p.ckv_ts);
     const i32x4 krs = seq_rsrc(p.krope + (int64_t)b * p.kr_bs, t1, p.kr_ts);
+    const int slot = k + b;
+    float* acc_row = p.acc + ((int64_t)slot * H + head) * DC + 4 * kg;
 
     // earlier stores and loads of this wave done; all waves left the
     // previous segment's LDS tiles
@@ -255,30 +334,35 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(Params p) {
 #pragma unroll
       for (int ks = 0; ks < C::KS + 2; ++ks) q[ks] = *(const bf16x8*)(qrow + 32 * ks);
     }
+    // Q lives in AGPRs (MFMA reads its B operand from there), leaving the
+    // VGPRs to the fragments and the softmax
+#pragma unroll
+    for (int ks = 0; ks < C::KS + 2; ++ks) asm volatile("" : "+a"(q[ks]));
     // Q complete before any DMA is in flight: the compiler then needs no vmcnt
     // wait for Q inside the tile loop (such a wait would also drain the DMA)
     wait_vm<0>();
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-      if (s < ntiles)
-        issue_tile<DC, NB, NW>(smem + s * C::STAGE, crs, krs, p.ckv_ts, p.kr_ts, t0 + s * kT,
-                               t1, wave, lane);
+    for (int s = 0; s < NS - 1; ++s) {
+      if (s < ntiles - 1)
+        issue_tile<DC, NB, NW, false>(smem + s * C::STAGE, crs, krs, p.ckv_ts, p.kr_ts,
+                                      t0 + s * kT, t1, wave, lane, voff);
+      else if (s == ntiles - 1)
+        issue_tile<DC, NB, NW, true>(smem + s * C::STAGE, crs, krs, p.ckv_ts, p.kr_ts,
+                                     t0 + s * kT, t1, wave, lane, voff);
+    }
 
     f32x4 o[C::MB];
 #pragma unroll
     for (int i = 0; i < C::MB; ++i) o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
     float m_run[NB], l_run[NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) { m_run[j] = -INFINITY; l_run[j] = 0.f; }
+    for (int j = 0; j < NB; ++j) {
+      m_run[j] = -INFINITY;
+      l_run[j] = 0.f;
+    }
 
-    for (int it = 0; it < ntiles; ++it) {
-      const int ahead = min(NS - 2, ntiles - 1 - it);
-      wait_tiles<DC, NB, NW, NS>(ahead, wave);
-      __builtin_amdgcn_s_barrier();
-      const char LDS_AS* st = smem + (it % NS) * C::STAGE;
-      const int valid = min(kT, t1 - (t0 + it * kT));
-
-      // ---- fragment loads of one group into F[0..7]
+    // one 32-token tile; valid < kT only for the segment's last tile
+    auto tile = [&](const char LDS_AS* st, int valid) {
       auto load = [&](int gid, bf16x8* F) {
         if (gid == 0) {
 #pragma unroll
@@ -298,14 +382,14 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(Params p) {
             for (int kk = 0; kk < SC::QGK; ++kk) {
               const int ks = j * SC::KPB + r * SC::QGK + kk;
               F[mb * SC::QGK + kk] = *(const bf16x8 LDS_AS*)(st + (16 * mb + l16) * DC * 2 +
-                                                            256 * (ks >> 2) +
-                                                            16 * ((4 * (ks & 3)) ^ qk_x));
+                                                            512 * (ks >> 3) +
+                                                            16 * ((4 * (ks & 7)) ^ qk_y));
             }
         } else {
 #pragma unroll
           for (int i = 0; i < SC::PGM; ++i) {
             const int mb = j * SC::MPB + (r - SC::QG) * SC::PGM + i;
-            const int coff = 256 * (mb >> 3) + 16 * ((2 * (mb & 7)) ^ pv_y);
+            const int coff = 512 * (mb >> 4) + 16 * ((2 * (mb & 15)) ^ pv_w);
             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (i16x4 LDS_AS*)(st + pv_row_lo + coff));
             const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -318,13 +402,14 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(Params p) {
 
       f32x4 R[2], S[2];
       bf16x8 P;
-      // ---- MFMAs of one group (and the branch softmax after its last QK group)
       auto compute = [&](int gid, const bf16x8* F) {
         if (gid == 0) {
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb) {
-            R[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(F[2 * mb], q[C::KS], (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            R[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(F[2 * mb + 1], q[C::KS + 1], R[mb], 0, 0, 0);
+            R[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(F[2 * mb], q[C::KS],
+                                                            (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            R[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(F[2 * mb + 1], q[C::KS + 1], R[mb],
+                                                            0, 0, 0);
           }
           return;
         }
@@ -341,23 +426,23 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(Params p) {
             }
           }
           if (r == SC::QG - 1) {
-            // softmax of branch j over this tile's 32 tokens
-            if (valid < kT) {
+            // softmax of branch j over this tile's 32 tokens; tokens past the
+            // segment end (last tile only) get score -inf
 #pragma unroll
-              for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                  if (16 * mb + 4 * kg + e >= valid) S[mb][e] = -INFINITY;
-            }
+              for (int e = 0; e < 4; ++e)
+                if (16 * mb + 4 * kg + e >= valid) S[mb][e] = -INFINITY;
             float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
                              fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mt = mx * kLog2e;
+            const float mt = max4(mx) * kLog2e;
+            // the segment's first tile sets the reference; afterwards it only
+            // moves when a tile max exceeds it by more than kRescale (rare)
+            m_run[j] = m_run[j] == -INFINITY ? mt : m_run[j];
             const bool need = mt > m_run[j] + kRescale;
-            if (__any(need)) {
+            if (__builtin_expect(__any(need), 0)) {
               const float mn = need ? mt : m_run[j];
-              const float f = need ? __builtin_amdgcn_exp2f(m_run[j] - mn) : 1.f;
+              const float f = __builtin_amdgcn_exp2f(m_run[j] - mn);
               l_run[j] *= f;
 #pragma unroll
               for (int mb = j * C::MPB; mb < (j + 1) * C::MPB; ++mb) o[mb] *= f;
@@ -386,10 +471,6 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(Params p) {
 
       bf16x8 F[2][8];
       load(0, F[0]);
-      // the DMA for a later tile overlaps the first fragment reads
-      if (it + NS - 1 < ntiles)
-        issue_tile<DC, NB, NW>(smem + ((it + NS - 1) % NS) * C::STAGE, crs, krs, p.ckv_ts,
-                               p.kr_ts, t0 + (it + NS - 1) * kT, t1, wave, lane);
 #pragma unroll
       for (int gid = 0; gid < SC::NG; ++gid) {
         if (gid + 1 < SC::NG) load(gid + 1, F[(gid + 1) & 1]);
@@ -397,37 +478,34 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(Params p) {
         compute(gid, F[gid & 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
+    };
+
+    for (int it = 0; it < ntiles; ++it) {
+      const int ahead = min(NS - 2, ntiles - 1 - it);
+      wait_tiles<DC, NB, NW, NS>(ahead, wave);
+      __builtin_amdgcn_s_barrier();
+      const int nt = it + NS - 1;  // tile whose DMA goes out now
+      if (nt < ntiles - 1)
+        issue_tile<DC, NB, NW, false>(smem + (nt % NS) * C::STAGE, crs, krs, p.ckv_ts, p.kr_ts,
+                                      t0 + nt * kT, t1, wave, lane, voff);
+      else if (nt == ntiles - 1)
+        issue_tile<DC, NB, NW, true>(smem + (nt % NS) * C::STAGE, crs, krs, p.ckv_ts, p.kr_ts,
+                                     t0 + nt * kT, t1, wave, lane, voff);
+      tile(smem + (it % NS) * C::STAGE, min(kT, t1 - (t0 + it * kT)));
     }
 
     // partial state of this segment: m, l as [slot][n][H]; acc as
-    // [slot][H][d_c] (one contiguous row per head) through an LDS transpose
-    const int slot = k + b;
+    // [slot][H][d_c], 16-byte stores of 4 consecutive latent columns
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      float lt = l_run[j] + __shfl_xor(l_run[j], 16);
-      lt += __shfl_xor(lt, 32);
+      const float lt = sum4(l_run[j]);
       if (kg == 0) {
         p.m[((int64_t)slot * NB + j) * H + head] = m_run[j];
         p.l[((int64_t)slot * NB + j) * H + head] = lt;
       }
     }
-    wait_lgkm0();
-    __builtin_amdgcn_s_barrier();  // every wave is done with the tile stages
-    {
-      constexpr int RS = DC + 4;   // padded row (floats): conflict-free transposed writes
-      float LDS_AS* tb = (float LDS_AS*)smem + wave * 16 * RS;
 #pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-        *(f32x4 LDS_AS*)(tb + l16 * RS + 16 * mb + 4 * kg) = o[mb];
-      wait_lgkm0();
-      float* rows = p.acc + ((int64_t)slot * H + hg * C::HWG + wave * 16) * DC;
-      constexpr int CH = DC / 4;   // 16-byte chunks per head row
-#pragma unroll
-      for (int i = 0; i < 16 * CH / 64; ++i) {
-        const int qi = lane + 64 * i, hh = qi / CH, c4 = qi % CH;
-        *(f32x4*)(rows + hh * DC + 4 * c4) = *(const f32x4 LDS_AS*)(tb + hh * RS + 4 * c4);
-      }
-    }
+    for (int mb = 0; mb < C::MB; ++mb) *(f32x4*)(acc_row + 16 * mb) = o[mb];
     start = seg_end;
     ++b;
   }
