@@ -29,7 +29,9 @@ METRIC = "decode attn tokens/s and KV-cache GB/s (% HBM peak) at B=16, L=32K, 1 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "latent_decode_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "branch_rank_amd", "csrc", "decode_mfma.hip")
+KERNEL_SRC = {"branch": "branch_rank_amd/csrc/decode_branch.hip",
+              "head_group": "branch_rank_amd/csrc/decode_mfma.hip",
+              "portable": "branch_rank_amd/csrc/kernels_generic.hip"}
 
 
 def log(*a):
@@ -44,6 +46,8 @@ def parse():
     ap.add_argument("--workload", default="mlra4_b16_l32k")
     ap.add_argument("--also", default="mla_b16_l32k",
                     help="comma-separated extra workloads reported beside (empty: none)")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "portable", "head_group", "branch"],
+                    help="split-KV decode kernel (auto: the library's choice)")
     ap.add_argument("--cache-bytes-min", type=float, default=2.0,
                     help="GiB of rotating cache copies (>= 8x the Infinity Cache)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
@@ -64,21 +68,24 @@ def kernel_flops_bytes(w, lens):
     return tokens * row * esz, tokens * w.heads * 2 * (row + w.d_c), tokens
 
 
-def traffic_for(workload):
+def traffic_for(workload, kernel):
     """HBM bytes per decode launch from the committed counter summary, if it
-    was taken on the current kernel source and this workload; else None."""
+    was taken on this workload, this decode kernel and the kernel's current
+    source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-        sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-        if t.get("kernel_sha256") != sha or t.get("workload") != workload:
+        src = KERNEL_SRC[kernel]
+        sha = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
+        if (t.get("kernel_source") != src or t.get("kernel_sha256") != sha
+                or t.get("workload") != workload):
             return None
         return int(t["hbm_bytes_per_launch"])
     except (OSError, ValueError, KeyError):
         return None
 
 
-def run_workload(name, steps, warmup, cache_gib, torch, br, synth):
+def run_workload(name, steps, warmup, cache_gib, torch, br, synth, kernel="auto"):
     w = synth.WORKLOADS[name]
     inp = synth.make_inputs(w, parts=("q_nope", "q_rope", "w_uk", "w_uv"))
     lens = inp["lens"]
@@ -89,13 +96,15 @@ def run_workload(name, steps, warmup, cache_gib, torch, br, synth):
     log(f"[bench] {name}: B={w.batch} tokens={tokens} cache={kv_bytes / 1e6:.1f} MB x {copies} copies")
     lens_dev = torch.from_numpy(lens).cuda()
     cfg = br.make_config(w.heads, w.d_c, w.d_r, w.d_n, w.d_v, n=w.n, sm_scale=w.tau,
-                         alpha_q=w.alpha_q, alpha_kv=w.alpha_kv, theta=w.theta, dtype=w.dtype)
+                         alpha_q=w.alpha_q, alpha_kv=w.alpha_kv, theta=w.theta, dtype=w.dtype,
+                         kernel=kernel)
     views, bufs = [], []
     for i in range(copies):
         buf, _ = synth.make_cache_device(w, seed=w.seed + 7919 * (i + 1), lens=lens)
         bufs.append(buf)
         views.append(br.cache_view(buf[..., :w.d_c], buf[..., w.d_c:], lens_dev, cfg))
     ws = br.alloc_workspace(cfg, w.batch, bufs[0].shape[1])
+    kname = br.select_decode_kernel(cfg, views[0])
     out = torch.empty(w.batch, w.heads, w.d_v, dtype=torch.float32, device="cuda")
 
     def step(i):
@@ -124,6 +133,7 @@ def run_workload(name, steps, warmup, cache_gib, torch, br, synth):
     assert torch.isfinite(out).all().item(), "non-finite output"
     del bufs, views
     return dict(w=w, lens=lens, kv_bytes=kv_bytes, flops=flops, tokens=tokens, copies=copies,
+                kernel=kname,
                 ms_step=ms_step, gpu_ms_step=gpu_ms_step, kernel_ms=k_ms)
 
 
@@ -185,13 +195,16 @@ def main():
     if a.probe_copy:
         probe_copy(torch)
         return
-    main_r = run_workload(a.workload, a.steps, a.warmup, a.cache_bytes_min, torch, br, synth)
+    main_r = run_workload(a.workload, a.steps, a.warmup, a.cache_bytes_min, torch, br, synth,
+                          a.kernel)
     extras = {}
     for name in [x for x in a.also.split(",") if x and x != a.workload]:
-        r = run_workload(name, a.steps, a.warmup, a.cache_bytes_min, torch, br, synth)
+        r = run_workload(name, a.steps, a.warmup, a.cache_bytes_min, torch, br, synth, a.kernel
+                         if a.kernel in ("auto", "portable") else "auto")
         extras[name] = {
             "tokens_per_s": r["w"].batch / (r["ms_step"] / 1e3),
             "ms_per_step": r["ms_step"],
+            "decode_kernel": r["kernel"],
             "decode_kernel_us": r["kernel_ms"] * 1e3,
             "kv_cache_gbs_kernel": r["kv_bytes"] / (r["kernel_ms"] / 1e3) / 1e9,
             "kv_cache_gbs_step": r["kv_bytes"] / (r["ms_step"] / 1e3) / 1e9,
@@ -218,6 +231,7 @@ def main():
                    "heads": w.heads, "d_c": w.d_c, "d_r": w.d_r, "d_nope": w.d_n, "d_v": w.d_v,
                    "branches": w.n, "alpha_q": round(w.alpha_q, 6),
                    "alpha_kv": round(w.alpha_kv, 6), "cache_copies": main_r["copies"],
+                   "decode_kernel": main_r["kernel"],
                    "parallelism": "none (1 GPU)"},
         "kv_cache_gbs": kv_gbs_step,
         "kv_cache_frac_hbm_peak": kv_gbs_step / HBM_PEAK_GBS,
@@ -228,7 +242,7 @@ def main():
         "decode_kernel_mfma_frac": main_r["flops"] / k_s / 1e12 / BF16_PEAK_TFLOPS,
         "roofline": {"bound": "hbm", "achieved": kv_gbs_kernel, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": kv_gbs_kernel / HBM_PEAK_GBS,
-                     "traffic": traffic_for(w.name)},
+                     "traffic": traffic_for(w.name, main_r["kernel"])},
         "also": extras,
     }
     if not a.no_cpu_baseline:

@@ -20,10 +20,13 @@ LIB_PATH = os.environ.get("MLRA_LIB") or os.path.join(_HERE, "libmlra.so")
 MLRA_OK, MLRA_ERR_INVALID_ARG, MLRA_ERR_UNSUPPORTED, MLRA_ERR_WORKSPACE, \
     MLRA_ERR_NO_DEVICE, MLRA_ERR_HIP = range(6)
 MLRA_BF16, MLRA_FP32 = 0, 1
+MLRA_KERNEL_AUTO, MLRA_KERNEL_PORTABLE, MLRA_KERNEL_HEAD_GROUP, MLRA_KERNEL_BRANCH = 0, 1, 2, 3
+KERNELS = {"auto": MLRA_KERNEL_AUTO, "portable": MLRA_KERNEL_PORTABLE,
+           "head_group": MLRA_KERNEL_HEAD_GROUP, "branch": MLRA_KERNEL_BRANCH}
 
 EXPORTS = ("mlra_workspace_size", "mla_absorb_q", "mla_decode_attn", "mla_out_proj",
-           "mlra_decode", "mlra_set_kernel_timing", "mlra_status_string",
-           "mlra_last_error_detail")
+           "mlra_decode", "mlra_select_decode_kernel", "mlra_set_kernel_timing",
+           "mlra_status_string", "mlra_last_error_detail")
 
 
 class MlraError(RuntimeError):
@@ -38,7 +41,8 @@ class Config(ctypes.Structure):
                 ("d_v", ctypes.c_int32), ("num_branches", ctypes.c_int32),
                 ("sm_scale", ctypes.c_float), ("alpha_q", ctypes.c_float),
                 ("alpha_kv", ctypes.c_float), ("rope_theta", ctypes.c_float),
-                ("dtype", ctypes.c_int), ("kv_chunk", ctypes.c_int32)]
+                ("dtype", ctypes.c_int), ("kv_chunk", ctypes.c_int32),
+                ("decode_kernel", ctypes.c_int)]
 
 
 class Cache(ctypes.Structure):
@@ -67,6 +71,7 @@ def lib():
         "mla_decode_attn": [CP, I32, P, KP, P, SZ, P, P],
         "mla_out_proj": [CP, I32, P, P, P, ctypes.c_int, P],
         "mlra_decode": [CP, I32, I32, P, P, P, P, P, KP, P, SZ, P, ctypes.c_int, P],
+        "mlra_select_decode_kernel": [CP, I32, KP, ctypes.POINTER(ctypes.c_int)],
         "mlra_set_kernel_timing": [P, P],
         "mlra_status_string": [ctypes.c_int],
         "mlra_last_error_detail": [],
@@ -95,9 +100,10 @@ def check(st):
 # ------------------------------------------------------------ config ----
 
 def make_config(heads, d_latent, d_rope, d_nope, d_v, n=1, sm_scale=0.0, alpha_q=1.0,
-                alpha_kv=1.0, theta=10000.0, dtype="bf16", kv_chunk=0):
+                alpha_kv=1.0, theta=10000.0, dtype="bf16", kv_chunk=0, kernel="auto"):
+    """kernel: "auto", "portable", "head_group" or "branch" (mlra_kernel_t)."""
     return Config(heads, d_latent, d_rope, d_nope, d_v, n, sm_scale, alpha_q, alpha_kv, theta,
-                  MLRA_BF16 if dtype == "bf16" else MLRA_FP32, kv_chunk)
+                  MLRA_BF16 if dtype == "bf16" else MLRA_FP32, kv_chunk, KERNELS[kernel])
 
 
 def workspace_size(cfg, batch, max_len):
@@ -158,6 +164,15 @@ def cache_view(ckv, krope, cache_lens, cfg):
     c._keep = (ckv, krope, cache_lens)  # keep the tensors alive with the view
     c._batch = B
     return c
+
+
+def select_decode_kernel(cfg, cache):
+    """Name of the decode kernel ("portable", "head_group" or "branch") that
+    the decode calls run for this config and cache view (host-only)."""
+    k = ctypes.c_int(-1)
+    check(lib().mlra_select_decode_kernel(ctypes.byref(cfg), cache._batch, ctypes.byref(cache),
+                                          ctypes.byref(k)))
+    return {v: n for n, v in KERNELS.items()}[k.value]
 
 
 # ------------------------------------------------------------ calls ----

@@ -15,7 +15,12 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmlra.so")
 
-SOURCES = ["mlra_api.cpp", "kernels_generic.hip", "decode_mfma.hip", "proj_mfma.hip"]
+SOURCES = ["mlra_api.cpp", "kernels_generic.hip", "decode_mfma.hip", "decode_branch.hip",
+           "proj_mfma.hip"]
+# The split-KV decode kernels hold no NaN by construction (finite scores, -inf
+# for masked tokens): without NaN semantics their max reductions need no
+# canonicalising moves.
+EXTRA = {"decode_mfma.hip": ["-fno-honor-nans"], "decode_branch.hip": ["-fno-honor-nans"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -29,7 +34,8 @@ FLAGS = [
 
 def _compile(src):
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     return src, obj, r.returncode, r.stdout + r.stderr, cmd
 

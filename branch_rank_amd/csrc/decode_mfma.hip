@@ -34,43 +34,16 @@
 //    x 1 chunk per 16 lanes) and the transposed PV reads (4 rows x 2 chunks per
 //    16 lanes) are free of bank conflicts.
 
-#include "internal.h"
+#include "device_common.h"
 
 namespace mlra {
 namespace {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
-typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
-#define LDS_AS __attribute__((address_space(3)))
+using namespace dev;
 
 constexpr int kT = 32;   // tokens per tile
 constexpr int kDR = 64;  // RoPE width
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescale = 16.f;  // log2 headroom before the running max moves
-
-struct Params {
-  const __bf16* q_abs;
-  const __bf16* ckv;
-  const __bf16* krope;
-  int64_t ckv_bs, kr_bs;
-  int ckv_ts, kr_ts;  // token strides in elements (host checks the byte ranges fit 31 bits)
-  const PlanHeader* hdr;
-  const int32_t* prefix;
-  float* m;
-  float* l;
-  float* acc;
-  int B;
-};
-
-// s_waitcnt vmcnt(N), leaving lgkmcnt/expcnt alone (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Latent-row swizzle (16-byte chunk index XOR per row). Measured on gfx950
 // (rocprofv3 SQ_LDS_BANK_CONFLICT on the two read patterns): for rows of
@@ -85,15 +58,6 @@ __device__ __forceinline__ int swz(int t) {
 }
 // RoPE-row swizzle (128-byte rows): 16 rows of one chunk hit distinct banks.
 __device__ __forceinline__ int swz_r(int t) { return (t >> 1) & 7; }
-
-__device__ __forceinline__ int find_seq(const int32_t* prefix, int B, int pos) {
-  int lo = 0, hi = B;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (prefix[mid] <= pos) lo = mid; else hi = mid;
-  }
-  return lo;
-}
 
 template <int DC, int NB, int NW>
 struct Cfg {
@@ -115,35 +79,6 @@ struct Cfg {
   static_assert(CPR >= 16 && 64 % CPR == 0, "latent width must be 128, 256 or 512");
   static_assert(KPB >= 1 && MPB >= 1, "branch slice must be >= 32 columns");
 };
-
-// Raw buffer descriptor (gfx9 layout: base, stride 0, byte range, word 3)
-// over one sequence's rows [0, rows).
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4 seq_rsrc(const __bf16* base, int rows, int ts) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4 r;  // wave-uniform values, made explicit for the SGPR operands
-  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
-  r.z = __builtin_amdgcn_readfirstlane(rows * ts * 2);
-  r.w = 0x00020000;
-  return r;
-}
-
-// One LDS-DMA instruction: 16 bytes per lane from rsrc + voff + soff into
-// LDS at lds_base + 16 * lane. Issued from asm so that the compiler does not
-// add its own (conservative) vmcnt waits before later LDS reads; every wait
-// for this data is placed by hand (wait_tiles). No output registers.
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_base, uint32_t voff,
-                                      uint32_t soff) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, %3 offen lds"
-      :
-      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(rsrc),
-        "s"(__builtin_amdgcn_readfirstlane(soff))
-      : "memory");
-}
 
 // Row t and logical chunk of the u-th DMA instruction of this wave.
 template <int DC, int NB, int NW>
@@ -232,40 +167,8 @@ struct Sched {
   static_assert(QG * QGK == KPB && PG * PGM == MPB && 2 * QGK <= 8 && PGM <= 8, "schedule");
 };
 
-// Reductions over the four lanes that hold one head (l16 + 16 kg) with the
-// gfx950 lane swaps (VALU, no LDS): permlane16_swap(x, x) gives, per lane,
-// x of this lane and of lane ^ 16; permlane32_swap likewise for lane ^ 32.
-// The lane swaps are issued from asm with both registers as in/out
-// operands: this compiler's permlane*_swap builtins return the first result
-// for both halves of the pair. s_nop 1 on either side covers the VALU ->
-// permlane and permlane -> VALU operand hazards.
-__device__ __forceinline__ void swap16(float x, float& lo, float& hi) {
-  float y = x;
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
-  lo = x;
-  hi = y;
-}
-__device__ __forceinline__ void swap32(float x, float& lo, float& hi) {
-  float y = x;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
-  lo = x;
-  hi = y;
-}
-__device__ __forceinline__ float max4(float x) {
-  float a, b;
-  swap16(x, a, b);
-  swap32(fmaxf(a, b), a, b);
-  return fmaxf(a, b);
-}
-__device__ __forceinline__ float sum4(float x) {
-  float a, b;
-  swap16(x, a, b);
-  swap32(a + b, a, b);
-  return a + b;
-}
-
 template <int DC, int NB, int NW, int NS, int HSPLIT>
-__global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(Params p) {
+__global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(DecodeParams p) {
   using C = Cfg<DC, NB, NW>;
   using SC = Sched<DC, NB>;
   constexpr int H = C::HWG * HSPLIT;
@@ -520,7 +423,7 @@ hipError_t launch_t(const Geom& g, const void* q_abs, const void* ckv, const voi
   constexpr int NS_VM = 2 * C::PER_HI < 64 ? 4 : 3;
   constexpr int NS = NS_LDS < NS_VM ? NS_LDS : NS_VM;
   static_assert(NS >= 2, "tile does not fit LDS");
-  Params p;
+  DecodeParams p;
   p.q_abs = (const __bf16*)q_abs;
   p.ckv = (const __bf16*)ckv;
   p.krope = (const __bf16*)krope;

@@ -1,0 +1,119 @@
+// Device helpers shared by the gfx950 split-KV decode kernels: vector types,
+// hand-placed wait counts, raw buffer descriptors, the LDS-DMA load, the
+// sequence lookup of a token position and the 4-lane reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "internal.h"
+
+namespace mlra {
+namespace dev {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Arguments of the split-KV decode kernels (one struct, passed by value).
+struct DecodeParams {
+  const __bf16* q_abs;
+  const __bf16* ckv;
+  const __bf16* krope;
+  int64_t ckv_bs, kr_bs;
+  int ckv_ts, kr_ts;  // token strides in elements (host checks the byte ranges fit 31 bits)
+  const PlanHeader* hdr;
+  const int32_t* prefix;
+  float* m;
+  float* l;
+  float* acc;
+  int B;
+};
+
+// s_waitcnt vmcnt(N), leaving lgkmcnt/expcnt alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Raw buffer descriptor (gfx9 layout: base, stride 0, byte range, word 3)
+// over one sequence's rows [0, rows).
+__device__ __forceinline__ i32x4 seq_rsrc(const __bf16* base, int rows, int ts) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;  // wave-uniform values, made explicit for the SGPR operands
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
+  r.z = __builtin_amdgcn_readfirstlane(rows * ts * 2);
+  r.w = 0x00020000;
+  return r;
+}
+
+// One LDS-DMA instruction: 16 bytes per lane from rsrc + voff + soff into
+// LDS at lds_base + 16 * lane. Issued from asm so that the compiler does not
+// add its own (conservative) vmcnt waits before later LDS reads; every wait
+// for this data is placed by hand. No output registers.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_base, uint32_t voff,
+                                      uint32_t soff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(rsrc),
+        "s"(__builtin_amdgcn_readfirstlane(soff))
+      : "memory");
+}
+
+// Sequence holding token position pos of the batch-wide token stream.
+__device__ __forceinline__ int find_seq(const int32_t* prefix, int B, int pos) {
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= pos) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Reductions over the four lanes l16 + 16 kg (kg = 0..3) with the gfx950
+// lane swaps (VALU, no LDS): v_permlane16_swap exchanges the odd 16-lane rows
+// of its first operand with the even rows of its second, so with both
+// operands equal to x the pair holds x of this lane and of lane ^ 16;
+// v_permlane32_swap likewise for lane ^ 32. The swaps are issued from asm with
+// both registers as in/out operands: this compiler's permlane*_swap builtins
+// return the first result for both halves of the pair. s_nop 1 on either side
+// covers the VALU -> permlane and permlane -> VALU operand hazards.
+__device__ __forceinline__ void swap16(float x, float& lo, float& hi) {
+  float y = x;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+  lo = x;
+  hi = y;
+}
+__device__ __forceinline__ void swap32(float x, float& lo, float& hi) {
+  float y = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+  lo = x;
+  hi = y;
+}
+__device__ __forceinline__ float max4(float x) {
+  float a, b;
+  swap16(x, a, b);
+  swap32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum4(float x) {
+  float a, b;
+  swap16(x, a, b);
+  swap32(a + b, a, b);
+  return a + b;
+}
+
+}  // namespace dev
+}  // namespace mlra

@@ -63,6 +63,12 @@ hipError_t launch_out_proj_generic(const Geom& g, const float* latent, const T* 
 
 // Fast bf16 MFMA decode. Returns hipErrorNotSupported when the shape has no
 // specialisation (the caller then uses the generic kernel).
+bool decode_branch_supported(const Geom& g);
+int decode_branch_wgs_per_item(const Geom& g);
+hipError_t launch_decode_branch(const Geom& g, const void* q_abs, const void* ckv,
+                                const void* krope, const Workspace& ws, int grid_items,
+                                hipStream_t s);
+
 bool decode_mfma_supported(const Geom& g);
 int decode_mfma_wgs_per_item(const Geom& g);
 hipError_t launch_decode_mfma(const Geom& g, const void* q_abs, const void* ckv,

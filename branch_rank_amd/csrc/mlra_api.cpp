@@ -61,6 +61,8 @@ mlra_status_t check_cfg(const mlra_config_t* c) {
   if (!std::isfinite(c->alpha_q) || !std::isfinite(c->alpha_kv) || !std::isfinite(c->sm_scale))
     return fail(MLRA_ERR_INVALID_ARG, "scales must be finite");
   if (c->kv_chunk < 0) return fail(MLRA_ERR_INVALID_ARG, "kv_chunk must be >= 0");
+  if (c->decode_kernel < MLRA_KERNEL_AUTO || c->decode_kernel > MLRA_KERNEL_BRANCH)
+    return fail(MLRA_ERR_INVALID_ARG, "unknown decode_kernel %d", (int)c->decode_kernel);
   if (c->d_latent > kMaxLatent || c->d_rope > kMaxRope || c->d_nope > kMaxNope ||
       c->num_branches > kMaxBranches || c->num_heads * c->num_branches > kMaxHeadBranch ||
       c->d_v > 4096)
@@ -152,18 +154,6 @@ mlra_status_t current_device(int* dev, int* cus) {
   return MLRA_OK;
 }
 
-enum class DecodePath { Auto, Generic, Mfma };
-
-DecodePath path_override() {
-  static DecodePath p = [] {
-    const char* s = std::getenv("MLRA_DECODE_PATH");
-    if (s && !std::strcmp(s, "generic")) return DecodePath::Generic;
-    if (s && !std::strcmp(s, "mfma")) return DecodePath::Mfma;
-    return DecodePath::Auto;
-  }();
-  return p;
-}
-
 Geom make_geom(const mlra_config_t* c, int32_t batch, const mlra_cache_t* cache) {
   Geom g;
   g.B = batch;
@@ -243,26 +233,41 @@ mlra_status_t run_absorb(const mlra_config_t* c, const Geom& g, const void* q_no
   return MLRA_OK;
 }
 
+// The decode kernel that runs for this configuration and cache view.
+mlra_status_t select_kernel(const mlra_config_t* c, const Geom& g, const mlra_cache_t* k,
+                            mlra_kernel_t* out) {
+  // the MFMA kernels address one sequence's rows through 31-bit buffer offsets
+  const bool mfma_ok = c->dtype == MLRA_BF16 &&
+                       (int64_t)k->max_len * k->ckv_token_stride * 2 < 0x7fffffffLL &&
+                       (int64_t)k->max_len * k->krope_token_stride * 2 < 0x7fffffffLL;
+  const bool branch_ok = mfma_ok && decode_branch_supported(g);
+  const bool group_ok = mfma_ok && decode_mfma_supported(g);
+  mlra_kernel_t kern = c->decode_kernel;
+  if (kern == MLRA_KERNEL_AUTO)
+    kern = branch_ok ? MLRA_KERNEL_BRANCH : group_ok ? MLRA_KERNEL_HEAD_GROUP : MLRA_KERNEL_PORTABLE;
+  if ((kern == MLRA_KERNEL_BRANCH && !branch_ok) || (kern == MLRA_KERNEL_HEAD_GROUP && !group_ok))
+    return fail(MLRA_ERR_UNSUPPORTED, "decode_kernel %d does not support this configuration",
+                (int)kern);
+  *out = kern;
+  return MLRA_OK;
+}
+
 // Plan + split-KV decode into the workspace partials. *fast tells which
-// decode ran: the MFMA kernel (partial acc as [slot][H][d_c]) or the portable
-// one ([slot][d_c][H]); the merge must match.
+// kind of decode ran: an MFMA kernel (partial acc as [slot][H][d_c]) or the
+// portable one ([slot][d_c][H]); the merge must match.
 mlra_status_t run_decode(const mlra_config_t* c, const Geom& g, int cus, const void* q_abs,
                          const mlra_cache_t* k, const Workspace& ws, const Layout& L, bool* fast_out,
                          hipStream_t s) {
   const int64_t imax = L.slots - g.B;
-  bool fast = c->dtype == MLRA_BF16 && decode_mfma_supported(g) &&
-              (int64_t)k->max_len * k->ckv_token_stride * 2 < 0x7fffffffLL &&
-              (int64_t)k->max_len * k->krope_token_stride * 2 < 0x7fffffffLL;
-  const DecodePath over = path_override();
-  if (over == DecodePath::Generic) fast = false;
-  if (over == DecodePath::Mfma && !fast)
-    return fail(MLRA_ERR_UNSUPPORTED, "MLRA_DECODE_PATH=mfma but no MFMA kernel for this shape");
+  mlra_kernel_t kern;
+  TRY(select_kernel(c, g, k, &kern));
   int target;
-  if (fast) {
+  if (kern == MLRA_KERNEL_BRANCH)
+    target = cus / decode_branch_wgs_per_item(g);
+  else if (kern == MLRA_KERNEL_HEAD_GROUP)
     target = cus / decode_mfma_wgs_per_item(g);
-  } else {
+  else
     target = cus * 4 / g.H;
-  }
   if (target < 1) target = 1;
   if (target > kMaxAutoItems) target = kMaxAutoItems;
   if (target > imax && imax > 0) target = (int)imax;
@@ -270,7 +275,9 @@ mlra_status_t run_decode(const mlra_config_t* c, const Geom& g, int cus, const v
   if (imax > 0) {
     if (g_ev_before) TRY_HIP(hipEventRecord(g_ev_before, s), "hipEventRecord");
     hipError_t e;
-    if (fast)
+    if (kern == MLRA_KERNEL_BRANCH)
+      e = launch_decode_branch(g, q_abs, k->ckv, k->krope, ws, (int)imax, s);
+    else if (kern == MLRA_KERNEL_HEAD_GROUP)
       e = launch_decode_mfma(g, q_abs, k->ckv, k->krope, ws, (int)imax, s);
     else if (c->dtype == MLRA_BF16)
       e = launch_decode_generic<__bf16>(g, (const __bf16*)q_abs, (const __bf16*)k->ckv,
@@ -281,7 +288,7 @@ mlra_status_t run_decode(const mlra_config_t* c, const Geom& g, int cus, const v
     TRY_HIP(e, "decode launch");
     if (g_ev_after) TRY_HIP(hipEventRecord(g_ev_after, s), "hipEventRecord");
   }
-  *fast_out = fast;
+  *fast_out = kern != MLRA_KERNEL_PORTABLE;
   return MLRA_OK;
 }
 
@@ -397,6 +404,15 @@ mlra_status_t mla_decode_attn(const mlra_config_t* cfg, int32_t batch, const voi
   bool fast = false;
   TRY(run_decode(cfg, g, cus, q_abs, cache, ws, L, &fast, s));
   return run_merge(g, ws, fast, latent_out, s);
+}
+
+mlra_status_t mlra_select_decode_kernel(const mlra_config_t* cfg, int32_t batch,
+                                        const mlra_cache_t* cache, mlra_kernel_t* kernel) {
+  g_detail.clear();
+  TRY(check_cfg(cfg));
+  TRY(check_cache(cfg, cache, batch));
+  if (!kernel) return fail(MLRA_ERR_INVALID_ARG, "kernel is NULL");
+  return select_kernel(cfg, make_geom(cfg, batch, cache), cache, kernel);
 }
 
 mlra_status_t mla_out_proj(const mlra_config_t* cfg, int32_t batch, const float* latent_out,

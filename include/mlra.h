@@ -64,6 +64,21 @@ typedef enum {
 
 typedef enum { MLRA_BF16 = 0, MLRA_FP32 = 1 } mlra_dtype_t;
 
+/* Which split-KV decode kernel runs (all compute the same partial state;
+ * results agree within the bf16 tolerance). A forced kernel that does not
+ * support the configuration gives MLRA_ERR_UNSUPPORTED at the decode call. */
+typedef enum {
+  MLRA_KERNEL_AUTO = 0,        /* the fastest kernel that supports the shape */
+  MLRA_KERNEL_PORTABLE = 1,    /* scalar FMA kernel: any shape, bf16 and fp32 */
+  MLRA_KERNEL_HEAD_GROUP = 2,  /* bf16 MFMA, 16 heads per wave over all branches:
+                                  d_rope = 64, d_latent in {128, 256, 512},
+                                  d_latent / n >= 32, n in {1, 2, 4},
+                                  heads in {32, 64, 128} */
+  MLRA_KERNEL_BRANCH = 3       /* bf16 MFMA, one 128-wide branch and 32 heads per
+                                  wave: n = 4, d_latent = 512, d_rope = 64,
+                                  heads in {64, 128} */
+} mlra_kernel_t;
+
 typedef struct {
   int32_t num_heads;     /* H >= 1 */
   int32_t d_latent;      /* d_c, total latent width (all branches) */
@@ -77,6 +92,7 @@ typedef struct {
   float rope_theta;      /* RoPE base, e.g. 10000 */
   mlra_dtype_t dtype;
   int32_t kv_chunk;      /* tokens per split-KV work item; 0 = chosen by the library */
+  mlra_kernel_t decode_kernel;  /* MLRA_KERNEL_AUTO unless a kernel is to be forced */
 } mlra_config_t;
 
 /* Strided view of the latent cache. Element strides (not bytes). Row t of
@@ -124,6 +140,14 @@ MLRA_API mlra_status_t mla_absorb_q(const mlra_config_t* cfg, int32_t batch, con
 MLRA_API mlra_status_t mla_decode_attn(const mlra_config_t* cfg, int32_t batch, const void* q_abs,
                               const mlra_cache_t* cache, void* workspace, size_t ws_bytes,
                               float* latent_out, void* stream);
+
+/* The split-KV decode kernel that mla_decode_attn and mlra_decode run for
+ * this configuration, batch and cache view (cfg->decode_kernel resolved).
+ * Host-only; launches nothing and needs no device. Same validation as
+ * mla_decode_attn for cfg and cache; MLRA_ERR_UNSUPPORTED when a forced
+ * kernel does not support the configuration. */
+MLRA_API mlra_status_t mlra_select_decode_kernel(const mlra_config_t* cfg, int32_t batch,
+                                                 const mlra_cache_t* cache, mlra_kernel_t* kernel);
 
 /* Step 3, output up-projection and branch sum ("Multi-Head Low-Rank
  * Attention", 方法步骤详情 step 3 and the sum over branches in 核心方法):

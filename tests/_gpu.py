@@ -18,10 +18,10 @@ def torch_dtype(w):
     return torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
 
-def config_for(w, n=None, kv_chunk=0):
+def config_for(w, n=None, kv_chunk=0, kernel="auto"):
     return br.make_config(w.heads, w.d_c, w.d_r, w.d_n, w.d_v, n=w.n if n is None else n,
                           sm_scale=w.tau, alpha_q=w.alpha_q, alpha_kv=w.alpha_kv,
-                          theta=w.theta, dtype=w.dtype, kv_chunk=kv_chunk)
+                          theta=w.theta, dtype=w.dtype, kv_chunk=kv_chunk, kernel=kernel)
 
 
 class Dev:

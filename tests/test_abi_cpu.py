@@ -34,7 +34,7 @@ def gpu_present():
 def test_library_exports_every_declared_symbol():
     L = br.lib()
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(br.EXPORTS)
@@ -73,6 +73,51 @@ def test_config_validation(kw, status):
     st = br.lib().mlra_workspace_size(ctypes.byref(c), 4, 128, ctypes.byref(out))
     assert st == status
     assert br.lib().mlra_last_error_detail().decode() != ""
+
+
+@pytest.mark.parametrize("value", [-1, 4, 99])
+def test_unknown_decode_kernel_is_invalid(value):
+    c = cfg()
+    c.decode_kernel = value
+    out = ctypes.c_size_t(0)
+    assert br.lib().mlra_workspace_size(ctypes.byref(c), 4, 128, ctypes.byref(out)) == \
+        br.MLRA_ERR_INVALID_ARG
+
+
+def _fake_cache(c, batch, max_len, ts=None):
+    # host-only calls never dereference these (16-byte aligned) addresses
+    ts = c.d_latent + c.d_rope if ts is None else ts
+    k = br.Cache(0x100000, 0x100000 + 2 * c.d_latent, max_len * ts, ts, max_len * ts, ts,
+                 0x200000, max_len)
+    k._batch = batch
+    return k
+
+
+@pytest.mark.parametrize("kw,max_len,kernel,expect", [
+    (dict(), 32768, "auto", "branch"),                            # MLRA-4, d_c = 512, H = 128
+    (dict(heads=64), 4096, "auto", "branch"),
+    (dict(n=1), 4096, "auto", "head_group"),                      # MLA
+    (dict(n=2), 4096, "auto", "head_group"),
+    (dict(n=1, d_latent=128), 4096, "auto", "head_group"),        # one branch shard
+    (dict(), 4096, "head_group", "head_group"),
+    (dict(), 4096, "portable", "portable"),
+    (dict(dtype="fp32"), 4096, "auto", "portable"),
+    (dict(heads=96), 4096, "auto", "portable"),
+    (dict(), 2_000_000, "auto", "portable"),                      # rows beyond 31-bit offsets
+])
+def test_kernel_selection_host_only(kw, max_len, kernel, expect):
+    c = cfg(kernel=kernel, **kw)
+    assert br.select_decode_kernel(c, _fake_cache(c, 2, max_len)) == expect
+
+
+@pytest.mark.parametrize("kw,kernel", [(dict(n=1), "branch"), (dict(heads=96), "branch"),
+                                       (dict(heads=96), "head_group"),
+                                       (dict(dtype="fp32"), "head_group")])
+def test_forced_kernel_outside_its_shapes(kw, kernel):
+    c = cfg(kernel=kernel, **kw)
+    with pytest.raises(br.MlraError) as e:
+        br.select_decode_kernel(c, _fake_cache(c, 2, 4096))
+    assert e.value.status == br.MLRA_ERR_UNSUPPORTED
 
 
 def test_null_config_and_bad_batch():

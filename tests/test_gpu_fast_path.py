@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+import branch_rank_amd as br
 import oracle
 from synth import WORKLOADS, make_inputs
 from tests._gpu import Dev, config_for, host, row_rel_err, say
@@ -57,38 +58,46 @@ def small(w, B=3, L=(300, 1, 77), Lmax=320):
     return w.replace(batch=B), np.array(L, np.int32), Lmax
 
 
-@pytest.mark.parametrize("name,n", [("mla_b16_l4k", 1), ("mlra4_b16_l32k", 2),
-                                    ("mlra4_b16_l32k", 4)])
+# (workload, branches, decode kernel); "auto" picks the branch-per-wave kernel
+# for MLRA-4 at d_c = 512 and the head-group kernel otherwise
+KERNEL_CASES = [("mla_b16_l4k", 1, "auto"), ("mlra4_b16_l32k", 2, "auto"),
+                ("mlra4_b16_l32k", 4, "branch"), ("mlra4_b16_l32k", 4, "head_group"),
+                ("mlra4_b16_l32k", 4, "portable")]
+
+
+@pytest.mark.parametrize("name,n,kernel", KERNEL_CASES)
 @pytest.mark.parametrize("chunk", [0, 32, 100, 4096])
-def test_small_ragged_every_split(name, n, chunk):
+def test_small_ragged_every_split(name, n, kernel, chunk):
     # several tiles, a ragged tail, a one-token sequence; every split size
     base = WORKLOADS[name]
     alphas = pages_alphas(base, n) if n > 1 else {}
     w, lens, Lmax = small(base.replace(n=n, **alphas))
     inp = make_inputs(w, lens=lens, max_len=Lmax)
-    say(f"{name} n={n} chunk={chunk}")
-    got = host(Dev(w, inp).decode(config_for(w, kv_chunk=chunk)))
+    say(f"{name} n={n} kernel={kernel} chunk={chunk}")
+    got = host(Dev(w, inp).decode(config_for(w, kv_chunk=chunk, kernel=kernel)))
     ref = absorbed_oracle(w, inp, np.arange(w.batch))
     err = row_rel_err(got, ref)
     say(f"  rel err {err:.2e}")
     assert err <= TOL
 
 
-def test_empty_sequences_give_zero():
+@pytest.mark.parametrize("kernel", ["branch", "head_group"])
+def test_empty_sequences_give_zero(kernel):
     w = WORKLOADS["mlra4_b16_l32k"].replace(batch=4)
     lens = np.array([0, 64, 0, 33], np.int32)
     inp = make_inputs(w, lens=lens, max_len=64)
-    got = host(Dev(w, inp).decode(config_for(w)))
+    got = host(Dev(w, inp).decode(config_for(w, kernel=kernel)))
     assert np.all(got[0] == 0) and np.all(got[2] == 0)
     assert row_rel_err(got, absorbed_oracle(w, inp, np.arange(4))) <= TOL
 
 
-def test_latent_step_against_oracle_query():
+@pytest.mark.parametrize("kernel", ["branch", "head_group"])
+def test_latent_step_against_oracle_query(kernel):
     # decode step alone, fed the oracle's absorbed query (rounded to bf16)
     w = WORKLOADS["mlra4_b16_l32k"].replace(batch=2)
     inp = make_inputs(w, lens=np.array([1000, 517], np.int32), max_len=1024)
     d = Dev(w, inp)
-    cfg = config_for(w)
+    cfg = config_for(w, kernel=kernel)
     qa = oracle.absorb_q_ref(inp["q_nope"], inp["q_rope"], inp["w_uk"], inp["lens"] - 1, w.tau,
                              w.alpha_q)
     qa_dev = torch.from_numpy(qa.astype(np.float32)).cuda().to(torch.bfloat16)
@@ -97,7 +106,7 @@ def test_latent_step_against_oracle_query():
     # with the query rounding taken out, what remains is P in bf16 and fp32
     # accumulation: well below the end-to-end bar
     err = row_rel_err(host(d.latent(cfg, qa_dev)), lo_ref)
-    say(f"decode step on the oracle's bf16 query: rel err {err:.2e}")
+    say(f"decode step ({kernel}) on the oracle's bf16 query: rel err {err:.2e}")
     assert err <= 5e-3
     # absorbed query itself
     assert row_rel_err(host(d.absorb(cfg)), qa) <= TOL
@@ -120,16 +129,39 @@ def test_shard_sum_equals_four_branch_call():
     assert row_rel_err(total, full) <= TOL
 
 
+@pytest.mark.parametrize("kernel", ["branch", "head_group"])
+def test_sixty_four_heads(kernel):
+    # 64 heads: one workgroup holds every head of a work item
+    w = WORKLOADS["mlra4_b16_l32k"].replace(heads=64)
+    w, lens, Lmax = small(w)
+    inp = make_inputs(w, lens=lens, max_len=Lmax)
+    got = host(Dev(w, inp).decode(config_for(w, kernel=kernel)))
+    err = row_rel_err(got, absorbed_oracle(w, inp, np.arange(w.batch)))
+    say(f"H=64 {kernel}: rel err {err:.2e}")
+    assert err <= TOL
+
+
+def test_forced_kernel_outside_its_shapes_is_unsupported():
+    w = WORKLOADS["mla_b16_l4k"]
+    w, lens, Lmax = small(w)
+    inp = make_inputs(w, lens=lens, max_len=Lmax)
+    with pytest.raises(br.MlraError) as e:
+        Dev(w, inp).decode(config_for(w, kernel="branch"))  # n = 1
+    assert e.value.status == br.MLRA_ERR_UNSUPPORTED
+
+
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["mlra4_b16_l32k", "mla_b16_l32k"])
-def test_headline_b16_l32k_sampled(name):
+@pytest.mark.parametrize("name,kernel", [("mlra4_b16_l32k", "auto"),
+                                         ("mlra4_b16_l32k", "head_group"),
+                                         ("mla_b16_l32k", "auto")])
+def test_headline_b16_l32k_sampled(name, kernel):
     w = WORKLOADS[name]
-    say(f"{name}: inputs")
+    say(f"{name} ({kernel}): inputs")
     inp = make_inputs(w)
     d = Dev(w, inp)
     say("  gpu")
-    got = host(d.decode(config_for(w)))
-    again = host(d.decode(config_for(w)))
+    got = host(d.decode(config_for(w, kernel=kernel)))
+    again = host(d.decode(config_for(w, kernel=kernel)))
     assert np.array_equal(got, again), "not run-to-run deterministic"
     seqs = np.array([0, 5, 15])
     say("  oracle")
