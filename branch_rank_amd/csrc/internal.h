@@ -86,9 +86,6 @@ hipError_t launch_absorb_q_mfma(const Geom& g, const __bf16* q_nope, const __bf1
 hipError_t launch_combine_hc(const Geom& g, const Workspace& ws, float* latent_out,
                              hipStream_t s);
 template <typename TO>
-hipError_t launch_combine_out(const Geom& g, const Workspace& ws, const __bf16* w_uv, TO* out,
-                              float alpha_kv, hipStream_t s);
-template <typename TO>
 hipError_t launch_out_proj_mfma(const Geom& g, const float* latent, const __bf16* w_uv, TO* out,
                                 float alpha_kv, hipStream_t s);
 

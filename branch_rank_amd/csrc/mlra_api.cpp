@@ -464,15 +464,6 @@ mlra_status_t mlra_decode(const mlra_config_t* cfg_in, int32_t num_branches, int
   TRY(run_absorb(&cfg, g, q_nope, q_rope, q_pos, cache->cache_lens, w_uk, ws.q_abs, s));
   bool fast = false;
   TRY(run_decode(&cfg, g, cus, ws.q_abs, cache, ws, L, &fast, s));
-  if (fast && proj_mfma_supported(g)) {  // merge fused into the output projection
-    hipError_t e = out_dtype == MLRA_BF16
-                       ? launch_combine_out<__bf16>(g, ws, (const __bf16*)w_uv, (__bf16*)out,
-                                                    cfg.alpha_kv, s)
-                       : launch_combine_out<float>(g, ws, (const __bf16*)w_uv, (float*)out,
-                                                   cfg.alpha_kv, s);
-    TRY_HIP(e, "combine_out launch");
-    return MLRA_OK;
-  }
   TRY(run_merge(g, ws, fast, ws.latent, s));
   return run_out_proj(&cfg, g, ws.latent, w_uv, out, out_dtype, s);
 }

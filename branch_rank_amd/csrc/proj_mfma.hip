@@ -4,14 +4,13 @@
 //    ("Multi-Head Low-Rank Attention", 方法步骤详情 step 1), one small GEMM per
 //    head (M = sequences, N = d_c, K = d_n) on v_mfma_f32_16x16x32_bf16, plus
 //    the RoPE rotation of the query's rotary part in double precision.
-//  * combine_out   - merge of the split-KV partials per branch (online-softmax
-//    rescaling) fused with the output up-projection and branch sum
+//  * combine_hc    - merge of the split-KV partials per branch (online-softmax
+//    rescaling) into the branch-normalised latent_out [B][H][d_c] fp32.
+//  * out_proj      - output up-projection and branch sum
 //    o[b][h] = alpha_kv W_UV[h]^T concat_j o~_j (方法步骤详情 step 3, 核心方法).
-//    The merged fp32 latent is split into bf16 hi + lo parts so that the MFMA
-//    product keeps fp32 accuracy; W_UV[h] is staged in LDS once and read
-//    transposed with ds_read_b64_tr_b16. With FROM_PARTIALS = false the same
-//    kernel is the plain output projection of a given latent_out.
-//  * combine_hc    - the merge alone, writing latent_out [B][H][d_c] fp32.
+//    The fp32 latent is split into bf16 hi + lo parts so that the MFMA product
+//    keeps fp32 accuracy; W_UV[h] is staged in LDS once and read transposed
+//    with ds_read_b64_tr_b16.
 //
 // Partials come from decode_mfma_kernel: m, l as [slot][n][H] (m in log2
 // units), acc as [slot][H][d_c]; sequence b's slots are k + b for the work
@@ -103,55 +102,85 @@ __global__ __launch_bounds__(256) void absorb_q_mfma(Geom g, const __bf16* __res
   }
 }
 
-// -------------------------------------------------------- merge helpers ----
-
-// Merge weights of sequence b, head h, branch j over its slots: writes
-// M (max, log2 units) and 1/L where L = sum_k 2^(m_k - M) l_k.
-__device__ __forceinline__ void branch_norm(const Workspace& ws, int H, int NB, int b, int h,
-                                            int j, int kf, int kl, float& M, float& Linv) {
-  float mx = -INFINITY;
-  for (int k = kf; k <= kl; ++k) mx = fmaxf(mx, ws.m[((size_t)(k + b) * NB + j) * H + h]);
-  float L = 0.f;
-  for (int k = kf; k <= kl; ++k) {
-    const size_t i = ((size_t)(k + b) * NB + j) * H + h;
-    L += exp2f(ws.m[i] - mx) * ws.l[i];
-  }
-  M = mx;
-  Linv = 1.f / L;
-}
-
-// Four consecutive latent columns c0..c0+3 (one branch) of sequence b, head h.
-__device__ __forceinline__ f32x4 merged4(const Workspace& ws, const PlanHeader& hd, int H,
-                                         int DC, int NB, int b, int h, int c0) {
-  const int p0 = ws.prefix[b], p1 = ws.prefix[b + 1];
-  f32x4 r = {0.f, 0.f, 0.f, 0.f};
-  if (p1 <= p0) return r;
-  const int kf = p0 / hd.chunk, kl = (p1 - 1) / hd.chunk;
-  const int j = c0 / (DC / NB);
-  float M, Linv;
-  branch_norm(ws, H, NB, b, h, j, kf, kl, M, Linv);
-  for (int k = kf; k <= kl; ++k) {
-    const float w = exp2f(ws.m[((size_t)(k + b) * NB + j) * H + h] - M) * Linv;
-    const f32x4 a = *(const f32x4*)(ws.acc + ((size_t)(k + b) * H + h) * DC + c0);
-    r += w * a;
-  }
-  return r;
-}
-
 // ----------------------------------------------------------- combine_hc ----
 
-// grid (B, H); DC/4 threads: latent_out[b][h][:] from the partials
-__global__ __launch_bounds__(128) void combine_hc(Geom g, Workspace ws,
+// Merge of the split-KV partials of sequence b into its branch-normalised
+// latent, o~_j[h] = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k over the
+// slots k of the sequence (textbook online-softmax merge; one softmax per
+// branch, "Multi-Head Low-Rank Attention", 核心方法). grid (B, H / kMH);
+// the weights 2^(m_k - M) / L of (slot, branch, head) are computed once into
+// LDS, kMS slots at a time, then each thread sums 16-byte partial rows.
+constexpr int kMH = 4;    // heads per workgroup
+constexpr int kMS = 64;   // slots per weight table
+constexpr int kMNB = 8;   // most branches
+
+__global__ __launch_bounds__(256) void combine_hc(Geom g, Workspace ws,
                                                   float* __restrict__ latent_out) {
-  const int b = blockIdx.x, h = blockIdx.y;
+  __shared__ float stat[2 * kMNB * kMH];        // M, 1/L per (branch, head)
+  __shared__ float wt[kMS * kMNB * kMH];        // weights of kMS slots
+  const int b = blockIdx.x, h0 = blockIdx.y * kMH, tid = threadIdx.x;
+  const int H = g.H, DC = g.dc, NB = g.n, C4 = g.dc / 4, NP = NB * kMH;
+  const int hn = min(kMH, H - h0);
   const PlanHeader hd = *ws.hdr;
-  for (int c4 = threadIdx.x; c4 < g.dc / 4; c4 += blockDim.x) {
-    const f32x4 r = merged4(ws, hd, g.H, g.dc, g.n, b, h, 4 * c4);
-    *(f32x4*)(latent_out + ((size_t)b * g.H + h) * g.dc + 4 * c4) = r;
+  const int p0 = ws.prefix[b], p1 = ws.prefix[b + 1];
+  float* out = latent_out + ((size_t)b * H + h0) * DC;
+  if (p1 <= p0) {  // empty sequence: o = 0
+    for (int q = tid; q < hn * C4; q += 256) *(f32x4*)(out + 4 * q) = (f32x4){0.f, 0.f, 0.f, 0.f};
+    return;
+  }
+  const int kf = p0 / hd.chunk, kl = (p1 - 1) / hd.chunk;
+  // per (branch, head): the max M and 1/L over the sequence's slots
+  for (int q = tid; q < NP; q += 256) {
+    const int j = q / kMH, hh = q % kMH;
+    if (hh < hn) {
+      const size_t base = (size_t)j * H + h0 + hh;
+      float mx = -INFINITY;
+      for (int k = kf; k <= kl; ++k) mx = fmaxf(mx, ws.m[(size_t)(k + b) * NB * H + base]);
+      float L = 0.f;
+      for (int k = kf; k <= kl; ++k) {
+        const size_t i = (size_t)(k + b) * NB * H + base;
+        L += exp2f(ws.m[i] - mx) * ws.l[i];
+      }
+      stat[2 * q] = mx;
+      stat[2 * q + 1] = 1.f / L;
+    }
+  }
+  // thread -> (head hh, 4 latent columns 4 c4 of branch j)
+  const int per = hn * C4;
+  f32x4 r[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) r[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int k0 = kf; k0 <= kl; k0 += kMS) {
+    const int nk = min(kMS, kl - k0 + 1);
+    __syncthreads();  // stats ready / previous table consumed
+    for (int q = tid; q < nk * NP; q += 256) {
+      const int kk = q / NP, pr = q % NP, j = pr / kMH, hh = pr % kMH;
+      float w = 0.f;
+      if (hh < hn)
+        w = exp2f(ws.m[((size_t)(k0 + kk + b) * NB + j) * H + h0 + hh] - stat[2 * pr]) *
+            stat[2 * pr + 1];
+      wt[q] = w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = tid + 256 * u;
+      if (q < per) {
+        const int hh = q / C4, c4 = q % C4, j = (4 * c4) / (DC / NB);
+        const float* src = ws.acc + ((size_t)(k0 + b) * H + h0 + hh) * DC + 4 * c4;
+        for (int kk = 0; kk < nk; ++kk)
+          r[u] += wt[kk * NP + j * kMH + hh] * *(const f32x4*)(src + (size_t)kk * H * DC);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int q = tid + 256 * u;
+    if (q < per) *(f32x4*)(out + 4 * q) = r[u];
   }
 }
 
-// ---------------------------------------------------------- combine_out ----
+// ------------------------------------------------------------- out_proj ----
 
 // W_UV rows of one v-half staged in LDS: 64 bf16 (128 B) per latent column,
 // padded to 160 B so that the transposed reads (4 rows x 32 B per 16 lanes)
@@ -168,11 +197,10 @@ struct OutLds {
 
 // grid H * 2 (the two v-halves of a head share an XCD); 4 waves, wave w owns
 // output columns [16 w, 16 w + 16) of its half.
-template <int DC, bool FROM_PARTIALS, typename TO>
-__global__ __launch_bounds__(256) void combine_out(Geom g, Workspace ws,
-                                                   const float* __restrict__ latent_in,
-                                                   const __bf16* __restrict__ w_uv,
-                                                   TO* __restrict__ out, float alpha_kv) {
+template <int DC, typename TO>
+__global__ __launch_bounds__(256) void out_proj(Geom g, const float* __restrict__ latent_in,
+                                                const __bf16* __restrict__ w_uv,
+                                                TO* __restrict__ out, float alpha_kv) {
   using LD = OutLds<DC>;
   __shared__ __attribute__((aligned(16))) char smem_raw[LD::TOTAL];
   char LDS_AS* smem = (char LDS_AS*)smem_raw;
@@ -184,8 +212,6 @@ __global__ __launch_bounds__(256) void combine_out(Geom g, Workspace ws,
   if (h >= g.H) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, kg = lane >> 4;
-  PlanHeader hd;
-  if (FROM_PARTIALS) hd = *ws.hdr;
 
   // stage W_UV[h][:, 64 vh .. 64 vh + 64)
   {
@@ -206,10 +232,7 @@ __global__ __launch_bounds__(256) void combine_out(Geom g, Workspace ws,
       const int bb = q / (DC / 4), c4 = q % (DC / 4), b = b0 + bb;
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
       if (b < g.B) {
-        if (FROM_PARTIALS)
-          v = merged4(ws, hd, g.H, DC, g.n, b, h, 4 * c4);
-        else
-          v = *(const f32x4*)(latent_in + ((size_t)b * g.H + h) * DC + 4 * c4);
+        v = *(const f32x4*)(latent_in + ((size_t)b * g.H + h) * DC + 4 * c4);
       }
       __bf16 hi[4], lo[4];
 #pragma unroll
@@ -247,24 +270,12 @@ __global__ __launch_bounds__(256) void combine_out(Geom g, Workspace ws,
   }
 }
 
-template <int DC, bool FP, typename TO>
-hipError_t launch_out_t(const Geom& g, const Workspace& ws, const float* lat, const __bf16* w_uv,
-                        TO* out, float alpha_kv, hipStream_t s) {
+template <int DC, typename TO>
+hipError_t launch_out_t(const Geom& g, const float* lat, const __bf16* w_uv, TO* out,
+                        float alpha_kv, hipStream_t s) {
   const int grid = ((g.H + 7) / 8) * 8 * 2;
-  hipLaunchKernelGGL((combine_out<DC, FP, TO>), dim3(grid), dim3(256), 0, s, g, ws, lat, w_uv,
-                     out, alpha_kv);
+  hipLaunchKernelGGL((out_proj<DC, TO>), dim3(grid), dim3(256), 0, s, g, lat, w_uv, out, alpha_kv);
   return hipGetLastError();
-}
-
-template <bool FP, typename TO>
-hipError_t launch_out_dc(const Geom& g, const Workspace& ws, const float* lat,
-                         const __bf16* w_uv, TO* out, float alpha_kv, hipStream_t s) {
-  switch (g.dc) {
-    case 128: return launch_out_t<128, FP, TO>(g, ws, lat, w_uv, out, alpha_kv, s);
-    case 256: return launch_out_t<256, FP, TO>(g, ws, lat, w_uv, out, alpha_kv, s);
-    case 512: return launch_out_t<512, FP, TO>(g, ws, lat, w_uv, out, alpha_kv, s);
-  }
-  return hipErrorNotSupported;
 }
 
 template <int KSN>
@@ -306,27 +317,23 @@ hipError_t launch_absorb_q_mfma(const Geom& g, const __bf16* q_nope, const __bf1
 
 hipError_t launch_combine_hc(const Geom& g, const Workspace& ws, float* latent_out,
                              hipStream_t s) {
-  hipLaunchKernelGGL(combine_hc, dim3(g.B, g.H), dim3(128), 0, s, g, ws, latent_out);
+  if (g.n > kMNB) return hipErrorNotSupported;
+  hipLaunchKernelGGL(combine_hc, dim3(g.B, (g.H + kMH - 1) / kMH), dim3(256), 0, s, g, ws,
+                     latent_out);
   return hipGetLastError();
-}
-
-template <typename TO>
-hipError_t launch_combine_out(const Geom& g, const Workspace& ws, const __bf16* w_uv, TO* out,
-                              float alpha_kv, hipStream_t s) {
-  return launch_out_dc<true, TO>(g, ws, nullptr, w_uv, out, alpha_kv, s);
 }
 
 template <typename TO>
 hipError_t launch_out_proj_mfma(const Geom& g, const float* latent, const __bf16* w_uv, TO* out,
                                 float alpha_kv, hipStream_t s) {
-  Workspace none{};
-  return launch_out_dc<false, TO>(g, none, latent, w_uv, out, alpha_kv, s);
+  switch (g.dc) {
+    case 128: return launch_out_t<128, TO>(g, latent, w_uv, out, alpha_kv, s);
+    case 256: return launch_out_t<256, TO>(g, latent, w_uv, out, alpha_kv, s);
+    case 512: return launch_out_t<512, TO>(g, latent, w_uv, out, alpha_kv, s);
+  }
+  return hipErrorNotSupported;
 }
 
-template hipError_t launch_combine_out<float>(const Geom&, const Workspace&, const __bf16*,
-                                              float*, float, hipStream_t);
-template hipError_t launch_combine_out<__bf16>(const Geom&, const Workspace&, const __bf16*,
-                                               __bf16*, float, hipStream_t);
 template hipError_t launch_out_proj_mfma<float>(const Geom&, const float*, const __bf16*, float*,
                                                 float, hipStream_t);
 template hipError_t launch_out_proj_mfma<__bf16>(const Geom&, const float*, const __bf16*,
