@@ -62,20 +62,34 @@ __global__ __launch_bounds__(256) void absorb_q_mfma(Geom g, const __bf16* __res
         A[m][ks] = (bf16x8){};
     }
   }
-  // N blocks of 16 latent columns: this half's blocks, spread over the 4 waves
+  // N blocks of 16 latent columns: this half's blocks, spread over the 4
+  // waves, NBW per wave (d_c <= 512); every W_UK fragment of the wave is
+  // loaded before the first MFMA, so the loads overlap
+  constexpr int NBW = 4;
   const int nblk = g.dc / 16, per_half = nblk / 2;
   const __bf16* w = w_uk + (size_t)h * g.dc * dn;
-  for (int nb = half * per_half + wave; nb < (half + 1) * per_half; nb += 4) {
-    const int c = 16 * nb + l16;
-    bf16x8 Bf[KSN];
+  bf16x8 Bf[NBW][KSN];
 #pragma unroll
-    for (int ks = 0; ks < KSN; ++ks) Bf[ks] = *(const bf16x8*)(w + (size_t)c * dn + 32 * ks + 8 * kg);
+  for (int u = 0; u < NBW; ++u) {
+    const int nb = half * per_half + wave + 4 * u;
+    const int c = 16 * nb + l16;
+#pragma unroll
+    for (int ks = 0; ks < KSN; ++ks)
+      Bf[u][ks] = nb < (half + 1) * per_half
+                      ? *(const bf16x8*)(w + (size_t)c * dn + 32 * ks + 8 * kg)
+                      : (bf16x8){};
+  }
+#pragma unroll
+  for (int u = 0; u < NBW; ++u) {
+    const int nb = half * per_half + wave + 4 * u;
+    if (nb >= (half + 1) * per_half) break;
+    const int c = 16 * nb + l16;
 #pragma unroll
     for (int m = 0; m < MBLK; ++m) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KSN; ++ks)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[m][ks], Bf[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[m][ks], Bf[u][ks], acc, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int b = b0 + 16 * m + 4 * kg + i;
@@ -135,8 +149,10 @@ __global__ __launch_bounds__(256) void combine_hc(Geom g, Workspace ws,
     if (hh < hn) {
       const size_t base = (size_t)j * H + h0 + hh;
       float mx = -INFINITY;
+#pragma unroll 8
       for (int k = kf; k <= kl; ++k) mx = fmaxf(mx, ws.m[(size_t)(k + b) * NB * H + base]);
       float L = 0.f;
+#pragma unroll 8
       for (int k = kf; k <= kl; ++k) {
         const size_t i = (size_t)(k + b) * NB * H + base;
         L += exp2f(ws.m[i] - mx) * ws.l[i];
@@ -168,6 +184,7 @@ __global__ __launch_bounds__(256) void combine_hc(Geom g, Workspace ws,
       if (q < per) {
         const int hh = q / C4, c4 = q % C4, j = (4 * c4) / (DC / NB);
         const float* src = ws.acc + ((size_t)(k0 + b) * H + h0 + hh) * DC + 4 * c4;
+#pragma unroll 8
         for (int kk = 0; kk < nk; ++kk)
           r[u] += wt[kk * NP + j * kMH + hh] * *(const f32x4*)(src + (size_t)kk * H * DC);
       }
@@ -213,12 +230,20 @@ __global__ __launch_bounds__(256) void out_proj(Geom g, const float* __restrict_
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, kg = lane >> 4;
 
-  // stage W_UV[h][:, 64 vh .. 64 vh + 64)
+  // stage W_UV[h][:, 64 vh .. 64 vh + 64): all loads of a thread first
   {
     const __bf16* w = w_uv + (size_t)h * DC * g.dv + kDVH * vh;
-    for (int q = tid; q < DC * 8; q += 256) {
-      const int c = q >> 3, ch = q & 7;
-      *(bf16x8 LDS_AS*)(wl + c * kWRow + 16 * ch) = *(const bf16x8*)(w + (size_t)c * g.dv + 8 * ch);
+    constexpr int NQ = DC * 8 / 256;
+    bf16x8 st[NQ];
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int q = tid + 256 * u, c = q >> 3, ch = q & 7;
+      st[u] = *(const bf16x8*)(w + (size_t)c * g.dv + 8 * ch);
+    }
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int q = tid + 256 * u, c = q >> 3, ch = q & 7;
+      *(bf16x8 LDS_AS*)(wl + c * kWRow + 16 * ch) = st[u];
     }
   }
   // per-lane offsets of the transposed W reads (rows 4 r + {0..3}, column quad q)
@@ -299,7 +324,8 @@ bool proj_mfma_supported(const Geom& g) {
 }
 
 bool absorb_mfma_supported(const Geom& g) {
-  return g.dc % 32 == 0 && (g.dn == 64 || g.dn == 128 || g.dn == 256);
+  // <= 4 blocks of 16 columns per wave and half: d_c <= 512
+  return g.dc % 32 == 0 && g.dc <= 512 && (g.dn == 64 || g.dn == 128 || g.dn == 256);
 }
 
 hipError_t launch_absorb_q_mfma(const Geom& g, const __bf16* q_nope, const __bf16* q_rope,
