@@ -117,6 +117,9 @@ def run_workload(name, steps, warmup, cache_gib, torch, br, synth, kernel="auto"
     kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for a, b in kev:  # create the hipEvents outside the timed region
+        a.record()
+        b.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     g0.record()

@@ -251,13 +251,17 @@ def mlra_decode(cfg, num_branches, q_nope, q_rope, w_uk, w_uv, cache, workspace,
 
 
 def set_kernel_timing(before=None, after=None):
-    """Record torch.cuda.Event `before`/`after` around the split-KV decode
-    kernel of later calls on this thread (None, None stops)."""
+    """Have the split-KV decode dispatch of later calls on this thread stamp
+    torch.cuda.Event `before` at its start and `after` at its end (None, None
+    stops). An event whose hipEvent does not exist yet is recorded once here
+    to create it; record the events before a timed region so that this adds
+    nothing to it."""
     if before is None or after is None:
         check(lib().mlra_set_kernel_timing(None, None))
         return
     for e in (before, after):
-        e.record()  # makes sure the underlying hipEvent exists
+        if not e.cuda_event:
+            e.record()  # torch creates the underlying hipEvent on first record
     check(lib().mlra_set_kernel_timing(ctypes.c_void_p(before.cuda_event),
                                        ctypes.c_void_p(after.cuda_event)))
 

@@ -38,6 +38,8 @@
 //    and l rescaled. fp32 and bf16 hold such p with their usual relative
 //    precision.
 
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 
 namespace mlra {
@@ -381,7 +383,7 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
 
 template <int NBR, int NSPLIT, int HPW, int NHG>
 hipError_t launch_b(const Geom& g, const void* q_abs, const void* ckv, const void* krope,
-                    const Workspace& ws, int items, hipStream_t s) {
+                    const Workspace& ws, int items, hipStream_t s, const KernelTiming& t) {
   using C = BCfg<NBR, NSPLIT, HPW, NHG>;
   // a deep ring: up to 7 stages of 20 KB keep up to 6 tiles in flight per CU
   constexpr int NS = (160 * 1024) / C::STAGE < 7 ? (160 * 1024) / C::STAGE : 7;
@@ -402,8 +404,8 @@ hipError_t launch_b(const Geom& g, const void* q_abs, const void* ckv, const voi
   p.B = g.B;
   int grid = items;
   if (NSPLIT > 1) grid = ((items + 7) / 8) * 8 * NSPLIT;  // whole XCD rounds
-  hipLaunchKernelGGL((decode_branch_kernel<NBR, NSPLIT, HPW, NHG, NS>), dim3(grid),
-                     dim3(64 * C::NW), 0, s, p);
+  hipExtLaunchKernelGGL((decode_branch_kernel<NBR, NSPLIT, HPW, NHG, NS>), dim3(grid),
+                        dim3(64 * C::NW), 0, s, t.start, t.stop, 0, p);
   return hipGetLastError();
 }
 
@@ -418,10 +420,10 @@ int decode_branch_wgs_per_item(const Geom&) { return 2; }
 
 hipError_t launch_decode_branch(const Geom& g, const void* q_abs, const void* ckv,
                                 const void* krope, const Workspace& ws, int items,
-                                hipStream_t s) {
+                                hipStream_t s, const KernelTiming& t) {
   if (!decode_branch_supported(g)) return hipErrorNotSupported;
-  if (g.H == 64) return launch_b<4, 2, 16, 4>(g, q_abs, ckv, krope, ws, items, s);
-  return launch_b<4, 2, 32, 4>(g, q_abs, ckv, krope, ws, items, s);
+  if (g.H == 64) return launch_b<4, 2, 16, 4>(g, q_abs, ckv, krope, ws, items, s, t);
+  return launch_b<4, 2, 32, 4>(g, q_abs, ckv, krope, ws, items, s, t);
 }
 
 }  // namespace mlra

@@ -34,6 +34,8 @@
 //    x 1 chunk per 16 lanes) and the transposed PV reads (4 rows x 2 chunks per
 //    16 lanes) are free of bank conflicts.
 
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 
 namespace mlra {
@@ -416,7 +418,8 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(DecodeParams p)
 
 template <int DC, int NB, int NW, int HSPLIT>
 hipError_t launch_t(const Geom& g, const void* q_abs, const void* ckv, const void* krope,
-                    const Workspace& ws, int items, hipStream_t s) {
+                    const Workspace& ws, int items, hipStream_t s,
+                    const KernelTiming& t) {
   using C = Cfg<DC, NB, NW>;
   // as many stages as LDS holds (<= 4) and the 6-bit vmcnt can track
   constexpr int NS_LDS = (160 * 1024) / C::STAGE;
@@ -439,30 +442,32 @@ hipError_t launch_t(const Geom& g, const void* q_abs, const void* ckv, const voi
   p.B = g.B;
   int grid = items;
   if (HSPLIT > 1) grid = ((items + 7) / 8) * 8 * HSPLIT;  // whole XCD rounds
-  hipLaunchKernelGGL((decode_mfma_kernel<DC, NB, NW, NS, HSPLIT>), dim3(grid), dim3(64 * NW), 0,
-                     s, p);
+  hipExtLaunchKernelGGL((decode_mfma_kernel<DC, NB, NW, NS, HSPLIT>), dim3(grid), dim3(64 * NW),
+                        0, s, t.start, t.stop, 0, p);
   return hipGetLastError();
 }
 
 // heads -> (waves per workgroup, head groups per item)
 template <int DC, int NB>
 hipError_t launch_h(const Geom& g, const void* q, const void* c, const void* k,
-                    const Workspace& ws, int items, hipStream_t s) {
+                    const Workspace& ws, int items, hipStream_t s,
+                    const KernelTiming& t) {
   switch (g.H) {
-    case 32: return launch_t<DC, NB, 2, 1>(g, q, c, k, ws, items, s);
-    case 64: return launch_t<DC, NB, 4, 1>(g, q, c, k, ws, items, s);
-    case 128: return launch_t<DC, NB, 4, 2>(g, q, c, k, ws, items, s);
+    case 32: return launch_t<DC, NB, 2, 1>(g, q, c, k, ws, items, s, t);
+    case 64: return launch_t<DC, NB, 4, 1>(g, q, c, k, ws, items, s, t);
+    case 128: return launch_t<DC, NB, 4, 2>(g, q, c, k, ws, items, s, t);
   }
   return hipErrorNotSupported;
 }
 
 template <int DC>
 hipError_t launch_nb(const Geom& g, const void* q, const void* c, const void* k,
-                     const Workspace& ws, int items, hipStream_t s) {
+                     const Workspace& ws, int items, hipStream_t s,
+                     const KernelTiming& t) {
   switch (g.n) {
-    case 1: return launch_h<DC, 1>(g, q, c, k, ws, items, s);
-    case 2: return launch_h<DC, 2>(g, q, c, k, ws, items, s);
-    case 4: return launch_h<DC, 4>(g, q, c, k, ws, items, s);
+    case 1: return launch_h<DC, 1>(g, q, c, k, ws, items, s, t);
+    case 2: return launch_h<DC, 2>(g, q, c, k, ws, items, s, t);
+    case 4: return launch_h<DC, 4>(g, q, c, k, ws, items, s, t);
   }
   return hipErrorNotSupported;
 }
@@ -483,11 +488,11 @@ int decode_mfma_wgs_per_item(const Geom& g) { return g.H == 128 ? 2 : 1; }
 
 hipError_t launch_decode_mfma(const Geom& g, const void* q_abs, const void* ckv,
                               const void* krope, const Workspace& ws, int items,
-                              hipStream_t s) {
+                              hipStream_t s, const KernelTiming& t) {
   switch (g.dc) {
-    case 128: return launch_nb<128>(g, q_abs, ckv, krope, ws, items, s);
-    case 256: return launch_nb<256>(g, q_abs, ckv, krope, ws, items, s);
-    case 512: return launch_nb<512>(g, q_abs, ckv, krope, ws, items, s);
+    case 128: return launch_nb<128>(g, q_abs, ckv, krope, ws, items, s, t);
+    case 256: return launch_nb<256>(g, q_abs, ckv, krope, ws, items, s, t);
+    case 512: return launch_nb<512>(g, q_abs, ckv, krope, ws, items, s, t);
   }
   return hipErrorNotSupported;
 }

@@ -32,6 +32,12 @@ struct Workspace {
   float* latent;    // [B][H][d_c]       (mlra_decode only)
 };
 
+// Optional events stamped by the decode dispatch itself at its start and end
+// (hipExtLaunchKernel), so that timing adds no packets to the stream.
+struct KernelTiming {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
 struct Geom {
   int B, H, dc, dr, dn, dv, n;
   int max_len;
@@ -53,7 +59,8 @@ hipError_t launch_absorb_q_generic(const Geom& g, const T* q_nope, const T* q_ro
 
 template <typename T>
 hipError_t launch_decode_generic(const Geom& g, const T* q_abs, const T* ckv, const T* krope,
-                                 const Workspace& ws, int grid_items, hipStream_t s);
+                                 const Workspace& ws, int grid_items, hipStream_t s,
+                                 const KernelTiming& t);
 
 hipError_t launch_combine(const Geom& g, const Workspace& ws, float* latent_out, hipStream_t s);
 
@@ -67,13 +74,13 @@ bool decode_branch_supported(const Geom& g);
 int decode_branch_wgs_per_item(const Geom& g);
 hipError_t launch_decode_branch(const Geom& g, const void* q_abs, const void* ckv,
                                 const void* krope, const Workspace& ws, int grid_items,
-                                hipStream_t s);
+                                hipStream_t s, const KernelTiming& t);
 
 bool decode_mfma_supported(const Geom& g);
 int decode_mfma_wgs_per_item(const Geom& g);
 hipError_t launch_decode_mfma(const Geom& g, const void* q_abs, const void* ckv,
                               const void* krope, const Workspace& ws, int grid_items,
-                              hipStream_t s);
+                              hipStream_t s, const KernelTiming& t);
 
 // bf16 MFMA projections and the merge for the MFMA decode's partial layout
 // ([slot][H][d_c] acc), see proj_mfma.hip.

@@ -12,6 +12,7 @@
 // The split-KV merge is the standard online-softmax rescaling.
 
 #include <float.h>
+#include <hip/hip_ext.h>
 #include <math.h>
 
 #include "internal.h"
@@ -404,10 +405,11 @@ hipError_t launch_absorb_q_generic(const Geom& g, const T* q_nope, const T* q_ro
 
 template <typename T>
 hipError_t launch_decode_generic(const Geom& g, const T* q_abs, const T* ckv, const T* krope,
-                                 const Workspace& ws, int grid_items, hipStream_t s) {
+                                 const Workspace& ws, int grid_items, hipStream_t s,
+                                 const KernelTiming& t) {
   const size_t sh = sizeof(float) * (g.dc + g.dr + g.n * kTok);
-  hipLaunchKernelGGL(decode_generic<T>, dim3(grid_items, g.H), dim3(256), sh, s, g, q_abs, ckv,
-                     krope, ws);
+  hipExtLaunchKernelGGL(decode_generic<T>, dim3(grid_items, g.H), dim3(256), sh, s, t.start,
+                        t.stop, 0, g, q_abs, ckv, krope, ws);
   return hipGetLastError();
 }
 
@@ -442,10 +444,10 @@ template hipError_t launch_absorb_q_generic<__bf16>(const Geom&, const __bf16*, 
                                                     hipStream_t);
 template hipError_t launch_decode_generic<float>(const Geom&, const float*, const float*,
                                                  const float*, const Workspace&, int,
-                                                 hipStream_t);
+                                                 hipStream_t, const KernelTiming&);
 template hipError_t launch_decode_generic<__bf16>(const Geom&, const __bf16*, const __bf16*,
                                                   const __bf16*, const Workspace&, int,
-                                                  hipStream_t);
+                                                  hipStream_t, const KernelTiming&);
 template hipError_t launch_out_proj_generic<float, float>(const Geom&, const float*,
                                                           const float*, float*, float,
                                                           hipStream_t);

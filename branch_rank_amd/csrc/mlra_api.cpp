@@ -273,20 +273,21 @@ mlra_status_t run_decode(const mlra_config_t* c, const Geom& g, int cus, const v
   if (target > imax && imax > 0) target = (int)imax;
   TRY_HIP(launch_plan(k->cache_lens, g.B, g.max_len, target, c->kv_chunk, ws, s), "plan launch");
   if (imax > 0) {
-    if (g_ev_before) TRY_HIP(hipEventRecord(g_ev_before, s), "hipEventRecord");
+    KernelTiming t;
+    t.start = g_ev_before;
+    t.stop = g_ev_after;
     hipError_t e;
     if (kern == MLRA_KERNEL_BRANCH)
-      e = launch_decode_branch(g, q_abs, k->ckv, k->krope, ws, (int)imax, s);
+      e = launch_decode_branch(g, q_abs, k->ckv, k->krope, ws, (int)imax, s, t);
     else if (kern == MLRA_KERNEL_HEAD_GROUP)
-      e = launch_decode_mfma(g, q_abs, k->ckv, k->krope, ws, (int)imax, s);
+      e = launch_decode_mfma(g, q_abs, k->ckv, k->krope, ws, (int)imax, s, t);
     else if (c->dtype == MLRA_BF16)
       e = launch_decode_generic<__bf16>(g, (const __bf16*)q_abs, (const __bf16*)k->ckv,
-                                        (const __bf16*)k->krope, ws, (int)imax, s);
+                                        (const __bf16*)k->krope, ws, (int)imax, s, t);
     else
       e = launch_decode_generic<float>(g, (const float*)q_abs, (const float*)k->ckv,
-                                       (const float*)k->krope, ws, (int)imax, s);
+                                       (const float*)k->krope, ws, (int)imax, s, t);
     TRY_HIP(e, "decode launch");
-    if (g_ev_after) TRY_HIP(hipEventRecord(g_ev_after, s), "hipEventRecord");
   }
   *fast_out = kern != MLRA_KERNEL_PORTABLE;
   return MLRA_OK;

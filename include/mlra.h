@@ -166,10 +166,12 @@ MLRA_API mlra_status_t mlra_decode(const mlra_config_t* cfg, int32_t num_branche
                           void* workspace, size_t ws_bytes, void* out, mlra_dtype_t out_dtype,
                           void* stream);
 
-/* Instrumentation: when both are non-NULL hipEvent_t handles, every later call
- * made on this thread records `before` immediately before and `after`
- * immediately after the split-KV decode kernel, on the call's stream. Pass
- * NULL, NULL to stop. */
+/* Instrumentation: when both are non-NULL hipEvent_t handles (created by the
+ * caller, owned by the caller, valid until timing is stopped), every later
+ * call made on this thread has the split-KV decode dispatch stamp `before`
+ * when it starts and `after` when it ends (hipExtLaunchKernel), so that
+ * hipEventElapsedTime gives that kernel's duration and the stream carries no
+ * extra packets. Pass NULL, NULL to stop. Giving only one is INVALID_ARG. */
 MLRA_API mlra_status_t mlra_set_kernel_timing(void* before, void* after);
 
 /* Static text for a status code. */
