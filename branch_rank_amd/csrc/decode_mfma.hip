@@ -13,12 +13,12 @@
 //    is less than all heads, the workgroups of one item's head groups are
 //    placed on the same XCD back to back so that the second read of every KV
 //    tile hits that XCD's L2.
-//  * KV tiles (32 tokens) stream HBM -> LDS with global_load_lds_dwordx4 (no
-//    VGPR staging) through an NS-stage ring shared by all waves; vmcnt waits
-//    are placed by hand because the compiler does not order LDS-DMA against
-//    ds_read.
+//  * KV tiles (32 tokens) stream HBM -> LDS with buffer_load_dwordx4 ... lds
+//    (no VGPR staging) through an NS-stage ring shared by all waves; vmcnt
+//    waits are placed by hand because the compiler does not order LDS-DMA
+//    against ds_read.
 //  * QK: S^T[t][h] = sum_d K[t][d] Q[h][d] on v_mfma_f32_16x16x32_bf16 with 16
-//    tokens as M and the wave's 16 heads as N; Q^T stays in VGPRs for the
+//    tokens as M and the wave's 16 heads as N; Q^T stays in AGPRs for the
 //    whole segment. The RoPE part is computed once per tile and shared by all
 //    branches.
 //  * The S^T accumulators (lane = head, 4 token rows per M block) are exactly
