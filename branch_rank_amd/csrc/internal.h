@@ -20,6 +20,16 @@ struct PlanHeader {
   int32_t pad;
 };
 
+// Inputs and outputs of the split-KV plan (plan_device.h).
+struct PlanArgs {
+  const int32_t* lens;  // [B] cache lengths (clamped to [0, max_len])
+  int B, max_len;
+  int target_items;     // wanted number of work items (automatic chunk)
+  int forced_chunk;     // > 0: fixed chunk size in tokens
+  PlanHeader* hdr;      // nullptr: no plan to compute
+  int32_t* prefix;      // [B + 1]
+};
+
 // Partial softmax state per slot: m and l as [slot][n][H] fp32 (m in log2
 // units, i.e. max of score*log2(e)), acc as [slot][d_c][H] fp32 (unnormalised).
 struct Workspace {
@@ -86,10 +96,12 @@ hipError_t launch_decode_mfma(const Geom& g, const void* q_abs, const void* ckv,
 // ([slot][H][d_c] acc), see proj_mfma.hip.
 bool proj_mfma_supported(const Geom& g);   // out projection / fused merge
 bool absorb_mfma_supported(const Geom& g);
+// With plan.hdr set, one extra workgroup of the launch also computes the
+// split-KV plan (as launch_plan would).
 hipError_t launch_absorb_q_mfma(const Geom& g, const __bf16* q_nope, const __bf16* q_rope,
                                 const int32_t* q_pos, const int32_t* lens, const __bf16* w_uk,
                                 __bf16* q_abs, float tau, float alpha_q, float theta,
-                                hipStream_t s);
+                                const PlanArgs& plan, hipStream_t s);
 hipError_t launch_combine_hc(const Geom& g, const Workspace& ws, float* latent_out,
                              hipStream_t s);
 template <typename TO>

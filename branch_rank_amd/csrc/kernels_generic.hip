@@ -16,6 +16,7 @@
 #include <math.h>
 
 #include "internal.h"
+#include "plan_device.h"
 
 namespace mlra {
 
@@ -61,52 +62,7 @@ __device__ float block_sum256(float v, float* red) {
 
 // ---------------------------------------------------------------- plan ----
 
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ lens, int B,
-                                                    int max_len, int target_items,
-                                                    int forced_chunk, PlanHeader* hdr,
-                                                    int32_t* __restrict__ prefix) {
-  __shared__ int32_t wsum[16];
-  __shared__ int32_t carry_s;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  if (tid == 0) carry_s = 0;
-  __syncthreads();
-  for (int base = 0; base < B; base += 1024) {
-    const int i = base + tid;
-    const int v = i < B ? clamp_len(lens[i], max_len) : 0;
-    int x = v;  // inclusive scan within the wave
-    for (int o = 1; o < 64; o <<= 1) {
-      int y = __shfl_up(x, o);
-      if (lane >= o) x += y;
-    }
-    if (lane == 63) wsum[wid] = x;
-    __syncthreads();
-    int before = carry_s;
-    for (int w = 0; w < wid; ++w) before += wsum[w];
-    if (i < B) prefix[i] = before + x - v;
-    __syncthreads();
-    if (tid == 0) {
-      int t = 0;
-      for (int w = 0; w < 16; ++w) t += wsum[w];
-      carry_s += t;
-    }
-    __syncthreads();
-  }
-  if (tid == 0) {
-    const int total = carry_s;
-    prefix[B] = total;
-    int chunk = forced_chunk;
-    if (chunk <= 0) {
-      chunk = (total + target_items - 1) / target_items;
-      if (chunk < kMinChunk) chunk = kMinChunk;
-    }
-    PlanHeader h;
-    h.chunk = chunk;
-    h.n_items = total > 0 ? (total + chunk - 1) / chunk : 0;
-    h.total = total;
-    h.pad = 0;
-    *hdr = h;
-  }
-}
+__global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) { plan_block(a); }
 
 // -------------------------------------------------------------- absorb_q ----
 
@@ -387,8 +343,15 @@ __global__ __launch_bounds__(256) void out_proj_generic(Geom g, const float* __r
 
 hipError_t launch_plan(const int32_t* lens, int B, int max_len, int target_items,
                        int forced_chunk, const Workspace& ws, hipStream_t s) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, lens, B, max_len, target_items,
-                     forced_chunk, ws.hdr, ws.prefix);
+  PlanArgs a;
+  a.lens = lens;
+  a.B = B;
+  a.max_len = max_len;
+  a.target_items = target_items;
+  a.forced_chunk = forced_chunk;
+  a.hdr = ws.hdr;
+  a.prefix = ws.prefix;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 

@@ -212,16 +212,21 @@ mlra_status_t check_ptr(const void* p, const char* name) {
 
 // ---- launches (arguments already validated) ----
 
+// Query absorption. When `plan` is given and the MFMA kernel runs, the split-KV
+// plan rides along in that launch and *plan_done is set.
 mlra_status_t run_absorb(const mlra_config_t* c, const Geom& g, const void* q_nope,
                          const void* q_rope, const int32_t* q_pos, const int32_t* lens,
-                         const void* w_uk, void* q_abs, hipStream_t s) {
+                         const void* w_uk, void* q_abs, hipStream_t s,
+                         const PlanArgs* plan = nullptr, bool* plan_done = nullptr) {
   const float tau = tau_of(c);
   hipError_t e;
-  if (c->dtype == MLRA_BF16 && absorb_mfma_supported(g))
+  if (c->dtype == MLRA_BF16 && absorb_mfma_supported(g)) {
+    PlanArgs none{};
     e = launch_absorb_q_mfma(g, (const __bf16*)q_nope, (const __bf16*)q_rope, q_pos, lens,
                              (const __bf16*)w_uk, (__bf16*)q_abs, tau, c->alpha_q, c->rope_theta,
-                             s);
-  else if (c->dtype == MLRA_BF16)
+                             plan ? *plan : none, s);
+    if (plan && plan_done) *plan_done = true;
+  } else if (c->dtype == MLRA_BF16)
     e = launch_absorb_q_generic<__bf16>(g, (const __bf16*)q_nope, (const __bf16*)q_rope, q_pos,
                                         lens, (const __bf16*)w_uk, (__bf16*)q_abs, tau,
                                         c->alpha_q, c->rope_theta, s);
@@ -252,26 +257,44 @@ mlra_status_t select_kernel(const mlra_config_t* c, const Geom& g, const mlra_ca
   return MLRA_OK;
 }
 
-// Plan + split-KV decode into the workspace partials. *fast tells which
-// kind of decode ran: an MFMA kernel (partial acc as [slot][H][d_c]) or the
-// portable one ([slot][d_c][H]); the merge must match.
-mlra_status_t run_decode(const mlra_config_t* c, const Geom& g, int cus, const void* q_abs,
-                         const mlra_cache_t* k, const Workspace& ws, const Layout& L, bool* fast_out,
-                         hipStream_t s) {
+// The split-KV plan for this decode: kernel choice and work-item target.
+mlra_status_t plan_for(const mlra_config_t* c, const Geom& g, int cus, const mlra_cache_t* k,
+                       const Workspace& ws, const Layout& L, mlra_kernel_t* kern, PlanArgs* a) {
   const int64_t imax = L.slots - g.B;
-  mlra_kernel_t kern;
-  TRY(select_kernel(c, g, k, &kern));
+  TRY(select_kernel(c, g, k, kern));
   int target;
-  if (kern == MLRA_KERNEL_BRANCH)
+  if (*kern == MLRA_KERNEL_BRANCH)
     target = cus / decode_branch_wgs_per_item(g);
-  else if (kern == MLRA_KERNEL_HEAD_GROUP)
+  else if (*kern == MLRA_KERNEL_HEAD_GROUP)
     target = cus / decode_mfma_wgs_per_item(g);
   else
     target = cus * 4 / g.H;
   if (target < 1) target = 1;
   if (target > kMaxAutoItems) target = kMaxAutoItems;
   if (target > imax && imax > 0) target = (int)imax;
-  TRY_HIP(launch_plan(k->cache_lens, g.B, g.max_len, target, c->kv_chunk, ws, s), "plan launch");
+  a->lens = k->cache_lens;
+  a->B = g.B;
+  a->max_len = g.max_len;
+  a->target_items = target;
+  a->forced_chunk = c->kv_chunk;
+  a->hdr = ws.hdr;
+  a->prefix = ws.prefix;
+  return MLRA_OK;
+}
+
+// Split-KV decode into the workspace partials, after the plan (launched here
+// unless plan_done). *fast tells which kind of decode ran: an MFMA kernel
+// (partial acc as [slot][H][d_c]) or the portable one ([slot][d_c][H]); the
+// merge must match.
+mlra_status_t run_decode(const mlra_config_t* c, const Geom& g, const void* q_abs,
+                         const mlra_cache_t* k, const Workspace& ws, const Layout& L,
+                         mlra_kernel_t kern, const PlanArgs& plan, bool plan_done, bool* fast_out,
+                         hipStream_t s) {
+  const int64_t imax = L.slots - g.B;
+  if (!plan_done)
+    TRY_HIP(launch_plan(plan.lens, plan.B, plan.max_len, plan.target_items, plan.forced_chunk, ws,
+                        s),
+            "plan launch");
   if (imax > 0) {
     KernelTiming t;
     t.start = g_ev_before;
@@ -402,8 +425,11 @@ mlra_status_t mla_decode_attn(const mlra_config_t* cfg, int32_t batch, const voi
   const Geom g = make_geom(cfg, batch, cache);
   const Workspace ws = carve(L, workspace);
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  mlra_kernel_t kern;
+  PlanArgs plan;
+  TRY(plan_for(cfg, g, cus, cache, ws, L, &kern, &plan));
   bool fast = false;
-  TRY(run_decode(cfg, g, cus, q_abs, cache, ws, L, &fast, s));
+  TRY(run_decode(cfg, g, q_abs, cache, ws, L, kern, plan, false, &fast, s));
   return run_merge(g, ws, fast, latent_out, s);
 }
 
@@ -462,9 +488,14 @@ mlra_status_t mlra_decode(const mlra_config_t* cfg_in, int32_t num_branches, int
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const Geom g = make_geom(&cfg, batch, cache);
   const Workspace ws = carve(L, workspace);
-  TRY(run_absorb(&cfg, g, q_nope, q_rope, q_pos, cache->cache_lens, w_uk, ws.q_abs, s));
+  mlra_kernel_t kern;
+  PlanArgs plan;
+  TRY(plan_for(&cfg, g, cus, cache, ws, L, &kern, &plan));
+  bool plan_done = false;
+  TRY(run_absorb(&cfg, g, q_nope, q_rope, q_pos, cache->cache_lens, w_uk, ws.q_abs, s, &plan,
+                 &plan_done));
   bool fast = false;
-  TRY(run_decode(&cfg, g, cus, ws.q_abs, cache, ws, L, &fast, s));
+  TRY(run_decode(&cfg, g, ws.q_abs, cache, ws, L, kern, plan, plan_done, &fast, s));
   TRY(run_merge(g, ws, fast, ws.latent, s));
   return run_out_proj(&cfg, g, ws.latent, w_uv, out, out_dtype, s);
 }

@@ -19,6 +19,7 @@
 #include <math.h>
 
 #include "internal.h"
+#include "plan_device.h"
 
 namespace mlra {
 namespace {
@@ -35,7 +36,8 @@ __device__ __forceinline__ int clamp_len(int v, int max_len) {
 
 // ------------------------------------------------------------- absorb_q ----
 
-// grid (H, ceil(B / (16 MBLK)), 2 halves of d_c); 4 waves
+// grid (H (+1 when the plan rides along), ceil(B / (16 MBLK)), 2 halves of
+// d_c); 4 waves
 template <int KSN, int MBLK>
 __global__ __launch_bounds__(256) void absorb_q_mfma(Geom g, const __bf16* __restrict__ q_nope,
                                                      const __bf16* __restrict__ q_rope,
@@ -43,7 +45,11 @@ __global__ __launch_bounds__(256) void absorb_q_mfma(Geom g, const __bf16* __res
                                                      const int32_t* __restrict__ lens,
                                                      const __bf16* __restrict__ w_uk,
                                                      __bf16* __restrict__ q_abs, float scale,
-                                                     float tau, float theta) {
+                                                     float tau, float theta, PlanArgs plan) {
+  if (blockIdx.x == g.H) {  // the extra column of workgroups: plan (first one only)
+    if (blockIdx.y == 0 && blockIdx.z == 0) plan_block(plan);
+    return;
+  }
   const int h = blockIdx.x, b0 = blockIdx.y * 16 * MBLK, half = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, kg = lane >> 4;
@@ -306,13 +312,14 @@ hipError_t launch_out_t(const Geom& g, const float* lat, const __bf16* w_uv, TO*
 template <int KSN>
 hipError_t launch_absorb_k(const Geom& g, const __bf16* qn, const __bf16* qr, const int32_t* qp,
                            const int32_t* lens, const __bf16* w, __bf16* qa, float scale,
-                           float tau, float theta, hipStream_t s) {
+                           float tau, float theta, const PlanArgs& plan, hipStream_t s) {
+  const int gx = g.H + (plan.hdr ? 1 : 0);
   if (g.B > 32) {
-    hipLaunchKernelGGL((absorb_q_mfma<KSN, 4>), dim3(g.H, (g.B + 63) / 64, 2), dim3(256), 0, s,
-                       g, qn, qr, qp, lens, w, qa, scale, tau, theta);
+    hipLaunchKernelGGL((absorb_q_mfma<KSN, 4>), dim3(gx, (g.B + 63) / 64, 2), dim3(256), 0, s,
+                       g, qn, qr, qp, lens, w, qa, scale, tau, theta, plan);
   } else {
-    hipLaunchKernelGGL((absorb_q_mfma<KSN, 1>), dim3(g.H, (g.B + 15) / 16, 2), dim3(256), 0, s,
-                       g, qn, qr, qp, lens, w, qa, scale, tau, theta);
+    hipLaunchKernelGGL((absorb_q_mfma<KSN, 1>), dim3(gx, (g.B + 15) / 16, 2), dim3(256), 0, s,
+                       g, qn, qr, qp, lens, w, qa, scale, tau, theta, plan);
   }
   return hipGetLastError();
 }
@@ -331,12 +338,12 @@ bool absorb_mfma_supported(const Geom& g) {
 hipError_t launch_absorb_q_mfma(const Geom& g, const __bf16* q_nope, const __bf16* q_rope,
                                 const int32_t* q_pos, const int32_t* lens, const __bf16* w_uk,
                                 __bf16* q_abs, float tau, float alpha_q, float theta,
-                                hipStream_t s) {
+                                const PlanArgs& plan, hipStream_t s) {
   const float scale = alpha_q * tau;
   switch (g.dn) {
-    case 64: return launch_absorb_k<2>(g, q_nope, q_rope, q_pos, lens, w_uk, q_abs, scale, tau, theta, s);
-    case 128: return launch_absorb_k<4>(g, q_nope, q_rope, q_pos, lens, w_uk, q_abs, scale, tau, theta, s);
-    case 256: return launch_absorb_k<8>(g, q_nope, q_rope, q_pos, lens, w_uk, q_abs, scale, tau, theta, s);
+    case 64: return launch_absorb_k<2>(g, q_nope, q_rope, q_pos, lens, w_uk, q_abs, scale, tau, theta, plan, s);
+    case 128: return launch_absorb_k<4>(g, q_nope, q_rope, q_pos, lens, w_uk, q_abs, scale, tau, theta, plan, s);
+    case 256: return launch_absorb_k<8>(g, q_nope, q_rope, q_pos, lens, w_uk, q_abs, scale, tau, theta, plan, s);
   }
   return hipErrorNotSupported;
 }
