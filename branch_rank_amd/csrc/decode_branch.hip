@@ -21,11 +21,18 @@
 //  * A workgroup has NBW x NHG waves: wave (b, g) owns branch hg*NBW + b for
 //    the HPW heads of head group g. Its registers hold Q for those heads over
 //    the branch slice plus the RoPE part and O over the slice, small enough
-//    for two waves per SIMD, so one wave's softmax overlaps the other's MFMAs.
+//    for two waves per SIMD.
+//  * Every tile runs in two phases between workgroup barriers: a matrix phase
+//    (PV of the previous tile, QK of this one) and a vector phase (softmax,
+//    V^T fragments into registers). Waves w and w + NW/2 share a SIMD and the
+//    second group runs one phase behind the first, so on every SIMD one
+//    wave's MFMAs run beside the other wave's softmax instead of both waves
+//    doing the same kind of work at once.
 //  * 32-token tiles stream HBM -> LDS with buffer_load_dwordx4 ... lds (no
 //    VGPR staging): one instruction per two 512-byte latent half-rows and per
 //    eight 128-byte RoPE rows, shared by all waves, through an NS-stage ring
-//    (20 KB per stage, so several tiles are in flight per CU). LDS rows are
+//    (20 KB per stage, so several tiles are in flight per CU); a stage is
+//    reloaded once the lagging group's vector phase has read it. LDS rows are
 //    XOR-swizzled in 16-byte chunks (chunk ^ 2*(row & 15) for latent rows,
 //    measured free of bank conflicts for both read patterns below).
 //  * QK: S^T[t][h] on v_mfma_f32_16x16x32_bf16, 16 tokens as M, 16 heads as N;
@@ -39,6 +46,8 @@
 //    precision.
 
 #include <hip/hip_ext.h>
+
+#include <type_traits>
 
 #include "device_common.h"
 
@@ -133,7 +142,7 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
   constexpr int H = C::H;
   constexpr int DC = C::DC;
   constexpr int D = NS - 1;  // tiles issued ahead of the one in use
-  static_assert(D >= 1 && D <= 6, "tile ring");
+  static_assert(D >= 2 && D <= 6, "tile ring");
   __shared__ __attribute__((aligned(1024))) char smem_raw[NS * C::STAGE];
   char LDS_AS* smem = (char LDS_AS*)smem_raw;
   const uint32_t sbase = (uint32_t)(uintptr_t)smem;
@@ -157,6 +166,7 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
   const int j = hg * C::NBW + b;     // branch of this wave
   const int l16 = lane & 15, kg = lane >> 4;
   const int head0 = g * HPW;         // first head of this wave
+  const bool lag = wave >= C::NW / 2;  // second group: one phase behind
 
   // Per-lane LDS byte offsets within a stage. QK A operand: token row
   // 16 mb + l16 (+ 16 rows for mb = 1), branch columns 32 ks + 8 kg .. +7.
@@ -257,37 +267,85 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) bias[mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    int cur_off = 0;  // stage of tile it
-    for (int it = 0; it < ntiles; ++it) {
-      wait_tiles<C, D - 1>(min(D - 1, ntiles - 1 - it), wave);
+    // Two phases per tile, each between two workgroup barriers: the matrix
+    // phase M(t) (PV of tile t - 1, then QK of tile t) and the vector phase
+    // V(t) (softmax of tile t, V^T fragments of tile t into registers). The
+    // waves w and w + NW/2 share a SIMD; the second group runs one phase
+    // behind the first, so on every SIMD one wave's MFMAs run beside the
+    // other wave's softmax.
+    f32x4 S[2][C::NBLK];   // scores of the tile between M(t) and V(t)
+    bf16x8 P[C::NBLK];     // P^T of tile t, from V(t) to M(t + 1)
+    bf16x8 V[C::CB];       // V^T of tile t, from V(t) to M(t + 1)
+    int m_off = 0, v_off = 0;  // stages of the tiles the next M and V phases read
+
+    // a phase boundary: no instruction is scheduled across it (the phases
+    // exist to keep MFMA and VALU work apart), and no LDS access moves over it
+    auto bar = [] {
+      __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_barrier();
-      // the stage of tile it + D last held tile it - 1, which every wave has
-      // finished before this barrier
-      if (it + D < ntiles) issue(it + D);
-      const char LDS_AS* st = smem + __builtin_amdgcn_readfirstlane(cur_off);
-      cur_off = next_stage(cur_off);
-      const int valid = t1 - (t0 + it * kT);
-      if (valid < kT) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto wait_tile = [&](int t) { wait_tiles<C, NS - 2>(min(NS - 2, ntiles - 1 - t), wave); };
+    auto issue_if = [&](int t) {
+      if (t < ntiles) issue(t);
+    };
+
+    auto mphase = [&](int t, auto pv_tag, auto qk_tag) {
+      constexpr bool PV = decltype(pv_tag)::value, QK = decltype(qk_tag)::value;
+      bf16x8 A[2][C::KS];
+      if constexpr (QK) {
+        const char LDS_AS* st = smem + __builtin_amdgcn_readfirstlane(m_off);
+        m_off = next_stage(m_off);
+        const int valid = t1 - (t0 + t * kT);
+        if (valid < kT) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bias[mb][e] = 16 * mb + 4 * kg + e < valid ? 0.f : -INFINITY;
+        }
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+          for (int ks = 0; ks < C::KL; ++ks)
+            A[mb][ks] = *(const bf16x8 LDS_AS*)((const char LDS_AS*)(((uintptr_t)(st + qk_lat)) ^ (64 * ks)) +
+                                                mb * 16 * C::ROWB);
+          A[mb][C::KL] = *(const bf16x8 LDS_AS*)(st + qk_rp + mb * 2048);
+          A[mb][C::KL + 1] =
+              *(const bf16x8 LDS_AS*)((const char LDS_AS*)(((uintptr_t)(st + qk_rp)) ^ 64) + mb * 2048);
+        }
+      }
+      if constexpr (PV) {
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+          for (int nb = 0; nb < C::NBLK; ++nb)
+            o[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(V[cb], P[nb], o[cb][nb], 0, 0, 0);
+      }
+      if constexpr (QK) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) bias[mb][e] = 16 * mb + 4 * kg + e < valid ? 0.f : -INFINITY;
+          for (int nb = 0; nb < C::NBLK; ++nb) {
+            S[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][0], q[0][nb], bias[mb], 0, 0, 0);
+#pragma unroll
+            for (int ks = 1; ks < C::KS; ++ks)
+              S[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][ks], q[ks][nb], S[mb][nb],
+                                                                  0, 0, 0);
+          }
       }
+    };
 
-      // ---- LDS fragments: K for the scores, V^T for PV (read now, used after
-      // the softmax, so their latency hides behind the QK MFMAs)
-      bf16x8 A[2][C::KS];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int ks = 0; ks < C::KL; ++ks)
-          A[mb][ks] = *(const bf16x8 LDS_AS*)((const char LDS_AS*)(((uintptr_t)(st + qk_lat)) ^ (64 * ks)) +
-                                              mb * 16 * C::ROWB);
-        A[mb][C::KL] = *(const bf16x8 LDS_AS*)(st + qk_rp + mb * 2048);
-        A[mb][C::KL + 1] =
-            *(const bf16x8 LDS_AS*)((const char LDS_AS*)(((uintptr_t)(st + qk_rp)) ^ 64) + mb * 2048);
-      }
-      bf16x8 V[C::CB];
+    // V(t): this branch's online softmax of S, per 16-head block. P is taken
+    // against the running reference m_run without a tile max: a per-lane sum
+    // of P above kSumLimit (or inf: no reference yet, or an overflow) means
+    // some score passed the reference by more than 2^16, and only then
+    // (rare) the exact tile max moves the reference, O and l are rescaled and
+    // P is recomputed. Otherwise every p stays below 2^20. O holds the tiles
+    // before t here (PV of tile t - 1 ran in M(t)).
+    auto vphase = [&]() {
+      const char LDS_AS* st = smem + __builtin_amdgcn_readfirstlane(v_off);
+      v_off = next_stage(v_off);
 #pragma unroll
       for (int cb = 0; cb < C::CB; ++cb) {
         const char LDS_AS* a = (const char LDS_AS*)(((uintptr_t)(st + pv_lat)) ^ (32 * cb));
@@ -296,27 +354,6 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
         const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         V[cb] = __builtin_bit_cast(bf16x8, v);
       }
-
-      // ---- scores S^T = K Q^T over the branch slice and the RoPE part
-      f32x4 S[2][C::NBLK];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < C::NBLK; ++nb) {
-          S[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][0], q[0][nb], bias[mb], 0, 0, 0);
-#pragma unroll
-          for (int ks = 1; ks < C::KS; ++ks)
-            S[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][ks], q[ks][nb], S[mb][nb],
-                                                                0, 0, 0);
-        }
-
-      // ---- this branch's online softmax, per 16-head block. P is taken
-      // against the running reference m_run without a tile max: a per-lane
-      // sum of P above kSumLimit (or inf: no reference yet, or an overflow)
-      // means some score passed the reference by more than 2^16, and only
-      // then (rare) the exact tile max moves the reference, O and l are
-      // rescaled and P is recomputed. Otherwise every p stays below 2^20.
-      bf16x8 P[C::NBLK];
       float ps[C::NBLK];
       bool need = false;
       auto probs = [&](int nb) {
@@ -353,13 +390,55 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
       }
 #pragma unroll
       for (int nb = 0; nb < C::NBLK; ++nb) l_run[nb] += ps[nb];
+    };
 
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int cb = 0; cb < C::CB; ++cb)
-#pragma unroll
-        for (int nb = 0; nb < C::NBLK; ++nb)
-          o[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(V[cb], P[nb], o[cb][nb], 0, 0, 0);
+    using T_ = std::integral_constant<bool, true>;
+    using F_ = std::integral_constant<bool, false>;
+    // Barriers: b(2t + 1) opens M(t) of the first group, b(2t + 2) its V(t);
+    // the second group's M(t) and V(t) start one barrier later. Tile t is in
+    // LDS (every wave waited for its own loads) before b(2t + 1); its stage
+    // is read for the last time in the second group's V(t), which ends at
+    // b(2t + 4), after which tile t + NS (same stage) is loaded: tile
+    // u + NS - 1 is issued right after b(2u + 2), at the start of V(u) in the
+    // first group and of M(u) in the second. Both groups pass 2 ntiles + 2
+    // barriers per segment.
+    if (!lag) {
+      wait_tile(0);
+      bar();
+      mphase(0, F_{}, T_{});
+      bar();
+      issue_if(D);
+      vphase();
+      for (int t = 1; t < ntiles; ++t) {
+        wait_tile(t);
+        bar();
+        mphase(t, T_{}, T_{});
+        bar();
+        issue_if(t + D);
+        vphase();
+      }
+      bar();
+      mphase(ntiles, T_{}, F_{});
+      bar();
+    } else {
+      wait_tile(0);
+      bar();
+      bar();
+      issue_if(D);
+      mphase(0, F_{}, T_{});
+      if (1 < ntiles) wait_tile(1);
+      bar();
+      vphase();
+      bar();
+      for (int t = 1; t < ntiles; ++t) {
+        issue_if(t + D);
+        mphase(t, T_{}, T_{});
+        if (t + 1 < ntiles) wait_tile(t + 1);
+        bar();
+        vphase();
+        bar();
+      }
+      mphase(ntiles, T_{}, F_{});
     }
 
     // partial state of this segment: m, l as [slot][n][H]; acc as
