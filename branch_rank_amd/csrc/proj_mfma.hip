@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void absorb_q_mfma(Geom g, const __bf16* __res
     if (blockIdx.y == 0 && blockIdx.z == 0) plan_block(plan);
     return;
   }
-  const int h = blockIdx.x, b0 = blockIdx.y * 16 * MBLK, half = blockIdx.z;
+  const int h = blockIdx.x, b0 = blockIdx.y * 16 * MBLK, part = blockIdx.z, parts = gridDim.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, kg = lane >> 4;
   const int row = g.dc + g.dr;
@@ -68,27 +68,28 @@ __global__ __launch_bounds__(256) void absorb_q_mfma(Geom g, const __bf16* __res
         A[m][ks] = (bf16x8){};
     }
   }
-  // N blocks of 16 latent columns: this half's blocks, spread over the 4
-  // waves, NBW per wave (d_c <= 512); every W_UK fragment of the wave is
-  // loaded before the first MFMA, so the loads overlap
+  // N blocks of 16 latent columns: this part's blocks (of `parts` equal
+  // parts), spread over the 4 waves, at most NBW per wave (d_c <= 512 with 2
+  // parts); every W_UK fragment of the wave is loaded before the first MFMA,
+  // so the loads overlap
   constexpr int NBW = 4;
-  const int nblk = g.dc / 16, per_half = nblk / 2;
+  const int nblk = g.dc / 16, per_part = nblk / parts;
   const __bf16* w = w_uk + (size_t)h * g.dc * dn;
   bf16x8 Bf[NBW][KSN];
 #pragma unroll
   for (int u = 0; u < NBW; ++u) {
-    const int nb = half * per_half + wave + 4 * u;
+    const int nb = part * per_part + wave + 4 * u;
     const int c = 16 * nb + l16;
 #pragma unroll
     for (int ks = 0; ks < KSN; ++ks)
-      Bf[u][ks] = nb < (half + 1) * per_half
+      Bf[u][ks] = nb < (part + 1) * per_part
                       ? *(const bf16x8*)(w + (size_t)c * dn + 32 * ks + 8 * kg)
                       : (bf16x8){};
   }
 #pragma unroll
   for (int u = 0; u < NBW; ++u) {
-    const int nb = half * per_half + wave + 4 * u;
-    if (nb >= (half + 1) * per_half) break;
+    const int nb = part * per_part + wave + 4 * u;
+    if (nb >= (part + 1) * per_part) break;
     const int c = 16 * nb + l16;
 #pragma unroll
     for (int m = 0; m < MBLK; ++m) {
@@ -103,22 +104,22 @@ __global__ __launch_bounds__(256) void absorb_q_mfma(Geom g, const __bf16* __res
       }
     }
   }
-  // RoPE on the query's rotary part (angle in double precision): half 0 only
-  if (half == 0) {
-    const int hp = g.dr / 2;
-    for (int i = threadIdx.x; i < 16 * MBLK * hp; i += 256) {
-      const int b = b0 + i / hp, k = i % hp;
-      if (b >= g.B) continue;
-      const int p = q_pos ? q_pos[b] : clamp_len(lens[b], g.max_len) - 1;
-      const double omega = pow((double)theta, -2.0 * (double)k / (double)g.dr);
-      double sn, cs;
-      sincos((double)p * omega, &sn, &cs);
-      const size_t qi = ((size_t)b * g.H + h) * g.dr + 2 * k;
-      const double x0 = (float)q_rope[qi], x1 = (float)q_rope[qi + 1];
-      __bf16* o = q_abs + ((size_t)b * g.H + h) * row + g.dc + 2 * k;
-      o[0] = (__bf16)(float)(tau * (x0 * cs - x1 * sn));
-      o[1] = (__bf16)(float)(tau * (x0 * sn + x1 * cs));
-    }
+
+  // RoPE on the query's rotary part (angle in double precision), its
+  // (sequence, pair) elements spread over the parts' threads
+  const int hp = g.dr / 2;
+  for (int i = threadIdx.x + 256 * part; i < 16 * MBLK * hp; i += 256 * parts) {
+    const int b = b0 + i / hp, k = i % hp;
+    if (b >= g.B) continue;
+    const int p = q_pos ? q_pos[b] : clamp_len(lens[b], g.max_len) - 1;
+    const double omega = pow((double)theta, -2.0 * (double)k / (double)g.dr);
+    double sn, cs;
+    sincos((double)p * omega, &sn, &cs);
+    const size_t qi = ((size_t)b * g.H + h) * g.dr + 2 * k;
+    const double x0 = (float)q_rope[qi], x1 = (float)q_rope[qi + 1];
+    __bf16* o = q_abs + ((size_t)b * g.H + h) * row + g.dc + 2 * k;
+    o[0] = (__bf16)(float)(tau * (x0 * cs - x1 * sn));
+    o[1] = (__bf16)(float)(tau * (x0 * sn + x1 * cs));
   }
 }
 
@@ -314,12 +315,22 @@ hipError_t launch_absorb_k(const Geom& g, const __bf16* qn, const __bf16* qr, co
                            const int32_t* lens, const __bf16* w, __bf16* qa, float scale,
                            float tau, float theta, const PlanArgs& plan, hipStream_t s) {
   const int gx = g.H + (plan.hdr ? 1 : 0);
+  // latent column parts per head: the most (<= 8) that split the 16-column
+  // blocks evenly, so that more workgroups share the W_UK read (1032 at
+  // H = 128, d_c = 512)
+  const int nblk = g.dc / 16;
+  int parts = 2;
+  for (int p = 8; p > 2; p >>= 1)
+    if (nblk % p == 0) {
+      parts = p;
+      break;
+    }
   if (g.B > 32) {
-    hipLaunchKernelGGL((absorb_q_mfma<KSN, 4>), dim3(gx, (g.B + 63) / 64, 2), dim3(256), 0, s,
-                       g, qn, qr, qp, lens, w, qa, scale, tau, theta, plan);
+    hipLaunchKernelGGL((absorb_q_mfma<KSN, 4>), dim3(gx, (g.B + 63) / 64, parts), dim3(256), 0,
+                       s, g, qn, qr, qp, lens, w, qa, scale, tau, theta, plan);
   } else {
-    hipLaunchKernelGGL((absorb_q_mfma<KSN, 1>), dim3(gx, (g.B + 15) / 16, 2), dim3(256), 0, s,
-                       g, qn, qr, qp, lens, w, qa, scale, tau, theta, plan);
+    hipLaunchKernelGGL((absorb_q_mfma<KSN, 1>), dim3(gx, (g.B + 15) / 16, parts), dim3(256), 0,
+                       s, g, qn, qr, qp, lens, w, qa, scale, tau, theta, plan);
   }
   return hipGetLastError();
 }
