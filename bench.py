@@ -51,6 +51,8 @@ def parse():
                     help="split-KV decode kernel (auto: the library's choice)")
     ap.add_argument("--cache-bytes-min", type=float, default=2.0,
                     help="GiB of rotating cache copies (>= 8x the Infinity Cache)")
+    ap.add_argument("--no-shards", action="store_true",
+                    help="skip the per-device tensor-parallel shard comparison")
     ap.add_argument("--time-every", type=int, default=4,
                     help="stamp the decode dispatch's start/end events on every N-th timed step")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
@@ -223,6 +225,26 @@ def main():
             "kv_cache_gbs_kernel": r["kv_bytes"] / (r["kernel_ms"] / 1e3) / 1e9,
             "kv_cache_gbs_step": r["kv_bytes"] / (r["ms_step"] / 1e3) / 1e9,
         }
+    shards = None
+    if not a.no_shards:
+        shards = {}
+        for tag in ("l32k", "l128k"):
+            pair = {}
+            for scheme, name in (("mla_tp4", f"mla_tp4_b16_{tag}"),
+                                 ("mlra4_branch_shard", f"mlra4_shard_b16_{tag}")):
+                r = run_workload(name, a.steps, a.warmup, a.cache_bytes_min, torch, br, synth,
+                                 "auto", a.time_every)
+                pair[scheme] = {"workload": name, "heads": r["w"].heads,
+                                "row_bytes": (r["w"].d_c + r["w"].d_r) * 2,
+                                "kv_bytes": r["kv_bytes"], "ms_per_step": r["ms_step"],
+                                "decode_kernel": r["kernel"],
+                                "decode_kernel_us": r["kernel_ms"] * 1e3,
+                                "kv_cache_gbs_kernel": r["kv_bytes"] / (r["kernel_ms"] / 1e3) / 1e9}
+            m, s_ = pair["mla_tp4"], pair["mlra4_branch_shard"]
+            pair["byte_ratio"] = m["kv_bytes"] / s_["kv_bytes"]
+            pair["step_time_ratio"] = m["ms_per_step"] / s_["ms_per_step"]
+            pair["kernel_time_ratio"] = m["decode_kernel_us"] / s_["decode_kernel_us"]
+            shards[tag] = pair
     w = main_r["w"]
     ms = main_r["ms_step"]
     k_s = main_r["kernel_ms"] / 1e3
@@ -259,6 +281,7 @@ def main():
                      "unit": "GB/s", "frac": kv_gbs_kernel / HBM_PEAK_GBS,
                      "traffic": traffic_for(w.name, main_r["kernel"])},
         "also": extras,
+        "shard_compare": shards,
     }
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)

@@ -101,6 +101,20 @@ WORKLOADS = {
     "shard_b64_ragged": Workload("shard_b64_ragged", 64, 128, 128, 64, 128, 128, 1,
                                  65536, ragged_min=1024, alpha_q=_AQ4, alpha_kv=_AKV4,
                                  w_std=1.0 / math.sqrt(512), seed=1005),
+    # one GPU's share of 4-way tensor parallelism, per scheme: MLA splits heads
+    # (32 of 128) but every device streams the full 576-wide rows; MLRA-4
+    # splits branches (one 128-wide latent slice + the RoPE key, 192-wide
+    # rows, all 128 heads). B=16 at L=32768 and L=131072
+    "mla_tp4_b16_l32k": Workload("mla_tp4_b16_l32k", 16, 32, 512, 64, 128, 128, 1, 32768,
+                                 seed=1006),
+    "mlra4_shard_b16_l32k": Workload("mlra4_shard_b16_l32k", 16, 128, 128, 64, 128, 128, 1,
+                                     32768, alpha_q=_AQ4, alpha_kv=_AKV4,
+                                     w_std=1.0 / math.sqrt(512), seed=1006),
+    "mla_tp4_b16_l128k": Workload("mla_tp4_b16_l128k", 16, 32, 512, 64, 128, 128, 1, 131072,
+                                  seed=1007),
+    "mlra4_shard_b16_l128k": Workload("mlra4_shard_b16_l128k", 16, 128, 128, 64, 128, 128, 1,
+                                      131072, alpha_q=_AQ4, alpha_kv=_AKV4,
+                                      w_std=1.0 / math.sqrt(512), seed=1007),
 }
 
 

@@ -199,6 +199,24 @@ def test_shard_b64_ragged_sampled():
     assert err <= TOL
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["mla_tp4_b16_l32k", "mlra4_shard_b16_l32k"])
+def test_tensor_parallel_shards_sampled(name):
+    # one device's share under 4-way tensor parallelism: MLA with 32 heads over
+    # 576-wide rows, one MLRA-4 branch with 128 heads over 192-wide rows
+    w = WORKLOADS[name]
+    say(f"{name}: inputs")
+    inp = make_inputs(w)
+    got = host(Dev(w, inp).decode(config_for(w)))
+    seqs = np.array([0, 9, 15])
+    say("  oracle")
+    err = row_rel_err(got[seqs], absorbed_oracle(w, inp, seqs))
+    say(f"  rel err {err:.2e}")
+    assert err <= TOL
+    rows = [(3, 0), (12, w.heads - 1)]
+    assert row_rel_err(np.stack([got[b, h] for b, h in rows]), unabsorbed_rows(w, inp, rows)) <= TOL
+
+
 @pytest.mark.parametrize("batch", [16, 64, 3])
 def test_out_proj_step_bf16(batch):
     # output projection alone on the oracle's fp32 latent: the fp32 latent is
