@@ -153,6 +153,30 @@ def run_workload(name, steps, warmup, cache_gib, torch, br, synth, kernel="auto"
                 ms_step=ms_step, gpu_ms_step=gpu_ms_step, kernel_ms=k_ms)
 
 
+def time_cache_append(w, steps, warmup, torch, br):
+    """Mean time of one mlra_cache_append call (one token per sequence) at the
+    workload's shape, on a cache with room: the step before each decode."""
+    L = steps + warmup + 1
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    buf = torch.zeros(w.batch, L, w.d_c + w.d_r, dtype=dt, device="cuda")
+    lens = torch.zeros(w.batch, dtype=torch.int32, device="cuda")
+    rows = torch.randn(w.batch, w.d_c + w.d_r, dtype=torch.float32, device="cuda")
+    cfg = br.make_config(w.heads, w.d_c, w.d_r, w.d_n, w.d_v, n=w.n, sm_scale=w.tau,
+                         alpha_q=w.alpha_q, alpha_kv=w.alpha_kv, theta=w.theta, dtype=w.dtype)
+    ckv, kr = buf[..., :w.d_c], buf[..., w.d_c:]
+    for _ in range(warmup):
+        br.cache_append(cfg, rows, ckv, kr, lens)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        br.cache_append(cfg, rows, ckv, kr, lens)
+    e1.record()
+    torch.cuda.synchronize()
+    assert int(lens.min().item()) == steps + warmup
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
 def cpu_baseline(w, seconds):
     """The float64 oracle (unabsorbed definition) on host cores, one sequence
     at a time of the same workload recipe until `seconds` have elapsed."""
@@ -225,6 +249,7 @@ def main():
             "kv_cache_gbs_kernel": r["kv_bytes"] / (r["kernel_ms"] / 1e3) / 1e9,
             "kv_cache_gbs_step": r["kv_bytes"] / (r["ms_step"] / 1e3) / 1e9,
         }
+    append_us = time_cache_append(main_r["w"], a.steps, a.warmup, torch, br)
     shards = None
     if not a.no_shards:
         shards = {}
@@ -280,6 +305,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": kv_gbs_kernel, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": kv_gbs_kernel / HBM_PEAK_GBS,
                      "traffic": traffic_for(w.name, main_r["kernel"])},
+        "cache_append_us": append_us,
         "also": extras,
         "shard_compare": shards,
     }

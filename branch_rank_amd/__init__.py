@@ -25,8 +25,8 @@ KERNELS = {"auto": MLRA_KERNEL_AUTO, "portable": MLRA_KERNEL_PORTABLE,
            "head_group": MLRA_KERNEL_HEAD_GROUP, "branch": MLRA_KERNEL_BRANCH}
 
 EXPORTS = ("mlra_workspace_size", "mla_absorb_q", "mla_decode_attn", "mla_out_proj",
-           "mlra_decode", "mlra_select_decode_kernel", "mlra_set_kernel_timing",
-           "mlra_status_string", "mlra_last_error_detail")
+           "mlra_decode", "mlra_select_decode_kernel", "mlra_cache_append",
+           "mlra_set_kernel_timing", "mlra_status_string", "mlra_last_error_detail")
 
 
 class MlraError(RuntimeError):
@@ -72,6 +72,8 @@ def lib():
         "mla_out_proj": [CP, I32, P, P, P, ctypes.c_int, P],
         "mlra_decode": [CP, I32, I32, P, P, P, P, P, KP, P, SZ, P, ctypes.c_int, P],
         "mlra_select_decode_kernel": [CP, I32, KP, ctypes.POINTER(ctypes.c_int)],
+        "mlra_cache_append": [CP, I32, P, P, ctypes.c_float, P, P, ctypes.c_int64,
+                              ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, I32, P],
         "mlra_set_kernel_timing": [P, P],
         "mlra_status_string": [ctypes.c_int],
         "mlra_last_error_detail": [],
@@ -164,6 +166,28 @@ def cache_view(ckv, krope, cache_lens, cfg):
     c._keep = (ckv, krope, cache_lens)  # keep the tensors alive with the view
     c._batch = B
     return c
+
+
+def cache_append(cfg, new_rows, ckv, krope, cache_lens, gain=None, eps=1e-6, stream=None):
+    """Append one token per sequence: new_rows [B, d_c + d_r] fp32 (latent,
+    then the unrotated RoPE key) go to row L_b of ckv [B, L_max, d_c] and
+    krope [B, L_max, d_r] (RMS-normalised latent, rotated key, cache dtype),
+    and cache_lens [B] int32 is incremented in place (mlra_cache_append)."""
+    t = _torch()
+    B, Lmax, dc = ckv.shape
+    if dc != cfg.d_latent or tuple(krope.shape) != (B, Lmax, cfg.d_rope):
+        raise ValueError("cache shapes do not match the config")
+    for x, name in ((ckv, "ckv"), (krope, "krope")):
+        if x.dtype != _dtype(cfg) or not x.is_cuda:
+            raise ValueError(f"{name}: wrong dtype or device")
+        if x.stride(2) != 1 and x.shape[2] > 1:
+            raise ValueError(f"{name}: last dimension must be dense")
+    rows = _need(new_rows, "new_rows", (B, cfg.d_latent + cfg.d_rope), t.float32)
+    g = _need(gain, "gain", (cfg.d_latent,), t.float32) if gain is not None else None
+    lens = _need(cache_lens, "cache_lens", (B,), t.int32)
+    check(lib().mlra_cache_append(ctypes.byref(cfg), B, rows, g, float(eps), ckv.data_ptr(),
+                                  krope.data_ptr(), ckv.stride(0), ckv.stride(1),
+                                  krope.stride(0), krope.stride(1), lens, Lmax, _stream(stream)))
 
 
 def select_decode_kernel(cfg, cache):

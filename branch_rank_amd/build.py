@@ -16,7 +16,7 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmlra.so")
 
 SOURCES = ["mlra_api.cpp", "kernels_generic.hip", "decode_mfma.hip", "decode_branch.hip",
-           "proj_mfma.hip"]
+           "proj_mfma.hip", "cache_append.hip"]
 # The split-KV decode kernels hold no NaN by construction (finite scores, -inf
 # for masked tokens): without NaN semantics their max reductions need no
 # canonicalising moves.

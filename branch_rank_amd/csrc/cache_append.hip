@@ -1,0 +1,76 @@
+// Appending one decoded token per sequence to the latent KV cache, the step
+// that precedes the decode attention.
+//
+// What it computes ("vllbc02MLA", 猛猿大佬思路: the projected row is split into
+// the compressed latent and the decoupled RoPE key, the latent is
+// RMS-normalised, the RoPE key is rotated by the token's position;
+// "从MHA到MLA" 3.2: the cache is updated by writing the new latent at that
+// position; "MLA多头潜在注意力机制" 3: only the latent and the RoPE key are
+// cached): for sequence b with L_b tokens, row L_b of the cache receives
+// [RMSNorm(c) * gain || RoPE(k^R, L_b)] in the cache dtype and L_b becomes
+// L_b + 1. A sequence already holding max_len tokens is left unchanged.
+//
+// One workgroup per sequence; the bytes are a few KB per step, so this is a
+// latency-bound kernel, not a streaming one.
+
+#include <math.h>
+
+#include "internal.h"
+
+namespace mlra {
+namespace {
+
+__device__ __forceinline__ void store_as(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_as(__bf16* p, float v) { *p = (__bf16)v; }
+
+template <typename T>
+__global__ __launch_bounds__(256) void cache_append_kernel(AppendArgs a) {
+  __shared__ float red[4];
+  __shared__ int pos_s;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (tid == 0) pos_s = max(a.lens[b], 0);
+  __syncthreads();
+  const int p = pos_s;  // position of the new token
+  if (p >= a.max_len) return;  // no room: the sequence stays as it is
+
+  const float* row = a.rows + (int64_t)b * (a.d_c + a.d_r);
+  // mean of squares over the latent (fp32, two-level tree)
+  float ss = 0.f;
+  for (int i = tid; i < a.d_c; i += 256) ss = fmaf(row[i], row[i], ss);
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  if (lane == 0) red[wid] = ss;
+  __syncthreads();
+  const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)a.d_c + a.eps);
+
+  T* c = (T*)a.ckv + (int64_t)b * a.ckv_bs + (int64_t)p * a.ckv_ts;
+  for (int i = tid; i < a.d_c; i += 256) {
+    const float g = a.gain ? a.gain[i] : 1.f;
+    store_as(c + i, row[i] * inv * g);
+  }
+  // RoPE key rotated to position p (angle in double precision)
+  T* k = (T*)a.krope + (int64_t)b * a.kr_bs + (int64_t)p * a.kr_ts;
+  const float* kr = row + a.d_c;
+  for (int i = tid; i < a.d_r / 2; i += 256) {
+    const double omega = pow((double)a.theta, -2.0 * (double)i / (double)a.d_r);
+    double sn, cs;
+    sincos((double)p * omega, &sn, &cs);
+    const double x0 = kr[2 * i], x1 = kr[2 * i + 1];
+    store_as(k + 2 * i, (float)(x0 * cs - x1 * sn));
+    store_as(k + 2 * i + 1, (float)(x0 * sn + x1 * cs));
+  }
+  __syncthreads();  // pos_s was read by every thread before the length moves
+  if (tid == 0) a.lens[b] = p + 1;
+}
+
+}  // namespace
+
+hipError_t launch_cache_append(const AppendArgs& a, bool bf16, int batch, hipStream_t s) {
+  if (batch <= 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(cache_append_kernel<__bf16>, dim3(batch), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(cache_append_kernel<float>, dim3(batch), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mlra

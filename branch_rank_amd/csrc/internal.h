@@ -20,6 +20,21 @@ struct PlanHeader {
   int32_t pad;
 };
 
+// Arguments of the cache append (cache_append.hip): rows [B][d_c + d_r] fp32
+// (latent, then the unrotated RoPE key), written to row L_b of each sequence.
+struct AppendArgs {
+  const float* rows;
+  const float* gain;   // [d_c] or nullptr (1)
+  void* ckv;
+  void* krope;
+  int64_t ckv_bs, ckv_ts, kr_bs, kr_ts;  // element strides
+  int32_t* lens;
+  int max_len, d_c, d_r;
+  float eps, theta;
+};
+
+hipError_t launch_cache_append(const AppendArgs& a, bool bf16, int batch, hipStream_t s);
+
 // Inputs and outputs of the split-KV plan (plan_device.h).
 struct PlanArgs {
   const int32_t* lens;  // [B] cache lengths (clamped to [0, max_len])

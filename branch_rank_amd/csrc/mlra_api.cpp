@@ -433,6 +433,44 @@ mlra_status_t mla_decode_attn(const mlra_config_t* cfg, int32_t batch, const voi
   return run_merge(g, ws, fast, latent_out, s);
 }
 
+mlra_status_t mlra_cache_append(const mlra_config_t* cfg, int32_t batch, const float* new_rows,
+                                const float* gain, float eps, void* ckv, void* krope,
+                                int64_t ckv_batch_stride, int64_t ckv_token_stride,
+                                int64_t krope_batch_stride, int64_t krope_token_stride,
+                                int32_t* cache_lens, int32_t max_len, void* stream) {
+  g_detail.clear();
+  TRY(check_cfg(cfg));
+  TRY(check_batch(batch, max_len));
+  if (batch == 0 || max_len == 0) return MLRA_OK;
+  if (!new_rows || !cache_lens || !ckv || (cfg->d_rope > 0 && !krope))
+    return fail(MLRA_ERR_INVALID_ARG, "new_rows, cache_lens and the cache pointers must be set");
+  if (!std::isfinite(eps) || eps < 0.f) return fail(MLRA_ERR_INVALID_ARG, "eps must be >= 0");
+  if (ckv_token_stride < cfg->d_latent || ckv_batch_stride < 0 ||
+      (cfg->d_rope > 0 && (krope_token_stride < cfg->d_rope || krope_batch_stride < 0)))
+    return fail(MLRA_ERR_INVALID_ARG,
+                "cache strides: token stride >= the row width, batch stride >= 0");
+  int dev, cus;
+  TRY(current_device(&dev, &cus));
+  AppendArgs a;
+  a.rows = new_rows;
+  a.gain = gain;
+  a.ckv = ckv;
+  a.krope = krope;
+  a.ckv_bs = ckv_batch_stride;
+  a.ckv_ts = ckv_token_stride;
+  a.kr_bs = krope_batch_stride;
+  a.kr_ts = krope_token_stride;
+  a.lens = cache_lens;
+  a.max_len = max_len;
+  a.d_c = cfg->d_latent;
+  a.d_r = cfg->d_rope;
+  a.eps = eps;
+  a.theta = cfg->rope_theta;
+  TRY_HIP(launch_cache_append(a, cfg->dtype == MLRA_BF16, batch, static_cast<hipStream_t>(stream)),
+          "cache_append launch");
+  return MLRA_OK;
+}
+
 mlra_status_t mlra_select_decode_kernel(const mlra_config_t* cfg, int32_t batch,
                                         const mlra_cache_t* cache, mlra_kernel_t* kernel) {
   g_detail.clear();

@@ -166,6 +166,39 @@ MLRA_API mlra_status_t mlra_decode(const mlra_config_t* cfg, int32_t num_branche
                           void* workspace, size_t ws_bytes, void* out, mlra_dtype_t out_dtype,
                           void* stream);
 
+/* The step before the decode: append one token per sequence to the latent
+ * cache ("vllbc02MLA", 猛猿大佬思路: the projected row splits into the
+ * compressed latent, which is RMS-normalised, and the decoupled RoPE key,
+ * rotated by the token's position; "从MHA到MLA" 3.2: the new latent is written
+ * at that position; "MLA多头潜在注意力机制" 3: only these two are cached).
+ *
+ *   new_rows   device [batch][d_latent + d_rope] fp32, row-major: the new
+ *              token's latent c (pre-normalisation) then its RoPE key k^R
+ *              (unrotated), as produced by the model's down-projection.
+ *   gain       device [d_latent] fp32 RMSNorm weight, or NULL for all ones.
+ *   eps        RMSNorm epsilon (> 0 or 0; DeepSeek uses 1e-6).
+ *   ckv, krope device cache buffers of cfg->dtype, written through the same
+ *              element strides as mlra_cache_t (krope unused when d_rope = 0).
+ *   cache_lens device [batch] int32, read and updated in place.
+ *   max_len    rows each sequence can hold.
+ *
+ * For each sequence b with p = max(L_b, 0) < max_len: row p of the latent
+ * cache gets c / sqrt(mean(c^2) + eps) * gain, row p of the RoPE cache gets
+ * RoPE(k^R, p) (pairs (2i, 2i+1), angle p * theta^(-2i/d_rope), angle in
+ * double precision), both rounded to the cache dtype (bf16: RNE), then L_b
+ * becomes p + 1. A sequence with L_b >= max_len is left unchanged, since that
+ * cannot be reported without a synchronisation. The next decode call's
+ * query then sits at position p, the new token. Sizes, pointer and stride
+ * checks as for the decode: INVALID_ARG on a NULL pointer or a negative
+ * size or stride, UNSUPPORTED for sizes beyond the decode's limits. Enqueued
+ * on `stream`; nothing is allocated. */
+MLRA_API mlra_status_t mlra_cache_append(const mlra_config_t* cfg, int32_t batch,
+                                         const float* new_rows, const float* gain, float eps,
+                                         void* ckv, void* krope, int64_t ckv_batch_stride,
+                                         int64_t ckv_token_stride, int64_t krope_batch_stride,
+                                         int64_t krope_token_stride, int32_t* cache_lens,
+                                         int32_t max_len, void* stream);
+
 /* Instrumentation: when both are non-NULL hipEvent_t handles (created by the
  * caller, owned by the caller, valid until timing is stopped), every later
  * call made on this thread has the split-KV decode dispatch stamp `before`

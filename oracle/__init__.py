@@ -32,4 +32,6 @@ from .mlra_ref import (  # noqa: F401
     merge_partials,
     kv_elems_per_token_per_device,
     variance_scales,
+    rms_norm,
+    cache_append_ref,
 )

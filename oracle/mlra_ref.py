@@ -306,3 +306,56 @@ def variance_scales(d, d_c, n):
     if d_c % n:
         raise ValueError("d_c must be a multiple of n")
     return math.sqrt(d / (d_c // n)), math.sqrt(d / d_c)
+
+
+def rms_norm(x, gain=None, eps=1e-6):
+    """RMS normalisation of each row: x / sqrt(mean(x^2) + eps), times ``gain``.
+
+    Page: "vllbc02MLA", 猛猿大佬思路 (code walk-through): the compressed KV
+    latent passes through an RMSNorm (``kv_a_layernorm`` over kv_lora_rank)
+    before it is cached. Pinned by unit RMS of the output, invariance under
+    a positive rescaling of the input, and an elementwise gain.
+    """
+    x = _f64(x)
+    r = np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    y = x / r
+    return y if gain is None else y * _f64(gain)
+
+
+def cache_append_ref(ckv, krope, lens, new_c, new_kr, max_len, gain=None, eps=1e-6,
+                     theta=10000.0, round_to=None):
+    """Append one token per sequence to the latent cache.
+
+    Pages: "vllbc02MLA", 猛猿大佬思路 (the projected row is split into the
+    latent and the RoPE key; the latent is RMS-normalised; the RoPE key is
+    rotated by the token's position and comes from the input, not from the
+    latent); "从MHA到MLA" 3.2 (the cache is updated by writing the new latent
+    at the token's position); "MLA多头潜在注意力机制" 3 (only the latent and
+    the decoupled RoPE key are cached).
+
+    Sequence b's new token sits at position p = L_b (0-based), so row p gets
+    [RMSNorm(new_c[b]) * gain || RoPE(new_kr[b], p)] and L_b becomes L_b + 1.
+    A sequence with L_b >= max_len is left unchanged (no room). ``round_to``
+    (a function) rounds the written values to the cache's storage type.
+    Returns new (ckv, krope, lens) arrays; the inputs are not modified.
+    Pinned by the RMS and rotation properties of the written row, untouched
+    rows and full sequences, and decode after append against the decode of
+    a cache built with the row in place.
+    """
+    ckv = _f64(ckv).copy()
+    krope = _f64(krope).copy()
+    lens = np.asarray(lens, dtype=np.int64).copy()
+    new_c, new_kr = _f64(new_c), _f64(new_kr)
+    for b in range(len(lens)):
+        p = int(lens[b])
+        if p >= max_len:
+            continue
+        c = rms_norm(new_c[b], gain, eps)
+        k = rope(new_kr[b], p, theta)
+        if round_to is not None:
+            c, k = _f64(round_to(c)), _f64(round_to(k))
+        ckv[b, p] = c
+        krope[b, p] = k
+        lens[b] = p + 1
+    return ckv, krope, lens.astype(np.int32)
+

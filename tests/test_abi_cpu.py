@@ -34,7 +34,7 @@ def gpu_present():
 def test_library_exports_every_declared_symbol():
     L = br.lib()
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(br.EXPORTS)
@@ -174,9 +174,35 @@ def test_other_entry_points_validate():
     assert L.mlra_set_kernel_timing(None, None) == br.MLRA_OK
 
 
+def append(c, rows=FAKE, gain=None, eps=1e-6, ckv=FAKE, kr=FAKE, ts=576, kts=576, lens=FAKE,
+           B=4, max_len=128):
+    return br.lib().mlra_cache_append(ctypes.byref(c), B, rows, gain, eps, ckv, kr, 128 * 576, ts,
+                                      128 * 576, kts, lens, max_len, None)
+
+
+def test_cache_append_validation():
+    c = cfg()
+    assert append(c, rows=0) == br.MLRA_ERR_INVALID_ARG
+    assert append(c, lens=0) == br.MLRA_ERR_INVALID_ARG
+    assert append(c, ckv=0) == br.MLRA_ERR_INVALID_ARG
+    assert append(c, kr=0) == br.MLRA_ERR_INVALID_ARG
+    assert append(c, eps=-1.0) == br.MLRA_ERR_INVALID_ARG
+    assert append(c, eps=float("nan")) == br.MLRA_ERR_INVALID_ARG
+    assert append(c, ts=100) == br.MLRA_ERR_INVALID_ARG       # token stride below d_latent
+    assert append(c, kts=10) == br.MLRA_ERR_INVALID_ARG       # below d_rope
+    assert append(c, B=-1) == br.MLRA_ERR_INVALID_ARG
+    assert append(c, max_len=-1) == br.MLRA_ERR_INVALID_ARG
+    # nothing to do: succeeds without a device
+    assert append(c, B=0) == br.MLRA_OK
+    assert append(c, max_len=0) == br.MLRA_OK
+    # a RoPE-free config needs no krope buffer
+    assert append(cfg(d_rope=0), kr=0, kts=0) in (br.MLRA_OK, br.MLRA_ERR_NO_DEVICE)
+
+
 @pytest.mark.skipif(gpu_present(), reason="valid arguments would launch on a real device")
 def test_valid_arguments_without_device_report_no_device():
     c = cfg()
     assert decode(c, cache()) == br.MLRA_ERR_NO_DEVICE
     L = br.lib()
     assert L.mla_out_proj(ctypes.byref(c), 4, FAKE, FAKE, FAKE, 0, None) == br.MLRA_ERR_NO_DEVICE
+    assert append(c) == br.MLRA_ERR_NO_DEVICE

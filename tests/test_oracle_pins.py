@@ -17,9 +17,9 @@ import pytest
 import torch
 
 import oracle
-from oracle import (absorb_q_ref, branch_slices, kv_elems_per_token_per_device,
+from oracle import (absorb_q_ref, branch_slices, cache_append_ref, kv_elems_per_token_per_device,
                     latent_attn_ref, merge_partials, mla_decode_ref, mlra_decode_ref,
-                    out_proj_ref, partial_state, rope, variance_scales)
+                    out_proj_ref, partial_state, rms_norm, rope, variance_scales)
 from synth import WORKLOADS, make_inputs, round_bf16
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -303,6 +303,79 @@ def test_variance_scales_do_what_the_page_says():
     # the MLRA-4 values at the DeepSeek-V3 width d = 7168, d_c = 512
     aq4, akv4 = variance_scales(7168, 512, 4)
     assert abs(aq4 - math.sqrt(56)) < 1e-12 and abs(akv4 - math.sqrt(14)) < 1e-12
+
+
+# ------------------------------------------------------- cache append ----
+
+def test_rms_norm_closed_form_and_torch():
+    # worked example: [3, 4] has mean square 12.5
+    y = rms_norm(np.array([3.0, 4.0]), eps=0.0)
+    assert np.allclose(y, np.array([3.0, 4.0]) / math.sqrt(12.5), rtol=0, atol=1e-15)
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((5, 512)) * 3.0
+    g = rng.standard_normal(512)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (512,), torch.from_numpy(g), 1e-6)
+    assert np.allclose(rms_norm(x, g, 1e-6), ref.numpy(), rtol=1e-12, atol=1e-12)
+    # unit RMS without gain, and no change under a positive rescaling (eps = 0)
+    y = rms_norm(x, eps=0.0)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, atol=1e-12)
+    assert np.allclose(rms_norm(7.5 * x, eps=0.0), y, atol=1e-12)
+
+
+def test_cache_append_writes_one_row_and_counts():
+    rng = np.random.default_rng(4)
+    B, Lmax, d_c, d_r = 4, 6, 32, 8
+    ckv = rng.standard_normal((B, Lmax, d_c))
+    kr = rng.standard_normal((B, Lmax, d_r))
+    lens = np.array([0, 3, 6, 5], np.int32)  # sequence 2 is full
+    new_c = rng.standard_normal((B, d_c)) * 5.0
+    new_k = rng.standard_normal((B, d_r))
+    c2, k2, l2 = cache_append_ref(ckv, kr, lens, new_c, new_k, Lmax)
+    assert l2.tolist() == [1, 4, 6, 6]
+    for b in range(B):
+        p = int(lens[b])
+        for t in range(Lmax):
+            if t == p and p < Lmax:
+                continue
+            assert np.array_equal(c2[b, t], ckv[b, t]) and np.array_equal(k2[b, t], kr[b, t])
+    # inputs are not modified
+    assert lens.tolist() == [0, 3, 6, 5]
+    for b, p in ((0, 0), (1, 3), (3, 5)):
+        # the latent row has unit RMS (eps is negligible here)
+        assert abs(math.sqrt(np.mean(c2[b, p] ** 2)) - 1.0) < 1e-6
+        assert np.allclose(c2[b, p] * np.sqrt(np.mean(new_c[b] ** 2)), new_c[b], rtol=1e-6)
+        # the key is turned by exactly p: a query rotated to p sees the
+        # unrotated dot product, and each pair keeps its length
+        q = rng.standard_normal(d_r)
+        assert math.isclose(float(rope(q, p) @ k2[b, p]), float(q @ new_k[b]), rel_tol=1e-12,
+                            abs_tol=1e-12)
+        pair = lambda v: np.hypot(v[0::2], v[1::2])  # noqa: E731
+        assert np.allclose(pair(k2[b, p]), pair(new_k[b]))
+    # position 0 is the identity rotation
+    assert np.allclose(k2[0, 0], new_k[0])
+
+
+def test_append_then_decode_sees_the_new_token():
+    # the next decode step's query sits at the new token (p = L_b after the
+    # append): its output changes only through that row, and equals the
+    # decode of the cache with the row in place
+    rng = np.random.default_rng(6)
+    B, H, d_c, d_r, d_n, d_v, Lmax = 2, 3, 32, 8, 16, 16, 9
+    ckv = rng.standard_normal((B, Lmax, d_c))
+    kr = rng.standard_normal((B, Lmax, d_r))
+    lens = np.array([4, 8], np.int32)
+    qn, qr = rng.standard_normal((B, H, d_n)), rng.standard_normal((B, H, d_r))
+    wk, wv = rng.standard_normal((H, d_c, d_n)) / 6, rng.standard_normal((H, d_c, d_v)) / 6
+    c2, k2, l2 = cache_append_ref(ckv, kr, lens, rng.standard_normal((B, d_c)),
+                                  rng.standard_normal((B, d_r)), Lmax)
+    got = mlra_decode_ref(qn, qr, wk, wv, c2, k2, l2, 1)
+    # the same tokens placed by hand (rows past the old lengths are ignored)
+    ckv_h, kr_h = ckv.copy(), kr.copy()
+    for b in range(B):
+        ckv_h[b, lens[b]] = c2[b, lens[b]]
+        kr_h[b, lens[b]] = k2[b, lens[b]]
+    assert np.allclose(got, mlra_decode_ref(qn, qr, wk, wv, ckv_h, kr_h, lens + 1, 1))
+    assert not np.allclose(got, mlra_decode_ref(qn, qr, wk, wv, ckv, kr, lens + 1, 1))
 
 
 # -------------------------------------------------------- input recipe ----
