@@ -51,6 +51,8 @@ def parse():
                     help="split-KV decode kernel (auto: the library's choice)")
     ap.add_argument("--cache-bytes-min", type=float, default=2.0,
                     help="GiB of rotating cache copies (>= 8x the Infinity Cache)")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip sampling the clock and power under load (rocm-smi)")
     ap.add_argument("--no-shards", action="store_true",
                     help="skip the per-device tensor-parallel shard comparison")
     ap.add_argument("--time-every", type=int, default=4,
@@ -90,7 +92,48 @@ def traffic_for(workload, kernel):
         return None
 
 
-def run_workload(name, steps, warmup, cache_gib, torch, br, synth, kernel="auto", every=4):
+def sample_clock(step, torch, limit_s=30.0):
+    """Shader/memory clock and power while decode steps keep the GPU busy:
+    rocm-smi runs as a child process after half a second of steps."""
+    import re
+    import subprocess
+    import threading
+    out = {}
+
+    def probe():
+        time.sleep(0.5)
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"],
+                               capture_output=True, text=True, timeout=20)
+            d = json.loads(r.stdout[r.stdout.index("{"):])
+            for k, v in next(iter(d.values())).items():
+                m = re.search(r"([0-9]+(\.[0-9]+)?)", str(v))
+                if not m:
+                    continue
+                if "sclk clock speed" in k:
+                    out["sclk_mhz"] = float(m.group(1))
+                elif "mclk clock speed" in k:
+                    out["mclk_mhz"] = float(m.group(1))
+                elif "Power" in k and "(W)" in k:
+                    out["power_w"] = float(m.group(1))
+        except Exception as e:  # noqa: BLE001 - best effort, reported as such
+            out["error"] = f"{type(e).__name__}: {str(e)[:120]}"
+
+    th = threading.Thread(target=probe)
+    th.start()
+    t0, i = time.time(), 0
+    while th.is_alive() and time.time() - t0 < limit_s:
+        for _ in range(50):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
+    th.join()
+    out["sampled_during"] = "back-to-back decode steps of the main workload"
+    return out
+
+
+def run_workload(name, steps, warmup, cache_gib, torch, br, synth, kernel="auto", every=4,
+                 clock=False):
     w = synth.WORKLOADS[name]
     inp = synth.make_inputs(w, parts=("q_nope", "q_rope", "w_uk", "w_uv"))
     lens = inp["lens"]
@@ -145,11 +188,15 @@ def run_workload(name, steps, warmup, cache_gib, torch, br, synth, kernel="auto"
     br.set_kernel_timing(None, None)
     ms_step = (t1 - t0) * 1e3 / steps
     gpu_ms_step = g0.elapsed_time(g1) / steps
-    k_ms = sum(a.elapsed_time(b) for a, b in kev) / len(kev)
+    k_all = sorted(a.elapsed_time(b) for a, b in kev)
+    k_ms = sum(k_all) / len(k_all)
+    pct = lambda q: k_all[min(len(k_all) - 1, int(round(q * (len(k_all) - 1))))] * 1e3  # noqa: E731
     assert torch.isfinite(out).all().item(), "non-finite output"
+    clk = sample_clock(step, torch) if clock else None  # after the timed region
     del bufs, views
     return dict(w=w, lens=lens, kv_bytes=kv_bytes, flops=flops, tokens=tokens, copies=copies,
                 kernel=kname, timed_launches=len(kev),
+                kernel_us_p10_p50_p90=[pct(0.1), pct(0.5), pct(0.9)], clock=clk,
                 ms_step=ms_step, gpu_ms_step=gpu_ms_step, kernel_ms=k_ms)
 
 
@@ -236,7 +283,7 @@ def main():
         probe_copy(torch)
         return
     main_r = run_workload(a.workload, a.steps, a.warmup, a.cache_bytes_min, torch, br, synth,
-                          a.kernel, a.time_every)
+                          a.kernel, a.time_every, clock=not a.no_clock)
     extras = {}
     for name in [x for x in a.also.split(",") if x and x != a.workload]:
         r = run_workload(name, a.steps, a.warmup, a.cache_bytes_min, torch, br, synth, a.kernel
@@ -299,6 +346,8 @@ def main():
         "gpu_ms_per_step": main_r["gpu_ms_step"],
         "decode_kernel_us": main_r["kernel_ms"] * 1e3,
         "decode_kernel_timed_launches": main_r["timed_launches"],
+        "decode_kernel_us_p10_p50_p90": main_r["kernel_us_p10_p50_p90"],
+        "clock_under_load": main_r["clock"],
         "decode_kernel_kv_gbs": kv_gbs_kernel,
         "decode_kernel_mfma_tflops": main_r["flops"] / k_s / 1e12,
         "decode_kernel_mfma_frac": main_r["flops"] / k_s / 1e12 / BF16_PEAK_TFLOPS,
