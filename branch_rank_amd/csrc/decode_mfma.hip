@@ -416,13 +416,20 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(DecodeParams p)
   }
 }
 
+// Workgroups resident per CU: enough waves for all four SIMDs. At d_c = 128 a
+// wave needs <= 256 registers, so two fit per SIMD; wider latents need up to
+// 512 (Q and O of 16 heads), one per SIMD. The tile ring takes that share of
+// the 160 KB of LDS.
+constexpr int wgs_per_cu(int dc, int nw) { return (dc == 128 ? 8 : 4) / nw; }
+
 template <int DC, int NB, int NW, int HSPLIT>
 hipError_t launch_t(const Geom& g, const void* q_abs, const void* ckv, const void* krope,
                     const Workspace& ws, int items, hipStream_t s,
                     const KernelTiming& t) {
   using C = Cfg<DC, NB, NW>;
-  // as many stages as LDS holds (<= 4) and the 6-bit vmcnt can track
-  constexpr int NS_LDS = (160 * 1024) / C::STAGE;
+  // as many stages as this workgroup's share of LDS holds (<= 4) and the
+  // 6-bit vmcnt can track
+  constexpr int NS_LDS = (160 * 1024) / wgs_per_cu(DC, NW) / C::STAGE;
   constexpr int NS_VM = 2 * C::PER_HI < 64 ? 4 : 3;
   constexpr int NS = NS_LDS < NS_VM ? NS_LDS : NS_VM;
   static_assert(NS >= 2, "tile does not fit LDS");
@@ -483,8 +490,12 @@ bool decode_mfma_supported(const Geom& g) {
   return true;
 }
 
-// Workgroups per work item (head groups); one workgroup runs per CU.
-int decode_mfma_wgs_per_item(const Geom& g) { return g.H == 128 ? 2 : 1; }
+// Work items that keep every CU busy: workgroups resident per CU over the
+// workgroups (head groups) of one item.
+int decode_mfma_target_items(const Geom& g, int cus) {
+  const int nw = g.H == 32 ? 2 : 4, hsplit = g.H == 128 ? 2 : 1;
+  return cus * wgs_per_cu(g.dc, nw) / hsplit;
+}
 
 hipError_t launch_decode_mfma(const Geom& g, const void* q_abs, const void* ckv,
                               const void* krope, const Workspace& ws, int items,

@@ -102,7 +102,7 @@ hipError_t launch_decode_branch(const Geom& g, const void* q_abs, const void* ck
                                 hipStream_t s, const KernelTiming& t);
 
 bool decode_mfma_supported(const Geom& g);
-int decode_mfma_wgs_per_item(const Geom& g);
+int decode_mfma_target_items(const Geom& g, int cus);
 hipError_t launch_decode_mfma(const Geom& g, const void* q_abs, const void* ckv,
                               const void* krope, const Workspace& ws, int grid_items,
                               hipStream_t s, const KernelTiming& t);

@@ -266,7 +266,7 @@ mlra_status_t plan_for(const mlra_config_t* c, const Geom& g, int cus, const mlr
   if (*kern == MLRA_KERNEL_BRANCH)
     target = cus / decode_branch_wgs_per_item(g);
   else if (*kern == MLRA_KERNEL_HEAD_GROUP)
-    target = cus / decode_mfma_wgs_per_item(g);
+    target = decode_mfma_target_items(g, cus);
   else
     target = cus * 4 / g.H;
   if (target < 1) target = 1;
