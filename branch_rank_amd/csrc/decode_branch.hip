@@ -32,7 +32,9 @@
 //    VGPR staging): one instruction per two 512-byte latent half-rows and per
 //    eight 128-byte RoPE rows, shared by all waves, through an NS-stage ring
 //    (20 KB per stage, so several tiles are in flight per CU); a stage is
-//    reloaded once the lagging group's vector phase has read it. LDS rows are
+//    reloaded once the lagging group's vector phase has read it. All but a
+//    segment's last few tiles run a branch-free steady body (fixed wait depth,
+//    full tiles, no row mask); the general body handles the tail. LDS rows are
 //    XOR-swizzled in 16-byte chunks (chunk ^ 2*(row & 15) for latent rows,
 //    measured free of bank conflicts for both read patterns below).
 //  * QK: S^T[t][h] on v_mfma_f32_16x16x32_bf16, 16 tokens as M, 16 heads as N;
@@ -290,15 +292,29 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
     auto issue_if = [&](int t) {
       if (t < ntiles) issue(t);
     };
+    // steady tiles (1 <= t < ntiles - D - 1): the wait keeps NS - 2 tiles in
+    // flight, the tile loaded is full and not the last, and no row is masked
+    auto wait_steady = [&] {
+      if (wave < C::NR) wait_vm<(NS - 2) * (C::NL / C::NW + 1)>();
+      else wait_vm<(NS - 2) * (C::NL / C::NW)>();
+    };
+    auto issue_full = [&](int tile) {
+      const uint32_t sa = sbase + dma_off;
+      dma_off = next_stage(dma_off);
+      issue_tile<C, false>(sa, crs, krs, p.ckv_ts, p.kr_ts, t0 + tile * kT, t1, wave, lane, lat_voff,
+                           lat_c, rope_t, rope_c);
+    };
+    const int steady_end = ntiles - D - 1;
 
-    auto mphase = [&](int t, auto pv_tag, auto qk_tag) {
+    auto mphase = [&](int t, auto pv_tag, auto qk_tag, auto steady_tag) {
       constexpr bool PV = decltype(pv_tag)::value, QK = decltype(qk_tag)::value;
+      constexpr bool STEADY = decltype(steady_tag)::value;
       bf16x8 A[2][C::KS];
       if constexpr (QK) {
         const char LDS_AS* st = smem + __builtin_amdgcn_readfirstlane(m_off);
         m_off = next_stage(m_off);
         const int valid = t1 - (t0 + t * kT);
-        if (valid < kT) {
+        if (!STEADY && valid < kT) {
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -405,40 +421,58 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
     if (!lag) {
       wait_tile(0);
       bar();
-      mphase(0, F_{}, T_{});
+      mphase(0, F_{}, T_{}, F_{});
       bar();
       issue_if(D);
       vphase();
-      for (int t = 1; t < ntiles; ++t) {
+      int t = 1;
+      for (; t < steady_end; ++t) {
+        wait_steady();
+        bar();
+        mphase(t, T_{}, T_{}, T_{});
+        bar();
+        issue_full(t + D);
+        vphase();
+      }
+      for (; t < ntiles; ++t) {
         wait_tile(t);
         bar();
-        mphase(t, T_{}, T_{});
+        mphase(t, T_{}, T_{}, F_{});
         bar();
         issue_if(t + D);
         vphase();
       }
       bar();
-      mphase(ntiles, T_{}, F_{});
+      mphase(ntiles, T_{}, F_{}, F_{});
       bar();
     } else {
       wait_tile(0);
       bar();
       bar();
       issue_if(D);
-      mphase(0, F_{}, T_{});
+      mphase(0, F_{}, T_{}, F_{});
       if (1 < ntiles) wait_tile(1);
       bar();
       vphase();
       bar();
-      for (int t = 1; t < ntiles; ++t) {
+      int t = 1;
+      for (; t < steady_end; ++t) {
+        issue_full(t + D);
+        mphase(t, T_{}, T_{}, T_{});
+        wait_steady();
+        bar();
+        vphase();
+        bar();
+      }
+      for (; t < ntiles; ++t) {
         issue_if(t + D);
-        mphase(t, T_{}, T_{});
+        mphase(t, T_{}, T_{}, F_{});
         if (t + 1 < ntiles) wait_tile(t + 1);
         bar();
         vphase();
         bar();
       }
-      mphase(ntiles, T_{}, F_{});
+      mphase(ntiles, T_{}, F_{}, F_{});
     }
 
     // partial state of this segment: m, l as [slot][n][H]; acc as
