@@ -36,6 +36,8 @@
 
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace mlra {
@@ -267,7 +269,8 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(DecodeParams p)
     }
 
     // one 32-token tile; valid < kT only for the segment's last tile
-    auto tile = [&](const char LDS_AS* st, int valid) {
+    auto tile = [&](const char LDS_AS* st, int valid, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
       auto load = [&](int gid, bf16x8* F) {
         if (gid == 0) {
 #pragma unroll
@@ -333,11 +336,13 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(DecodeParams p)
           if (r == SC::QG - 1) {
             // softmax of branch j over this tile's 32 tokens; tokens past the
             // segment end (last tile only) get score -inf
+            if constexpr (MASK) {
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+              for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (16 * mb + 4 * kg + e >= valid) S[mb][e] = -INFINITY;
+                for (int e = 0; e < 4; ++e)
+                  if (16 * mb + 4 * kg + e >= valid) S[mb][e] = -INFINITY;
+            }
             float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
                              fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
             const float mt = max4(mx) * kLog2e;
@@ -385,7 +390,22 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(DecodeParams p)
       }
     };
 
-    for (int it = 0; it < ntiles; ++it) {
+    using MaskOn = std::integral_constant<bool, true>;
+    using MaskOff = std::integral_constant<bool, false>;
+    // steady tiles (it < ntiles - NS): NS - 2 tiles stay in flight, the tile
+    // loaded is full and not the last, and no row is masked; the general body
+    // handles the tail. Only for one branch: with two or four, the second
+    // copy of the tile body makes the compiler spill.
+    int it = 0;
+    for (; NB == 1 && it < ntiles - NS; ++it) {
+      wait_tiles<DC, NB, NW, NS>(NS - 2, wave);
+      __builtin_amdgcn_s_barrier();
+      const int nt = it + NS - 1;  // tile whose DMA goes out now
+      issue_tile<DC, NB, NW, false>(smem + (nt % NS) * C::STAGE, crs, krs, p.ckv_ts, p.kr_ts,
+                                    t0 + nt * kT, t1, wave, lane, voff);
+      tile(smem + (it % NS) * C::STAGE, kT, MaskOff{});
+    }
+    for (; it < ntiles; ++it) {
       const int ahead = min(NS - 2, ntiles - 1 - it);
       wait_tiles<DC, NB, NW, NS>(ahead, wave);
       __builtin_amdgcn_s_barrier();
@@ -396,7 +416,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(DecodeParams p)
       else if (nt == ntiles - 1)
         issue_tile<DC, NB, NW, true>(smem + (nt % NS) * C::STAGE, crs, krs, p.ckv_ts, p.kr_ts,
                                      t0 + nt * kT, t1, wave, lane, voff);
-      tile(smem + (it % NS) * C::STAGE, min(kT, t1 - (t0 + it * kT)));
+      tile(smem + (it % NS) * C::STAGE, min(kT, t1 - (t0 + it * kT)), MaskOn{});
     }
 
     // partial state of this segment: m, l as [slot][n][H]; acc as
