@@ -16,11 +16,12 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmlra.so")
 
 SOURCES = ["mlra_api.cpp", "kernels_generic.hip", "decode_mfma.hip", "decode_branch.hip",
-           "proj_mfma.hip", "cache_append.hip"]
+           "proj_mfma.hip", "cache_append.hip", "prefill_branch.hip"]
 # The split-KV decode kernels hold no NaN by construction (finite scores, -inf
 # for masked tokens): without NaN semantics their max reductions need no
 # canonicalising moves.
-EXTRA = {"decode_mfma.hip": ["-fno-honor-nans"], "decode_branch.hip": ["-fno-honor-nans"]}
+EXTRA = {"decode_mfma.hip": ["-fno-honor-nans"], "decode_branch.hip": ["-fno-honor-nans"],
+         "prefill_branch.hip": ["-fno-honor-nans"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -25,6 +25,7 @@ from .mlra_ref import (  # noqa: F401
     branch_slices,
     mlra_decode_ref,
     mla_decode_ref,
+    mlra_prefill_ref,
     absorb_q_ref,
     latent_attn_ref,
     out_proj_ref,

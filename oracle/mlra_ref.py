@@ -245,6 +245,60 @@ def out_proj_ref(latent_out, w_uv, alpha_kv):
     return out
 
 
+def mlra_prefill_ref(q_nope, q_rope, w_uk, w_uv, ckv, krope, lens, n,
+                     tau=None, alpha_q=1.0, alpha_kv=1.0, theta=10000.0):
+    """Causal MLRA-n prefill in the unabsorbed (MHA) form.
+
+    The prompt's positions attend causally: position t of sequence b sees the
+    cached tokens u <= t ("MLA多头潜在注意力机制" 3.3: a key whose position
+    lies after the query's is masked out), and the prefill takes the form with
+    explicit up-projected keys and values ("vllbc02MLA", 苏神思路: prefill with
+    the MHA form, generation with the MQA form). Per branch j with slice S_j
+    ("Multi-Head Low-Rank Attention", 核心方法):
+
+    * K^N_j = C[:, S_j] W_UK[h][S_j], V_j = C[:, S_j] W_UV[h][S_j];
+    * S_j[t, u] = tau (alpha_q q^N_t . K^N_j[u] + RoPE(q^R_t, t) . k^R_u), and
+      -inf for u > t;
+    * o[t] = alpha_kv sum_j softmax_u(S_j[t]) V_j.
+
+    Inputs: q_nope [B, T, H, d_n], q_rope [B, T, H, d_r] (unrotated; row t is
+    position t), cache arrays as for the decode with T = L_max. Returns
+    [B, T, H, d_v] float64, zero for t >= L_b.
+    Pinned by: every row against ``mlra_decode_ref`` on the cache cut after
+    that row with the query at its position; torch's float64 causal
+    scaled-dot-product attention per branch; the first row's closed form
+    (one key: alpha_kv c_0 W_UV[h]); causality (later rows and later queries
+    change nothing).
+    """
+    q_nope, q_rope = _f64(q_nope), _f64(q_rope)
+    w_uk, w_uv = _f64(w_uk), _f64(w_uv)
+    B, T, H, d_n = q_nope.shape
+    d_c, d_v = w_uv.shape[1], w_uv.shape[2]
+    d_r = q_rope.shape[-1]
+    if tau is None:
+        tau = 1.0 / math.sqrt(d_n + d_r)
+    out = np.zeros((B, T, H, d_v))
+    for b in range(B):
+        L = min(max(int(lens[b]), 0), T)
+        if L == 0:
+            continue
+        C = _f64(ckv[b, :L])
+        KR = _f64(krope[b, :L])
+        later = np.arange(L)[None, :] > np.arange(L)[:, None]   # [t, u]: u > t
+        for h in range(H):
+            QN = q_nope[b, :L, h]                               # [L, d_n]
+            rho = rope(q_rope[b, :L, h], np.arange(L), theta)   # [L, d_r]
+            rope_part = rho @ KR.T
+            for S in branch_slices(d_c, n):
+                KN = C[:, S] @ w_uk[h][S, :]
+                V = C[:, S] @ w_uv[h][S, :]
+                s = tau * (alpha_q * (QN @ KN.T) + rope_part)
+                s[later] = -np.inf
+                e = np.exp(s - s.max(axis=1, keepdims=True))
+                out[b, :L, h] += alpha_kv * ((e / e.sum(axis=1, keepdims=True)) @ V)
+    return out
+
+
 def partial_state(scores, values):
     """Softmax state of one token range: (m, l, acc) with m = max s,
     l = sum exp(s - m), acc = sum exp(s - m) v. An empty range gives

@@ -110,6 +110,10 @@ WORKLOADS = {
     "mlra4_shard_b16_l32k": Workload("mlra4_shard_b16_l32k", 16, 128, 128, 64, 128, 128, 1,
                                      32768, alpha_q=_AQ4, alpha_kv=_AKV4,
                                      w_std=1.0 / math.sqrt(512), seed=1006),
+    # causal prefill of MLRA-4 at the DeepSeek-V3 attention shape: 4 prompts of
+    # 4096 tokens, one query per position (q_rows = 4096)
+    "mlra4_prefill_b4_t4k": Workload("mlra4_prefill_b4_t4k", 4, n=4, cache_len=4096,
+                                     alpha_q=_AQ4, alpha_kv=_AKV4, seed=1008, **DSV3),
     "mla_tp4_b16_l128k": Workload("mla_tp4_b16_l128k", 16, 32, 512, 64, 128, 128, 1, 131072,
                                   seed=1007),
     "mlra4_shard_b16_l128k": Workload("mlra4_shard_b16_l128k", 16, 128, 128, 64, 128, 128, 1,
@@ -123,7 +127,7 @@ def ragged_lens(rng, batch, lo, hi):
 
 
 def make_inputs(w: Workload, seed: Optional[int] = None, lens=None, max_len=None,
-                parts=("ckv", "krope", "q_nope", "q_rope", "w_uk", "w_uv")):
+                parts=("ckv", "krope", "q_nope", "q_rope", "w_uk", "w_uv"), q_rows=None):
     """Draw the inputs of workload ``w``.
 
     Returns a dict of float32 arrays (bf16-representable for bf16 workloads):
@@ -131,7 +135,9 @@ def make_inputs(w: Workload, seed: Optional[int] = None, lens=None, max_len=None
     q_rope [B, H, d_r], w_uk [H, d_c, d_n], w_uv [H, d_c, d_v], plus
     lens [B] int32. ``lens`` / ``max_len`` override the workload's lengths.
     ``parts`` limits which tensors are drawn (the others are skipped but the
-    per-tensor streams stay the same).
+    per-tensor streams stay the same). ``q_rows`` draws one query per
+    position instead (a prompt): q_nope [B, q_rows, H, d_n], q_rope
+    [B, q_rows, H, d_r].
     """
     ss = np.random.SeedSequence(w.seed if seed is None else seed)
     g = [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(7)]
@@ -164,10 +170,12 @@ def make_inputs(w: Workload, seed: Optional[int] = None, lens=None, max_len=None
             k *= np.float32(1.0 / math.sqrt(w.d_r))
         out["krope"] = rnd(k)
     if "q_nope" in parts:
-        q = g[3].standard_normal((B, H, w.d_n), dtype=np.float32)
+        qs = (B, H) if q_rows is None else (B, q_rows, H)
+        q = g[3].standard_normal(qs + (w.d_n,), dtype=np.float32)
         out["q_nope"] = rnd(q / math.sqrt(w.d_n) if fan else q)
     if "q_rope" in parts:
-        q = g[4].standard_normal((B, H, w.d_r), dtype=np.float32)
+        qs = (B, H) if q_rows is None else (B, q_rows, H)
+        q = g[4].standard_normal(qs + (w.d_r,), dtype=np.float32)
         out["q_rope"] = rnd(q / math.sqrt(w.d_r) if fan else q)
     if "w_uk" in parts:
         out["w_uk"] = rnd(g[5].standard_normal((H, w.d_c, w.d_n), dtype=np.float32) * np.float32(w_std))

@@ -19,7 +19,7 @@ import torch
 import oracle
 from oracle import (absorb_q_ref, branch_slices, cache_append_ref, kv_elems_per_token_per_device,
                     latent_attn_ref, merge_partials, mla_decode_ref, mlra_decode_ref,
-                    out_proj_ref, partial_state, rms_norm, rope, variance_scales)
+                    mlra_prefill_ref, out_proj_ref, partial_state, rms_norm, rope, variance_scales)
 from synth import WORKLOADS, make_inputs, round_bf16
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -376,6 +376,87 @@ def test_append_then_decode_sees_the_new_token():
         kr_h[b, lens[b]] = k2[b, lens[b]]
     assert np.allclose(got, mlra_decode_ref(qn, qr, wk, wv, ckv_h, kr_h, lens + 1, 1))
     assert not np.allclose(got, mlra_decode_ref(qn, qr, wk, wv, ckv, kr, lens + 1, 1))
+
+
+# ------------------------------------------------------------- prefill ----
+
+def prefill_tiny(seed, B=2, H=3, d_c=64, d_r=16, d_n=32, d_v=24, L=(9, 5), T=11):
+    rng = np.random.default_rng(seed)
+    return dict(
+        q_nope=rng.standard_normal((B, T, H, d_n)),
+        q_rope=rng.standard_normal((B, T, H, d_r)),
+        w_uk=rng.standard_normal((H, d_c, d_n)) / math.sqrt(d_c),
+        w_uv=rng.standard_normal((H, d_c, d_v)) / math.sqrt(d_c),
+        ckv=rng.standard_normal((B, T, d_c)),
+        krope=rng.standard_normal((B, T, d_r)),
+        lens=np.array(L, dtype=np.int32),
+    )
+
+
+@pytest.mark.parametrize("n", [1, 2, 4])
+def test_prefill_rows_are_decode_steps(n):
+    # row t of the prefill is the decode of a cache holding tokens 0..t with
+    # the query of position t (a separately written loop over one query)
+    t = prefill_tiny(20 + n)
+    kw = dict(n=n, tau=0.21, alpha_q=1.7, alpha_kv=0.6, theta=500.0)
+    got = mlra_prefill_ref(**t, **kw)
+    B, T = t["q_nope"].shape[:2]
+    for b in range(B):
+        for r in range(T):
+            if r >= t["lens"][b]:
+                assert not np.any(got[b, r])
+                continue
+            want = mlra_decode_ref(t["q_nope"][b:b + 1, r], t["q_rope"][b:b + 1, r], t["w_uk"],
+                                   t["w_uv"], t["ckv"][b:b + 1], t["krope"][b:b + 1],
+                                   np.array([r + 1]), q_pos=np.array([r]), **kw)
+            assert rel(got[b, r], want[0]) < 1e-12, (b, r)
+
+
+@pytest.mark.parametrize("n", [1, 4])
+def test_prefill_against_torch_causal_sdpa(n):
+    # per branch, torch's float64 causal attention on the explicit keys
+    # [alpha_q C_j W_UK_j || K_R], queries [q^N || RoPE(q^R, t)], values C_j W_UV_j
+    t = prefill_tiny(30, L=(11, 6))
+    tau, aq, akv = 0.19, 1.3, 0.9
+    ref = mlra_prefill_ref(**t, n=n, tau=tau, alpha_q=aq, alpha_kv=akv)
+    d_c = t["w_uk"].shape[1]
+    for b in range(2):
+        L = int(t["lens"][b])
+        C, KR = torch.from_numpy(t["ckv"][b, :L]), torch.from_numpy(t["krope"][b, :L])
+        for h in range(3):
+            q_r = torch.from_numpy(np.stack([rope(t["q_rope"][b, r, h], r) for r in range(L)]))
+            q = torch.cat([torch.from_numpy(t["q_nope"][b, :L, h]), q_r], 1)
+            o = torch.zeros(L, t["w_uv"].shape[2], dtype=torch.float64)
+            for S in branch_slices(d_c, n):
+                K = torch.cat([aq * C[:, S] @ torch.from_numpy(t["w_uk"][h][S]), KR], 1)
+                V = C[:, S] @ torch.from_numpy(t["w_uv"][h][S])
+                o += torch.nn.functional.scaled_dot_product_attention(
+                    q[None], K[None], V[None], is_causal=True, scale=tau)[0]
+            assert rel(ref[b, :L, h], akv * o.numpy()) < 1e-12
+
+
+def test_prefill_first_row_and_causality():
+    t = prefill_tiny(40, L=(10, 10), T=10)
+    kw = dict(n=4, tau=0.3, alpha_q=1.1, alpha_kv=0.7)
+    ref = mlra_prefill_ref(**t, **kw)
+    # position 0 sees one key: weight 1 in every branch, so the branch sum is
+    # alpha_kv c_0 W_UV[h] whatever the query
+    for b in range(2):
+        for h in range(3):
+            assert rel(ref[b, 0, h], 0.7 * t["ckv"][b, 0] @ t["w_uv"][h]) < 1e-13
+    # later cache rows and later queries leave rows 0..4 unchanged; row 5 moves
+    u = {k: v.copy() for k, v in t.items()}
+    rng = np.random.default_rng(41)
+    for k in ("ckv", "krope", "q_nope", "q_rope"):
+        u[k][:, 5:] = rng.standard_normal(u[k][:, 5:].shape)
+    ref2 = mlra_prefill_ref(**u, **kw)
+    np.testing.assert_array_equal(ref2[:, :5], ref[:, :5])
+    assert rel(ref2[:, 5], ref[:, 5]) > 1e-3
+    # shorter lengths cut the output, not the rows before the cut
+    u = dict(t, lens=np.array([4, 0], np.int32))
+    ref3 = mlra_prefill_ref(**u, **kw)
+    assert rel(ref3[0, :4], ref[0, :4]) < 1e-13   # equal up to the matmul's summation order
+    assert not np.any(ref3[0, 4:]) and not np.any(ref3[1])
 
 
 # -------------------------------------------------------- input recipe ----
