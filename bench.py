@@ -55,6 +55,9 @@ def parse():
                     help="skip sampling the clock and power under load (rocm-smi)")
     ap.add_argument("--no-shards", action="store_true",
                     help="skip the per-device tensor-parallel shard comparison")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the causal prefill leg (MLRA-4, 4 prompts of 4096 tokens)")
+    ap.add_argument("--prefill-workload", default="mlra4_prefill_b4_t4k")
     ap.add_argument("--time-every", type=int, default=4,
                     help="stamp the decode dispatch's start/end events on every N-th timed step")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
@@ -224,6 +227,73 @@ def time_cache_append(w, steps, warmup, torch, br):
     return e0.elapsed_time(e1) * 1e3 / steps
 
 
+def prefill_flops(w, lens):
+    """Algorithmic work of the prefill kernel: each of the L(L+1)/2 (query,
+    key) pairs of a sequence costs, per head, 2 (d_c' + d_r) flop per branch
+    for the score and 2 d_c' for the value (2 (n d_r + 2 d_c) in all); each
+    position and head adds the absorption (2 d_c d_n) and the output
+    projection (2 d_c d_v). Returns (attention part, total, pairs)."""
+    pairs = sum(int(L) * (int(L) + 1) // 2 for L in lens)
+    attn = pairs * w.heads * 2 * (w.n * w.d_r + 2 * w.d_c)
+    rows = int(sum(int(L) for L in lens))
+    proj = rows * w.heads * 2 * w.d_c * (w.d_n + w.d_v)
+    return attn, attn + proj, pairs
+
+
+def time_prefill(name, steps, warmup, torch, br, synth):
+    """One mlra_prefill call per step over B full prompts (one kernel); its
+    dispatch stamps a pair of HIP events every step."""
+    w = synth.WORKLOADS[name]
+    T = w.cache_len
+    inp = synth.make_inputs(w, parts=("w_uk", "w_uv"))
+    lens = inp["lens"]
+    buf, _ = synth.make_cache_device(w, seed=w.seed + 7919, lens=lens)
+    lens_dev = torch.from_numpy(lens).cuda()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    qn = torch.randn(w.batch, T, w.heads, w.d_n, generator=gen, device="cuda").to(torch.bfloat16)
+    qr = torch.randn(w.batch, T, w.heads, w.d_r, generator=gen, device="cuda").to(torch.bfloat16)
+    wk = torch.from_numpy(inp["w_uk"]).cuda().to(torch.bfloat16)
+    wv = torch.from_numpy(inp["w_uv"]).cuda().to(torch.bfloat16)
+    cfg = br.make_config(w.heads, w.d_c, w.d_r, w.d_n, w.d_v, n=w.n, sm_scale=w.tau,
+                         alpha_q=w.alpha_q, alpha_kv=w.alpha_kv, theta=w.theta, dtype=w.dtype)
+    cache = br.cache_view(buf[..., :w.d_c], buf[..., w.d_c:], lens_dev, cfg)
+    out = torch.empty(w.batch, T, w.heads, w.d_v, dtype=torch.bfloat16, device="cuda")
+    log(f"[bench] prefill {name}: B={w.batch} T={T}")
+
+    def call():
+        br.mlra_prefill(cfg, w.n, qn, qr, wk, wv, cache, out)
+
+    for _ in range(warmup):
+        call()
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for x, y in kev:
+        x.record()
+        y.record()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    g0.record()
+    for i in range(steps):
+        br.set_kernel_timing(*kev[i])
+        call()
+    g1.record()
+    torch.cuda.synchronize()
+    br.set_kernel_timing(None, None)
+    assert torch.isfinite(out.float()).all().item(), "non-finite prefill output"
+    ms = g0.elapsed_time(g1) / steps
+    k_ms = sum(x.elapsed_time(y) for x, y in kev) / steps
+    attn, total, pairs = prefill_flops(w, lens)
+    tf = total / (k_ms / 1e3) / 1e12
+    return {"workload": name, "batch": w.batch, "prompt_len": T, "heads": w.heads,
+            "branches": w.n, "steps": steps, "ms_per_call": ms,
+            "prompt_tokens_per_s": int(sum(int(L) for L in lens)) / (ms / 1e3),
+            "kernel_ms": k_ms, "kernel_flops": total, "attention_flops": attn,
+            "attn_pairs": pairs,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS, "traffic": None}}
+
+
 def cpu_baseline(w, seconds):
     """The float64 oracle (unabsorbed definition) on host cores, one sequence
     at a time of the same workload recipe until `seconds` have elapsed."""
@@ -297,6 +367,9 @@ def main():
             "kv_cache_gbs_step": r["kv_bytes"] / (r["ms_step"] / 1e3) / 1e9,
         }
     append_us = time_cache_append(main_r["w"], a.steps, a.warmup, torch, br)
+    prefill = None
+    if not a.no_prefill:
+        prefill = time_prefill(a.prefill_workload, max(2, min(a.steps, 10)), 2, torch, br, synth)
     shards = None
     if not a.no_shards:
         shards = {}
@@ -357,6 +430,7 @@ def main():
         "cache_append_us": append_us,
         "also": extras,
         "shard_compare": shards,
+        "prefill": prefill,
     }
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)

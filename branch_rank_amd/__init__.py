@@ -26,7 +26,7 @@ KERNELS = {"auto": MLRA_KERNEL_AUTO, "portable": MLRA_KERNEL_PORTABLE,
 
 EXPORTS = ("mlra_workspace_size", "mla_absorb_q", "mla_decode_attn", "mla_out_proj",
            "mlra_decode", "mlra_select_decode_kernel", "mlra_cache_append",
-           "mlra_prefill_workspace_size", "mlra_prefill",
+           "mlra_prefill",
            "mlra_set_kernel_timing", "mlra_status_string", "mlra_last_error_detail")
 
 
@@ -75,8 +75,7 @@ def lib():
         "mlra_select_decode_kernel": [CP, I32, KP, ctypes.POINTER(ctypes.c_int)],
         "mlra_cache_append": [CP, I32, P, P, ctypes.c_float, P, P, ctypes.c_int64,
                               ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, I32, P],
-        "mlra_prefill_workspace_size": [CP, I32, I32, ctypes.POINTER(SZ)],
-        "mlra_prefill": [CP, I32, I32, P, P, P, P, KP, P, SZ, P, ctypes.c_int, P],
+        "mlra_prefill": [CP, I32, I32, P, P, P, P, KP, P, ctypes.c_int, P],
         "mlra_set_kernel_timing": [P, P],
         "mlra_status_string": [ctypes.c_int],
         "mlra_last_error_detail": [],
@@ -277,20 +276,7 @@ def mlra_decode(cfg, num_branches, q_nope, q_rope, w_uk, w_uv, cache, workspace,
                             ctypes.byref(cache), wp, wn, op, od, _stream(stream)))
 
 
-def prefill_workspace_size(cfg, batch, max_len):
-    out = ctypes.c_size_t()
-    check(lib().mlra_prefill_workspace_size(ctypes.byref(cfg), batch, max_len, ctypes.byref(out)))
-    return out.value
-
-
-def alloc_prefill_workspace(cfg, batch, max_len, device="cuda"):
-    t = _torch()
-    return t.empty(max(prefill_workspace_size(cfg, batch, max_len), 256), dtype=t.uint8,
-                   device=device)
-
-
-def mlra_prefill(cfg, num_branches, q_nope, q_rope, w_uk, w_uv, cache, workspace, out,
-                 stream=None):
+def mlra_prefill(cfg, num_branches, q_nope, q_rope, w_uk, w_uv, cache, out, stream=None):
     """Causal prefill (mlra_prefill): q_nope [B][T][H][d_nope], q_rope
     [B][T][H][d_rope] for positions 0..T-1 of each sequence, T = cache.max_len;
     out [B][T][H][d_v] (float32 or bfloat16), zero for t >= cache_lens[b]."""
@@ -298,8 +284,6 @@ def mlra_prefill(cfg, num_branches, q_nope, q_rope, w_uk, w_uv, cache, workspace
     B, T = cache._batch, cache.max_len
     dt = _dtype(cfg)
     H = cfg.num_heads
-    c2 = Config.from_buffer_copy(cfg)
-    c2.num_branches = num_branches
     qn = _need(q_nope, "q_nope", (B, T, H, cfg.d_nope), dt)
     qr = _need(q_rope, "q_rope", (B, T, H, cfg.d_rope), dt)
     wk = _need(w_uk, "w_uk", (H, cfg.d_latent, cfg.d_nope), dt)
@@ -308,14 +292,8 @@ def mlra_prefill(cfg, num_branches, q_nope, q_rope, w_uk, w_uv, cache, workspace
         raise ValueError("out must be float32 or bfloat16")
     op = _need(out, "out", (B, T, H, cfg.d_v), out.dtype)
     od = MLRA_BF16 if out.dtype == t.bfloat16 else MLRA_FP32
-    need = prefill_workspace_size(c2, B, T)
-    if workspace.dtype != t.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous uint8 device tensor")
-    if workspace.numel() < need:
-        raise ValueError(f"workspace has {workspace.numel()} bytes, needs {need}")
     check(lib().mlra_prefill(ctypes.byref(cfg), num_branches, B, qn, qr, wk, wv,
-                             ctypes.byref(cache), workspace.data_ptr(), workspace.numel(), op, od,
-                             _stream(stream)))
+                             ctypes.byref(cache), op, od, _stream(stream)))
 
 
 def set_kernel_timing(before=None, after=None):

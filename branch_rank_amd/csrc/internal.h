@@ -69,15 +69,15 @@ struct Geom {
   int64_t ckv_bs, ckv_ts, kr_bs, kr_ts;  // element strides
 };
 
-// Causal prefill of MLRA-n with 128-wide branches (prefill_branch.hip): the
-// branch-normalised latent [B][T][H][d_c] of every position t < L_b from the
-// absorbed queries q_abs [B][T][H][d_c + d_r]; zeros for t >= L_b.
+// Causal prefill of MLRA-4 with 128-wide branches (prefill_branch.hip): one
+// kernel from the queries q^N, q^R [B][T][H][.] and the cache to the output
+// [B][T][H][d_v] (bf16 or fp32), zeros for t >= L_b.
 bool prefill_branch_supported(const Geom& g);
-hipError_t launch_prefill_branch(const Geom& g, int T, const void* q_abs, const void* ckv,
-                                 const void* krope, const int32_t* lens, float* latent,
-                                 hipStream_t s);
-// pos[b * T + t] = t
-hipError_t launch_fill_positions(int32_t* pos, int B, int T, hipStream_t s);
+hipError_t launch_prefill_branch(const Geom& g, int T, const void* q_nope, const void* q_rope,
+                                 const void* w_uk, const void* w_uv, const void* ckv,
+                                 const void* krope, const int32_t* lens, void* out, bool out_bf16,
+                                 float tau, float alpha_q, float alpha_kv, float theta,
+                                 hipStream_t s, const KernelTiming& t);
 
 constexpr int kMinChunk = 64;      // smallest automatic work item, tokens
 constexpr int kMaxAutoItems = 512; // upper bound on automatic work items

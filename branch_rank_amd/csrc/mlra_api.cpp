@@ -127,24 +127,7 @@ Workspace carve(const Layout& L, void* base) {
   return w;
 }
 
-// Prefill workspace: positions [B*T] int32, absorbed queries [B*T][H][d_c+d_r]
-// (cache dtype), branch-normalised latent [B*T][H][d_c] fp32.
 constexpr int kMaxPrefillRows = 1 << 22;
-
-struct PrefillLayout {
-  size_t pos, q_abs, latent, total;
-};
-
-PrefillLayout prefill_layout(const mlra_config_t* c, int32_t batch, int32_t max_len) {
-  PrefillLayout L;
-  const size_t rows = (size_t)batch * (size_t)max_len, H = c->num_heads;
-  size_t off = 0;
-  L.pos = off;    off = round_up(off + 4 * rows, 256);
-  L.q_abs = off;  off = round_up(off + elt_size(c->dtype) * rows * H * (c->d_latent + c->d_rope), 256);
-  L.latent = off; off = round_up(off + 4 * rows * H * c->d_latent, 256);
-  L.total = off;
-  return L;
-}
 
 // ---- per-device properties, filled once per device ----
 constexpr int kMaxDevices = 64;
@@ -490,20 +473,10 @@ mlra_status_t mlra_cache_append(const mlra_config_t* cfg, int32_t batch, const f
   return MLRA_OK;
 }
 
-mlra_status_t mlra_prefill_workspace_size(const mlra_config_t* cfg, int32_t batch, int32_t max_len,
-                                          size_t* bytes) {
-  g_detail.clear();
-  TRY(check_cfg(cfg));
-  TRY(check_batch(batch, max_len));
-  if (!bytes) return fail(MLRA_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = prefill_layout(cfg, batch, max_len).total;
-  return MLRA_OK;
-}
-
 mlra_status_t mlra_prefill(const mlra_config_t* cfg_in, int32_t num_branches, int32_t batch,
                            const void* q_nope, const void* q_rope, const void* w_uk,
-                           const void* w_uv, const mlra_cache_t* cache, void* workspace,
-                           size_t ws_bytes, void* out, mlra_dtype_t out_dtype, void* stream) {
+                           const void* w_uv, const mlra_cache_t* cache, void* out,
+                           mlra_dtype_t out_dtype, void* stream) {
   g_detail.clear();
   if (!cfg_in) return fail(MLRA_ERR_INVALID_ARG, "cfg is NULL");
   mlra_config_t cfg = *cfg_in;
@@ -523,34 +496,22 @@ mlra_status_t mlra_prefill(const mlra_config_t* cfg_in, int32_t num_branches, in
                          (int64_t)cache->max_len * cache->krope_token_stride * 2 < 0x7fffffffLL;
   if (cfg.dtype != MLRA_BF16 || !prefill_branch_supported(g) || !ranges_ok)
     return fail(MLRA_ERR_UNSUPPORTED,
-                "prefill supports bf16 MLRA with 128-wide branches (num_branches = 4, "
-                "d_latent = 512, d_rope = 64) and per-sequence byte ranges below 2^31");
-  // every (sequence, position) pair is one row of the projections
+                "prefill supports bf16 MLRA-4 at d_latent 512, d_rope 64, d_nope 128, d_v 128 "
+                "and per-sequence byte ranges below 2^31");
   if ((int64_t)batch * cache->max_len > kMaxPrefillRows)
     return fail(MLRA_ERR_UNSUPPORTED, "batch * max_len must stay at or below %d prompt rows",
                 kMaxPrefillRows);
-  const PrefillLayout L = prefill_layout(&cfg, batch, cache->max_len);
-  if (!workspace || ws_bytes < L.total)
-    return fail(MLRA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", L.total, ws_bytes);
-  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
-    return fail(MLRA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   int dev, cus;
   TRY(current_device(&dev, &cus));
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  char* w = static_cast<char*>(workspace);
-  int32_t* pos = reinterpret_cast<int32_t*>(w + L.pos);
-  void* q_abs = w + L.q_abs;
-  float* latent = reinterpret_cast<float*>(w + L.latent);
-  const int T = cache->max_len;
-  // every (sequence, position) row as one batch row of the decode step's
-  // absorb_q and out_proj, with the row's own position
-  Geom rows = make_geom(&cfg, batch * T, nullptr);
-  rows.max_len = 0x7fffffff;
-  TRY_HIP(launch_fill_positions(pos, batch, T, s), "positions launch");
-  TRY(run_absorb(&cfg, rows, q_nope, q_rope, pos, nullptr, w_uk, q_abs, s));
-  TRY_HIP(launch_prefill_branch(g, T, q_abs, cache->ckv, cache->krope, cache->cache_lens, latent, s),
+  KernelTiming timing;
+  timing.start = g_ev_before;
+  timing.stop = g_ev_after;
+  TRY_HIP(launch_prefill_branch(g, cache->max_len, q_nope, q_rope, w_uk, w_uv, cache->ckv,
+                                cache->krope, cache->cache_lens, out, out_dtype == MLRA_BF16,
+                                tau_of(&cfg), cfg.alpha_q, cfg.alpha_kv, cfg.rope_theta, static_cast<hipStream_t>(stream),
+                                timing),
           "prefill launch");
-  return run_out_proj(&cfg, rows, latent, w_uv, out, out_dtype, s);
+  return MLRA_OK;
 }
 
 mlra_status_t mlra_select_decode_kernel(const mlra_config_t* cfg, int32_t batch,

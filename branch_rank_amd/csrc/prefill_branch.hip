@@ -1,204 +1,328 @@
-// Causal multi-query latent attention for the prefill of MLRA-n with 128-wide
-// branch slices, gfx950 (MI355X).
+// Causal prefill of MLRA-4 (128-wide branch slices) in one kernel, gfx950
+// (MI355X): query absorption, causal latent attention and the W_UV output
+// projection, with no intermediate in HBM.
 //
-// What it computes ("Multi-Head Low-Rank Attention", 核心方法: one softmax per
-// branch over its latent slice plus the shared RoPE key; "vllbc02MLA",
-// 苏神思路: the prompt attends causally, every position t to the tokens
-// 0..t): for every cached position t < L_b of sequence b, every head h and
-// branch j, the branch-normalised latent
-//   o~_j[t, h] = sum_{u <= t} softmax_u(q~_j[t, h] . c_u[S_j] + rho[t, h] . k^R_u) c_u[S_j],
-// with q~ and rho the absorbed query of position t (absorb_q). With a
-// branch width d_c' equal to d_n and d_v (128 at MLRA-4) the absorbed form
-// costs what the unabsorbed one does: 192 + 128 multiply-adds per (query,
-// key) pair, and a 128 x 128 projection per token and branch on either side.
+// What it computes ("Multi-Head Low-Rank Attention", 核心方法 and 方法步骤详情:
+// one softmax per branch over its latent slice plus the shared RoPE key,
+// outputs summed and scaled by alpha_kv; "MLA多头潜在注意力机制" 3.3: a key
+// after the query's position is masked out): for every position t < L_b of
+// sequence b and head h,
+//   q~_j  = alpha_q tau W_UK[h][S_j] q^N_t,   rho = tau RoPE(q^R_t, t),
+//   o~_j  = sum_{u <= t} softmax_u(q~_j . c_u[S_j] + rho . k^R_u) c_u[S_j],
+//   o_t,h = alpha_kv sum_j W_UV[h][S_j]^T o~_j,
+// and zeros for L_b <= t < T. This is the decode step's absorbed form with
+// one query per position. With d_c' = d_n = d_v = 128 it costs what the
+// unabsorbed form costs (192 + 128 multiply-adds per query, key and branch;
+// two 128 x 128 projections per position and branch).
 //
-// Mapping onto CDNA4 (the decode's branch-per-wave layout with queries in
-// place of heads): a workgroup takes one sequence, one block of 128 query
-// positions, one head and one branch pair; wave (b, g) owns branch b of the
-// pair for the 32 queries of group g. Keys 0 .. the block's end stream
-// through the same LDS-DMA tile ring as the decode (branch_tiles.h). S^T =
-// K Q^T on v_mfma_f32_16x16x32_bf16 with 16 keys as M and 16 queries as N;
-// the S^T accumulators are the B operand of O^T = V^T P^T, so P stays in its
-// lane. The causal mask enters as the accumulators' start on each wave's
-// diagonal tile; tiles entirely after a wave's queries are skipped (the
-// wave still takes part in the barriers and the loads). The epilogue divides
-// by each query's softmax sum and writes the latent rows; positions t >= L_b
-// of the block get zeros.
+// Mapping onto CDNA4: a workgroup takes one sequence, one block of 64
+// positions and one head; wave (j, g) owns branch j for the 32 positions of
+// group g. Keys 0 .. the block's end stream through a ring of four LDS stages
+// (32 cached rows, all four branch slices and the RoPE key) by LDS-DMA.
+//   prologue  q~_j by MFMA from W_UK rows read straight into the A operand,
+//             laid out as the score MFMA's B operand; RoPE of the 64 queries
+//             once per workgroup through LDS; the first tiles in flight.
+//   loop      S^T = K Q^T (16 keys x 16 queries per v_mfma_f32_16x16x32_bf16),
+//             the causal mask as the accumulator start on a wave's diagonal
+//             tile, lazily rescaled online softmax per query lane, and
+//             O^T += V^T P^T with P kept in its lanes.
+//   epilogue  W_UV[h] staged in the ring; out^T = W_UV^T o~^T per branch on
+//             MFMA with o~ split into bf16 high and low parts (fp32-accurate
+//             product); the four branch partials summed in LDS in a fixed
+//             order and stored.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
+#include <math.h>
 
-#include "branch_tiles.h"
+#include "device_common.h"
 
 namespace mlra {
 namespace {
 
 using namespace dev;
-using namespace bt;
 
-// Arguments of the prefill kernel (one struct, passed by value).
+constexpr int kT = 32;                // keys per tile
+constexpr int kDC = 512;              // latent width
+constexpr int kBW = 128;              // branch width d_c'
+constexpr int kDR = 64;               // RoPE width
+constexpr int kDN = 128;              // NoPE query width
+constexpr int kDV = 128;              // value width
+constexpr int kNW = 8;                // waves: 4 branches x 2 position groups
+constexpr int kQW = 32;               // positions per wave
+constexpr int kQWG = 2 * kQW;         // positions per workgroup
+constexpr int kRowB = kDC * 2;        // LDS bytes of a cached latent row
+constexpr int kLat = kT * kRowB;      // latent part of a stage
+constexpr int kStage = kLat + kT * kDR * 2;
+constexpr int kNS = 4;                // ring stages
+constexpr int kD = kNS - 1;           // tiles in flight ahead of the one in use
+constexpr int kRing = kNS * kStage;
+constexpr int kRopeQ = kRing;         // RoPE queries [64][64] bf16
+constexpr int kLds = kRing + kQWG * kDR * 2;
+constexpr int kWPitch = kDV * 2 + 32; // staged W_UV row (padding spreads the banks)
+constexpr int kKL = kBW / 32;         // latent k-steps of a score
+constexpr int kKS = kKL + kDR / 32;   // plus the RoPE k-steps
+constexpr int kCB = kBW / 16;         // 16-row blocks of a branch's output
+constexpr int kNBLK = kQW / 16;       // 16-query blocks per wave
+constexpr int kVB = kDV / 16;         // 16-row blocks of the projected output
+constexpr float kRescale = 16.f;      // log2 headroom kept when the reference moves
+constexpr float kSumLimit = 1048576.f;  // 2^20: per-lane P sum that moves the reference
+// "no reference yet": finite, so masked scores (-inf) still give p = 0 while
+// every real score overflows to p = inf and forces the exact path
+constexpr float kNoRef = -3.0e38f;
+static_assert(kDC * kWPitch <= kRing, "W_UV fits the ring");
+static_assert(kNW * 64 * kVB * kNBLK * 16 <= kRing, "output partials fit the ring");
+static_assert(kLds <= 160 * 1024, "LDS");
+
+// 16-byte chunk swizzles: cached latent rows (1 KB) by row & 7, RoPE rows
+// (128 B) by (row >> 1) & 7
+__device__ __forceinline__ int swz_l(int t) { return 2 * (t & 7); }
+__device__ __forceinline__ int swz_r(int t) { return (t >> 1) & 7; }
+
 struct PrefillParams {
-  const __bf16* q_abs;  // [B][T][H][d_c + d_r]
+  const __bf16* q_nope;  // [B][T][H][d_n]
+  const __bf16* q_rope;  // [B][T][H][d_r], unrotated
+  const __bf16* w_uk;    // [H][d_c][d_n]
+  const __bf16* w_uv;    // [H][d_c][d_v]
   const __bf16* ckv;
   const __bf16* krope;
   int64_t ckv_bs, kr_bs;
-  int ckv_ts, kr_ts;
-  const int32_t* lens;  // [B]
-  float* latent;        // [B][T][H][d_c]
-  int B, T, H, QB;      // QB: 128-position query blocks per sequence
+  int ckv_ts, kr_ts;     // element strides (host checks the byte ranges fit 31 bits)
+  const int32_t* lens;   // [B]
+  void* out;             // [B][T][H][d_v]
+  int T, H, QB;          // QB: 64-position blocks per sequence
+  float scale_n, tau, alpha_kv, theta;
 };
 
-constexpr int kQW = 32;             // queries per wave
-constexpr int kQWG = 4 * kQW;       // queries per workgroup
+__device__ __forceinline__ void store4(float* p, f32x4 v) { *(f32x4*)p = v; }
+__device__ __forceinline__ void store4(__bf16* p, f32x4 v) {
+  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+  *(bf16x4*)p = (bf16x4){(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+}
 
-template <int NS>
-__global__ __launch_bounds__(512, 1) void prefill_branch_kernel(PrefillParams p) {
-  using C = BCfg<4, 2, kQW, 4>;  // two branches of the pair x four query groups
-  constexpr int D = NS - 1;
-  constexpr int DC = C::DC;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[NS * C::STAGE];
+// Workgroup barrier after this wave's LDS writes have completed; LDS-DMA
+// still in flight is not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <typename TO>
+__global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kLds];
   char LDS_AS* smem = (char LDS_AS*)smem_raw;
   const uint32_t sbase = (uint32_t)(uintptr_t)smem;
 
-  // workgroup -> (sequence, query block, head, branch pair); the pairs and
-  // heads of one query block are adjacent, so their K/V tiles meet in L2
-  // heads of one query block are adjacent, so their K/V tiles meet in L2;
-  // the longest (last) query blocks of each sequence are dispatched first
+  // workgroup -> (sequence, position block, head): the heads of one block
+  // are adjacent so that their key tiles meet in L2, and the longest (last)
+  // blocks of each sequence are dispatched first
   int i = blockIdx.x;
-  const int hg = i & 1;
-  i >>= 1;
   const int h = i % p.H;
   i /= p.H;
   const int qb = p.QB - 1 - i % p.QB, b = i / p.QB;
-  const int L = min(max(p.lens[b], 0), p.T);
+  const int T = p.T;
+  const int L = min(max(p.lens[b], 0), T);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int bw = wave % C::NBW, g = wave / C::NBW;
-  const int j = hg * C::NBW + bw;
+  const int j = wave & 3, g = wave >> 2;
   const int l16 = lane & 15, kg = lane >> 4;
-  const int q0 = qb * kQWG + g * kQW;  // this wave's first query position
-  const int row = DC + kDR;
+  const int q0 = qb * kQWG + g * kQW;  // this wave's first position
+  const int64_t orow = (int64_t)p.H * kDV;
+  TO* out_bh = (TO*)p.out + ((int64_t)b * T * p.H + h) * kDV;  // position t at + t * orow
 
-  if (qb * kQWG >= L) {  // the whole block lies past the sequence: zeros
+  if (qb * kQWG >= L) {  // every position of the block lies past the sequence
 #pragma unroll
-    for (int nb = 0; nb < C::NBLK; ++nb) {
+    for (int nb = 0; nb < kNBLK; ++nb) {
       const int t = q0 + 16 * nb + l16;
-      if (t >= p.T) continue;
-      float* dst = p.latent + (((int64_t)b * p.T + t) * p.H + h) * DC + kBW * j + 4 * kg;
+      if (t >= T) continue;
 #pragma unroll
-      for (int cb = 0; cb < C::CB; ++cb) *(f32x4*)(dst + 16 * cb) = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < 2; ++u)
+        store4(out_bh + t * orow + 16 * (2 * j + u) + 4 * kg, (f32x4){0.f, 0.f, 0.f, 0.f});
     }
     return;
   }
 
-  // per-lane LDS offsets, as in the decode (branch_tiles.h layout)
-  const int qk_lat = l16 * C::ROWB + 16 * ((16 * bw + kg) ^ swz_l(l16));
-  const int qk_rp = C::LAT + l16 * 128 + 16 * (kg ^ swz_r(l16));
-  int pv_lat;
-  {
-    const int t = 4 * kg + (l16 >> 2), half = l16 & 3;
-    pv_lat = t * C::ROWB + 16 * ((16 * bw + (half >> 1)) ^ swz_l(t)) + 8 * (half & 1);
-  }
-  const int lat_row = lane / (64 / C::RPI), lat_p = lane % (64 / C::RPI);
-  const int lat_c = 16 * (lat_p ^ swz_l(C::RPI * wave + lat_row)) + hg * C::ROWB;
-  const int rope_t = wave * 8 + (lane >> 3);
-  const int rope_c = 16 * ((lane & 7) ^ swz_r(rope_t));
-
+  // ---- key tiles: the first kD in flight while the queries are formed ----
   const int kend = min(L, qb * kQWG + kQWG);  // keys of this block: [0, kend)
   const int ntiles = (kend + kT - 1) / kT;
   const i32x4 crs = seq_rsrc(p.ckv + (int64_t)b * p.ckv_bs, kend, p.ckv_ts);
   const i32x4 krs = seq_rsrc(p.krope + (int64_t)b * p.kr_bs, kend, p.kr_ts);
-  const uint32_t lat_voff = (uint32_t)(lat_row * p.ckv_ts * 2 + lat_c);
-
-  // Q^T of this wave's queries (B operand): lane (query, kg) holds 8
-  // consecutive k of its query; positions past the sequence read row L - 1
-  bf16x8 q[C::KS][C::NBLK];
-#pragma unroll
-  for (int nb = 0; nb < C::NBLK; ++nb) {
-    const int t = min(q0 + 16 * nb + l16, L - 1);
-    const __bf16* qrow = p.q_abs + (((int64_t)b * p.T + t) * p.H + h) * row;
-#pragma unroll
-    for (int ks = 0; ks < C::KL; ++ks)
-      q[ks][nb] = *(const bf16x8*)(qrow + kBW * j + 32 * ks + 8 * kg);
-#pragma unroll
-    for (int ks = C::KL; ks < C::KS; ++ks)
-      q[ks][nb] = *(const bf16x8*)(qrow + DC + 32 * (ks - C::KL) + 8 * kg);
-  }
-  wait_vm<0>();
-
-  auto next_stage = [](int off) { return off + C::STAGE == NS * C::STAGE ? 0 : off + C::STAGE; };
+  // wave w fills latent rows w + 8u (u = 0..3) of a tile, all with row & 7 = w
+  const uint32_t lat_c = 16u * (uint32_t)(lane ^ swz_l(wave));
+  const int rope_t = wave * 8 + (lane >> 3);  // waves 0-3: RoPE rows
+  const int rope_c = 16 * ((lane & 7) ^ swz_r(rope_t));
   int dma_off = 0;
   auto issue = [&](int tile) {
     const uint32_t sa = sbase + dma_off;
-    dma_off = next_stage(dma_off);
+    dma_off = dma_off + kStage == kRing ? 0 : dma_off + kStage;
     const int ts0 = tile * kT;
-    if (ts0 + kT <= kend)
-      issue_tile<C, false>(sa, crs, krs, p.ckv_ts, p.kr_ts, ts0, kend, wave, lane, lat_voff,
-                           lat_c, rope_t, rope_c);
-    else
-      issue_tile<C, true>(sa, crs, krs, p.ckv_ts, p.kr_ts, ts0, kend, wave, lane, lat_voff, lat_c,
-                          rope_t, rope_c);
+    if (ts0 + kT <= kend) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = wave + 8 * u;
+        dma16(crs, sa + r * kRowB, lat_c, (uint32_t)((ts0 + r) * p.ckv_ts * 2));
+      }
+    } else {  // the block's last tile: rows past its keys repeat the last key
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = wave + 8 * u;
+        const int row = min(ts0 + r, kend - 1);
+        dma16(crs, sa + r * kRowB, (uint32_t)(row * p.ckv_ts * 2) + lat_c, 0u);
+      }
+    }
+    if (wave < 4) {
+      const int row = min(ts0 + rope_t, kend - 1);
+      dma16(krs, sa + kLat + wave * 1024, (uint32_t)(row * p.kr_ts * 2 + rope_c), 0u);
+    }
   };
 #pragma unroll
-  for (int s = 0; s < D; ++s)
+  for (int s = 0; s < kD; ++s)
     if (s < ntiles) issue(s);
 
-  f32x4 o[C::CB][C::NBLK];
+  // ---- RoPE queries of the 64 positions, once per workgroup ----
+  for (int e = threadIdx.x; e < kQWG * (kDR / 2); e += 64 * kNW) {
+    const int qi = e / (kDR / 2), k = e % (kDR / 2);
+    const int t = min(qb * kQWG + qi, T - 1);
+    const __bf16* x = p.q_rope + (((int64_t)b * T + t) * p.H + h) * kDR + 2 * k;
+    const double omega = pow((double)p.theta, -2.0 * (double)k / (double)kDR);
+    double sn, cs;
+    sincos((double)t * omega, &sn, &cs);
+    const double x0 = (float)x[0], x1 = (float)x[1];
+    __bf16 LDS_AS* d = (__bf16 LDS_AS*)(smem + kRopeQ + qi * (kDR * 2)) + 2 * k;
+    d[0] = (__bf16)(float)(p.tau * (x0 * cs - x1 * sn));
+    d[1] = (__bf16)(float)(p.tau * (x0 * sn + x1 * cs));
+  }
+
+  // ---- absorbed queries q~_j of this wave's positions (B operand of the
+  // scores: lane (position, kg) holds latent columns 32 ks + 8 kg + 0..7) ----
+  bf16x8 q[kKS][kNBLK];
+  {
+    bf16x8 qn[kDN / 32][kNBLK];
 #pragma unroll
-  for (int cb = 0; cb < C::CB; ++cb)
+    for (int nb = 0; nb < kNBLK; ++nb) {
+      const int t = min(q0 + 16 * nb + l16, T - 1);
+      const __bf16* r = p.q_nope + (((int64_t)b * T + t) * p.H + h) * kDN;
 #pragma unroll
-    for (int nb = 0; nb < C::NBLK; ++nb) o[cb][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m_run[C::NBLK], l_run[C::NBLK];
+      for (int kn = 0; kn < kDN / 32; ++kn) qn[kn][nb] = *(const bf16x8*)(r + 32 * kn + 8 * kg);
+    }
+    const __bf16* wk = p.w_uk + ((int64_t)h * kDC + kBW * j) * kDN;
 #pragma unroll
-  for (int nb = 0; nb < C::NBLK; ++nb) {
+    for (int ks = 0; ks < kKL; ++ks) {
+      // A row l16 of half s is latent column 32 ks + 8 (l16 >> 2) + 4 s +
+      // (l16 & 3), so that output row 4 kg + i lands on column 32 ks + 8 kg +
+      // 4 s + i of the query lane
+      f32x4 acc[2][kNBLK];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int c = 32 * ks + 8 * (l16 >> 2) + 4 * s + (l16 & 3);
+        bf16x8 a[kDN / 32];
+#pragma unroll
+        for (int kn = 0; kn < kDN / 32; ++kn) a[kn] = *(const bf16x8*)(wk + c * kDN + 32 * kn + 8 * kg);
+#pragma unroll
+        for (int nb = 0; nb < kNBLK; ++nb) {
+          acc[s][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kn = 0; kn < kDN / 32; ++kn)
+            acc[s][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kn], qn[kn][nb], acc[s][nb], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < kNBLK; ++nb)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) q[ks][nb][4 * s + e] = (__bf16)(p.scale_n * acc[s][nb][e]);
+    }
+  }
+  lds_barrier();  // RoPE queries staged
+#pragma unroll
+  for (int nb = 0; nb < kNBLK; ++nb) {
+    const int qi = g * kQW + 16 * nb + l16;
+#pragma unroll
+    for (int kr = 0; kr < kKS - kKL; ++kr)
+      q[kKL + kr][nb] = *(const bf16x8 LDS_AS*)(smem + kRopeQ + qi * (kDR * 2) + 64 * kr + 16 * kg);
+  }
+
+  // ---- per-lane LDS offsets within a stage ----
+  // score A operand (keys l16, l16 + 16): k-step ks at (qk_lat ^ 64 ks)
+  const int qk_lat = l16 * kRowB + 16 * ((16 * j + kg) ^ swz_l(l16));
+  const int qk_rp = kLat + l16 * 128 + 16 * (kg ^ swz_r(l16));
+  // value A operand (V^T, transposed 4 x 16 reads): block cb at (pv_lat ^ 32 cb)
+  int pv_lat;
+  {
+    const int t = 4 * kg + (l16 >> 2), half = l16 & 3;
+    pv_lat = t * kRowB + 16 * ((16 * j + (half >> 1)) ^ swz_l(t)) + 8 * (half & 1);
+  }
+
+  f32x4 o[kCB][kNBLK];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+    for (int nb = 0; nb < kNBLK; ++nb) o[cb][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m_run[kNBLK], l_run[kNBLK];
+#pragma unroll
+  for (int nb = 0; nb < kNBLK; ++nb) {
     m_run[nb] = kNoRef;
     l_run[nb] = 0.f;
   }
-  // this wave's diagonal tile (q0 is 32-aligned); a wave whose queries all
-  // lie past the sequence computes nothing (its rows are written as zeros)
+  // this wave's diagonal tile (q0 is 32-aligned); a wave whose positions all
+  // lie past the sequence computes nothing (its rows come out zero)
   const int last = q0 < L ? q0 / kT : -1;
 
   int cur_off = 0;
   for (int it = 0; it < ntiles; ++it) {
-    wait_tiles<C, D - 1>(min(D - 1, ntiles - 1 - it), wave);
+    // this wave's DMA of tile `it` has landed: waves 0-3 issue 5 loads per
+    // tile, waves 4-7 issue 4, and `ahead` later tiles may still be in flight
+    {
+      const int ahead = min(kD - 1, ntiles - 1 - it);
+      if (wave < 4) {
+        if (ahead >= 2) wait_vm<10>(); else if (ahead == 1) wait_vm<5>(); else wait_vm<0>();
+      } else {
+        if (ahead >= 2) wait_vm<8>(); else if (ahead == 1) wait_vm<4>(); else wait_vm<0>();
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    // the stage of tile it + D last held tile it - 1, which every wave has
+    // the stage of tile it + kD last held tile it - 1, which every wave has
     // finished before this barrier
-    if (it + D < ntiles) issue(it + D);
+    if (it + kD < ntiles) issue(it + kD);
     const char LDS_AS* st = smem + __builtin_amdgcn_readfirstlane(cur_off);
-    cur_off = next_stage(cur_off);
-    if (it > last) continue;  // keys after all of this wave's queries
+    cur_off = cur_off + kStage == kRing ? 0 : cur_off + kStage;
+    if (it > last) continue;  // keys after all of this wave's positions
 
-    bf16x8 A[2][C::KS];
+    bf16x8 A[2][kKS];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-      for (int ks = 0; ks < C::KL; ++ks)
+      for (int ks = 0; ks < kKL; ++ks)
         A[mb][ks] = *(const bf16x8 LDS_AS*)((const char LDS_AS*)(((uintptr_t)(st + qk_lat)) ^ (64 * ks)) +
-                                            mb * 16 * C::ROWB);
-      A[mb][C::KL] = *(const bf16x8 LDS_AS*)(st + qk_rp + mb * 2048);
-      A[mb][C::KL + 1] =
+                                            mb * 16 * kRowB);
+      A[mb][kKL] = *(const bf16x8 LDS_AS*)(st + qk_rp + mb * 2048);
+      A[mb][kKL + 1] =
           *(const bf16x8 LDS_AS*)((const char LDS_AS*)(((uintptr_t)(st + qk_rp)) ^ 64) + mb * 2048);
     }
-    bf16x8 V[C::CB];
+    bf16x8 V[kCB];
 #pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb) {
+    for (int cb = 0; cb < kCB; ++cb) {
       const char LDS_AS* a = (const char LDS_AS*)(((uintptr_t)(st + pv_lat)) ^ (32 * cb));
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)a);
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(a + 16 * C::ROWB));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(a + 16 * kRowB));
       const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       V[cb] = __builtin_bit_cast(bf16x8, v);
     }
 
     // S^T = K Q^T, starting from the causal mask on the diagonal tile: key
-    // row 16 mb + 4 kg + e of the tile against query column 16 nb + l16
-    f32x4 S[2][C::NBLK];
+    // row 16 mb + 4 kg + e of the tile against position column 16 nb + l16
+    f32x4 S[2][kNBLK];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < C::NBLK; ++nb) {
+      for (int nb = 0; nb < kNBLK; ++nb) {
         f32x4 init = {0.f, 0.f, 0.f, 0.f};
         if (it == last) {
 #pragma unroll
@@ -207,15 +331,15 @@ __global__ __launch_bounds__(512, 1) void prefill_branch_kernel(PrefillParams p)
         }
         S[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][0], q[0][nb], init, 0, 0, 0);
 #pragma unroll
-        for (int ks = 1; ks < C::KS; ++ks)
+        for (int ks = 1; ks < kKS; ++ks)
           S[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][ks], q[ks][nb], S[mb][nb], 0, 0, 0);
       }
 
-    // online softmax per query (lane), lazily rescaled as in the decode: P
-    // against the running reference, the exact tile max only when a lane's
-    // sum of P passes 2^20 or is infinite (no reference yet)
-    bf16x8 P[C::NBLK];
-    float ps[C::NBLK];
+    // online softmax per position (lane), lazily rescaled: P against the
+    // running reference, the exact tile max only when a lane's sum of P
+    // passes 2^20 or is infinite (no reference yet)
+    bf16x8 P[kNBLK];
+    float ps[kNBLK];
     bool need = false;
     auto probs = [&](int nb) {
       ps[nb] = 0.f;
@@ -229,13 +353,13 @@ __global__ __launch_bounds__(512, 1) void prefill_branch_kernel(PrefillParams p)
         }
     };
 #pragma unroll
-    for (int nb = 0; nb < C::NBLK; ++nb) {
+    for (int nb = 0; nb < kNBLK; ++nb) {
       probs(nb);
       need |= !(ps[nb] <= kSumLimit);
     }
     if (__builtin_expect(__any(need), 0)) {
 #pragma unroll
-      for (int nb = 0; nb < C::NBLK; ++nb) {
+      for (int nb = 0; nb < kNBLK; ++nb) {
         const float mx = fmaxf(fmaxf(fmaxf(S[0][nb][0], S[0][nb][1]), fmaxf(S[0][nb][2], S[0][nb][3])),
                                fmaxf(fmaxf(S[1][nb][0], S[1][nb][1]), fmaxf(S[1][nb][2], S[1][nb][3])));
         const float mt = max4(mx) * kLog2e;
@@ -244,61 +368,132 @@ __global__ __launch_bounds__(512, 1) void prefill_branch_kernel(PrefillParams p)
         const float f = __builtin_amdgcn_exp2f(mr - mn);
         l_run[nb] *= f;
 #pragma unroll
-        for (int cb = 0; cb < C::CB; ++cb) o[cb][nb] *= f;
+        for (int cb = 0; cb < kCB; ++cb) o[cb][nb] *= f;
         m_run[nb] = mn;
         probs(nb);
       }
     }
 #pragma unroll
-    for (int nb = 0; nb < C::NBLK; ++nb) l_run[nb] += ps[nb];
+    for (int nb = 0; nb < kNBLK; ++nb) l_run[nb] += ps[nb];
 
 #pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb)
+    for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
-      for (int nb = 0; nb < C::NBLK; ++nb)
+      for (int nb = 0; nb < kNBLK; ++nb)
         o[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(V[cb], P[nb], o[cb][nb], 0, 0, 0);
   }
 
-  // normalised branch latent of each query; positions past the sequence: 0
+  // ---- o~ normalised per position and split into bf16 high + low parts:
+  // B operand of out^T = W_UV^T o~^T, lane (position, kg) holding k index
+  // 8 kg + 4 s + i = latent column 32 pp + 16 s + 4 kg + i of the branch ----
+  bf16x8 oh[kCB / 2][kNBLK], ol[kCB / 2][kNBLK];
 #pragma unroll
-  for (int nb = 0; nb < C::NBLK; ++nb) {
+  for (int nb = 0; nb < kNBLK; ++nb) {
     const int t = q0 + 16 * nb + l16;
     const float lt = sum4(l_run[nb]);
-    if (t >= p.T) continue;
     const float inv = t < L ? 1.f / lt : 0.f;
-    float* dst = p.latent + (((int64_t)b * p.T + t) * p.H + h) * DC + kBW * j + 4 * kg;
 #pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb) *(f32x4*)(dst + 16 * cb) = o[cb][nb] * inv;
+    for (int pp = 0; pp < kCB / 2; ++pp)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = o[2 * pp + s][nb][e] * inv;
+          const __bf16 hv = (__bf16)v;
+          oh[pp][nb][4 * s + e] = hv;
+          ol[pp][nb][4 * s + e] = (__bf16)(v - (float)hv);
+        }
   }
-}
 
-__global__ void fill_positions(int32_t* pos, int B, int T) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < (int64_t)B * T) pos[i] = (int32_t)(i % T);
+  // ---- W_UV[h] into the ring as [c][v] rows of kWPitch bytes ----
+  lds_barrier();  // every wave is done with the key tiles
+  {
+    const __bf16* w = p.w_uv + (int64_t)h * kDC * kDV;
+    constexpr int NQ = kDC * kDV * 2 / 16 / (64 * kNW);  // 16-byte pieces per thread
+    bf16x8 stg[NQ];
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int e = threadIdx.x + 64 * kNW * u, c = e >> 4, ch = e & 15;
+      stg[u] = *(const bf16x8*)(w + c * kDV + 8 * ch);
+    }
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int e = threadIdx.x + 64 * kNW * u, c = e >> 4, ch = e & 15;
+      *(bf16x8 LDS_AS*)(smem + c * kWPitch + 16 * ch) = stg[u];
+    }
+  }
+  lds_barrier();
+
+  // ---- this branch's part of out^T: A = W_UV^T rows v (transposed reads of
+  // latent rows 32 pp + 4 kg + 0..3 and + 16), B = o~ high, then low ----
+  f32x4 acc[kVB][kNBLK];
+  {
+    const int r4 = l16 >> 2, q4 = l16 & 3;
+#pragma unroll
+    for (int vb = 0; vb < kVB; ++vb) {
+#pragma unroll
+      for (int nb = 0; nb < kNBLK; ++nb) acc[vb][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int pp = 0; pp < kCB / 2; ++pp) {
+        const char LDS_AS* a =
+            smem + (kBW * j + 32 * pp + 4 * kg + r4) * kWPitch + 2 * (16 * vb + 4 * q4);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)a);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(a + 16 * kWPitch));
+        const i16x8 wv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const bf16x8 W = __builtin_bit_cast(bf16x8, wv);
+#pragma unroll
+        for (int nb = 0; nb < kNBLK; ++nb) {
+          acc[vb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(W, oh[pp][nb], acc[vb][nb], 0, 0, 0);
+          acc[vb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(W, ol[pp][nb], acc[vb][nb], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- branch partials through LDS, summed j = 0..3 in order, stored ----
+  lds_barrier();  // every wave is done with W_UV
+  {
+    char LDS_AS* mine = smem + wave * (kVB * kNBLK * 1024) + lane * 16;
+#pragma unroll
+    for (int vb = 0; vb < kVB; ++vb)
+#pragma unroll
+      for (int nb = 0; nb < kNBLK; ++nb) *(f32x4 LDS_AS*)(mine + (vb * kNBLK + nb) * 1024) = acc[vb][nb];
+  }
+  lds_barrier();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int vb = 2 * j + u;
+#pragma unroll
+    for (int nb = 0; nb < kNBLK; ++nb) {
+      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        sum += *(const f32x4 LDS_AS*)(smem + (4 * g + jj) * (kVB * kNBLK * 1024) +
+                                      (vb * kNBLK + nb) * 1024 + lane * 16);
+      const int t = q0 + 16 * nb + l16;
+      if (t < T) store4(out_bh + t * orow + 16 * vb + 4 * kg, sum * p.alpha_kv);
+    }
+  }
 }
 
 }  // namespace
 
-hipError_t launch_fill_positions(int32_t* pos, int B, int T, hipStream_t s) {
-  const int64_t n = (int64_t)B * T;
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_positions, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, pos, B, T);
-  return hipGetLastError();
-}
-
 bool prefill_branch_supported(const Geom& g) {
-  return g.dr == kDR && g.dc == 4 * kBW && g.n == 4;
+  return g.dr == kDR && g.dc == kDC && g.n == kDC / kBW && g.dn == kDN && g.dv == kDV;
 }
 
-hipError_t launch_prefill_branch(const Geom& g, int T, const void* q_abs, const void* ckv,
-                                 const void* krope, const int32_t* lens, float* latent,
-                                 hipStream_t s) {
+hipError_t launch_prefill_branch(const Geom& g, int T, const void* q_nope, const void* q_rope,
+                                 const void* w_uk, const void* w_uv, const void* ckv,
+                                 const void* krope, const int32_t* lens, void* out, bool out_bf16,
+                                 float tau, float alpha_q, float alpha_kv, float theta,
+                                 hipStream_t s, const KernelTiming& t) {
   if (!prefill_branch_supported(g)) return hipErrorNotSupported;
   if (g.B <= 0 || T <= 0) return hipSuccess;
-  using C = BCfg<4, 2, kQW, 4>;
-  constexpr int NS = (160 * 1024) / C::STAGE < 7 ? (160 * 1024) / C::STAGE : 7;
   PrefillParams p;
-  p.q_abs = (const __bf16*)q_abs;
+  p.q_nope = (const __bf16*)q_nope;
+  p.q_rope = (const __bf16*)q_rope;
+  p.w_uk = (const __bf16*)w_uk;
+  p.w_uv = (const __bf16*)w_uv;
   p.ckv = (const __bf16*)ckv;
   p.krope = (const __bf16*)krope;
   p.ckv_bs = g.ckv_bs;
@@ -306,14 +501,22 @@ hipError_t launch_prefill_branch(const Geom& g, int T, const void* q_abs, const 
   p.kr_bs = g.kr_bs;
   p.kr_ts = (int)g.kr_ts;
   p.lens = lens;
-  p.latent = latent;
-  p.B = g.B;
+  p.out = out;
   p.T = T;
   p.H = g.H;
   p.QB = (T + kQWG - 1) / kQWG;
-  const int64_t grid = (int64_t)g.B * p.QB * g.H * 2;
+  p.scale_n = alpha_q * tau;
+  p.tau = tau;
+  p.alpha_kv = alpha_kv;
+  p.theta = theta;
+  const int64_t grid = (int64_t)g.B * p.QB * g.H;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_branch_kernel<NS>), dim3((unsigned)grid), dim3(64 * C::NW), 0, s, p);
+  if (out_bf16)
+    hipExtLaunchKernelGGL(prefill_kernel<__bf16>, dim3((unsigned)grid), dim3(64 * kNW), 0, s,
+                          t.start, t.stop, 0, p);
+  else
+    hipExtLaunchKernelGGL(prefill_kernel<float>, dim3((unsigned)grid), dim3(64 * kNW), 0, s,
+                          t.start, t.stop, 0, p);
   return hipGetLastError();
 }
 

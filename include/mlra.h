@@ -199,41 +199,37 @@ MLRA_API mlra_status_t mlra_cache_append(const mlra_config_t* cfg, int32_t batch
                                          int64_t krope_token_stride, int32_t* cache_lens,
                                          int32_t max_len, void* stream);
 
-/* Bytes of workspace mlra_prefill needs for `batch` sequences of up to
- * `max_len` positions (host only). */
-MLRA_API mlra_status_t mlra_prefill_workspace_size(const mlra_config_t* cfg, int32_t batch,
-                                                   int32_t max_len, size_t* bytes);
-
-/* Causal prefill over the cache ("vllbc02MLA", 苏神思路: a prompt attends
- * causally, each position to the tokens up to itself; "Multi-Head Low-Rank
- * Attention", 核心方法: one softmax per branch, outputs summed with alpha_kv).
- * For every position t < L_b of every sequence b, out[b][t][h] is what
- * mlra_decode returns for sequence b when its cache holds the rows 0..t and
- * its query sits at position t: the same absorbed form, with t's own query.
+/* Causal prefill over the cache ("MLA多头潜在注意力机制" 3.3: a key after the
+ * query's position is masked; "Multi-Head Low-Rank Attention", 核心方法 and
+ * 方法步骤详情: one softmax per branch, outputs summed with alpha_kv). For every
+ * position t < L_b of every sequence b, out[b][t][h] is what mlra_decode
+ * returns for sequence b when its cache holds the rows 0..t and its query
+ * sits at position t: the same absorbed form, with t's own query.
  *
  *   q_nope  device [batch][max_len][H][d_nope], q_rope [batch][max_len][H][d_rope]
- *           (unrotated; position t of sequence b is row (b, t)), cfg->dtype.
- *   cache   as for mlra_decode; rows 0..L_b-1 must hold the prompt (e.g. from
- *           mlra_cache_append). Its max_len is T.
+ *           (unrotated; position t of sequence b is row (b, t)), bf16.
+ *   w_uk, w_uv  as for mlra_decode.
+ *   cache   as for mlra_decode; rows 0..L_b-1 hold the prompt (for example
+ *           from mlra_cache_append); its max_len is the prompt length T.
  *   out     device [batch][max_len][H][d_v], out_dtype; rows t >= L_b get 0.
- *   workspace  mlra_prefill_workspace_size bytes, 256-byte aligned (about
- *           B*T*H*(2(d_c+d_r) + 4 d_c) bytes: absorbed queries and latents).
  *
- * Supported: bf16 MLRA with 128-wide branches (num_branches 4, d_latent 512,
- * d_rope 64) and batch * max_len <= 2^22 rows, else UNSUPPORTED; argument
- * checks as for mlra_decode. With
- * d_c' = d_nope = d_v, this absorbed form costs the same multiply-adds as the
- * unabsorbed one. Enqueued on `stream`; nothing is allocated. */
+ * One kernel: absorption, attention and the W_UV projection stay on chip, so
+ * no workspace is needed. Supported: bf16 MLRA-4 at d_latent 512, d_rope 64,
+ * d_nope 128, d_v 128, per-sequence byte ranges below 2^31 and
+ * batch * max_len <= 2^22 rows, else UNSUPPORTED; argument checks as for
+ * mlra_decode. With d_c' = d_nope = d_v this absorbed form costs the same
+ * multiply-adds as the unabsorbed one. Enqueued on `stream`; nothing is
+ * allocated. */
 MLRA_API mlra_status_t mlra_prefill(const mlra_config_t* cfg, int32_t num_branches, int32_t batch,
                                     const void* q_nope, const void* q_rope, const void* w_uk,
-                                    const void* w_uv, const mlra_cache_t* cache, void* workspace,
-                                    size_t ws_bytes, void* out, mlra_dtype_t out_dtype,
-                                    void* stream);
+                                    const void* w_uv, const mlra_cache_t* cache, void* out,
+                                    mlra_dtype_t out_dtype, void* stream);
 
 /* Instrumentation: when both are non-NULL hipEvent_t handles (created by the
  * caller, owned by the caller, valid until timing is stopped), every later
- * call made on this thread has the split-KV decode dispatch stamp `before`
- * when it starts and `after` when it ends (hipExtLaunchKernel), so that
+ * call made on this thread has the split-KV decode dispatch (mlra_decode,
+ * mla_decode_attn) or the causal attention dispatch (mlra_prefill) stamp
+ * `before` when it starts and `after` when it ends (hipExtLaunchKernel), so that
  * hipEventElapsedTime gives that kernel's duration and the stream carries no
  * extra packets. Pass NULL, NULL to stop. Giving only one is INVALID_ARG. */
 MLRA_API mlra_status_t mlra_set_kernel_timing(void* before, void* after);

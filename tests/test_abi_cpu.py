@@ -34,7 +34,7 @@ def gpu_present():
 def test_library_exports_every_declared_symbol():
     L = br.lib()
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(br.EXPORTS)
@@ -199,32 +199,27 @@ def test_cache_append_validation():
     assert append(cfg(d_rope=0), kr=0, kts=0) in (br.MLRA_OK, br.MLRA_ERR_NO_DEVICE)
 
 
-def prefill(c, n=4, q=FAKE, ws=FAKE, ws_bytes=None, out=FAKE, od=0, k=None, B=4):
+def prefill(c, n=4, q=FAKE, out=FAKE, od=0, k=None, B=4):
     k = cache() if k is None else k
-    if ws_bytes is None:
-        ws_bytes = br.prefill_workspace_size(c, B, k.max_len)
-    return br.lib().mlra_prefill(ctypes.byref(c), n, B, q, FAKE, FAKE, FAKE, ctypes.byref(k), ws,
-                                 ws_bytes, out, od, None)
+    return br.lib().mlra_prefill(ctypes.byref(c), n, B, q, FAKE, FAKE, FAKE, ctypes.byref(k), out,
+                                 od, None)
 
 
-def test_prefill_workspace_and_validation():
+def test_prefill_validation():
     c = cfg()
-    a = br.prefill_workspace_size(c, 2, 1024)
-    # positions + absorbed queries (bf16) + fp32 latents, 256-byte aligned parts
-    assert a % 256 == 0 and a >= 2 * 1024 * 128 * (2 * 576 + 4 * 512)
-    assert br.prefill_workspace_size(c, 4, 1024) > a
     assert prefill(c, n=3) == br.MLRA_ERR_INVALID_ARG             # 3 does not divide d_latent
     assert prefill(c, n=1) == br.MLRA_ERR_UNSUPPORTED              # MLA: no prefill kernel
     assert prefill(cfg(dtype="fp32")) == br.MLRA_ERR_UNSUPPORTED
     assert prefill(cfg(d_rope=32)) == br.MLRA_ERR_UNSUPPORTED
+    assert prefill(cfg(d_v=64)) == br.MLRA_ERR_UNSUPPORTED
     assert prefill(c, q=0) == br.MLRA_ERR_INVALID_ARG
     assert prefill(c, out=0) == br.MLRA_ERR_INVALID_ARG
+    assert prefill(c, out=FAKE + 4) == br.MLRA_ERR_INVALID_ARG      # 16-byte alignment
     assert prefill(c, od=7) == br.MLRA_ERR_INVALID_ARG
-    assert prefill(c, ws_bytes=1024) == br.MLRA_ERR_WORKSPACE
-    assert prefill(c, ws=0) == br.MLRA_ERR_WORKSPACE
-    assert prefill(c, ws=FAKE + 16) == br.MLRA_ERR_INVALID_ARG    # 256-B alignment
     assert prefill(c, k=cache(ckv=0)) == br.MLRA_ERR_INVALID_ARG
-    assert prefill(c, B=-1, ws_bytes=1 << 30) == br.MLRA_ERR_INVALID_ARG
+    assert prefill(c, B=-1) == br.MLRA_ERR_INVALID_ARG
+    big = cache(max_len=65536, bs=576 * 65536)
+    assert prefill(c, k=big, B=65) == br.MLRA_ERR_UNSUPPORTED        # over 2^22 prompt rows
     # nothing to do: succeeds without a device
     assert prefill(c, B=0) == br.MLRA_OK
     assert prefill(c, k=cache(max_len=0)) == br.MLRA_OK

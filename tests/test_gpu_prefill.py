@@ -28,8 +28,7 @@ def run_prefill(w, inp, d=None, out_dtype=torch.float32):
     cfg = config_for(w)
     B, T = d.B, d.Lmax
     out = torch.empty(B, T, w.heads, w.d_v, dtype=out_dtype, device="cuda")
-    ws = br.alloc_prefill_workspace(cfg, B, T)
-    br.mlra_prefill(cfg, w.n, d.q_nope, d.q_rope, d.w_uk, d.w_uv, d.cache(cfg), ws, out)
+    br.mlra_prefill(cfg, w.n, d.q_nope, d.q_rope, d.w_uk, d.w_uv, d.cache(cfg), out)
     torch.cuda.synchronize()
     return out, d
 
@@ -52,8 +51,8 @@ def check_rows(got, ref, lens):
 
 @pytest.mark.parametrize("lens,T", [([300, 1, 129, 0], 300), ([128, 127, 33], 160)])
 def test_prefill_all_rows_small(lens, T):
-    # several 128-position query blocks, ragged last blocks and tiles, a
-    # one-token prompt and an empty one
+    # several 64-position blocks, ragged last blocks and tiles, a one-token
+    # prompt and an empty one
     w = WORKLOADS["mlra4_prefill_b4_t4k"].replace(batch=len(lens), heads=8)
     inp = make_inputs(w, lens=np.array(lens, np.int32), max_len=T, q_rows=T)
     say(f"prefill lens {lens} T={T}")
