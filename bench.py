@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the causal prefill leg (MLRA-4, 4 prompts of 4096 tokens)")
     ap.add_argument("--prefill-workload", default="mlra4_prefill_b4_t4k")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the prefill leg: print its JSON object and stop")
     ap.add_argument("--time-every", type=int, default=4,
                     help="stamp the decode dispatch's start/end events on every N-th timed step")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
@@ -351,6 +353,9 @@ def main():
     br.lib()  # fails loudly when the HIP library is missing
     if a.probe_copy:
         probe_copy(torch)
+        return
+    if a.prefill_only:
+        print(json.dumps(time_prefill(a.prefill_workload, a.steps, a.warmup, torch, br, synth)))
         return
     main_r = run_workload(a.workload, a.steps, a.warmup, a.cache_bytes_min, torch, br, synth,
                           a.kernel, a.time_every, clock=not a.no_clock)

@@ -67,9 +67,6 @@ constexpr int kNBLK = kQW / 16;       // 16-query blocks per wave
 constexpr int kVB = kDV / 16;         // 16-row blocks of the projected output
 constexpr float kRescale = 16.f;      // log2 headroom kept when the reference moves
 constexpr float kSumLimit = 1048576.f;  // 2^20: per-lane P sum that moves the reference
-// "no reference yet": finite, so masked scores (-inf) still give p = 0 while
-// every real score overflows to p = inf and forces the exact path
-constexpr float kNoRef = -3.0e38f;
 static_assert(kDC * kWPitch <= kRing, "W_UV fits the ring");
 static_assert(kNW * 64 * kVB * kNBLK * 16 <= kRing, "output partials fit the ring");
 static_assert(kLds <= 160 * 1024, "LDS");
@@ -91,7 +88,8 @@ struct PrefillParams {
   const int32_t* lens;   // [B]
   void* out;             // [B][T][H][d_v]
   int T, H, QB;          // QB: 64-position blocks per sequence
-  float scale_n, tau, alpha_kv, theta;
+  float scale_n, scale_r;  // query scales, log2(e) folded in: alpha_q tau log2e, tau log2e
+  float alpha_kv, theta;
 };
 
 __device__ __forceinline__ void store4(float* p, f32x4 v) { *(f32x4*)p = v; }
@@ -182,23 +180,32 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
   for (int s = 0; s < kD; ++s)
     if (s < ntiles) issue(s);
 
-  // ---- RoPE queries of the 64 positions, once per workgroup ----
-  for (int e = threadIdx.x; e < kQWG * (kDR / 2); e += 64 * kNW) {
-    const int qi = e / (kDR / 2), k = e % (kDR / 2);
-    const int t = min(qb * kQWG + qi, T - 1);
-    const __bf16* x = p.q_rope + (((int64_t)b * T + t) * p.H + h) * kDR + 2 * k;
+  // ---- RoPE queries of the 64 positions, once per workgroup: the angle
+  // t * theta^(-2k/d_r) and its reduction to [-pi, pi] in double precision,
+  // sine and cosine of the reduced angle in float ----
+  {
+    static_assert((64 * kNW) % (kDR / 2) == 0, "one frequency per thread");
+    const int k = threadIdx.x % (kDR / 2);
     const double omega = pow((double)p.theta, -2.0 * (double)k / (double)kDR);
-    double sn, cs;
-    sincos((double)t * omega, &sn, &cs);
-    const double x0 = (float)x[0], x1 = (float)x[1];
-    __bf16 LDS_AS* d = (__bf16 LDS_AS*)(smem + kRopeQ + qi * (kDR * 2)) + 2 * k;
-    d[0] = (__bf16)(float)(p.tau * (x0 * cs - x1 * sn));
-    d[1] = (__bf16)(float)(p.tau * (x0 * sn + x1 * cs));
+    for (int e = threadIdx.x; e < kQWG * (kDR / 2); e += 64 * kNW) {
+      const int qi = e / (kDR / 2);
+      const int t = min(qb * kQWG + qi, T - 1);
+      const __bf16* x = p.q_rope + (((int64_t)b * T + t) * p.H + h) * kDR + 2 * k;
+      const double a = (double)t * omega;
+      const double r = a - 6.283185307179586 * rint(a * 0.15915494309189535);
+      float sn, cs;
+      sincosf((float)r, &sn, &cs);
+      const float x0 = (float)x[0], x1 = (float)x[1];
+      __bf16 LDS_AS* d = (__bf16 LDS_AS*)(smem + kRopeQ + qi * (kDR * 2)) + 2 * k;
+      d[0] = (__bf16)(p.scale_r * (x0 * cs - x1 * sn));
+      d[1] = (__bf16)(p.scale_r * (x0 * sn + x1 * cs));
+    }
   }
 
   // ---- absorbed queries q~_j of this wave's positions (B operand of the
   // scores: lane (position, kg) holds latent columns 32 ks + 8 kg + 0..7) ----
   bf16x8 q[kKS][kNBLK];
+  bf16x8 qlo[kKL][kNBLK];  // low bf16 parts of the latent columns: q~ = q + qlo
   {
     bf16x8 qn[kDN / 32][kNBLK];
 #pragma unroll
@@ -234,7 +241,12 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) q[ks][nb][4 * s + e] = (__bf16)(p.scale_n * acc[s][nb][e]);
+          for (int e = 0; e < 4; ++e) {
+            const float v = p.scale_n * acc[s][nb][e];
+            const __bf16 hi = (__bf16)v;
+            q[ks][nb][4 * s + e] = hi;
+            qlo[ks][nb][4 * s + e] = (__bf16)(v - (float)hi);
+          }
     }
   }
   lds_barrier();  // RoPE queries staged
@@ -262,10 +274,12 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
   for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
     for (int nb = 0; nb < kNBLK; ++nb) o[cb][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // scores come out of the MFMA in log2 units relative to the running
+  // reference m_run of their position (the accumulators start at -m_run)
   float m_run[kNBLK], l_run[kNBLK];
 #pragma unroll
   for (int nb = 0; nb < kNBLK; ++nb) {
-    m_run[nb] = kNoRef;
+    m_run[nb] = 0.f;
     l_run[nb] = 0.f;
   }
   // this wave's diagonal tile (q0 is 32-aligned); a wave whose positions all
@@ -316,45 +330,53 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
       V[cb] = __builtin_bit_cast(bf16x8, v);
     }
 
-    // S^T = K Q^T, starting from the causal mask on the diagonal tile: key
-    // row 16 mb + 4 kg + e of the tile against position column 16 nb + l16
+    // S^T - m_run = K Q^T - m_run (log2 units), the accumulators starting
+    // at -m_run of their position, or at -inf where the causal mask of the
+    // diagonal tile hides key row 16 mb + 4 kg + e from position column
+    // 16 nb + l16. The four (mb, nb) accumulations run interleaved k-step by
+    // k-step, so that consecutive MFMAs are independent.
     f32x4 S[2][kNBLK];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int nb = 0; nb < kNBLK; ++nb) {
-        f32x4 init = {0.f, 0.f, 0.f, 0.f};
+        S[mb][nb] = (f32x4){-m_run[nb], -m_run[nb], -m_run[nb], -m_run[nb]};
         if (it == last) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            init[e] = 16 * mb + 4 * kg + e > 16 * nb + l16 ? -INFINITY : 0.f;
+            if (16 * mb + 4 * kg + e > 16 * nb + l16) S[mb][nb][e] = -INFINITY;
         }
-        S[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][0], q[0][nb], init, 0, 0, 0);
-#pragma unroll
-        for (int ks = 1; ks < kKS; ++ks)
-          S[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][ks], q[ks][nb], S[mb][nb], 0, 0, 0);
       }
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < kNBLK; ++nb) {
+          S[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][ks], q[ks][nb], S[mb][nb], 0, 0, 0);
+          if (ks < kKL)  // the latent part also with the low half of q~
+            S[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][ks], qlo[ks][nb], S[mb][nb], 0, 0, 0);
+        }
 
-    // online softmax per position (lane), lazily rescaled: P against the
-    // running reference, the exact tile max only when a lane's sum of P
-    // passes 2^20 or is infinite (no reference yet)
+    // online softmax per position (lane), lazily rescaled: p = 2^(S - m_run)
+    // straight from the accumulators; the exact tile max only on the first
+    // tile (no reference yet) or when a lane's sum of P passes 2^20 (or is
+    // not finite), then the reference moves to 16 below the max and O, l
+    // are rescaled
     bf16x8 P[kNBLK];
     float ps[kNBLK];
-    bool need = false;
-    auto probs = [&](int nb) {
+    bool need = it == 0;
+#pragma unroll
+    for (int nb = 0; nb < kNBLK; ++nb) {
       ps[nb] = 0.f;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(S[mb][nb][e], kLog2e, -m_run[nb]));
+          const float pe = __builtin_amdgcn_exp2f(S[mb][nb][e]);
           ps[nb] += pe;
           P[nb][4 * mb + e] = (__bf16)pe;
         }
-    };
-#pragma unroll
-    for (int nb = 0; nb < kNBLK; ++nb) {
-      probs(nb);
       need |= !(ps[nb] <= kSumLimit);
     }
     if (__builtin_expect(__any(need), 0)) {
@@ -362,15 +384,24 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
       for (int nb = 0; nb < kNBLK; ++nb) {
         const float mx = fmaxf(fmaxf(fmaxf(S[0][nb][0], S[0][nb][1]), fmaxf(S[0][nb][2], S[0][nb][3])),
                                fmaxf(fmaxf(S[1][nb][0], S[1][nb][1]), fmaxf(S[1][nb][2], S[1][nb][3])));
-        const float mt = max4(mx) * kLog2e;
-        const float mr = m_run[nb] == kNoRef ? mt : m_run[nb];
+        const float mt = max4(mx) + m_run[nb];  // the tile max, log2 units
+        const float mr = it == 0 ? mt : m_run[nb];
         const float mn = fmaxf(mr, mt - kRescale);
         const float f = __builtin_amdgcn_exp2f(mr - mn);
         l_run[nb] *= f;
 #pragma unroll
         for (int cb = 0; cb < kCB; ++cb) o[cb][nb] *= f;
+        const float off = m_run[nb] - mn;
         m_run[nb] = mn;
-        probs(nb);
+        ps[nb] = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pe = __builtin_amdgcn_exp2f(S[mb][nb][e] + off);
+            ps[nb] += pe;
+            P[nb][4 * mb + e] = (__bf16)pe;
+          }
       }
     }
 #pragma unroll
@@ -505,8 +536,9 @@ hipError_t launch_prefill_branch(const Geom& g, int T, const void* q_nope, const
   p.T = T;
   p.H = g.H;
   p.QB = (T + kQWG - 1) / kQWG;
-  p.scale_n = alpha_q * tau;
-  p.tau = tau;
+  constexpr double kLog2eD = 1.4426950408889634;
+  p.scale_n = (float)((double)alpha_q * tau * kLog2eD);
+  p.scale_r = (float)((double)tau * kLog2eD);
   p.alpha_kv = alpha_kv;
   p.theta = theta;
   const int64_t grid = (int64_t)g.B * p.QB * g.H;
