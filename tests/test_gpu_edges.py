@@ -93,3 +93,20 @@ def test_single_long_sequence_over_all_items():
     err = row_rel_err(got, oracle.out_proj_ref(lo, inp["w_uv"], w.alpha_kv))
     say(f"B=1, L=65536: rel err {err:.2e}")
     assert err <= TOL["bf16"]
+
+
+def test_many_short_contexts_mlra4():
+    # 64 sequences of 2..200 tokens at MLRA-4's alpha_q: sharp softmax over
+    # few keys is where rounding q~ to bf16 shows most (8192 rows checked)
+    w = WORKLOADS["mlra4_b16_l32k"].replace(batch=64)
+    rng = np.random.default_rng(2003)
+    lens = rng.integers(2, 201, size=w.batch).astype(np.int32)
+    inp = make_inputs(w, lens=lens, max_len=int(lens.max()))
+    got = host(Dev(w, inp).decode(config_for(w)))
+    qa = oracle.absorb_q_ref(inp["q_nope"], inp["q_rope"], inp["w_uk"], lens - 1, w.tau, w.alpha_q,
+                             w.theta)
+    ref = oracle.out_proj_ref(oracle.latent_attn_ref(qa, inp["ckv"], inp["krope"], lens, w.n),
+                              inp["w_uv"], w.alpha_kv)
+    err = row_rel_err(got, ref)
+    say(f"64 short MLRA-4 contexts: worst row rel err {err:.2e}")
+    assert err <= TOL["bf16"]
