@@ -132,5 +132,10 @@ hipError_t launch_combine_hc(const Geom& g, const Workspace& ws, float* latent_o
 template <typename TO>
 hipError_t launch_out_proj_mfma(const Geom& g, const float* latent, const __bf16* w_uv, TO* out,
                                 float alpha_kv, hipStream_t s);
+// combine_hc followed by launch_out_proj_mfma in one kernel (the merged
+// latent stays in LDS); for the MFMA decodes' partial layout.
+template <typename TO>
+hipError_t launch_merge_out_proj(const Geom& g, const Workspace& ws, const __bf16* w_uv, TO* out,
+                                 float alpha_kv, hipStream_t s);
 
 }  // namespace mlra

@@ -577,6 +577,15 @@ mlra_status_t mlra_decode(const mlra_config_t* cfg_in, int32_t num_branches, int
                  &plan_done));
   bool fast = false;
   TRY(run_decode(&cfg, g, ws.q_abs, cache, ws, L, kern, plan, plan_done, &fast, s));
+  if (fast && cfg.dtype == MLRA_BF16 && proj_mfma_supported(g)) {
+    // merge and out projection in one kernel: the latent stays on chip
+    const __bf16* wv = static_cast<const __bf16*>(w_uv);
+    TRY_HIP(out_dtype == MLRA_BF16
+                ? launch_merge_out_proj<__bf16>(g, ws, wv, static_cast<__bf16*>(out), cfg.alpha_kv, s)
+                : launch_merge_out_proj<float>(g, ws, wv, static_cast<float*>(out), cfg.alpha_kv, s),
+            "merge_out launch");
+    return MLRA_OK;
+  }
   TRY(run_merge(g, ws, fast, ws.latent, s));
   return run_out_proj(&cfg, g, ws.latent, w_uv, out, out_dtype, s);
 }

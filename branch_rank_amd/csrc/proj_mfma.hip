@@ -6,6 +6,8 @@
 //    the RoPE rotation of the query's rotary part in double precision.
 //  * combine_hc    - merge of the split-KV partials per branch (online-softmax
 //    rescaling) into the branch-normalised latent_out [B][H][d_c] fp32.
+//  * merge_out     - combine_hc followed by out_proj in one kernel (mlra_decode):
+//    the merged latent stays in LDS.
 //  * out_proj      - output up-projection and branch sum
 //    o[b][h] = alpha_kv W_UV[h]^T concat_j o~_j (方法步骤详情 step 3, 核心方法).
 //    The fp32 latent is split into bf16 hi + lo parts so that the MFMA product
@@ -302,6 +304,235 @@ __global__ __launch_bounds__(256) void out_proj(Geom g, const float* __restrict_
   }
 }
 
+// ------------------------------------------------------------ merge_out ----
+
+// combine_hc and out_proj in one kernel, for mlra_decode: workgroup (head h,
+// sequence half sh) takes blocks of 8 sequences (16 it + 8 sh + 0..7), merges
+// head h's partials of each into its branch-normalised latent row (bf16 hi +
+// lo in LDS, as out_proj stages them) and projects the rows with W_UV[h],
+// staged one 64-column half at a time. The merged latent never goes to
+// memory and every partial row is read once. The two workgroups of a head
+// run on one XCD (8 apart in launch order), so W_UV[h] comes from L2 the
+// second time. Weights 2^(m_k - M) / L of up to kMOS slots per (sequence,
+// branch) at a time sit in an LDS table.
+constexpr int kMOS = 32;  // slots per weight table pass
+constexpr int kMSQ = 8;   // sequences per block
+
+template <int DC>
+struct MergeLds {
+  using LD = OutLds<DC>;
+  static constexpr int WT_FLOATS = kMSQ * kMOS * kMNB;  // [sequence][slot][branch]
+  static constexpr int ST_FLOATS = kMSQ * kMNB * 2;     // M, 1/L per (sequence, branch)
+  static constexpr int TOTAL = LD::TOTAL + 4 * (2 * WT_FLOATS + ST_FLOATS) + 8 * kMSQ;
+};
+
+template <int DC, typename TO>
+__global__ __launch_bounds__(512) void merge_out(Geom g, Workspace ws,
+                                                 const __bf16* __restrict__ w_uv,
+                                                 TO* __restrict__ out, float alpha_kv) {
+  using LD = OutLds<DC>;
+  using MD = MergeLds<DC>;
+  __shared__ __attribute__((aligned(16))) char smem_raw[MD::TOTAL];
+  char LDS_AS* smem = (char LDS_AS*)smem_raw;
+  char LDS_AS* wl = smem;
+  char LDS_AS* lhi = smem + LD::W_BYTES;
+  char LDS_AS* llo = lhi + LD::L_BYTES;
+  float LDS_AS* mt = (float LDS_AS*)(smem + LD::TOTAL);  // m, then the weights
+  float LDS_AS* lt = mt + MD::WT_FLOATS;                  // l
+  float LDS_AS* st = lt + MD::WT_FLOATS;
+  int LDS_AS* rng = (int LDS_AS*)(st + MD::ST_FLOATS);    // kf, kl per sequence of the block
+  const int i = blockIdx.x, x = i & 7, jj = i >> 3;
+  const int h = (jj >> 1) * 8 + x, sh = jj & 1;
+  if (h >= g.H) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, kg = lane >> 4;
+  const int NB = g.n, H = g.H, C4 = DC / 4, bw = DC / NB;
+  const int chunk = ws.hdr->chunk;
+  const int r4 = l16 >> 2, q4 = l16 & 3;
+  const int wcol = 2 * (16 * wave + 4 * q4);
+  constexpr int NT = 512;                               // threads
+  constexpr int NQ = (kMSQ * (DC / 4) + NT - 1) / NT;  // column quads per thread in a block
+  constexpr int KU = 4;     // slots whose loads are in flight together
+  constexpr int NW = DC * 8 / NT;  // 16-byte pieces of a W_UV half per thread
+  const int NE = kMSQ * kMOS * NB;  // table entries
+
+  // rows kMSQ..15 of the MFMA's 16-row A operand stay zero
+  for (int q = tid; q < (16 - kMSQ) * LD::LROW / 4; q += NT) {
+    ((int LDS_AS*)(lhi + kMSQ * LD::LROW))[q] = 0;
+    ((int LDS_AS*)(llo + kMSQ * LD::LROW))[q] = 0;
+  }
+  auto load_w = [&](int vh, bf16x8* stg) {
+    const __bf16* w = w_uv + (size_t)h * DC * g.dv + kDVH * vh;
+#pragma unroll
+    for (int u = 0; u < NW; ++u) {
+      const int q = tid + NT * u, c = q >> 3, ch = q & 7;
+      stg[u] = *(const bf16x8*)(w + (size_t)c * g.dv + 8 * ch);
+    }
+  };
+  // (m, l) of slots kf + s0 .. + kMOS - 1 of each sequence of the block
+  auto load_ml = [&](int b0, int s0, bool with_l) {
+    for (int q = tid; q < NE; q += NT) {
+      const int bb = q / (kMOS * NB), kk = (q / NB) % kMOS, j = q % NB;
+      const int k = rng[2 * bb] + s0 + kk;
+      float m = -INFINITY, l = 0.f;
+      if (k <= rng[2 * bb + 1]) {
+        const size_t e = ((size_t)(k + b0 + bb) * NB + j) * H + h;
+        m = ws.m[e];
+        if (with_l) l = ws.l[e];
+      }
+      mt[q] = m;
+      if (with_l) lt[q] = l;
+    }
+  };
+
+  for (int b0 = kMSQ * sh; b0 < g.B; b0 += 2 * kMSQ) {
+    const int nbq = min(kMSQ, g.B - b0);
+    bf16x8 stg[NW];
+    load_w(0, stg);  // in flight while the partials are merged
+    __syncthreads();  // the previous block's LDS consumed
+    if (tid < kMSQ) {
+      int kf = 0, kl = -1;
+      if (tid < nbq) {
+        const int p0 = ws.prefix[b0 + tid], p1 = ws.prefix[b0 + tid + 1];
+        kf = p0 / chunk;
+        kl = p1 > p0 ? (p1 - 1) / chunk : kf - 1;
+      }
+      rng[2 * tid] = kf;
+      rng[2 * tid + 1] = kl;
+    }
+    __syncthreads();
+    int maxs = 0;
+#pragma unroll
+    for (int bb = 0; bb < kMSQ; ++bb) maxs = max(maxs, rng[2 * bb + 1] - rng[2 * bb] + 1);
+    // pass 1: M and L per (sequence, branch), online over the slot chunks
+    float M = -INFINITY, L = 0.f;
+    for (int s0 = 0; s0 < maxs; s0 += kMOS) {
+      load_ml(b0, s0, true);
+      __syncthreads();
+      if (tid < kMSQ * NB) {
+        const int bb = tid / NB, j = tid % NB;
+        for (int kk = 0; kk < kMOS; ++kk) {
+          const float m = mt[(bb * kMOS + kk) * NB + j], l = lt[(bb * kMOS + kk) * NB + j];
+          if (l > 0.f || m > -INFINITY) {
+            const float mn = fmaxf(M, m);
+            L = L * exp2f(M - mn) + l * exp2f(m - mn);
+            M = mn;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    if (tid < kMSQ * NB) {
+      st[2 * tid] = M;
+      st[2 * tid + 1] = L > 0.f ? 1.f / L : 0.f;  // empty sequence: weights 0, o = 0
+    }
+    // pass 2: weights and the weighted sum of the partial rows; thread ->
+    // (sequence bb, column quad c4) for q = tid + NT u
+    f32x4 r[NQ];
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) r[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < maxs; s0 += kMOS) {
+      if (maxs > kMOS) {  // the table holds the last chunk of pass 1: reload m
+        __syncthreads();
+        load_ml(b0, s0, false);
+      }
+      __syncthreads();  // m of this chunk and the stats in LDS
+      for (int q = tid; q < NE; q += NT) {
+        const int bb = q / (kMOS * NB), j = q % NB;
+        const float m = mt[q];
+        mt[q] = m > -INFINITY ? exp2f(m - st[2 * (bb * NB + j)]) * st[2 * (bb * NB + j) + 1] : 0.f;
+      }
+      __syncthreads();
+      const float* src[NQ];
+      int nk[NQ], wi[NQ];
+      int kmax = 0;
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) {
+        const int q = min(tid + NT * u, kMSQ * C4 - 1), bb = q / C4, c4 = q % C4;
+        const int j = (4 * c4) / bw;
+        const int kf = rng[2 * bb], kl = rng[2 * bb + 1];
+        nk[u] = tid + NT * u < kMSQ * C4 ? min(kMOS, kl - kf - s0 + 1) : 0;
+        kmax = max(kmax, nk[u]);
+        src[u] = ws.acc + ((size_t)(kf + s0 + b0 + bb) * H + h) * DC + 4 * c4;
+        wi[u] = bb * kMOS * NB + j;
+      }
+      // KU slots at a time, all their loads issued before the first use
+      for (int k0 = 0; k0 < kmax; k0 += KU) {
+        f32x4 v[KU][NQ];
+#pragma unroll
+        for (int kk = 0; kk < KU; ++kk)
+#pragma unroll
+          for (int u = 0; u < NQ; ++u)
+            v[kk][u] = k0 + kk < nk[u] ? *(const f32x4*)(src[u] + (size_t)(k0 + kk) * H * DC)
+                                       : (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KU; ++kk)
+#pragma unroll
+          for (int u = 0; u < NQ; ++u)
+            if (k0 + kk < nk[u]) r[u] += mt[wi[u] + (k0 + kk) * NB] * v[kk][u];
+      }
+    }
+    // the block's latent rows as bf16 hi + lo
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int q = tid + NT * u, bb = q / C4, c4 = q % C4;
+      if (q >= kMSQ * C4) break;
+      __bf16 hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = (__bf16)r[u][e];
+        lo[e] = (__bf16)(r[u][e] - (float)hi[e]);
+      }
+      __bf16 LDS_AS* ph = (__bf16 LDS_AS*)(lhi + bb * LD::LROW) + 4 * c4;
+      __bf16 LDS_AS* pl = (__bf16 LDS_AS*)(llo + bb * LD::LROW) + 4 * c4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { ph[e] = hi[e]; pl[e] = lo[e]; }
+    }
+    // both 64-column halves of W_UV[h], one after the other; the second
+    // half's loads overlap the first half's MFMAs
+    for (int vh = 0; vh < 2; ++vh) {
+      __syncthreads();  // latent rows written / the previous half's reads done
+#pragma unroll
+      for (int u = 0; u < NW; ++u) {
+        const int q = tid + NT * u, c = q >> 3, ch = q & 7;
+        *(bf16x8 LDS_AS*)(wl + c * kWRow + 16 * ch) = stg[u];
+      }
+      __syncthreads();
+      if (vh == 0) load_w(1, stg);
+      if (wave >= 4) continue;  // four waves cover the half's 64 columns
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int ks = 0; ks < DC / 32; ++ks) {
+        const int aoff = l16 * LD::LROW + 2 * (32 * ks + 8 * kg);
+        const bf16x8 ah = *(const bf16x8 LDS_AS*)(lhi + aoff);
+        const bf16x8 al = *(const bf16x8 LDS_AS*)(llo + aoff);
+        const int wr = (32 * ks + 8 * kg + r4) * kWRow + wcol;
+        const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(wl + wr));
+        const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(wl + wr + 4 * kWRow));
+        const i16x8 wv = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        const bf16x8 wb = __builtin_bit_cast(bf16x8, wv);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wb, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wb, acc, 0, 0, 0);
+      }
+      // D[row][v]: rows 4 kg + e of the block (only rows < nbq are sequences)
+      const int v = kDVH * vh + 16 * wave + l16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int bb = 4 * kg + e;
+        if (bb < nbq) out[((size_t)(b0 + bb) * g.H + h) * g.dv + v] = (TO)(alpha_kv * acc[e]);
+      }
+    }
+  }
+}
+
+template <int DC, typename TO>
+hipError_t launch_merge_out_t(const Geom& g, const Workspace& ws, const __bf16* w_uv, TO* out,
+                              float alpha_kv, hipStream_t s) {
+  const int grid = ((g.H + 7) / 8) * 8 * 2;
+  hipLaunchKernelGGL((merge_out<DC, TO>), dim3(grid), dim3(512), 0, s, g, ws, w_uv, out, alpha_kv);
+  return hipGetLastError();
+}
+
 template <int DC, typename TO>
 hipError_t launch_out_t(const Geom& g, const float* lat, const __bf16* w_uv, TO* out,
                         float alpha_kv, hipStream_t s) {
@@ -377,6 +608,23 @@ hipError_t launch_out_proj_mfma(const Geom& g, const float* latent, const __bf16
   }
   return hipErrorNotSupported;
 }
+
+template <typename TO>
+hipError_t launch_merge_out_proj(const Geom& g, const Workspace& ws, const __bf16* w_uv, TO* out,
+                                 float alpha_kv, hipStream_t s) {
+  if (g.n > kMNB || g.B <= 0) return g.B <= 0 ? hipSuccess : hipErrorNotSupported;
+  switch (g.dc) {
+    case 128: return launch_merge_out_t<128, TO>(g, ws, w_uv, out, alpha_kv, s);
+    case 256: return launch_merge_out_t<256, TO>(g, ws, w_uv, out, alpha_kv, s);
+    case 512: return launch_merge_out_t<512, TO>(g, ws, w_uv, out, alpha_kv, s);
+  }
+  return hipErrorNotSupported;
+}
+
+template hipError_t launch_merge_out_proj<float>(const Geom&, const Workspace&, const __bf16*,
+                                                 float*, float, hipStream_t);
+template hipError_t launch_merge_out_proj<__bf16>(const Geom&, const Workspace&, const __bf16*,
+                                                  __bf16*, float, hipStream_t);
 
 template hipError_t launch_out_proj_mfma<float>(const Geom&, const float*, const __bf16*, float*,
                                                 float, hipStream_t);
