@@ -30,7 +30,9 @@ METRIC = "decode attn tokens/s and KV-cache GB/s (% HBM peak) at B=16, L=32K, 1 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "latent_decode_traffic.json")
-KERNEL_SRC = {"branch": "branch_rank_amd/csrc/decode_branch.hip",
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
+KERNEL_SRC = {"prefill": "branch_rank_amd/csrc/prefill_branch.hip",
+              "branch": "branch_rank_amd/csrc/decode_branch.hip",
               "head_group": "branch_rank_amd/csrc/decode_mfma.hip",
               "portable": "branch_rank_amd/csrc/kernels_generic.hip"}
 
@@ -80,12 +82,11 @@ def kernel_flops_bytes(w, lens):
     return tokens * row * esz, tokens * w.heads * 2 * (row + w.d_c), tokens
 
 
-def traffic_for(workload, kernel):
-    """HBM bytes per decode launch from the committed counter summary, if it
-    was taken on this workload, this decode kernel and the kernel's current
-    source; else None."""
+def traffic_for(workload, kernel, path=TRAFFIC_FILE):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on this workload, this kernel and the kernel's current source; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
         src = KERNEL_SRC[kernel]
         sha = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
@@ -293,7 +294,8 @@ def time_prefill(name, steps, warmup, torch, br, synth):
             "kernel_ms": k_ms, "kernel_flops": total, "attention_flops": attn,
             "attn_pairs": pairs,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS, "traffic": None}}
+                         "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
+                         "traffic": traffic_for(name, "prefill", PREFILL_TRAFFIC_FILE)}}
 
 
 def cpu_baseline(w, seconds):

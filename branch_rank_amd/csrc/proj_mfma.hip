@@ -107,21 +107,33 @@ __global__ __launch_bounds__(256) void absorb_q_mfma(Geom g, const __bf16* __res
     }
   }
 
-  // RoPE on the query's rotary part (angle in double precision), its
-  // (sequence, pair) elements spread over the parts' threads
+  // RoPE on the query's rotary part, its (sequence, pair) elements spread over
+  // the parts' threads: the angle p * theta^(-2k/d_r) and its reduction to
+  // [-pi, pi] in double precision, sine and cosine of the reduced angle in
+  // float; the frequency is recomputed only when a thread's pair index k
+  // changes (never when the stride is a multiple of d_r / 2)
   const int hp = g.dr / 2;
-  for (int i = threadIdx.x + 256 * part; i < 16 * MBLK * hp; i += 256 * parts) {
-    const int b = b0 + i / hp, k = i % hp;
-    if (b >= g.B) continue;
-    const int p = q_pos ? q_pos[b] : clamp_len(lens[b], g.max_len) - 1;
-    const double omega = pow((double)theta, -2.0 * (double)k / (double)g.dr);
-    double sn, cs;
-    sincos((double)p * omega, &sn, &cs);
-    const size_t qi = ((size_t)b * g.H + h) * g.dr + 2 * k;
-    const double x0 = (float)q_rope[qi], x1 = (float)q_rope[qi + 1];
-    __bf16* o = q_abs + ((size_t)b * g.H + h) * row + g.dc + 2 * k;
-    o[0] = (__bf16)(float)(tau * (x0 * cs - x1 * sn));
-    o[1] = (__bf16)(float)(tau * (x0 * sn + x1 * cs));
+  {
+    int kc = -1;
+    double omega = 0.0;
+    for (int i = threadIdx.x + 256 * part; i < 16 * MBLK * hp; i += 256 * parts) {
+      const int b = b0 + i / hp, k = i % hp;
+      if (b >= g.B) continue;
+      if (k != kc) {
+        omega = pow((double)theta, -2.0 * (double)k / (double)g.dr);
+        kc = k;
+      }
+      const int p = q_pos ? q_pos[b] : clamp_len(lens[b], g.max_len) - 1;
+      const double a = (double)p * omega;
+      const double r = a - 6.283185307179586 * rint(a * 0.15915494309189535);
+      float sn, cs;
+      sincosf((float)r, &sn, &cs);
+      const size_t qi = ((size_t)b * g.H + h) * g.dr + 2 * k;
+      const float x0 = (float)q_rope[qi], x1 = (float)q_rope[qi + 1];
+      __bf16* o = q_abs + ((size_t)b * g.H + h) * row + g.dc + 2 * k;
+      o[0] = (__bf16)(tau * (x0 * cs - x1 * sn));
+      o[1] = (__bf16)(tau * (x0 * sn + x1 * cs));
+    }
   }
 }
 
