@@ -231,3 +231,28 @@ def test_out_proj_step_bf16(batch):
     err = row_rel_err(got, ref)
     say(f"out_proj bf16 B={batch}: rel err {err:.2e}")
     assert err <= 1e-4
+
+
+@pytest.mark.parametrize("name,kernel", [("mlra4_b16_l32k", "branch"), ("mla_b16_l4k", "head_group"),
+                                         ("shard_b64_ragged", "head_group")])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_fused_merge_matches_separate_calls(name, kernel, out_dtype):
+    # mlra_decode merges the split-KV partials and projects them in one
+    # kernel (blocks of 8 sequences, two per head); the separate calls
+    # (mla_decode_attn, then mla_out_proj) merge into a latent in memory
+    # first. 17 sequences cross the blocks; empty sequences give zero rows.
+    w = WORKLOADS[name].replace(batch=17)
+    rng = np.random.default_rng(77)
+    lens = rng.integers(1, 700, size=w.batch).astype(np.int32)
+    lens[[3, 16]] = 0
+    inp = make_inputs(w, lens=lens, max_len=700)
+    cfg = config_for(w, kernel=kernel)
+    d = Dev(w, inp)
+    assert br.select_decode_kernel(cfg, d.cache(cfg)) == kernel
+    fused = host(d.decode(cfg, out_dtype=out_dtype))
+    sep = host(d.out_proj(cfg, d.latent(cfg, d.absorb(cfg)), out_dtype=out_dtype))
+    assert not np.any(fused[[3, 16]])
+    tol = 1e-5 if out_dtype == torch.float32 else 2.0 ** -7  # one bf16 rounding apart
+    err = row_rel_err(fused, sep)
+    say(f"{name} {kernel} {out_dtype}: fused vs separate rel err {err:.2e}")
+    assert err <= tol
