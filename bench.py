@@ -47,7 +47,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mlra4_b16_l32k")
-    ap.add_argument("--also", default="mla_b16_l32k",
+    ap.add_argument("--also", default="mla_b16_l32k,mla_b16_l4k,mlra4_b2_l128k,mla_b2_l128k,"
+                                      "shard_b64_ragged",
                     help="comma-separated extra workloads reported beside (empty: none)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "portable", "head_group", "branch"],
                     help="split-KV decode kernel (auto: the library's choice)")
