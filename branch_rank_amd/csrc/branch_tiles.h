@@ -1,7 +1,7 @@
-// Tile machinery of the branch-per-wave kernels (split-KV decode and causal
-// prefill, gfx950): 32-token tiles of the latent cache, two 128-column branch
-// slices plus the shared RoPE key per workgroup, streamed HBM -> LDS by
-// LDS-DMA into a ring of stages with XOR-swizzled 16-byte chunks.
+// Tile machinery of the branch-per-wave split-KV decode (gfx950): 32-token
+// tiles of the latent cache, one or two 128-column branch slices plus the
+// shared RoPE key per workgroup, streamed HBM -> LDS by LDS-DMA into a ring of
+// stages with XOR-swizzled 16-byte chunks.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -38,14 +38,17 @@ struct BCfg {
   static constexpr int KL = kBW / 32;             // latent k-steps of a branch score
   static constexpr int KS = KL + kDR / 32;        // plus the RoPE k-steps
   static constexpr int CB = kBW / 16;             // PV output row blocks of a branch
-  static_assert(NBR % NSPLIT == 0 && ROWB == 512, "two 128-column branches per workgroup");
+  static_assert(NBR % NSPLIT == 0 && (ROWB == 512 || ROWB == 256),
+                "one or two 128-column branches per workgroup");
   static_assert(HPW % 16 == 0 && NW <= 16, "wave shape");
   static_assert(NL % NW == 0 && NR <= NW, "DMA assignment");
 };
 
-// Chunk swizzles: latent rows (16-byte chunk index ^ 2 * (row & 15)); RoPE
-// rows of 128 bytes (chunk ^ ((row >> 1) & 7)).
-__device__ __forceinline__ int swz_l(int t) { return 2 * (t & 15); }
+// Chunk swizzles: latent rows of ROWB bytes (16-byte chunk index ^ 2 * (row &
+// (ROWB / 32 - 1)), which stays inside the row: row & 15 for two branches,
+// row & 7 for one); RoPE rows of 128 bytes (chunk ^ ((row >> 1) & 7)).
+template <int ROWB>
+__device__ __forceinline__ int swz_l(int t) { return 2 * (t & (ROWB / 32 - 1)); }
 __device__ __forceinline__ int swz_r(int t) { return (t >> 1) & 7; }
 
 // DMA of one tile into the stage at LDS byte address `stage`. Wave w issues

@@ -100,22 +100,22 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
   // multiple of 20 KB from a 1 KB-aligned array) leave zero: the address of
   // k-step ks is (base + qk_lat) ^ (64 ks), of block cb (base + pv_lat) ^
   // (32 cb), and the second RoPE k-step is (base + qk_rp) ^ 64.
-  static_assert(C::STAGE % 4096 == 0 && C::ROWB == 512, "XOR addressing");
-  const int qk_lat = l16 * C::ROWB + 16 * ((16 * b + kg) ^ swz_l(l16));
+  static_assert(C::STAGE % 4096 == 0 && (C::ROWB == 512 || C::ROWB == 256), "XOR addressing");
+  const int qk_lat = l16 * C::ROWB + 16 * ((16 * b + kg) ^ swz_l<C::ROWB>(l16));
   const int qk_rp = C::LAT + l16 * 128 + 16 * (kg ^ swz_r(l16));
   int pv_lat;
   {
     const int t = 4 * kg + (l16 >> 2), half = l16 & 3;
-    pv_lat = t * C::ROWB + 16 * ((16 * b + (half >> 1)) ^ swz_l(t)) + 8 * (half & 1);
+    pv_lat = t * C::ROWB + 16 * ((16 * b + (half >> 1)) ^ swz_l<C::ROWB>(t)) + 8 * (half & 1);
   }
   // DMA lane constants. Latent: lane -> row RPI*q + lat_row of the
-  // instruction, LDS chunk lat_p, which holds logical chunk lat_p ^ swz_l(row);
+  // instruction, LDS chunk lat_p, which holds logical chunk lat_p ^ swz_l<C::ROWB>(row);
   // the row's parity within 16 (2 q + lat_row with q = wave + NW u, NW even)
   // is the same for every instruction of the wave. RoPE: this lane's part of
   // the wave's instruction (waves < NR).
-  static_assert(C::NW % 8 == 0 || C::RPI * C::NW % 16 == 0, "row parity per wave");
+  static_assert((C::RPI * C::NW) % (C::ROWB / 32) == 0, "row parity per wave");
   const int lat_row = lane / (64 / C::RPI), lat_p = lane % (64 / C::RPI);
-  const int lat_c = 16 * (lat_p ^ swz_l(C::RPI * wave + lat_row)) + hg * C::ROWB;
+  const int lat_c = 16 * (lat_p ^ swz_l<C::ROWB>(C::RPI * wave + lat_row)) + hg * C::ROWB;
   const int rope_t = wave * 8 + (lane >> 3);
   const int rope_c = 16 * ((lane & 7) ^ swz_r(rope_t));
 
@@ -445,17 +445,23 @@ hipError_t launch_b(const Geom& g, const void* q_abs, const void* ckv, const voi
 
 }  // namespace
 
+// MLRA-4 with 128-wide branches (two workgroups per item, one per branch
+// pair) and one such branch alone, a tensor-parallel shard (one workgroup
+// per item).
 bool decode_branch_supported(const Geom& g) {
-  return g.dr == kDR && g.dc == 4 * kBW && g.n == 4 && (g.H == 64 || g.H == 128);
+  if (g.dr != kDR) return false;
+  if (g.dc == 4 * kBW && g.n == 4) return g.H == 64 || g.H == 128;
+  return g.dc == kBW && g.n == 1 && g.H == 128;
 }
 
-// Workgroups per work item (branch pairs); one workgroup per CU.
-int decode_branch_wgs_per_item(const Geom&) { return 2; }
+// Workgroups per work item; one workgroup per CU.
+int decode_branch_wgs_per_item(const Geom& g) { return g.n == 1 ? 1 : 2; }
 
 hipError_t launch_decode_branch(const Geom& g, const void* q_abs, const void* ckv,
                                 const void* krope, const Workspace& ws, int items,
                                 hipStream_t s, const KernelTiming& t) {
   if (!decode_branch_supported(g)) return hipErrorNotSupported;
+  if (g.n == 1) return launch_b<1, 1, 16, 8>(g, q_abs, ckv, krope, ws, items, s, t);
   if (g.H == 64) return launch_b<4, 2, 16, 4>(g, q_abs, ckv, krope, ws, items, s, t);
   return launch_b<4, 2, 32, 4>(g, q_abs, ckv, krope, ws, items, s, t);
 }

@@ -319,13 +319,12 @@ __global__ __launch_bounds__(256) void out_proj(Geom g, const float* __restrict_
 // ------------------------------------------------------------ merge_out ----
 
 // combine_hc and out_proj in one kernel, for mlra_decode: workgroup (head h,
-// sequence half sh) takes blocks of 8 sequences (16 it + 8 sh + 0..7), merges
-// head h's partials of each into its branch-normalised latent row (bf16 hi +
-// lo in LDS, as out_proj stages them) and projects the rows with W_UV[h],
-// staged one 64-column half at a time. The merged latent never goes to
-// memory and every partial row is read once. The two workgroups of a head
-// run on one XCD (8 apart in launch order), so W_UV[h] comes from L2 the
-// second time. Weights 2^(m_k - M) / L of up to kMOS slots per (sequence,
+// block of 8 sequences) merges head h's partials of each sequence into its
+// branch-normalised latent row (bf16 hi + lo in LDS, as out_proj stages them)
+// and projects the rows with W_UV[h], staged one 64-column half at a time.
+// The merged latent never goes to memory and every partial row is read once.
+// The workgroups of a head run on one XCD (8 apart in launch order), so
+// W_UV[h] comes from L2 after the first. Weights 2^(m_k - M) / L of up to kMOS slots per (sequence,
 // branch) at a time sit in an LDS table.
 constexpr int kMOS = 32;  // slots per weight table pass
 constexpr int kMSQ = 8;   // sequences per block
@@ -353,8 +352,9 @@ __global__ __launch_bounds__(512) void merge_out(Geom g, Workspace ws,
   float LDS_AS* lt = mt + MD::WT_FLOATS;                  // l
   float LDS_AS* st = lt + MD::WT_FLOATS;
   int LDS_AS* rng = (int LDS_AS*)(st + MD::ST_FLOATS);    // kf, kl per sequence of the block
+  const int nblk = (g.B + kMSQ - 1) / kMSQ;
   const int i = blockIdx.x, x = i & 7, jj = i >> 3;
-  const int h = (jj >> 1) * 8 + x, sh = jj & 1;
+  const int h = (jj / nblk) * 8 + x, b0 = (jj % nblk) * kMSQ;
   if (h >= g.H) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, kg = lane >> 4;
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(512) void merge_out(Geom g, Workspace ws,
     }
   };
 
-  for (int b0 = kMSQ * sh; b0 < g.B; b0 += 2 * kMSQ) {
+  {
     const int nbq = min(kMSQ, g.B - b0);
     bf16x8 stg[NW];
     load_w(0, stg);  // in flight while the partials are merged
@@ -540,8 +540,10 @@ __global__ __launch_bounds__(512) void merge_out(Geom g, Workspace ws,
 template <int DC, typename TO>
 hipError_t launch_merge_out_t(const Geom& g, const Workspace& ws, const __bf16* w_uv, TO* out,
                               float alpha_kv, hipStream_t s) {
-  const int grid = ((g.H + 7) / 8) * 8 * 2;
-  hipLaunchKernelGGL((merge_out<DC, TO>), dim3(grid), dim3(512), 0, s, g, ws, w_uv, out, alpha_kv);
+  const int64_t grid = (int64_t)((g.H + 7) / 8) * 8 * ((g.B + kMSQ - 1) / kMSQ);
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((merge_out<DC, TO>), dim3((unsigned)grid), dim3(512), 0, s, g, ws, w_uv, out,
+                     alpha_kv);
   return hipGetLastError();
 }
 
