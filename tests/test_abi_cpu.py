@@ -98,7 +98,7 @@ def _fake_cache(c, batch, max_len, ts=None):
     (dict(heads=64), 4096, "auto", "branch"),
     (dict(n=1), 4096, "auto", "head_group"),                      # MLA
     (dict(n=2), 4096, "auto", "head_group"),
-    (dict(n=1, d_latent=128), 4096, "auto", "head_group"),        # one branch shard
+    (dict(n=1, d_latent=128), 4096, "auto", "branch"),            # one branch shard
     (dict(), 4096, "head_group", "head_group"),
     (dict(), 4096, "portable", "portable"),
     (dict(dtype="fp32"), 4096, "auto", "portable"),
