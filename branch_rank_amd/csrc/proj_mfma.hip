@@ -20,6 +20,7 @@
 
 #include <math.h>
 
+#include "device_common.h"
 #include "internal.h"
 #include "plan_device.h"
 
@@ -319,175 +320,221 @@ __global__ __launch_bounds__(256) void out_proj(Geom g, const float* __restrict_
 // ------------------------------------------------------------ merge_out ----
 
 // combine_hc and out_proj in one kernel, for mlra_decode: workgroup (head h,
-// block of 8 sequences) merges head h's partials of each sequence into its
-// branch-normalised latent row (bf16 hi + lo in LDS, as out_proj stages them)
-// and projects the rows with W_UV[h], staged one 64-column half at a time.
-// The merged latent never goes to memory and every partial row is read once.
-// The workgroups of a head run on one XCD (8 apart in launch order), so
-// W_UV[h] comes from L2 after the first. Weights 2^(m_k - M) / L of up to kMOS slots per (sequence,
-// branch) at a time sit in an LDS table.
+// block of kMSQ sequences) merges head h's partials of each sequence into its
+// branch-normalised latent row and projects the rows with W_UV[h]. The
+// merged latent never goes to memory and every partial row is read once.
+//
+// Waves 0-3 bring W_UV[h] (d_c rows of 128 bf16) into LDS by LDS-DMA as soon
+// as the workgroup starts; rows are 256 bytes with their 16-byte chunks
+// XOR-swizzled by kWSwz, so the transposed reads of the projection hit 64
+// distinct banks. Meanwhile waves 4-7 merge: a 16-lane group per (sequence,
+// branch) reads the slots' (m, l), reduces them to (M, 1/L) with lane
+// shuffles and writes the weights 2^(m_k - M) / L to an LDS table (kMOS
+// slots per pass); every thread's first kMKU partial rows are already in
+// flight by then. The latent rows go to LDS as bf16 hi + lo (rows 8..15 of
+// the MFMA's A operand are zero) and all 8 waves project 16 output columns
+// each. The workgroups of a head run on one XCD (8 apart in launch order),
+// so W_UV[h] comes from L2 after the first.
 constexpr int kMOS = 32;  // slots per weight table pass
 constexpr int kMSQ = 8;   // sequences per block
+constexpr int kMKU = 8;   // partial rows per (thread, column quad) in flight
+
+__device__ __forceinline__ int kWSwz(int row) { return 2 * ((row & 3) | (((row >> 3) & 1) << 2)); }
 
 template <int DC>
 struct MergeLds {
-  using LD = OutLds<DC>;
+  static constexpr int W_BYTES = DC * 256;       // W_UV[h], 128 columns per row
+  static constexpr int LROW = DC * 2 + 16;       // latent row (padded)
+  static constexpr int L_BYTES = kMSQ * LROW;
   static constexpr int WT_FLOATS = kMSQ * kMOS * kMNB;  // [sequence][slot][branch]
-  static constexpr int ST_FLOATS = kMSQ * kMNB * 2;     // M, 1/L per (sequence, branch)
-  static constexpr int TOTAL = LD::TOTAL + 4 * (2 * WT_FLOATS + ST_FLOATS) + 8 * kMSQ;
+  static constexpr int TOTAL = W_BYTES + 2 * L_BYTES + 4 * WT_FLOATS + 8 * kMSQ;
 };
+
+// (M, L) of an online softmax merged with (m, l); an empty side is M = -inf.
+__device__ __forceinline__ void ml_merge(float& M, float& L, float m, float l) {
+  if (m == -INFINITY) return;
+  if (M == -INFINITY) { M = m; L = l; return; }
+  const float mn = fmaxf(M, m);
+  L = L * exp2f(M - mn) + l * exp2f(m - mn);
+  M = mn;
+}
 
 template <int DC, typename TO>
 __global__ __launch_bounds__(512) void merge_out(Geom g, Workspace ws,
                                                  const __bf16* __restrict__ w_uv,
                                                  TO* __restrict__ out, float alpha_kv) {
-  using LD = OutLds<DC>;
   using MD = MergeLds<DC>;
+  static_assert(MD::TOTAL <= 163840, "LDS");
   __shared__ __attribute__((aligned(16))) char smem_raw[MD::TOTAL];
   char LDS_AS* smem = (char LDS_AS*)smem_raw;
   char LDS_AS* wl = smem;
-  char LDS_AS* lhi = smem + LD::W_BYTES;
-  char LDS_AS* llo = lhi + LD::L_BYTES;
-  float LDS_AS* mt = (float LDS_AS*)(smem + LD::TOTAL);  // m, then the weights
-  float LDS_AS* lt = mt + MD::WT_FLOATS;                  // l
-  float LDS_AS* st = lt + MD::WT_FLOATS;
-  int LDS_AS* rng = (int LDS_AS*)(st + MD::ST_FLOATS);    // kf, kl per sequence of the block
+  char LDS_AS* lhi = smem + MD::W_BYTES;
+  char LDS_AS* llo = lhi + MD::L_BYTES;
+  float LDS_AS* wt = (float LDS_AS*)(llo + MD::L_BYTES);
+  int LDS_AS* rng = (int LDS_AS*)(wt + MD::WT_FLOATS);  // kf, kl per sequence of the block
   const int nblk = (g.B + kMSQ - 1) / kMSQ;
   const int i = blockIdx.x, x = i & 7, jj = i >> 3;
   const int h = (jj / nblk) * 8 + x, b0 = (jj % nblk) * kMSQ;
   if (h >= g.H) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, kg = lane >> 4;
-  const int NB = g.n, H = g.H, C4 = DC / 4, bw = DC / NB;
-  const int chunk = ws.hdr->chunk;
-  const int r4 = l16 >> 2, q4 = l16 & 3;
-  const int wcol = 2 * (16 * wave + 4 * q4);
-  constexpr int NT = 512;                               // threads
-  constexpr int NQ = (kMSQ * (DC / 4) + NT - 1) / NT;  // column quads per thread in a block
-  constexpr int KU = 4;     // slots whose loads are in flight together
-  constexpr int NW = DC * 8 / NT;  // 16-byte pieces of a W_UV half per thread
-  const int NE = kMSQ * kMOS * NB;  // table entries
+  const int NB = g.n, H = g.H, bw = DC / NB;
+  constexpr int C4 = DC / 4;
+  constexpr int NQ = (kMSQ * C4 + 511) / 512;  // column quads per thread
+  const int nbq = min(kMSQ, g.B - b0);
 
-  // rows kMSQ..15 of the MFMA's 16-row A operand stay zero
-  for (int q = tid; q < (16 - kMSQ) * LD::LROW / 4; q += NT) {
-    ((int LDS_AS*)(lhi + kMSQ * LD::LROW))[q] = 0;
-    ((int LDS_AS*)(llo + kMSQ * LD::LROW))[q] = 0;
+  if (wave < 4) {
+    // W_UV[h] -> LDS: instruction u of wave w carries rows 4 (4 u + w) .. +3
+    // (lane: row + lane / 16, LDS chunk lane % 16, read from chunk
+    // (lane % 16) ^ kWSwz(row))
+    const uint64_t a = reinterpret_cast<uint64_t>(w_uv + (size_t)h * DC * 128);
+    dev::i32x4 rs;
+    rs.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    rs.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
+    rs.z = MD::W_BYTES;
+    rs.w = 0x00020000;
+    const uint32_t wbase = (uint32_t)reinterpret_cast<uintptr_t>(wl);
+#pragma unroll
+    for (int u = 0; u < DC / 16; ++u) {
+      const int q = 4 * u + wave, row = 4 * q + (lane >> 4);
+      dev::dma16(rs, wbase + 1024 * q, (uint32_t)(row * 256 + 16 * ((lane & 15) ^ kWSwz(row))), 0u);
+    }
+  } else if (tid < 256 + kMSQ) {
+    const int bb = tid - 256;
+    int kf = 0, kl = -1;
+    if (bb < nbq) {
+      const int chunk = ws.hdr->chunk;
+      const int p0 = ws.prefix[b0 + bb], p1 = ws.prefix[b0 + bb + 1];
+      kf = p0 / chunk;
+      kl = p1 > p0 ? (p1 - 1) / chunk : kf - 1;
+    }
+    rng[2 * bb] = kf;
+    rng[2 * bb + 1] = kl;
   }
-  auto load_w = [&](int vh, bf16x8* stg) {
-    const __bf16* w = w_uv + (size_t)h * DC * g.dv + kDVH * vh;
+  __syncthreads();
+  int maxs = 0;
 #pragma unroll
-    for (int u = 0; u < NW; ++u) {
-      const int q = tid + NT * u, c = q >> 3, ch = q & 7;
-      stg[u] = *(const bf16x8*)(w + (size_t)c * g.dv + 8 * ch);
-    }
-  };
-  // (m, l) of slots kf + s0 .. + kMOS - 1 of each sequence of the block
-  auto load_ml = [&](int b0, int s0, bool with_l) {
-    for (int q = tid; q < NE; q += NT) {
-      const int bb = q / (kMOS * NB), kk = (q / NB) % kMOS, j = q % NB;
-      const int k = rng[2 * bb] + s0 + kk;
-      float m = -INFINITY, l = 0.f;
-      if (k <= rng[2 * bb + 1]) {
-        const size_t e = ((size_t)(k + b0 + bb) * NB + j) * H + h;
-        m = ws.m[e];
-        if (with_l) l = ws.l[e];
-      }
-      mt[q] = m;
-      if (with_l) lt[q] = l;
-    }
-  };
+  for (int bb = 0; bb < kMSQ; ++bb) maxs = max(maxs, rng[2 * bb + 1] - rng[2 * bb] + 1);
 
-  {
-    const int nbq = min(kMSQ, g.B - b0);
-    bf16x8 stg[NW];
-    load_w(0, stg);  // in flight while the partials are merged
-    __syncthreads();  // the previous block's LDS consumed
-    if (tid < kMSQ) {
-      int kf = 0, kl = -1;
-      if (tid < nbq) {
-        const int p0 = ws.prefix[b0 + tid], p1 = ws.prefix[b0 + tid + 1];
-        kf = p0 / chunk;
-        kl = p1 > p0 ? (p1 - 1) / chunk : kf - 1;
-      }
-      rng[2 * tid] = kf;
-      rng[2 * tid + 1] = kl;
-    }
-    __syncthreads();
-    int maxs = 0;
+  // waves 4-7 reduce (m, l): group grp = (tid / 16) % 16 takes (sequence,
+  // branch) pairs grp, grp + 16, ...; every thread sums quads q = tid + 512 u
+  const int grp = (tid >> 4) & 15;
+  constexpr int PPG = kMSQ * kMNB / 16;  // most pairs per group
+  float Mp[PPG], Ip[PPG], mk[PPG][2], lk[PPG][2];
+  f32x4 r[NQ], v[kMKU][NQ];
+  const float* src[NQ];
+  int nsq[NQ], wi[NQ];
+  // (m, l) of the first 32 slots of each pair: loads on every wave without a
+  // branch (slot clamped into the sequence's range, or slot 0 when it has
+  // none), so that they stay in flight with the partial rows issued next;
+  // only waves 4-7 use them
 #pragma unroll
-    for (int bb = 0; bb < kMSQ; ++bb) maxs = max(maxs, rng[2 * bb + 1] - rng[2 * bb] + 1);
-    // pass 1: M and L per (sequence, branch), online over the slot chunks
-    float M = -INFINITY, L = 0.f;
-    for (int s0 = 0; s0 < maxs; s0 += kMOS) {
-      load_ml(b0, s0, true);
-      __syncthreads();
-      if (tid < kMSQ * NB) {
-        const int bb = tid / NB, j = tid % NB;
-        for (int kk = 0; kk < kMOS; ++kk) {
-          const float m = mt[(bb * kMOS + kk) * NB + j], l = lt[(bb * kMOS + kk) * NB + j];
-          if (l > 0.f || m > -INFINITY) {
-            const float mn = fmaxf(M, m);
-            L = L * exp2f(M - mn) + l * exp2f(m - mn);
-            M = mn;
-          }
+  for (int pj = 0; pj < PPG; ++pj) {
+    const int p = grp + 16 * pj, pv = p < kMSQ * NB, bb = pv ? p / NB : 0, j = p % NB;
+    const int kf = rng[2 * bb], ns = pv ? rng[2 * bb + 1] - kf + 1 : 0;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int s = l16 + 16 * e;
+      const size_t idx =
+          ns > 0 ? ((size_t)(kf + min(s, ns - 1) + b0 + bb) * NB + j) * H + h : (size_t)h;
+      mk[pj][e] = ws.m[idx];
+      lk[pj][e] = ws.l[idx];
+    }
+  }
+  // the first kMKU partial rows of every quad: in flight with the (m, l)
+  // loads (and, on waves 0-3, behind the W_UV DMA)
+#pragma unroll
+  for (int u = 0; u < NQ; ++u) {
+    const int q = min(tid + 512 * u, kMSQ * C4 - 1), bb = q / C4, c4 = q % C4;
+    const int kf = rng[2 * bb];
+    nsq[u] = tid + 512 * u < kMSQ * C4 ? rng[2 * bb + 1] - kf + 1 : 0;
+    src[u] = ws.acc + ((size_t)(kf + b0 + bb) * H + h) * DC + 4 * c4;
+    wi[u] = bb * kMOS * NB + (4 * c4) / bw;
+    r[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int k = 0; k < kMKU; ++k)
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      // no branch: a slot past the sequence re-reads its last one (or slot
+      // 0 of the workspace) and is zeroed
+      const float* a = nsq[u] > 0 ? src[u] + (size_t)min(k, nsq[u] - 1) * H * DC : ws.acc;
+      const f32x4 x = *(const f32x4*)a;
+      v[k][u] = k < nsq[u] ? x : (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+  if (wave >= 4) {
+    // (M, 1/L) per pair: online over this lane's slots, then over the 16 lanes
+#pragma unroll
+    for (int pj = 0; pj < PPG; ++pj) {
+      const int p = grp + 16 * pj, pv = p < kMSQ * NB, bb = pv ? p / NB : 0, j = p % NB;
+      const int kf = rng[2 * bb], ns = pv ? rng[2 * bb + 1] - kf + 1 : 0;
+      float M = -INFINITY, L = 0.f;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        if (l16 + 16 * e >= ns) mk[pj][e] = -INFINITY;
+        ml_merge(M, L, mk[pj][e], lk[pj][e]);
+      }
+      for (int s = l16 + 32; s < ns; s += 16) {  // more than 32 slots: rare
+        const size_t idx = ((size_t)(kf + s + b0 + bb) * NB + j) * H + h;
+        ml_merge(M, L, ws.m[idx], ws.l[idx]);
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
+        const float M2 = __shfl_xor(M, o), L2 = __shfl_xor(L, o);
+        ml_merge(M, L, M2, L2);
+      }
+      Mp[pj] = M;
+      Ip[pj] = L > 0.f ? 1.f / L : 0.f;  // empty sequence: weights 0, o = 0
+    }
+  }
+  // passes of kMOS slots: weights into the table, then the weighted sum
+  for (int s0 = 0; s0 < maxs; s0 += kMOS) {
+    if (s0 > 0) __syncthreads();  // the previous pass's table consumed
+    if (wave >= 4) {
+#pragma unroll
+      for (int pj = 0; pj < PPG; ++pj) {
+        const int p = grp + 16 * pj, bb = p / NB, j = p % NB;
+        if (p >= kMSQ * NB) break;
+        const int kf = rng[2 * bb], ns = rng[2 * bb + 1] - kf + 1;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int s = s0 + l16 + 16 * e;
+          float m = mk[pj][e];
+          if (s0 > 0 && s < ns) m = ws.m[((size_t)(kf + s + b0 + bb) * NB + j) * H + h];
+          wt[(bb * kMOS + l16 + 16 * e) * NB + j] =
+              s < ns && m > -INFINITY ? exp2f(m - Mp[pj]) * Ip[pj] : 0.f;
         }
       }
-      __syncthreads();
     }
-    if (tid < kMSQ * NB) {
-      st[2 * tid] = M;
-      st[2 * tid + 1] = L > 0.f ? 1.f / L : 0.f;  // empty sequence: weights 0, o = 0
-    }
-    // pass 2: weights and the weighted sum of the partial rows; thread ->
-    // (sequence bb, column quad c4) for q = tid + NT u
-    f32x4 r[NQ];
-#pragma unroll
-    for (int u = 0; u < NQ; ++u) r[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < maxs; s0 += kMOS) {
-      if (maxs > kMOS) {  // the table holds the last chunk of pass 1: reload m
-        __syncthreads();
-        load_ml(b0, s0, false);
-      }
-      __syncthreads();  // m of this chunk and the stats in LDS
-      for (int q = tid; q < NE; q += NT) {
-        const int bb = q / (kMOS * NB), j = q % NB;
-        const float m = mt[q];
-        mt[q] = m > -INFINITY ? exp2f(m - st[2 * (bb * NB + j)]) * st[2 * (bb * NB + j) + 1] : 0.f;
-      }
-      __syncthreads();
-      const float* src[NQ];
-      int nk[NQ], wi[NQ];
+    __syncthreads();
+    {
       int kmax = 0;
 #pragma unroll
-      for (int u = 0; u < NQ; ++u) {
-        const int q = min(tid + NT * u, kMSQ * C4 - 1), bb = q / C4, c4 = q % C4;
-        const int j = (4 * c4) / bw;
-        const int kf = rng[2 * bb], kl = rng[2 * bb + 1];
-        nk[u] = tid + NT * u < kMSQ * C4 ? min(kMOS, kl - kf - s0 + 1) : 0;
-        kmax = max(kmax, nk[u]);
-        src[u] = ws.acc + ((size_t)(kf + s0 + b0 + bb) * H + h) * DC + 4 * c4;
-        wi[u] = bb * kMOS * NB + j;
-      }
-      // KU slots at a time, all their loads issued before the first use
-      for (int k0 = 0; k0 < kmax; k0 += KU) {
-        f32x4 v[KU][NQ];
+      for (int u = 0; u < NQ; ++u) kmax = max(kmax, min(kMOS, nsq[u] - s0));
+      for (int k0 = 0; k0 < kmax; k0 += kMKU) {
+        if (s0 + k0 > 0) {
 #pragma unroll
-        for (int kk = 0; kk < KU; ++kk)
+          for (int k = 0; k < kMKU; ++k)
 #pragma unroll
-          for (int u = 0; u < NQ; ++u)
-            v[kk][u] = k0 + kk < nk[u] ? *(const f32x4*)(src[u] + (size_t)(k0 + kk) * H * DC)
-                                       : (f32x4){0.f, 0.f, 0.f, 0.f};
+            for (int u = 0; u < NQ; ++u)
+              v[k][u] = s0 + k0 + k < nsq[u] && k0 + k < kMOS
+                            ? *(const f32x4*)(src[u] + (size_t)(s0 + k0 + k) * H * DC)
+                            : (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-        for (int kk = 0; kk < KU; ++kk)
+        for (int k = 0; k < kMKU; ++k)
 #pragma unroll
           for (int u = 0; u < NQ; ++u)
-            if (k0 + kk < nk[u]) r[u] += mt[wi[u] + (k0 + kk) * NB] * v[kk][u];
+            if (s0 + k0 + k < nsq[u] && k0 + k < kMOS)
+              r[u] += wt[wi[u] + (k0 + k) * NB] * v[k][u];
       }
     }
+  }
+  {
     // the block's latent rows as bf16 hi + lo
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
-      const int q = tid + NT * u, bb = q / C4, c4 = q % C4;
+      const int q = tid + 512 * u, bb = q / C4, c4 = q % C4;
       if (q >= kMSQ * C4) break;
       __bf16 hi[4], lo[4];
 #pragma unroll
@@ -495,51 +542,50 @@ __global__ __launch_bounds__(512) void merge_out(Geom g, Workspace ws,
         hi[e] = (__bf16)r[u][e];
         lo[e] = (__bf16)(r[u][e] - (float)hi[e]);
       }
-      __bf16 LDS_AS* ph = (__bf16 LDS_AS*)(lhi + bb * LD::LROW) + 4 * c4;
-      __bf16 LDS_AS* pl = (__bf16 LDS_AS*)(llo + bb * LD::LROW) + 4 * c4;
+      __bf16 LDS_AS* ph = (__bf16 LDS_AS*)(lhi + bb * MD::LROW) + 4 * c4;
+      __bf16 LDS_AS* pl = (__bf16 LDS_AS*)(llo + bb * MD::LROW) + 4 * c4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) { ph[e] = hi[e]; pl[e] = lo[e]; }
     }
-    // both 64-column halves of W_UV[h], one after the other; the second
-    // half's loads overlap the first half's MFMAs
-    for (int vh = 0; vh < 2; ++vh) {
-      __syncthreads();  // latent rows written / the previous half's reads done
-#pragma unroll
-      for (int u = 0; u < NW; ++u) {
-        const int q = tid + NT * u, c = q >> 3, ch = q & 7;
-        *(bf16x8 LDS_AS*)(wl + c * kWRow + 16 * ch) = stg[u];
-      }
-      __syncthreads();
-      if (vh == 0) load_w(1, stg);
-      if (wave >= 4) continue;  // four waves cover the half's 64 columns
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  }
+  if (wave < 4) dev::wait_vm<0>();  // this wave's share of W_UV[h] is in LDS
+  __syncthreads();
+  // out[b][v] for the 16 columns v = 16 wave + l16: A = latent rows (lane
+  // row l16, zero past the block's 8), B = W_UV[h] read transposed
+  const int r4 = l16 >> 2, q4 = l16 & 3;
+  const int cb = 32 * wave + 8 * q4;  // byte column of this lane's 4 values
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-      for (int ks = 0; ks < DC / 32; ++ks) {
-        const int aoff = l16 * LD::LROW + 2 * (32 * ks + 8 * kg);
-        const bf16x8 ah = *(const bf16x8 LDS_AS*)(lhi + aoff);
-        const bf16x8 al = *(const bf16x8 LDS_AS*)(llo + aoff);
-        const int wr = (32 * ks + 8 * kg + r4) * kWRow + wcol;
-        const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(wl + wr));
-        const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(wl + wr + 4 * kWRow));
-        const i16x8 wv = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-        const bf16x8 wb = __builtin_bit_cast(bf16x8, wv);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wb, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wb, acc, 0, 0, 0);
-      }
-      // D[row][v]: rows 4 kg + e of the block (only rows < nbq are sequences)
-      const int v = kDVH * vh + 16 * wave + l16;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int bb = 4 * kg + e;
-        if (bb < nbq) out[((size_t)(b0 + bb) * g.H + h) * g.dv + v] = (TO)(alpha_kv * acc[e]);
-      }
+  for (int ks = 0; ks < DC / 32; ++ks) {
+    bf16x8 ah = {}, al = {};
+    if (l16 < kMSQ) {
+      const int aoff = l16 * MD::LROW + 2 * (32 * ks + 8 * kg);
+      ah = *(const bf16x8 LDS_AS*)(lhi + aoff);
+      al = *(const bf16x8 LDS_AS*)(llo + aoff);
     }
+    const int R = 32 * ks + 8 * kg + r4;
+    const int o0 = R * 256 + (((cb >> 4) ^ kWSwz(R)) << 4) + (cb & 15);
+    const int o1 = (R + 4) * 256 + (((cb >> 4) ^ kWSwz(R + 4)) << 4) + (cb & 15);
+    const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(wl + o0));
+    const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(wl + o1));
+    const i16x8 wv = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    const bf16x8 wb = __builtin_bit_cast(bf16x8, wv);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wb, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wb, acc, 0, 0, 0);
+  }
+  // D[row][v]: rows 4 kg + e of the block (only rows < nbq are sequences)
+  const int vc = 16 * wave + l16;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int bb = 4 * kg + e;
+    if (bb < nbq) out[((size_t)(b0 + bb) * g.H + h) * g.dv + vc] = (TO)(alpha_kv * acc[e]);
   }
 }
 
 template <int DC, typename TO>
 hipError_t launch_merge_out_t(const Geom& g, const Workspace& ws, const __bf16* w_uv, TO* out,
                               float alpha_kv, hipStream_t s) {
+  if (g.dv != 128 || g.n > kMNB || DC % g.n) return hipErrorNotSupported;
   const int64_t grid = (int64_t)((g.H + 7) / 8) * 8 * ((g.B + kMSQ - 1) / kMSQ);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((merge_out<DC, TO>), dim3((unsigned)grid), dim3(512), 0, s, g, ws, w_uv, out,
