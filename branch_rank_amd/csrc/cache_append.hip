@@ -24,7 +24,7 @@ __device__ __forceinline__ void store_as(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_as(__bf16* p, float v) { *p = (__bf16)v; }
 
 template <typename T>
-__global__ __launch_bounds__(256) void cache_append_kernel(AppendArgs a) {
+__global__ __launch_bounds__(256) void cache_append_kernel(AppendArgs a, RopeFreqs fr) {
   __shared__ float red[4];
   __shared__ int pos_s;
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -47,13 +47,16 @@ __global__ __launch_bounds__(256) void cache_append_kernel(AppendArgs a) {
     const float g = a.gain ? a.gain[i] : 1.f;
     store_as(c + i, row[i] * inv * g);
   }
-  // RoPE key rotated to position p (angle in double precision)
+  // RoPE key rotated to position p: the angle p * theta^(-2i/d_r) (frequency
+  // from the host's table), its reduction to [-pi, pi] and its sine and
+  // cosine in double precision
   T* k = (T*)a.krope + (int64_t)b * a.kr_bs + (int64_t)p * a.kr_ts;
   const float* kr = row + a.d_c;
   for (int i = tid; i < a.d_r / 2; i += 256) {
-    const double omega = pow((double)a.theta, -2.0 * (double)i / (double)a.d_r);
+    const double ang = (double)p * fr.w[i];
+    const double r = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
     double sn, cs;
-    sincos((double)p * omega, &sn, &cs);
+    sincos(r, &sn, &cs);
     const double x0 = kr[2 * i], x1 = kr[2 * i + 1];
     store_as(k + 2 * i, (float)(x0 * cs - x1 * sn));
     store_as(k + 2 * i + 1, (float)(x0 * sn + x1 * cs));
@@ -66,10 +69,11 @@ __global__ __launch_bounds__(256) void cache_append_kernel(AppendArgs a) {
 
 hipError_t launch_cache_append(const AppendArgs& a, bool bf16, int batch, hipStream_t s) {
   if (batch <= 0) return hipSuccess;
+  const RopeFreqs& fr = rope_freqs(a.theta, a.d_r);
   if (bf16)
-    hipLaunchKernelGGL(cache_append_kernel<__bf16>, dim3(batch), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(cache_append_kernel<__bf16>, dim3(batch), dim3(256), 0, s, a, fr);
   else
-    hipLaunchKernelGGL(cache_append_kernel<float>, dim3(batch), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(cache_append_kernel<float>, dim3(batch), dim3(256), 0, s, a, fr);
   return hipGetLastError();
 }
 

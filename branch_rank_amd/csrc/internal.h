@@ -79,6 +79,15 @@ hipError_t launch_prefill_branch(const Geom& g, int T, const void* q_nope, const
                                  float tau, float alpha_q, float alpha_kv, float theta,
                                  hipStream_t s, const KernelTiming& t);
 
+// Rotary frequencies omega_k = theta^(-2k / d_r), k < d_r / 2, in double,
+// computed on the host once per (theta, d_r) and passed to the kernels by
+// value, so that no kernel evaluates pow() per element.
+constexpr int kMaxRopePairs = 128;  // d_r <= 256
+struct RopeFreqs {
+  double w[kMaxRopePairs];
+};
+const RopeFreqs& rope_freqs(float theta, int dr);
+
 constexpr int kMinChunk = 64;      // smallest automatic work item, tokens
 constexpr int kMaxAutoItems = 512; // upper bound on automatic work items
 

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void absorb_q_generic(Geom g, const T* __restr
                                                         const int32_t* __restrict__ lens,
                                                         const T* __restrict__ w_uk,
                                                         T* __restrict__ q_abs, float tau,
-                                                        float alpha_q, float theta) {
+                                                        float alpha_q, RopeFreqs fr) {
   extern __shared__ float sq[];  // [kQB][dn]
   const int h = blockIdx.x, b0 = blockIdx.y * kQB;
   const int nb = min(kQB, g.B - b0);
@@ -100,14 +100,14 @@ __global__ __launch_bounds__(256) void absorb_q_generic(Geom g, const T* __restr
     for (int bb = 0; bb < nb; ++bb)
       q_abs[((size_t)(b0 + bb) * g.H + h) * row + c] = from_f32<T>(s * acc[bb]);
   }
-  // RoPE on the query's rotary part, angle in double precision.
+  // RoPE on the query's rotary part, angle in double precision (frequency
+  // from the host's table).
   const int half = g.dr / 2;
   for (int i = threadIdx.x; i < nb * half; i += blockDim.x) {
     const int bb = i / half, k = i % half, b = b0 + bb;
     const int p = q_pos ? q_pos[b] : clamp_len(lens[b], g.max_len) - 1;
-    const double omega = pow((double)theta, -2.0 * (double)k / (double)g.dr);
     double sn, cs;
-    sincos((double)p * omega, &sn, &cs);
+    sincos((double)p * fr.w[k], &sn, &cs);
     const size_t qi = ((size_t)b * g.H + h) * g.dr + 2 * k;
     const double x0 = to_f32(q_rope[qi]), x1 = to_f32(q_rope[qi + 1]);
     T* o = q_abs + ((size_t)b * g.H + h) * row + g.dc + 2 * k;
@@ -362,7 +362,8 @@ hipError_t launch_absorb_q_generic(const Geom& g, const T* q_nope, const T* q_ro
                                    hipStream_t s) {
   const size_t sh = sizeof(float) * kQB * g.dn;
   hipLaunchKernelGGL(absorb_q_generic<T>, dim3(g.H, (g.B + kQB - 1) / kQB), dim3(256), sh, s, g,
-                     q_nope, q_rope, q_pos, lens, w_uk, q_abs, tau, alpha_q, theta);
+                     q_nope, q_rope, q_pos, lens, w_uk, q_abs, tau, alpha_q,
+                     rope_freqs(theta, g.dr));
   return hipGetLastError();
 }
 

@@ -17,6 +17,21 @@
 
 using namespace mlra;
 
+// One cached table per thread: the launches of a decode loop share theta and
+// d_r, so pow() runs once per thread and configuration.
+const RopeFreqs& mlra::rope_freqs(float theta, int dr) {
+  thread_local RopeFreqs t;
+  thread_local float t_theta = 0.f;
+  thread_local int t_dr = -1;
+  if (t_theta != theta || t_dr != dr) {
+    for (int k = 0; k < dr / 2 && k < kMaxRopePairs; ++k)
+      t.w[k] = std::pow((double)theta, -2.0 * (double)k / (double)dr);
+    t_theta = theta;
+    t_dr = dr;
+  }
+  return t;
+}
+
 namespace {
 
 thread_local std::string g_detail;

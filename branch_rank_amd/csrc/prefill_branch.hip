@@ -89,7 +89,8 @@ struct PrefillParams {
   void* out;             // [B][T][H][d_v]
   int T, H, QB;          // QB: 64-position blocks per sequence
   float scale_n, scale_r;  // query scales, log2(e) folded in: alpha_q tau log2e, tau log2e
-  float alpha_kv, theta;
+  float alpha_kv;
+  double omega[kDR / 2];   // rotary frequencies theta^(-2k/d_r)
 };
 
 __device__ __forceinline__ void store4(float* p, f32x4 v) { *(f32x4*)p = v; }
@@ -181,12 +182,13 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
     if (s < ntiles) issue(s);
 
   // ---- RoPE queries of the 64 positions, once per workgroup: the angle
-  // t * theta^(-2k/d_r) and its reduction to [-pi, pi] in double precision,
-  // sine and cosine of the reduced angle in float ----
+  // t * theta^(-2k/d_r) (frequency from the host's table) and its reduction
+  // to [-pi, pi] in double precision, sine and cosine of the reduced angle in
+  // float ----
   {
     static_assert((64 * kNW) % (kDR / 2) == 0, "one frequency per thread");
     const int k = threadIdx.x % (kDR / 2);
-    const double omega = pow((double)p.theta, -2.0 * (double)k / (double)kDR);
+    const double omega = p.omega[k];
     for (int e = threadIdx.x; e < kQWG * (kDR / 2); e += 64 * kNW) {
       const int qi = e / (kDR / 2);
       const int t = min(qb * kQWG + qi, T - 1);
@@ -540,7 +542,8 @@ hipError_t launch_prefill_branch(const Geom& g, int T, const void* q_nope, const
   p.scale_n = (float)((double)alpha_q * tau * kLog2eD);
   p.scale_r = (float)((double)tau * kLog2eD);
   p.alpha_kv = alpha_kv;
-  p.theta = theta;
+  const RopeFreqs& fr = rope_freqs(theta, kDR);
+  for (int k = 0; k < kDR / 2; ++k) p.omega[k] = fr.w[k];
   const int64_t grid = (int64_t)g.B * p.QB * g.H;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (out_bf16)

@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void absorb_q_mfma(Geom g, const __bf16* __res
                                                      const int32_t* __restrict__ lens,
                                                      const __bf16* __restrict__ w_uk,
                                                      __bf16* __restrict__ q_abs, float scale,
-                                                     float tau, float theta, PlanArgs plan) {
+                                                     float tau, RopeFreqs fr, PlanArgs plan) {
   if (blockIdx.x == g.H) {  // the extra column of workgroups: plan (first one only)
     if (blockIdx.y == 0 && blockIdx.z == 0) plan_block(plan);
     return;
@@ -109,23 +109,16 @@ __global__ __launch_bounds__(256) void absorb_q_mfma(Geom g, const __bf16* __res
   }
 
   // RoPE on the query's rotary part, its (sequence, pair) elements spread over
-  // the parts' threads: the angle p * theta^(-2k/d_r) and its reduction to
-  // [-pi, pi] in double precision, sine and cosine of the reduced angle in
-  // float; the frequency is recomputed only when a thread's pair index k
-  // changes (never when the stride is a multiple of d_r / 2)
+  // the parts' threads: the angle p * theta^(-2k/d_r) (frequency from the
+  // host's table) and its reduction to [-pi, pi] in double precision, sine
+  // and cosine of the reduced angle in float
   const int hp = g.dr / 2;
   {
-    int kc = -1;
-    double omega = 0.0;
     for (int i = threadIdx.x + 256 * part; i < 16 * MBLK * hp; i += 256 * parts) {
       const int b = b0 + i / hp, k = i % hp;
       if (b >= g.B) continue;
-      if (k != kc) {
-        omega = pow((double)theta, -2.0 * (double)k / (double)g.dr);
-        kc = k;
-      }
       const int p = q_pos ? q_pos[b] : clamp_len(lens[b], g.max_len) - 1;
-      const double a = (double)p * omega;
+      const double a = (double)p * fr.w[k];
       const double r = a - 6.283185307179586 * rint(a * 0.15915494309189535);
       float sn, cs;
       sincosf((float)r, &sn, &cs);
@@ -606,6 +599,7 @@ hipError_t launch_absorb_k(const Geom& g, const __bf16* qn, const __bf16* qr, co
                            const int32_t* lens, const __bf16* w, __bf16* qa, float scale,
                            float tau, float theta, const PlanArgs& plan, hipStream_t s) {
   const int gx = g.H + (plan.hdr ? 1 : 0);
+  const RopeFreqs& fr = rope_freqs(theta, g.dr);
   // latent column parts per head: the most (<= 8) that split the 16-column
   // blocks evenly, so that more workgroups share the W_UK read (1032 at
   // H = 128, d_c = 512)
@@ -618,10 +612,10 @@ hipError_t launch_absorb_k(const Geom& g, const __bf16* qn, const __bf16* qr, co
     }
   if (g.B > 32) {
     hipLaunchKernelGGL((absorb_q_mfma<KSN, 4>), dim3(gx, (g.B + 63) / 64, parts), dim3(256), 0,
-                       s, g, qn, qr, qp, lens, w, qa, scale, tau, theta, plan);
+                       s, g, qn, qr, qp, lens, w, qa, scale, tau, fr, plan);
   } else {
     hipLaunchKernelGGL((absorb_q_mfma<KSN, 1>), dim3(gx, (g.B + 15) / 16, parts), dim3(256), 0,
-                       s, g, qn, qr, qp, lens, w, qa, scale, tau, theta, plan);
+                       s, g, qn, qr, qp, lens, w, qa, scale, tau, fr, plan);
   }
   return hipGetLastError();
 }
