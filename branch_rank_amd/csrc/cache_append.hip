@@ -25,43 +25,56 @@ __device__ __forceinline__ void store_as(__bf16* p, float v) { *p = (__bf16)v; }
 
 template <typename T>
 __global__ __launch_bounds__(256) void cache_append_kernel(AppendArgs a, RopeFreqs fr) {
+  constexpr int kPer = 4;  // latent values per thread (d_c <= 1024)
   __shared__ float red[4];
-  __shared__ int pos_s;
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  if (tid == 0) pos_s = max(a.lens[b], 0);
-  __syncthreads();
-  const int p = pos_s;  // position of the new token
-  if (p >= a.max_len) return;  // no room: the sequence stays as it is
-
   const float* row = a.rows + (int64_t)b * (a.d_c + a.d_r);
+  // every input is loaded up front, together with the length: this thread's
+  // latent values and gains, and its RoPE pair (d_r / 2 <= 128 pairs)
+  float xv[kPer], gv[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = tid + 256 * u;
+    xv[u] = i < a.d_c ? row[i] : 0.f;
+    gv[u] = i < a.d_c && a.gain ? a.gain[i] : 1.f;
+  }
+  const int hp = a.d_r / 2;
+  float k0 = 0.f, k1 = 0.f;
+  if (tid < hp) {
+    k0 = row[a.d_c + 2 * tid];
+    k1 = row[a.d_c + 2 * tid + 1];
+  }
+  const int p = max(a.lens[b], 0);  // position of the new token
+  if (p >= a.max_len) return;       // no room: the sequence stays as it is
+
   // mean of squares over the latent (fp32, two-level tree)
   float ss = 0.f;
-  for (int i = tid; i < a.d_c; i += 256) ss = fmaf(row[i], row[i], ss);
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) ss = fmaf(xv[u], xv[u], ss);
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
   if (lane == 0) red[wid] = ss;
-  __syncthreads();
+  __syncthreads();  // also: every thread has read the length
   const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)a.d_c + a.eps);
 
   T* c = (T*)a.ckv + (int64_t)b * a.ckv_bs + (int64_t)p * a.ckv_ts;
-  for (int i = tid; i < a.d_c; i += 256) {
-    const float g = a.gain ? a.gain[i] : 1.f;
-    store_as(c + i, row[i] * inv * g);
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = tid + 256 * u;
+    if (i < a.d_c) store_as(c + i, xv[u] * inv * gv[u]);
   }
   // RoPE key rotated to position p: the angle p * theta^(-2i/d_r) (frequency
   // from the host's table), its reduction to [-pi, pi] and its sine and
   // cosine in double precision
-  T* k = (T*)a.krope + (int64_t)b * a.kr_bs + (int64_t)p * a.kr_ts;
-  const float* kr = row + a.d_c;
-  for (int i = tid; i < a.d_r / 2; i += 256) {
-    const double ang = (double)p * fr.w[i];
+  if (tid < hp) {
+    T* k = (T*)a.krope + (int64_t)b * a.kr_bs + (int64_t)p * a.kr_ts;
+    const double ang = (double)p * fr.w[tid];
     const double r = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
     double sn, cs;
     sincos(r, &sn, &cs);
-    const double x0 = kr[2 * i], x1 = kr[2 * i + 1];
-    store_as(k + 2 * i, (float)(x0 * cs - x1 * sn));
-    store_as(k + 2 * i + 1, (float)(x0 * sn + x1 * cs));
+    const double x0 = k0, x1 = k1;
+    store_as(k + 2 * tid, (float)(x0 * cs - x1 * sn));
+    store_as(k + 2 * tid + 1, (float)(x0 * sn + x1 * cs));
   }
-  __syncthreads();  // pos_s was read by every thread before the length moves
   if (tid == 0) a.lens[b] = p + 1;
 }
 

@@ -37,6 +37,17 @@ __device__ __forceinline__ int clamp_len(int v, int max_len) {
   return v < 0 ? 0 : (v > max_len ? max_len : v);
 }
 
+// x if c, else zeros, through a mask the compiler cannot see through: written
+// as a select, the load feeding x is put back under a branch and waited for
+// at once, which serialises loads meant to be in flight together.
+__device__ __forceinline__ bf16x8 keep_if(bf16x8 x, bool c) {
+  typedef int i32x4v __attribute__((ext_vector_type(4)));
+  int m = c ? -1 : 0;
+  asm volatile("" : "+v"(m));
+  const i32x4v v = __builtin_bit_cast(i32x4v, x) & m;
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // ------------------------------------------------------------- absorb_q ----
 
 // grid (H (+1 when the plan rides along), ceil(B / (16 MBLK)), 2 halves of
@@ -58,17 +69,31 @@ __global__ __launch_bounds__(256) void absorb_q_mfma(Geom g, const __bf16* __res
   const int l16 = lane & 15, kg = lane >> 4;
   const int row = g.dc + g.dr;
   const int dn = KSN * 32;
+  // Every load below is unconditional (indices clamped into range, values
+  // masked afterwards), so that none waits for another: the RoPE inputs of
+  // this thread's first (sequence, pair) element, the q^N rows and the W_UK
+  // fragments are in flight together.
+  const int hp = g.dr / 2, i0 = threadIdx.x + 256 * part;
+  int rp;
+  float rx0, rx1;
+  {
+    const int ir = min(i0, max(16 * MBLK * hp - 1, 0));
+    const int b = min(b0 + (hp > 0 ? ir / hp : 0), g.B - 1), k = hp > 0 ? ir % hp : 0;
+    const int pv = (q_pos ? q_pos : lens)[b];
+    rp = q_pos ? pv : clamp_len(pv, g.max_len) - 1;
+    const __bf16* xr = hp > 0 ? q_rope + ((size_t)b * g.H + h) * g.dr + 2 * k : q_nope;
+    rx0 = (float)xr[0];
+    rx1 = (float)xr[hp > 0 ? 1 : 0];
+  }
   // A = q^N rows of this block's sequences: lane (b = l16, kg)
   bf16x8 A[MBLK][KSN];
 #pragma unroll
   for (int m = 0; m < MBLK; ++m) {
-    const int b = b0 + 16 * m + l16;
+    const int b = b0 + 16 * m + l16, bc = min(b, g.B - 1);
 #pragma unroll
     for (int ks = 0; ks < KSN; ++ks) {
-      if (b < g.B)
-        A[m][ks] = *(const bf16x8*)(q_nope + ((size_t)b * g.H + h) * dn + 32 * ks + 8 * kg);
-      else
-        A[m][ks] = (bf16x8){};
+      const bf16x8 x = *(const bf16x8*)(q_nope + ((size_t)bc * g.H + h) * dn + 32 * ks + 8 * kg);
+      A[m][ks] = keep_if(x, b < g.B);
     }
   }
   // N blocks of 16 latent columns: this part's blocks (of `parts` equal
@@ -78,22 +103,20 @@ __global__ __launch_bounds__(256) void absorb_q_mfma(Geom g, const __bf16* __res
   constexpr int NBW = 4;
   const int nblk = g.dc / 16, per_part = nblk / parts;
   const __bf16* w = w_uk + (size_t)h * g.dc * dn;
+  const int nu = (per_part - __builtin_amdgcn_readfirstlane(wave) + 3) / 4;  // blocks of this wave
   bf16x8 Bf[NBW][KSN];
 #pragma unroll
   for (int u = 0; u < NBW; ++u) {
-    const int nb = part * per_part + wave + 4 * u;
-    const int c = 16 * nb + l16;
+    if (u >= nu) break;
+    const int c = 16 * (part * per_part + wave + 4 * u) + l16;
 #pragma unroll
     for (int ks = 0; ks < KSN; ++ks)
-      Bf[u][ks] = nb < (part + 1) * per_part
-                      ? *(const bf16x8*)(w + (size_t)c * dn + 32 * ks + 8 * kg)
-                      : (bf16x8){};
+      Bf[u][ks] = *(const bf16x8*)(w + (size_t)c * dn + 32 * ks + 8 * kg);
   }
 #pragma unroll
   for (int u = 0; u < NBW; ++u) {
-    const int nb = part * per_part + wave + 4 * u;
-    if (nb >= (part + 1) * per_part) break;
-    const int c = 16 * nb + l16;
+    if (u >= nu) break;
+    const int c = 16 * (part * per_part + wave + 4 * u) + l16;
 #pragma unroll
     for (int m = 0; m < MBLK; ++m) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -112,18 +135,22 @@ __global__ __launch_bounds__(256) void absorb_q_mfma(Geom g, const __bf16* __res
   // the parts' threads: the angle p * theta^(-2k/d_r) (frequency from the
   // host's table) and its reduction to [-pi, pi] in double precision, sine
   // and cosine of the reduced angle in float
-  const int hp = g.dr / 2;
   {
-    for (int i = threadIdx.x + 256 * part; i < 16 * MBLK * hp; i += 256 * parts) {
+    for (int i = i0; i < 16 * MBLK * hp; i += 256 * parts) {
       const int b = b0 + i / hp, k = i % hp;
       if (b >= g.B) continue;
-      const int p = q_pos ? q_pos[b] : clamp_len(lens[b], g.max_len) - 1;
+      int p = rp;
+      float x0 = rx0, x1 = rx1;
+      const size_t qi = ((size_t)b * g.H + h) * g.dr + 2 * k;
+      if (i != i0) {  // a later element of this thread (B > 32 or a wide RoPE part)
+        p = q_pos ? q_pos[b] : clamp_len(lens[b], g.max_len) - 1;
+        x0 = (float)q_rope[qi];
+        x1 = (float)q_rope[qi + 1];
+      }
       const double a = (double)p * fr.w[k];
       const double r = a - 6.283185307179586 * rint(a * 0.15915494309189535);
       float sn, cs;
       sincosf((float)r, &sn, &cs);
-      const size_t qi = ((size_t)b * g.H + h) * g.dr + 2 * k;
-      const float x0 = (float)q_rope[qi], x1 = (float)q_rope[qi + 1];
       __bf16* o = q_abs + ((size_t)b * g.H + h) * row + g.dc + 2 * k;
       o[0] = (__bf16)(tau * (x0 * cs - x1 * sn));
       o[1] = (__bf16)(tau * (x0 * sn + x1 * cs));
