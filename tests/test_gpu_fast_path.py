@@ -256,3 +256,24 @@ def test_fused_merge_matches_separate_calls(name, kernel, out_dtype):
     err = row_rel_err(fused, sep)
     say(f"{name} {kernel} {out_dtype}: fused vs separate rel err {err:.2e}")
     assert err <= tol
+
+
+@pytest.mark.parametrize("name,kernel", [("mlra4_b16_l32k", "branch"), ("mla_b16_l4k", "head_group")])
+def test_fused_merge_many_slots(name, kernel):
+    # 64-token work items give up to 79 partial slots per sequence, so the
+    # fused merge runs its weight table in several 32-slot passes; a
+    # sequence of exactly one item, an empty one and one ending one token
+    # into an item cross the pass and item edges
+    w = WORKLOADS[name].replace(batch=5)
+    lens = np.array([5000, 2100, 64, 0, 4097], np.int32)
+    inp = make_inputs(w, lens=lens, max_len=5000)
+    cfg = config_for(w, kernel=kernel, kv_chunk=64)
+    d = Dev(w, inp)
+    fused = host(d.decode(cfg))
+    sep = host(d.out_proj(cfg, d.latent(cfg, d.absorb(cfg))))
+    assert not np.any(fused[3])
+    err = row_rel_err(fused, sep)
+    say(f"{name} {kernel} chunk 64: fused vs separate rel err {err:.2e}")
+    assert err <= 1e-5
+    ref = absorbed_oracle(w, inp, np.array([0, 2, 4]))
+    assert row_rel_err(fused[[0, 2, 4]], ref) <= TOL
