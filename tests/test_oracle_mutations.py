@@ -3,11 +3,11 @@
 Each case plants one mistake in a copy of the oracle's source (a wrong sign,
 frequency, index, slice, scale, axis or mask), loads that copy as a separate
 module and runs it against references that do not use the oracle: the scalar
-brute force of the pins, a direct softmax for the split-merge law, and that
-brute force row by row for the prefill. Every planted mistake must move at
-least one of them far outside rounding, while the unchanged source agrees
-with all of them to 1e-12. Only CPU work; nothing here touches the real
-oracle module.
+brute force of the pins, a direct softmax for the split-merge law, that brute
+force row by row for the prefill, and the appended row written out element by
+element. Every planted mistake must move at least one of them far outside
+rounding, while the unchanged source agrees with all of them to 1e-12. Only
+CPU work; nothing here touches the real oracle module.
 """
 
 import math
@@ -70,6 +70,13 @@ MUTATIONS = [
     ("prefill query rotated one position late",
      "            rho = rope(q_rope[b, :L, h], np.arange(L), theta)",
      "            rho = rope(q_rope[b, :L, h], np.arange(L) + 1, theta)"),
+    ("RMS over the sum instead of the mean",
+     "    r = np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)",
+     "    r = np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)"),
+    ("appended key rotated at the previous position",
+     "        k = rope(new_kr[b], p, theta)", "        k = rope(new_kr[b], p - 1, theta)"),
+    ("appended row written one row early",
+     "        ckv[b, p] = c\n        krope[b, p] = k", "        ckv[b, p - 1] = c\n        krope[b, p - 1] = k"),
     ("prefill without alpha_kv",
      "                out[b, :L, h] += alpha_kv * ((e / e.sum(axis=1, keepdims=True)) @ V)",
      "                out[b, :L, h] += ((e / e.sum(axis=1, keepdims=True)) @ V)"),
@@ -115,6 +122,27 @@ def check_errors(m):
                    ckv=P["ckv"], krope=P["krope"], lens=np.array([tq + 1], np.int32))
         worst = max(worst, rel(got[0, tq], _brute(row, 2, TAU, AQ, AKV)[0]))
     errs["prefill"] = worst
+    # cache append against the row written out directly: RMS-normalised latent
+    # times the gain, key turned pair by pair by p theta^(-2i/d_r), p = L_b
+    rng = np.random.default_rng(13)
+    B, Lmax, d_c, d_r, eps = 3, 4, 6, 4, 1e-6
+    ckv, krope = rng.standard_normal((B, Lmax, d_c)), rng.standard_normal((B, Lmax, d_r))
+    lens = np.array([0, 2, Lmax], np.int32)
+    nc, nk, gain = rng.standard_normal((B, d_c)), rng.standard_normal((B, d_r)), rng.standard_normal(d_c)
+    c2, k2, l2 = m.cache_append_ref(ckv, krope, lens, nc, nk, Lmax, gain=gain, eps=eps)
+    want_c, want_k = ckv.copy(), krope.copy()
+    for b in range(B):
+        p = int(lens[b])
+        if p >= Lmax:
+            continue
+        want_c[b, p] = nc[b] / math.sqrt(sum(x * x for x in nc[b]) / d_c + eps) * gain
+        for i in range(d_r // 2):
+            a = p * 10000.0 ** (-2.0 * i / d_r)
+            x0, x1 = nk[b, 2 * i], nk[b, 2 * i + 1]
+            want_k[b, p, 2 * i] = x0 * math.cos(a) - x1 * math.sin(a)
+            want_k[b, p, 2 * i + 1] = x0 * math.sin(a) + x1 * math.cos(a)
+    errs["append"] = max(rel(c2, want_c), rel(k2, want_k),
+                         0.0 if l2.tolist() == [1, 3, Lmax] else np.inf)
     return {k: (v if np.isfinite(v) else np.inf) for k, v in errs.items()}
 
 
