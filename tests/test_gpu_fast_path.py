@@ -277,3 +277,27 @@ def test_fused_merge_many_slots(name, kernel):
     assert err <= 1e-5
     ref = absorbed_oracle(w, inp, np.array([0, 2, 4]))
     assert row_rel_err(fused[[0, 2, 4]], ref) <= TOL
+
+
+@pytest.mark.parametrize("d_c,n,heads", [(256, 2, 64), (256, 1, 128), (128, 1, 32)])
+def test_other_latent_widths(d_c, n, heads):
+    # the MFMA path's d_c = 256 and d_c = 128 instantiations (absorb_q,
+    # head-group decode, fused merge + projection) against the oracle, and
+    # the fused merge against the separate calls. Unit scales: with
+    # alpha_q = sqrt(56) on 128-wide unit-RMS slices and W_UK of std 1/16,
+    # rounding q~ to bf16 alone moves these rows by up to 1.08e-2 (a numpy
+    # model of that rounding), above the bar for any bf16 query
+    w = WORKLOADS["mla_b16_l4k"].replace(d_c=d_c, n=n, heads=heads, batch=5)
+    lens = np.array([300, 1, 0, 77, 129], np.int32)
+    inp = make_inputs(w, lens=lens, max_len=320)
+    cfg = config_for(w)
+    d = Dev(w, inp)
+    kernel = br.select_decode_kernel(cfg, d.cache(cfg))
+    say(f"d_c={d_c} n={n} H={heads}: kernel {kernel}")
+    got = host(d.decode(cfg))
+    err = row_rel_err(got[[0, 1, 3, 4]], absorbed_oracle(w, inp, np.array([0, 1, 3, 4])))
+    say(f"  rel err {err:.2e}")
+    assert err <= TOL
+    assert not np.any(got[2])
+    sep = host(d.out_proj(cfg, d.latent(cfg, d.absorb(cfg))))
+    assert row_rel_err(got, sep) <= 1e-5
