@@ -35,6 +35,22 @@ KERNEL_SRC = {"prefill": "branch_rank_amd/csrc/prefill_branch.hip",
               "branch": "branch_rank_amd/csrc/decode_branch.hip",
               "head_group": "branch_rank_amd/csrc/decode_mfma.hip",
               "portable": "branch_rank_amd/csrc/kernels_generic.hip"}
+# headers each kernel's source includes (their text is part of the kernel)
+_CSRC = "branch_rank_amd/csrc/"
+KERNEL_DEPS = {"prefill": ["device_common.h", "internal.h"],
+               "branch": ["branch_tiles.h", "device_common.h", "internal.h"],
+               "head_group": ["device_common.h", "internal.h"],
+               "portable": ["internal.h", "plan_device.h"]}
+
+
+def source_sha(kernel):
+    """sha256 over a kernel's source file and the headers it includes, in a
+    fixed order: a change to any of them makes counters taken before stale."""
+    h = hashlib.sha256()
+    for f in [KERNEL_SRC[kernel]] + [_CSRC + d for d in KERNEL_DEPS[kernel]]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def log(*a):
@@ -90,7 +106,7 @@ def traffic_for(workload, kernel, path=TRAFFIC_FILE):
         with open(path) as f:
             t = json.load(f)
         src = KERNEL_SRC[kernel]
-        sha = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
+        sha = source_sha(kernel)
         if (t.get("kernel_source") != src or t.get("kernel_sha256") != sha
                 or t.get("workload") != workload):
             return None

@@ -51,7 +51,8 @@ template <int ROWB>
 __device__ __forceinline__ int swz_l(int t) { return 2 * (t & (ROWB / 32 - 1)); }
 __device__ __forceinline__ int swz_r(int t) { return (t >> 1) & 7; }
 
-// DMA of one tile into the stage at LDS byte address `stage`. Wave w issues
+// DMA of one tile into the stage at LDS byte address `stage` (streaming
+// loads, dma16_stream). Wave w issues
 // latent instructions q = w, w + NW, ... (rows RPI*q .. +RPI-1; lat_voff is
 // this lane's offset within such a row group, the tile row in soffset) and,
 // if w < NR, RoPE instruction w (8 rows; rope_t and rope_c are this lane's row
@@ -66,15 +67,15 @@ __device__ __forceinline__ void issue_tile(uint32_t stage, i32x4 crs, i32x4 krs,
   for (int u = 0; u < C::NL / C::NW; ++u) {
     const int q = wave + C::NW * u;
     if constexpr (!TAIL) {
-      dma16(crs, stage + q * 1024, lat_voff, (uint32_t)((tstart + C::RPI * q) * cts * 2));
+      dma16_stream(crs, stage + q * 1024, lat_voff, (uint32_t)((tstart + C::RPI * q) * cts * 2));
     } else {
       const int row = min(tstart + C::RPI * q + lane / (64 / C::RPI), tend - 1);
-      dma16(crs, stage + q * 1024, (uint32_t)(row * cts * 2 + lat_c), 0u);
+      dma16_stream(crs, stage + q * 1024, (uint32_t)(row * cts * 2 + lat_c), 0u);
     }
   }
   if (wave < C::NR) {
     const int row = min(tstart + rope_t, tend - 1);
-    dma16(krs, stage + C::LAT + wave * 1024, (uint32_t)(row * kts * 2 + rope_c), 0u);
+    dma16_stream(krs, stage + C::LAT + wave * 1024, (uint32_t)(row * kts * 2 + rope_c), 0u);
   }
 }
 

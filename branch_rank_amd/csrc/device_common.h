@@ -72,6 +72,24 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_base, uint32_t vo
       : "memory");
 }
 
+// The same load for data that streams through once, the decode's cache
+// tiles: device scope (sc1: not kept in the CU's vector cache) and
+// non-temporal (nt: evicted first from L2 and the Infinity Cache), so that
+// the step's weights and split-KV partials stay cached while hundreds of MB of
+// cache pass by. The second workgroup of an item still finds the shared RoPE
+// rows in L2 (fetched bytes past L2 are unchanged).
+__device__ __forceinline__ void dma16_stream(i32x4 rsrc, uint32_t lds_base, uint32_t voff,
+                                             uint32_t soff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen sc1 nt lds"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(rsrc),
+        "s"(__builtin_amdgcn_readfirstlane(soff))
+      : "memory");
+}
+
 // Sequence holding token position pos of the batch-wide token stream.
 __device__ __forceinline__ int find_seq(const int32_t* prefix, int B, int pos) {
   int lo = 0, hi = B;
