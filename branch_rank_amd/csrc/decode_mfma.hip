@@ -116,18 +116,18 @@ __device__ __forceinline__ void issue_tile(char LDS_AS* stage, i32x4 crs, i32x4 
     const i32x4 rs = rope ? krs : crs;
     const int ts = rope ? kts : cts;
     if constexpr (!TAIL && C::PRE_VOFF) {
-      dma16(rs, ldsb, voff[u], (uint32_t)(tstart * ts * 2));
+      dma16_stream(rs, ldsb, voff[u], (uint32_t)(tstart * ts * 2));
     } else if constexpr (!TAIL) {
       bool r_;
       int t, lc;
       dma_lane<DC, NB, NW>(u, wave, lane, r_, t, lc);
-      dma16(rs, ldsb, (uint32_t)(t * ts * 2 + lc * 16), (uint32_t)(tstart * ts * 2));
+      dma16_stream(rs, ldsb, (uint32_t)(t * ts * 2 + lc * 16), (uint32_t)(tstart * ts * 2));
     } else {
       bool r_;
       int t, lc;
       dma_lane<DC, NB, NW>(u, wave, lane, r_, t, lc);
       const int row = min(tstart + t, tend - 1);
-      dma16(rs, ldsb, (uint32_t)(row * ts * 2 + lc * 16), 0u);
+      dma16_stream(rs, ldsb, (uint32_t)(row * ts * 2 + lc * 16), 0u);
     }
   }
 }
