@@ -85,6 +85,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe-copy", action="store_true",
                     help="only run a 1 GiB device copy (scale factor for HBM counters)")
+    ap.add_argument("--probe-read", action="store_true",
+                    help="only run the HBM read-ceiling probe and print its JSON")
+    ap.add_argument("--no-probe-read", action="store_true",
+                    help="skip the read-ceiling probe in the full run")
     return ap.parse_args()
 
 
@@ -249,15 +253,19 @@ def time_cache_append(w, steps, warmup, torch, br):
 
 def prefill_flops(w, lens):
     """Algorithmic work of the prefill kernel: each of the L(L+1)/2 (query,
-    key) pairs of a sequence costs, per head, 2 (d_c' + d_r) flop per branch
-    for the score and 2 d_c' for the value (2 (n d_r + 2 d_c) in all); each
-    position and head adds the absorption (2 d_c d_n) and the output
-    projection (2 d_c d_v). Returns (attention part, total, pairs)."""
+    key) pairs of a sequence costs, per head, 2 d_c' flop per branch for the
+    latent part of the score, 2 d_r once for the RoPE part (one dot product
+    shared by the branches) and 2 d_c' per branch for the value: 2 (d_r +
+    2 d_c) in all (2176 at the DeepSeek-V3 shape); each position and head
+    adds the absorption (2 d_c d_n) and the output projection (2 d_c d_v).
+    Returns (attention part, total, pairs, attention part with the RoPE dot
+    counted once per branch, as a kernel that repeats it executes)."""
     pairs = sum(int(L) * (int(L) + 1) // 2 for L in lens)
-    attn = pairs * w.heads * 2 * (w.n * w.d_r + 2 * w.d_c)
+    attn = pairs * w.heads * 2 * (w.d_r + 2 * w.d_c)
+    attn_rep = pairs * w.heads * 2 * (w.n * w.d_r + 2 * w.d_c)
     rows = int(sum(int(L) for L in lens))
     proj = rows * w.heads * 2 * w.d_c * (w.d_n + w.d_v)
-    return attn, attn + proj, pairs
+    return attn, attn + proj, pairs, attn_rep
 
 
 def time_prefill(name, steps, warmup, torch, br, synth):
@@ -303,12 +311,15 @@ def time_prefill(name, steps, warmup, torch, br, synth):
     assert torch.isfinite(out.float()).all().item(), "non-finite prefill output"
     ms = g0.elapsed_time(g1) / steps
     k_ms = sum(x.elapsed_time(y) for x, y in kev) / steps
-    attn, total, pairs = prefill_flops(w, lens)
+    attn, total, pairs, attn_rep = prefill_flops(w, lens)
     tf = total / (k_ms / 1e3) / 1e12
     return {"workload": name, "batch": w.batch, "prompt_len": T, "heads": w.heads,
             "branches": w.n, "steps": steps, "ms_per_call": ms,
             "prompt_tokens_per_s": int(sum(int(L) for L in lens)) / (ms / 1e3),
             "kernel_ms": k_ms, "kernel_flops": total, "attention_flops": attn,
+            "flop_count": "RoPE score counted once per (query, key, head): 2 (d_r + 2 d_c) "
+                          "flop per pair and head",
+            "kernel_tflops_rope_per_branch": (total - attn + attn_rep) / (k_ms / 1e3) / 1e12,
             "attn_pairs": pairs,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
@@ -317,16 +328,30 @@ def time_prefill(name, steps, warmup, torch, br, synth):
 
 def cpu_baseline(w, seconds):
     """The float64 oracle (unabsorbed definition) on host cores, one sequence
-    at a time of the same workload recipe until `seconds` have elapsed."""
-    import numpy as np
+    at a time of the same workload recipe until `seconds` have elapsed. The
+    BLAS threads are set to the CPUs this process may run on (its affinity
+    mask), or to OMP_NUM_THREADS when that is set lower (the host's share
+    per GPU); `cores` is the count the oracle ran with."""
     import oracle
     import synth
+    affinity = len(os.sched_getaffinity(0))
+    cores = affinity
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and 0 < int(omp) < cores:
+        cores = int(omp)
     try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        cores = max((d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"), default=1)
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)
     except Exception:  # noqa: BLE001
-        cores = len(os.sched_getaffinity(0))
+        limiter = None
+    try:
+        return _cpu_baseline_run(w, seconds, oracle, synth, cores, affinity)
+    finally:
+        if limiter is not None:
+            limiter.restore_original_limits()
+
+
+def _cpu_baseline_run(w, seconds, oracle, synth, cores, affinity):
     done, spent = 0, 0.0
     L = None
     while spent < seconds and done < w.batch:
@@ -342,7 +367,54 @@ def cpu_baseline(w, seconds):
         log(f"[bench] oracle: {done} sequence(s) in {spent:.1f} s")
     return {"value": done / spent, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{done} of {w.batch} sequences (L={L}, all {w.heads} heads, {w.n} branch(es)), "
-                      f"float64 unabsorbed oracle, {spent:.1f} s"}
+                      f"float64 unabsorbed oracle, {spent:.1f} s, BLAS threads {cores} "
+                      f"(affinity mask {affinity} CPUs)"}
+
+
+def probe_read(torch, gib=4.0):
+    """Measured HBM read ceiling (include/mlra_probe.h): every byte of a
+    `gib` GiB buffer (16x the Infinity Cache) read once per launch, through
+    VGPR loads and through LDS-DMA, over a few launch shapes; the best
+    GB/s of each path. Each shape: one untimed launch, then 3 timed."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "branch_rank_amd", "libmlra_probe.so"))
+    lib.mlra_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mlra_probe_read.restype = ctypes.c_int
+    n = int(gib * 2**30)
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.fill_(3)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    # (mode, workgroups, waves, depth)
+    shapes = [(0, 1024, 4, 4), (0, 2048, 4, 4), (0, 4096, 4, 2), (0, 1024, 8, 8), (0, 512, 16, 4),
+              (1, 256, 8, 8), (1, 256, 8, 12), (1, 256, 16, 8), (1, 512, 8, 8), (1, 512, 4, 12),
+              (1, 1024, 4, 8)]
+    runs = []
+    for mode, wgs, waves, depth in shapes:
+        def go():
+            rc = lib.mlra_probe_read(buf.data_ptr(), n, mode, wgs, waves, depth, sink.data_ptr(),
+                                     stream)
+            if rc != 0:
+                raise RuntimeError(f"mlra_probe_read returned {rc}")
+        go()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            go()
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = 3 * n / (e0.elapsed_time(e1) / 1e3) / 1e9
+        runs.append({"path": "vgpr" if mode == 0 else "lds_dma", "workgroups": wgs,
+                     "waves": waves, "depth": depth, "gbs": round(gbs, 1)})
+        log(f"[bench] read probe {runs[-1]}")
+    del buf
+    best = {}
+    for r in runs:
+        if r["gbs"] > best.get(r["path"], {"gbs": 0})["gbs"]:
+            best[r["path"]] = r
+    return {"buffer_bytes": n, "best_gbs": max(r["gbs"] for r in runs), "vgpr": best["vgpr"],
+            "lds_dma": best["lds_dma"], "runs": runs}
 
 
 def probe_copy(torch):
@@ -372,6 +444,9 @@ def main():
     br.lib()  # fails loudly when the HIP library is missing
     if a.probe_copy:
         probe_copy(torch)
+        return
+    if a.probe_read:
+        print(json.dumps({"probe": "read", **probe_read(torch)}))
         return
     if a.prefill_only:
         print(json.dumps(time_prefill(a.prefill_workload, a.steps, a.warmup, torch, br, synth)))
@@ -414,6 +489,7 @@ def main():
             pair["step_time_ratio"] = m["ms_per_step"] / s_["ms_per_step"]
             pair["kernel_time_ratio"] = m["decode_kernel_us"] / s_["decode_kernel_us"]
             shards[tag] = pair
+    ceiling = None if a.no_probe_read else probe_read(torch)
     w = main_r["w"]
     ms = main_r["ms_step"]
     k_s = main_r["kernel_ms"] / 1e3
@@ -451,6 +527,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": kv_gbs_kernel, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": kv_gbs_kernel / HBM_PEAK_GBS,
                      "traffic": traffic_for(w.name, main_r["kernel"])},
+        "measured_read_ceiling": ceiling,
+        "roofline_frac_of_measured_ceiling":
+            kv_gbs_kernel / ceiling["best_gbs"] if ceiling else None,
         "cache_append_us": append_us,
         "also": extras,
         "shard_compare": shards,

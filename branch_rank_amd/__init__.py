@@ -10,7 +10,6 @@ missing, every call raises.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -43,7 +42,7 @@ class Config(ctypes.Structure):
                 ("sm_scale", ctypes.c_float), ("alpha_q", ctypes.c_float),
                 ("alpha_kv", ctypes.c_float), ("rope_theta", ctypes.c_float),
                 ("dtype", ctypes.c_int), ("kv_chunk", ctypes.c_int32),
-                ("decode_kernel", ctypes.c_int)]
+                ("decode_kernel", ctypes.c_int), ("q_residue", ctypes.c_int32)]
 
 
 class Cache(ctypes.Structure):
@@ -104,10 +103,19 @@ def check(st):
 # ------------------------------------------------------------ config ----
 
 def make_config(heads, d_latent, d_rope, d_nope, d_v, n=1, sm_scale=0.0, alpha_q=1.0,
-                alpha_kv=1.0, theta=10000.0, dtype="bf16", kv_chunk=0, kernel="auto"):
-    """kernel: "auto", "portable", "head_group" or "branch" (mlra_kernel_t)."""
+                alpha_kv=1.0, theta=10000.0, dtype="bf16", kv_chunk=0, kernel="auto",
+                q_residue=False):
+    """kernel: "auto", "portable", "head_group" or "branch" (mlra_kernel_t).
+    q_residue: the q_abs rows of mla_absorb_q / mla_decode_attn also carry
+    the bf16 residue of q~ (bf16 only)."""
     return Config(heads, d_latent, d_rope, d_nope, d_v, n, sm_scale, alpha_q, alpha_kv, theta,
-                  MLRA_BF16 if dtype == "bf16" else MLRA_FP32, kv_chunk, KERNELS[kernel])
+                  MLRA_BF16 if dtype == "bf16" else MLRA_FP32, kv_chunk, KERNELS[kernel],
+                  1 if q_residue else 0)
+
+
+def q_abs_width(cfg):
+    """Elements per q_abs row: d_latent + d_rope (+ d_latent with q_residue)."""
+    return cfg.d_latent + cfg.d_rope + (cfg.d_latent if cfg.q_residue else 0)
 
 
 def workspace_size(cfg, batch, max_len):
@@ -212,7 +220,7 @@ def mla_absorb_q(cfg, q_nope, q_rope, w_uk, q_abs, q_pos=None, cache_lens=None, 
             _need(q_pos, "q_pos", (B,), t.int32) if q_pos is not None else None,
             _need(cache_lens, "cache_lens", (B,), t.int32) if cache_lens is not None else None,
             _need(w_uk, "w_uk", (cfg.num_heads, cfg.d_latent, cfg.d_nope), dt),
-            _need(q_abs, "q_abs", (B, cfg.num_heads, cfg.d_latent + cfg.d_rope), dt))
+            _need(q_abs, "q_abs", (B, cfg.num_heads, q_abs_width(cfg)), dt))
     check(lib().mla_absorb_q(ctypes.byref(cfg), B, args[0], args[1], args[2], args[3], args[4],
                              args[5], _stream(stream)))
 
@@ -235,7 +243,7 @@ def alloc_workspace(cfg, batch, max_len, device="cuda"):
 def mla_decode_attn(cfg, q_abs, cache, workspace, latent_out, stream=None):
     t = _torch()
     B = cache._batch
-    qa = _need(q_abs, "q_abs", (B, cfg.num_heads, cfg.d_latent + cfg.d_rope), _dtype(cfg))
+    qa = _need(q_abs, "q_abs", (B, cfg.num_heads, q_abs_width(cfg)), _dtype(cfg))
     lo = _need(latent_out, "latent_out", (B, cfg.num_heads, cfg.d_latent), t.float32)
     wp, wn = _ws(workspace, cfg, B, cache.max_len)
     check(lib().mla_decode_attn(ctypes.byref(cfg), B, qa, ctypes.byref(cache), wp, wn, lo,
@@ -310,7 +318,3 @@ def set_kernel_timing(before=None, after=None):
             e.record()  # torch creates the underlying hipEvent on first record
     check(lib().mlra_set_kernel_timing(ctypes.c_void_p(before.cuda_event),
                                        ctypes.c_void_p(after.cuda_event)))
-
-
-def default_tau(d_nope, d_rope):
-    return 1.0 / math.sqrt(d_nope + d_rope)

@@ -14,6 +14,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmlra.so")
+# the benchmark's HBM read-ceiling probe (include/mlra_probe.h), a library of its own
+PROBE_SRC = "probe_read.hip"
+PROBE_LIB = os.path.join(PKG, "libmlra_probe.so")
 
 SOURCES = ["mlra_api.cpp", "kernels_generic.hip", "decode_mfma.hip", "decode_branch.hip",
            "proj_mfma.hip", "cache_append.hip", "prefill_branch.hip"]
@@ -41,26 +44,32 @@ def _compile(src):
     return src, obj, r.returncode, r.stdout + r.stderr, cmd
 
 
-def build(jobs=None, verbose=False):
-    os.makedirs(OBJ, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
-    objs = []
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        for src, obj, rc, out, cmd in ex.map(_compile, SOURCES):
-            if verbose or rc:
-                print(" ".join(cmd))
-                print(out)
-            if rc:
-                raise RuntimeError(f"hipcc failed on {src}")
-            objs.append(obj)
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode:
         print(" ".join(cmd))
         print(r.stdout + r.stderr)
-        raise RuntimeError("link failed")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link of {os.path.basename(lib)} failed")
+    os.replace(tmp, lib)
+
+
+def build(jobs=None, verbose=False):
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = SOURCES + [PROBE_SRC]
+    jobs = jobs or min(len(srcs), os.cpu_count() or 1)
+    objs = {}
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        for src, obj, rc, out, cmd in ex.map(_compile, srcs):
+            if verbose or rc:
+                print(" ".join(cmd))
+                print(out)
+            if rc:
+                raise RuntimeError(f"hipcc failed on {src}")
+            objs[src] = obj
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[PROBE_SRC]], PROBE_LIB)
     return LIB
 
 

@@ -59,7 +59,7 @@ namespace {
 using namespace dev;
 using namespace bt;
 
-template <int NBR, int NSPLIT, int HPW, int NHG, int NS>
+template <int NBR, int NSPLIT, int HPW, int NHG, int NS, bool QLO>
 __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_kernel(DecodeParams p) {
   using C = BCfg<NBR, NSPLIT, HPW, NHG>;
   constexpr int H = C::H;
@@ -139,14 +139,22 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
 
-    // Q^T as the B operand: lane (head, kg) holds 8 consecutive k of its head
+    // Q^T as the B operand: lane (head, kg) holds 8 consecutive k of its head;
+    // with QLO also q~'s bf16 residue over the branch's latent k-steps, whose
+    // products with the same K fragments go into the same scores
     bf16x8 q[C::KS][C::NBLK];
+    bf16x8 ql[QLO ? C::KL : 1][C::NBLK];
 #pragma unroll
     for (int nb = 0; nb < C::NBLK; ++nb) {
-      const __bf16* qrow = p.q_abs + ((int64_t)bseq * H + head0 + 16 * nb + l16) * (DC + kDR);
+      const __bf16* qrow = p.q_abs + ((int64_t)bseq * H + head0 + 16 * nb + l16) * p.q_stride;
 #pragma unroll
       for (int ks = 0; ks < C::KL; ++ks)
         q[ks][nb] = *(const bf16x8*)(qrow + kBW * j + 32 * ks + 8 * kg);
+      if constexpr (QLO) {
+#pragma unroll
+        for (int ks = 0; ks < C::KL; ++ks)
+          ql[ks][nb] = *(const bf16x8*)(qrow + p.q_lo + kBW * j + 32 * ks + 8 * kg);
+      }
 #pragma unroll
       for (int ks = C::KL; ks < C::KS; ++ks)
         q[ks][nb] = *(const bf16x8*)(qrow + DC + 32 * (ks - C::KL) + 8 * kg);
@@ -269,6 +277,12 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
             for (int ks = 1; ks < C::KS; ++ks)
               S[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][ks], q[ks][nb], S[mb][nb],
                                                                   0, 0, 0);
+            if constexpr (QLO) {
+#pragma unroll
+              for (int ks = 0; ks < C::KL; ++ks)
+                S[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][ks], ql[ks][nb],
+                                                                    S[mb][nb], 0, 0, 0);
+            }
           }
       }
     };
@@ -415,15 +429,17 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
   }
 }
 
-template <int NBR, int NSPLIT, int HPW, int NHG>
-hipError_t launch_b(const Geom& g, const void* q_abs, const void* ckv, const void* krope,
+template <int NBR, int NSPLIT, int HPW, int NHG, bool QLO>
+hipError_t launch_b(const Geom& g, const QView& q, const void* ckv, const void* krope,
                     const Workspace& ws, int items, hipStream_t s, const KernelTiming& t) {
   using C = BCfg<NBR, NSPLIT, HPW, NHG>;
   // a deep ring: up to 7 stages of 20 KB keep up to 6 tiles in flight per CU
   constexpr int NS = (160 * 1024) / C::STAGE < 7 ? (160 * 1024) / C::STAGE : 7;
   static_assert(NS >= 3, "tile ring does not fit LDS");
   DecodeParams p;
-  p.q_abs = (const __bf16*)q_abs;
+  p.q_abs = (const __bf16*)q.q;
+  p.q_stride = q.stride;
+  p.q_lo = QLO ? q.lo : 0;
   p.ckv = (const __bf16*)ckv;
   p.krope = (const __bf16*)krope;
   p.ckv_bs = g.ckv_bs;
@@ -438,7 +454,7 @@ hipError_t launch_b(const Geom& g, const void* q_abs, const void* ckv, const voi
   p.B = g.B;
   int grid = items;
   if (NSPLIT > 1) grid = ((items + 7) / 8) * 8 * NSPLIT;  // whole XCD rounds
-  hipExtLaunchKernelGGL((decode_branch_kernel<NBR, NSPLIT, HPW, NHG, NS>), dim3(grid),
+  hipExtLaunchKernelGGL((decode_branch_kernel<NBR, NSPLIT, HPW, NHG, NS, QLO>), dim3(grid),
                         dim3(64 * C::NW), 0, s, t.start, t.stop, 0, p);
   return hipGetLastError();
 }
@@ -457,13 +473,23 @@ bool decode_branch_supported(const Geom& g) {
 // Workgroups per work item; one workgroup per CU.
 int decode_branch_wgs_per_item(const Geom& g) { return g.n == 1 ? 1 : 2; }
 
-hipError_t launch_decode_branch(const Geom& g, const void* q_abs, const void* ckv,
+bool decode_branch_reads_residue(const Geom& g) { return g.n == 1; }
+
+hipError_t launch_decode_branch(const Geom& g, const QView& q, const void* ckv,
                                 const void* krope, const Workspace& ws, int items,
                                 hipStream_t s, const KernelTiming& t) {
   if (!decode_branch_supported(g)) return hipErrorNotSupported;
-  if (g.n == 1) return launch_b<1, 1, 16, 8>(g, q_abs, ckv, krope, ws, items, s, t);
-  if (g.H == 64) return launch_b<4, 2, 16, 4>(g, q_abs, ckv, krope, ws, items, s, t);
-  return launch_b<4, 2, 32, 4>(g, q_abs, ckv, krope, ws, items, s, t);
+  // one branch alone (a tensor-parallel shard) is one softmax over the
+  // branch: a bf16 query alone moves its output rows by up to ~1.1e-2 at the
+  // pages' scales, so the shard adds q~'s residue when the view has it. With
+  // four branches the summed output averages the branches' errors (<= 8.6e-3
+  // measured) and the residue's registers would cost the second wave per SIMD.
+  if (g.n == 1) {
+    if (q.lo > 0) return launch_b<1, 1, 16, 8, true>(g, q, ckv, krope, ws, items, s, t);
+    return launch_b<1, 1, 16, 8, false>(g, q, ckv, krope, ws, items, s, t);
+  }
+  if (g.H == 64) return launch_b<4, 2, 16, 4, false>(g, q, ckv, krope, ws, items, s, t);
+  return launch_b<4, 2, 32, 4, false>(g, q, ckv, krope, ws, items, s, t);
 }
 
 }  // namespace mlra

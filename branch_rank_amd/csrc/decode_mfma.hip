@@ -159,22 +159,25 @@ __device__ __forceinline__ void wait_tiles(int ahead, int wave) {
 // the branch softmax) and PG groups of PV MFMAs. Each group uses at most 8
 // A-fragments read from LDS; the fragments of group g+1 are read while group
 // g computes.
-template <int DC, int NB>
+template <int DC, int NB, int GF = 8>
 struct Sched {
   static constexpr int KS = DC / 32, KPB = KS / NB, MB = DC / 16, MPB = MB / NB;
-  static constexpr int QG = (KPB + 3) / 4;   // QK groups per branch
+  static constexpr int QG = (KPB + GF / 2 - 1) / (GF / 2);  // QK groups per branch
   static constexpr int QGK = KPB / QG;       // k-steps per QK group (2 M blocks each)
-  static constexpr int PG = (MPB + 7) / 8;   // PV groups per branch
+  static constexpr int PG = (MPB + GF - 1) / GF;  // PV groups per branch
   static constexpr int PGM = MPB / PG;       // output blocks per PV group
   static constexpr int GPB = QG + PG;
   static constexpr int NG = 1 + NB * GPB;
-  static_assert(QG * QGK == KPB && PG * PGM == MPB && 2 * QGK <= 8 && PGM <= 8, "schedule");
+  static_assert(QG * QGK == KPB && PG * PGM == MPB && 2 * QGK <= GF && PGM <= GF, "schedule");
 };
 
-template <int DC, int NB, int NW, int NS, int HSPLIT>
+template <int DC, int NB, int NW, int NS, int HSPLIT, bool QLO>
 __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(DecodeParams p) {
   using C = Cfg<DC, NB, NW>;
-  using SC = Sched<DC, NB>;
+  // groups of at most 4 fragments when the residue's registers are live at
+  // the widest latent, else 8
+  constexpr int GF = QLO && DC == 512 ? 4 : 8;
+  using SC = Sched<DC, NB, GF>;
   constexpr int H = C::HWG * HSPLIT;
   __shared__ __attribute__((aligned(1024))) char smem_raw[NS * C::STAGE];
   char LDS_AS* smem = (char LDS_AS*)smem_raw;
@@ -234,17 +237,25 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(DecodeParams p)
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
 
-    // Q^T as the B operand: lane (head, kg) holds q[head][32 ks + 8 kg .. +8]
+    // Q^T as the B operand: lane (head, kg) holds q[head][32 ks + 8 kg .. +8];
+    // with QLO also the bf16 residue of q~ (the latent k-steps), whose
+    // products with the same K fragments go into the same score accumulators
     bf16x8 q[C::KS + 2];
+    bf16x8 ql[QLO ? C::KS : 1];
     {
-      const __bf16* qrow = p.q_abs + ((int64_t)b * H + head) * (DC + kDR) + 8 * kg;
+      const __bf16* qrow = p.q_abs + ((int64_t)b * H + head) * p.q_stride + 8 * kg;
 #pragma unroll
       for (int ks = 0; ks < C::KS + 2; ++ks) q[ks] = *(const bf16x8*)(qrow + 32 * ks);
+      if constexpr (QLO) {
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) ql[ks] = *(const bf16x8*)(qrow + p.q_lo + 32 * ks);
+      }
     }
     // Q lives in AGPRs (MFMA reads its B operand from there), leaving the
     // VGPRs to the fragments and the softmax
 #pragma unroll
     for (int ks = 0; ks < C::KS + 2; ++ks) asm volatile("" : "+a"(q[ks]));
+
     // Q complete before any DMA is in flight: the compiler then needs no vmcnt
     // wait for Q inside the tile loop (such a wait would also drain the DMA)
     wait_vm<0>();
@@ -331,6 +342,9 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(DecodeParams p)
               const int ks = j * SC::KPB + r * SC::QGK + kk;
               S[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(F[mb * SC::QGK + kk], q[ks], S[mb],
                                                               0, 0, 0);
+              if constexpr (QLO)
+                S[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(F[mb * SC::QGK + kk], ql[ks],
+                                                                S[mb], 0, 0, 0);
             }
           }
           if (r == SC::QG - 1) {
@@ -379,7 +393,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(DecodeParams p)
         }
       };
 
-      bf16x8 F[2][8];
+      bf16x8 F[2][GF];
       load(0, F[0]);
 #pragma unroll
       for (int gid = 0; gid < SC::NG; ++gid) {
@@ -442,8 +456,8 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(DecodeParams p)
 // the 160 KB of LDS.
 constexpr int wgs_per_cu(int dc, int nw) { return (dc == 128 ? 8 : 4) / nw; }
 
-template <int DC, int NB, int NW, int HSPLIT>
-hipError_t launch_t(const Geom& g, const void* q_abs, const void* ckv, const void* krope,
+template <int DC, int NB, int NW, int HSPLIT, bool QLO>
+hipError_t launch_t(const Geom& g, const QView& q, const void* ckv, const void* krope,
                     const Workspace& ws, int items, hipStream_t s,
                     const KernelTiming& t) {
   using C = Cfg<DC, NB, NW>;
@@ -454,7 +468,9 @@ hipError_t launch_t(const Geom& g, const void* q_abs, const void* ckv, const voi
   constexpr int NS = NS_LDS < NS_VM ? NS_LDS : NS_VM;
   static_assert(NS >= 2, "tile does not fit LDS");
   DecodeParams p;
-  p.q_abs = (const __bf16*)q_abs;
+  p.q_abs = (const __bf16*)q.q;
+  p.q_stride = q.stride;
+  p.q_lo = q.lo;
   p.ckv = (const __bf16*)ckv;
   p.krope = (const __bf16*)krope;
   p.ckv_bs = g.ckv_bs;
@@ -469,26 +485,40 @@ hipError_t launch_t(const Geom& g, const void* q_abs, const void* ckv, const voi
   p.B = g.B;
   int grid = items;
   if (HSPLIT > 1) grid = ((items + 7) / 8) * 8 * HSPLIT;  // whole XCD rounds
-  hipExtLaunchKernelGGL((decode_mfma_kernel<DC, NB, NW, NS, HSPLIT>), dim3(grid), dim3(64 * NW),
-                        0, s, t.start, t.stop, 0, p);
+  hipExtLaunchKernelGGL((decode_mfma_kernel<DC, NB, NW, NS, HSPLIT, QLO>), dim3(grid),
+                        dim3(64 * NW), 0, s, t.start, t.stop, 0, p);
   return hipGetLastError();
 }
 
 // heads -> (waves per workgroup, head groups per item)
-template <int DC, int NB>
-hipError_t launch_h(const Geom& g, const void* q, const void* c, const void* k,
-                    const Workspace& ws, int items, hipStream_t s,
-                    const KernelTiming& t) {
+template <int DC, int NB, bool QLO>
+hipError_t launch_hq(const Geom& g, const QView& q, const void* c, const void* k,
+                     const Workspace& ws, int items, hipStream_t s,
+                     const KernelTiming& t) {
   switch (g.H) {
-    case 32: return launch_t<DC, NB, 2, 1>(g, q, c, k, ws, items, s, t);
-    case 64: return launch_t<DC, NB, 4, 1>(g, q, c, k, ws, items, s, t);
-    case 128: return launch_t<DC, NB, 4, 2>(g, q, c, k, ws, items, s, t);
+    case 32: return launch_t<DC, NB, 2, 1, QLO>(g, q, c, k, ws, items, s, t);
+    case 64: return launch_t<DC, NB, 4, 1, QLO>(g, q, c, k, ws, items, s, t);
+    case 128: return launch_t<DC, NB, 4, 2, QLO>(g, q, c, k, ws, items, s, t);
   }
   return hipErrorNotSupported;
 }
 
+// With or without q~'s residue (mlra_decode gives it; a caller's q_abs in
+// mla_decode_attn has it only with q_residue). A query rounded to one bf16
+// moves every score by about 2^-9 of its spread; with one softmax over the
+// whole latent (MLA at the pages' scales) that alone moves output rows by up
+// to ~1.3e-2, and narrower latents at the pages' alpha spread their scores
+// wider still.
+template <int DC, int NB>
+hipError_t launch_h(const Geom& g, const QView& q, const void* c, const void* k,
+                    const Workspace& ws, int items, hipStream_t s,
+                    const KernelTiming& t) {
+  if (q.lo > 0) return launch_hq<DC, NB, true>(g, q, c, k, ws, items, s, t);
+  return launch_hq<DC, NB, false>(g, q, c, k, ws, items, s, t);
+}
+
 template <int DC>
-hipError_t launch_nb(const Geom& g, const void* q, const void* c, const void* k,
+hipError_t launch_nb(const Geom& g, const QView& q, const void* c, const void* k,
                      const Workspace& ws, int items, hipStream_t s,
                      const KernelTiming& t) {
   switch (g.n) {
@@ -500,6 +530,8 @@ hipError_t launch_nb(const Geom& g, const void* q, const void* c, const void* k,
 }
 
 }  // namespace
+
+bool decode_mfma_reads_residue(const Geom&) { return true; }
 
 bool decode_mfma_supported(const Geom& g) {
   if (g.dr != kDR) return false;
@@ -517,13 +549,13 @@ int decode_mfma_target_items(const Geom& g, int cus) {
   return cus * wgs_per_cu(g.dc, nw) / hsplit;
 }
 
-hipError_t launch_decode_mfma(const Geom& g, const void* q_abs, const void* ckv,
+hipError_t launch_decode_mfma(const Geom& g, const QView& q, const void* ckv,
                               const void* krope, const Workspace& ws, int items,
                               hipStream_t s, const KernelTiming& t) {
   switch (g.dc) {
-    case 128: return launch_nb<128>(g, q_abs, ckv, krope, ws, items, s, t);
-    case 256: return launch_nb<256>(g, q_abs, ckv, krope, ws, items, s, t);
-    case 512: return launch_nb<512>(g, q_abs, ckv, krope, ws, items, s, t);
+    case 128: return launch_nb<128>(g, q, ckv, krope, ws, items, s, t);
+    case 256: return launch_nb<256>(g, q, ckv, krope, ws, items, s, t);
+    case 512: return launch_nb<512>(g, q, ckv, krope, ws, items, s, t);
   }
   return hipErrorNotSupported;
 }

@@ -23,7 +23,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // Arguments of the split-KV decode kernels (one struct, passed by value).
 struct DecodeParams {
-  const __bf16* q_abs;
+  const __bf16* q_abs;  // row (b, h) at q_abs + (b * H + h) * q_stride: q~ (d_c), rho (d_r)
+  int q_stride;         // elements per query row
+  int q_lo;             // > 0: the row's bf16 residue of q~ starts at this element
   const __bf16* ckv;
   const __bf16* krope;
   int64_t ckv_bs, kr_bs;

@@ -53,7 +53,7 @@ struct Workspace {
   float* m;         // [slots][n][H]
   float* l;         // [slots][n][H]
   float* acc;       // [slots][d_c][H]
-  void* q_abs;      // [B][H][d_c + d_r] (mlra_decode only)
+  void* q_abs;      // [B][H][d_c + d_r (+ d_c, bf16: q~'s residue)] (mlra_decode only)
   float* latent;    // [B][H][d_c]       (mlra_decode only)
 };
 
@@ -61,6 +61,17 @@ struct Workspace {
 // (hipExtLaunchKernel), so that timing adds no packets to the stream.
 struct KernelTiming {
   hipEvent_t start = nullptr, stop = nullptr;
+};
+
+// Absorbed queries as the decode kernels read them: row (b, h) starts at
+// element (b * H + h) * stride of q and holds q~ (d_c) then rho (d_r). With
+// lo > 0 (bf16 only), elements [lo, lo + d_c) of the row hold q~'s rounding
+// residue bf16(q~ - bf16(q~)), so that the two bf16 parts carry q~ to about
+// 16 significant bits; lo = 0 means the query is the bf16 q~ alone.
+struct QView {
+  const void* q;
+  int stride;
+  int lo;
 };
 
 struct Geom {
@@ -95,14 +106,16 @@ constexpr int kMaxAutoItems = 512; // upper bound on automatic work items
 hipError_t launch_plan(const int32_t* lens, int B, int max_len, int target_items,
                        int forced_chunk, const Workspace& ws, hipStream_t s);
 
+// Query absorption into rows of q_stride elements; lo_off > 0 (bf16 only)
+// also writes q~'s rounding residue at that element of each row (QView).
 template <typename T>
 hipError_t launch_absorb_q_generic(const Geom& g, const T* q_nope, const T* q_rope,
                                    const int32_t* q_pos, const int32_t* lens, const T* w_uk,
-                                   T* q_abs, float tau, float alpha_q, float theta,
-                                   hipStream_t s);
+                                   T* q_abs, int q_stride, int lo_off, float tau, float alpha_q,
+                                   float theta, hipStream_t s);
 
 template <typename T>
-hipError_t launch_decode_generic(const Geom& g, const T* q_abs, const T* ckv, const T* krope,
+hipError_t launch_decode_generic(const Geom& g, const QView& q, const T* ckv, const T* krope,
                                  const Workspace& ws, int grid_items, hipStream_t s,
                                  const KernelTiming& t);
 
@@ -116,13 +129,15 @@ hipError_t launch_out_proj_generic(const Geom& g, const float* latent, const T* 
 // specialisation (the caller then uses the generic kernel).
 bool decode_branch_supported(const Geom& g);
 int decode_branch_wgs_per_item(const Geom& g);
-hipError_t launch_decode_branch(const Geom& g, const void* q_abs, const void* ckv,
+bool decode_branch_reads_residue(const Geom& g);  // adds q~'s residue when the view has one
+hipError_t launch_decode_branch(const Geom& g, const QView& q, const void* ckv,
                                 const void* krope, const Workspace& ws, int grid_items,
                                 hipStream_t s, const KernelTiming& t);
 
 bool decode_mfma_supported(const Geom& g);
+bool decode_mfma_reads_residue(const Geom& g);  // adds q~'s residue when the view has one
 int decode_mfma_target_items(const Geom& g, int cus);
-hipError_t launch_decode_mfma(const Geom& g, const void* q_abs, const void* ckv,
+hipError_t launch_decode_mfma(const Geom& g, const QView& q, const void* ckv,
                               const void* krope, const Workspace& ws, int grid_items,
                               hipStream_t s, const KernelTiming& t);
 
@@ -134,8 +149,8 @@ bool absorb_mfma_supported(const Geom& g);
 // split-KV plan (as launch_plan would).
 hipError_t launch_absorb_q_mfma(const Geom& g, const __bf16* q_nope, const __bf16* q_rope,
                                 const int32_t* q_pos, const int32_t* lens, const __bf16* w_uk,
-                                __bf16* q_abs, float tau, float alpha_q, float theta,
-                                const PlanArgs& plan, hipStream_t s);
+                                __bf16* q_abs, int q_stride, int lo_off, float tau, float alpha_q,
+                                float theta, const PlanArgs& plan, hipStream_t s);
 hipError_t launch_combine_hc(const Geom& g, const Workspace& ws, float* latent_out,
                              hipStream_t s);
 template <typename TO>

@@ -74,12 +74,12 @@ __global__ __launch_bounds__(256) void absorb_q_generic(Geom g, const T* __restr
                                                         const int32_t* __restrict__ q_pos,
                                                         const int32_t* __restrict__ lens,
                                                         const T* __restrict__ w_uk,
-                                                        T* __restrict__ q_abs, float tau,
-                                                        float alpha_q, RopeFreqs fr) {
+                                                        T* __restrict__ q_abs, int row,
+                                                        int lo_off, float tau, float alpha_q,
+                                                        RopeFreqs fr) {
   extern __shared__ float sq[];  // [kQB][dn]
   const int h = blockIdx.x, b0 = blockIdx.y * kQB;
   const int nb = min(kQB, g.B - b0);
-  const int row = g.dc + g.dr;
   for (int i = threadIdx.x; i < nb * g.dn; i += blockDim.x) {
     const int bb = i / g.dn, e = i % g.dn;
     sq[bb * g.dn + e] = to_f32(q_nope[((size_t)(b0 + bb) * g.H + h) * g.dn + e]);
@@ -97,8 +97,14 @@ __global__ __launch_bounds__(256) void absorb_q_generic(Geom g, const T* __restr
       for (int bb = 0; bb < kQB; ++bb)
         if (bb < nb) acc[bb] += wv * sq[bb * g.dn + e];
     }
-    for (int bb = 0; bb < nb; ++bb)
-      q_abs[((size_t)(b0 + bb) * g.H + h) * row + c] = from_f32<T>(s * acc[bb]);
+    for (int bb = 0; bb < nb; ++bb) {
+      // q~ in the storage type and, when asked for, its rounding residue
+      const float v = s * acc[bb];
+      const T hi = from_f32<T>(v);
+      T* qr = q_abs + ((size_t)(b0 + bb) * g.H + h) * row;
+      qr[c] = hi;
+      if (lo_off > 0) qr[lo_off + c] = from_f32<T>(v - to_f32(hi));
+    }
   }
   // RoPE on the query's rotary part, angle in double precision (frequency
   // from the host's table).
@@ -134,6 +140,7 @@ __device__ __forceinline__ int find_seq(const int32_t* prefix, int B, int pos) {
 
 template <typename T>
 __global__ __launch_bounds__(256) void decode_generic(Geom g, const T* __restrict__ q_abs,
+                                                      int q_stride, int q_lo,
                                                       const T* __restrict__ ckv,
                                                       const T* __restrict__ krope,
                                                       Workspace ws) {
@@ -153,8 +160,10 @@ __global__ __launch_bounds__(256) void decode_generic(Geom g, const T* __restric
     while (ws.prefix[b + 1] <= start) ++b;  // skip empty sequences
     const int seg_end = min(end, ws.prefix[b + 1]);
     const int t0 = start - ws.prefix[b], t1 = seg_end - ws.prefix[b];
+    // the query in fp32: q~ (plus its bf16 residue when given) and rho
+    const T* qr = q_abs + ((size_t)b * g.H + h) * q_stride;
     for (int i = tid; i < row; i += blockDim.x)
-      q[i] = to_f32(q_abs[((size_t)b * g.H + h) * row + i]);
+      q[i] = to_f32(qr[i]) + (q_lo > 0 && i < g.dc ? to_f32(qr[q_lo + i]) : 0.f);
     __syncthreads();
     float m[kMaxBranches], l[kMaxBranches], acc[kMaxColsPerThr];
     for (int j = 0; j < kMaxBranches; ++j) { m[j] = -INFINITY; l[j] = 0.f; }
@@ -358,22 +367,23 @@ hipError_t launch_plan(const int32_t* lens, int B, int max_len, int target_items
 template <typename T>
 hipError_t launch_absorb_q_generic(const Geom& g, const T* q_nope, const T* q_rope,
                                    const int32_t* q_pos, const int32_t* lens, const T* w_uk,
-                                   T* q_abs, float tau, float alpha_q, float theta,
-                                   hipStream_t s) {
+                                   T* q_abs, int q_stride, int lo_off, float tau,
+                                   float alpha_q, float theta, hipStream_t s) {
   const size_t sh = sizeof(float) * kQB * g.dn;
   hipLaunchKernelGGL(absorb_q_generic<T>, dim3(g.H, (g.B + kQB - 1) / kQB), dim3(256), sh, s, g,
-                     q_nope, q_rope, q_pos, lens, w_uk, q_abs, tau, alpha_q,
+                     q_nope, q_rope, q_pos, lens, w_uk, q_abs, q_stride, lo_off, tau, alpha_q,
                      rope_freqs(theta, g.dr));
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_decode_generic(const Geom& g, const T* q_abs, const T* ckv, const T* krope,
+hipError_t launch_decode_generic(const Geom& g, const QView& q, const T* ckv, const T* krope,
                                  const Workspace& ws, int grid_items, hipStream_t s,
                                  const KernelTiming& t) {
   const size_t sh = sizeof(float) * (g.dc + g.dr + g.n * kTok);
   hipExtLaunchKernelGGL(decode_generic<T>, dim3(grid_items, g.H), dim3(256), sh, s, t.start,
-                        t.stop, 0, g, q_abs, ckv, krope, ws);
+                        t.stop, 0, g, static_cast<const T*>(q.q), q.stride, q.lo, ckv, krope,
+                        ws);
   return hipGetLastError();
 }
 
@@ -401,15 +411,16 @@ hipError_t launch_out_proj_generic(const Geom& g, const float* latent, const T* 
 
 template hipError_t launch_absorb_q_generic<float>(const Geom&, const float*, const float*,
                                                    const int32_t*, const int32_t*, const float*,
-                                                   float*, float, float, float, hipStream_t);
+                                                   float*, int, int, float, float, float,
+                                                   hipStream_t);
 template hipError_t launch_absorb_q_generic<__bf16>(const Geom&, const __bf16*, const __bf16*,
                                                     const int32_t*, const int32_t*,
-                                                    const __bf16*, __bf16*, float, float, float,
-                                                    hipStream_t);
-template hipError_t launch_decode_generic<float>(const Geom&, const float*, const float*,
+                                                    const __bf16*, __bf16*, int, int, float, float,
+                                                    float, hipStream_t);
+template hipError_t launch_decode_generic<float>(const Geom&, const QView&, const float*,
                                                  const float*, const Workspace&, int,
                                                  hipStream_t, const KernelTiming&);
-template hipError_t launch_decode_generic<__bf16>(const Geom&, const __bf16*, const __bf16*,
+template hipError_t launch_decode_generic<__bf16>(const Geom&, const QView&, const __bf16*,
                                                   const __bf16*, const Workspace&, int,
                                                   hipStream_t, const KernelTiming&);
 template hipError_t launch_out_proj_generic<float, float>(const Geom&, const float*,

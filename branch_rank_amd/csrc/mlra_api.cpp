@@ -78,6 +78,10 @@ mlra_status_t check_cfg(const mlra_config_t* c) {
   if (c->kv_chunk < 0) return fail(MLRA_ERR_INVALID_ARG, "kv_chunk must be >= 0");
   if (c->decode_kernel < MLRA_KERNEL_AUTO || c->decode_kernel > MLRA_KERNEL_BRANCH)
     return fail(MLRA_ERR_INVALID_ARG, "unknown decode_kernel %d", (int)c->decode_kernel);
+  if (c->q_residue != 0 && c->q_residue != 1)
+    return fail(MLRA_ERR_INVALID_ARG, "q_residue must be 0 or 1");
+  if (c->q_residue && c->dtype != MLRA_BF16)
+    return fail(MLRA_ERR_INVALID_ARG, "q_residue needs the bf16 dtype");
   if (c->d_latent > kMaxLatent || c->d_rope > kMaxRope || c->d_nope > kMaxNope ||
       c->num_branches > kMaxBranches || c->num_heads * c->num_branches > kMaxHeadBranch ||
       c->d_v > 4096)
@@ -108,6 +112,36 @@ int64_t items_max(const mlra_config_t* c, int32_t batch, int32_t max_len) {
   return by_min < kMaxAutoItems ? by_min : kMaxAutoItems;
 }
 
+// Elements per absorbed-query row in the workspace: q~ and rho, plus (bf16)
+// the bf16 residue of q~ after them (QView), which the head-group and
+// portable decodes add to their scores.
+size_t q_row(const mlra_config_t* c) {
+  return (size_t)c->d_latent + c->d_rope + (c->dtype == MLRA_BF16 ? c->d_latent : 0);
+}
+
+// The workspace's query rows for the decode kernel `kern`: the residue is
+// written and read only where that kernel adds it to its scores.
+// The caller's q_abs rows (mla_absorb_q, mla_decode_attn).
+QView user_qview(const mlra_config_t* c, const void* q) {
+  QView v;
+  v.q = q;
+  v.stride = c->d_latent + c->d_rope + (c->q_residue ? c->d_latent : 0);
+  v.lo = c->q_residue ? c->d_latent + c->d_rope : 0;
+  return v;
+}
+
+QView ws_qview(const mlra_config_t* c, const Geom& g, mlra_kernel_t kern, const void* q) {
+  const bool lo = c->dtype == MLRA_BF16 &&
+                  (kern == MLRA_KERNEL_PORTABLE ||
+                   (kern == MLRA_KERNEL_HEAD_GROUP && decode_mfma_reads_residue(g)) ||
+                   (kern == MLRA_KERNEL_BRANCH && decode_branch_reads_residue(g)));
+  QView v;
+  v.q = q;
+  v.stride = (int)q_row(c);
+  v.lo = lo ? c->d_latent + c->d_rope : 0;
+  return v;
+}
+
 struct Layout {
   size_t hdr, prefix, m, l, acc, q_abs, latent, total;
   int64_t slots;
@@ -123,7 +157,7 @@ Layout layout(const mlra_config_t* c, int32_t batch, int32_t max_len) {
   L.m = off;      off = round_up(off + 4 * (size_t)L.slots * n * H, 256);
   L.l = off;      off = round_up(off + 4 * (size_t)L.slots * n * H, 256);
   L.acc = off;    off = round_up(off + 4 * (size_t)L.slots * dc * H, 256);
-  L.q_abs = off;  off = round_up(off + elt_size(c->dtype) * (size_t)batch * H * (dc + dr), 256);
+  L.q_abs = off;  off = round_up(off + elt_size(c->dtype) * (size_t)batch * H * q_row(c), 256);
   L.latent = off; off = round_up(off + 4 * (size_t)batch * H * dc, 256);
   L.total = off;
   return L;
@@ -203,6 +237,11 @@ mlra_status_t check_cache(const mlra_config_t* c, const mlra_cache_t* k, int32_t
   if (k->ckv_token_stride < 1 || k->ckv_batch_stride < 0 ||
       (c->d_rope > 0 && (k->krope_token_stride < 1 || k->krope_batch_stride < 0)))
     return fail(MLRA_ERR_INVALID_ARG, "cache strides: token stride >= 1, batch stride >= 0");
+  // a row must fit its token stride: the MFMA kernels bound each sequence's
+  // rows by max_len * token stride bytes, the portable kernel reads whole rows
+  if (k->ckv_token_stride < c->d_latent || (c->d_rope > 0 && k->krope_token_stride < c->d_rope))
+    return fail(MLRA_ERR_INVALID_ARG, "cache token strides must be >= the row widths (%d, %d)",
+                c->d_latent, c->d_rope);
   if ((k->ckv_token_stride * e) % 16 || (k->ckv_batch_stride * e) % 16 ||
       (c->d_rope > 0 && ((k->krope_token_stride * e) % 16 || (k->krope_batch_stride * e) % 16)))
     return fail(MLRA_ERR_INVALID_ARG, "cache strides must be multiples of 16 bytes");
@@ -231,26 +270,28 @@ mlra_status_t check_ptr(const void* p, const char* name) {
 
 // Query absorption. When `plan` is given and the MFMA kernel runs, the split-KV
 // plan rides along in that launch and *plan_done is set.
+// Query absorption into rows described by `q` (stride, residue offset).
 mlra_status_t run_absorb(const mlra_config_t* c, const Geom& g, const void* q_nope,
                          const void* q_rope, const int32_t* q_pos, const int32_t* lens,
-                         const void* w_uk, void* q_abs, hipStream_t s,
+                         const void* w_uk, const QView& q, hipStream_t s,
                          const PlanArgs* plan = nullptr, bool* plan_done = nullptr) {
   const float tau = tau_of(c);
+  void* q_abs = const_cast<void*>(q.q);
   hipError_t e;
   if (c->dtype == MLRA_BF16 && absorb_mfma_supported(g)) {
     PlanArgs none{};
     e = launch_absorb_q_mfma(g, (const __bf16*)q_nope, (const __bf16*)q_rope, q_pos, lens,
-                             (const __bf16*)w_uk, (__bf16*)q_abs, tau, c->alpha_q, c->rope_theta,
-                             plan ? *plan : none, s);
+                             (const __bf16*)w_uk, (__bf16*)q_abs, q.stride, q.lo, tau, c->alpha_q,
+                             c->rope_theta, plan ? *plan : none, s);
     if (plan && plan_done) *plan_done = true;
   } else if (c->dtype == MLRA_BF16)
     e = launch_absorb_q_generic<__bf16>(g, (const __bf16*)q_nope, (const __bf16*)q_rope, q_pos,
-                                        lens, (const __bf16*)w_uk, (__bf16*)q_abs, tau,
-                                        c->alpha_q, c->rope_theta, s);
+                                        lens, (const __bf16*)w_uk, (__bf16*)q_abs, q.stride, q.lo,
+                                        tau, c->alpha_q, c->rope_theta, s);
   else
     e = launch_absorb_q_generic<float>(g, (const float*)q_nope, (const float*)q_rope, q_pos, lens,
-                                       (const float*)w_uk, (float*)q_abs, tau, c->alpha_q,
-                                       c->rope_theta, s);
+                                       (const float*)w_uk, (float*)q_abs, q.stride, 0, tau,
+                                       c->alpha_q, c->rope_theta, s);
   TRY_HIP(e, "absorb_q launch");
   return MLRA_OK;
 }
@@ -303,7 +344,7 @@ mlra_status_t plan_for(const mlra_config_t* c, const Geom& g, int cus, const mlr
 // unless plan_done). *fast tells which kind of decode ran: an MFMA kernel
 // (partial acc as [slot][H][d_c]) or the portable one ([slot][d_c][H]); the
 // merge must match.
-mlra_status_t run_decode(const mlra_config_t* c, const Geom& g, const void* q_abs,
+mlra_status_t run_decode(const mlra_config_t* c, const Geom& g, const QView& q,
                          const mlra_cache_t* k, const Workspace& ws, const Layout& L,
                          mlra_kernel_t kern, const PlanArgs& plan, bool plan_done, bool* fast_out,
                          hipStream_t s) {
@@ -318,15 +359,15 @@ mlra_status_t run_decode(const mlra_config_t* c, const Geom& g, const void* q_ab
     t.stop = g_ev_after;
     hipError_t e;
     if (kern == MLRA_KERNEL_BRANCH)
-      e = launch_decode_branch(g, q_abs, k->ckv, k->krope, ws, (int)imax, s, t);
+      e = launch_decode_branch(g, q, k->ckv, k->krope, ws, (int)imax, s, t);
     else if (kern == MLRA_KERNEL_HEAD_GROUP)
-      e = launch_decode_mfma(g, q_abs, k->ckv, k->krope, ws, (int)imax, s, t);
+      e = launch_decode_mfma(g, q, k->ckv, k->krope, ws, (int)imax, s, t);
     else if (c->dtype == MLRA_BF16)
-      e = launch_decode_generic<__bf16>(g, (const __bf16*)q_abs, (const __bf16*)k->ckv,
-                                        (const __bf16*)k->krope, ws, (int)imax, s, t);
+      e = launch_decode_generic<__bf16>(g, q, (const __bf16*)k->ckv, (const __bf16*)k->krope, ws,
+                                        (int)imax, s, t);
     else
-      e = launch_decode_generic<float>(g, (const float*)q_abs, (const float*)k->ckv,
-                                       (const float*)k->krope, ws, (int)imax, s, t);
+      e = launch_decode_generic<float>(g, q, (const float*)k->ckv, (const float*)k->krope, ws,
+                                       (int)imax, s, t);
     TRY_HIP(e, "decode launch");
   }
   *fast_out = kern != MLRA_KERNEL_PORTABLE;
@@ -419,7 +460,8 @@ mlra_status_t mla_absorb_q(const mlra_config_t* cfg, int32_t batch, const void* 
   TRY(current_device(&dev, &cus));
   Geom g = make_geom(cfg, batch, nullptr);
   g.max_len = 0x7fffffff;  // cache_lens - 1 is used as given (clamped below by 0)
-  return run_absorb(cfg, g, q_nope, q_rope, q_pos, cache_lens, w_uk, q_abs,
+  const QView qv = user_qview(cfg, q_abs);
+  return run_absorb(cfg, g, q_nope, q_rope, q_pos, cache_lens, w_uk, qv,
                     static_cast<hipStream_t>(stream));
 }
 
@@ -446,7 +488,8 @@ mlra_status_t mla_decode_attn(const mlra_config_t* cfg, int32_t batch, const voi
   PlanArgs plan;
   TRY(plan_for(cfg, g, cus, cache, ws, L, &kern, &plan));
   bool fast = false;
-  TRY(run_decode(cfg, g, q_abs, cache, ws, L, kern, plan, false, &fast, s));
+  const QView qv = user_qview(cfg, q_abs);
+  TRY(run_decode(cfg, g, qv, cache, ws, L, kern, plan, false, &fast, s));
   return run_merge(g, ws, fast, latent_out, s);
 }
 
@@ -588,10 +631,11 @@ mlra_status_t mlra_decode(const mlra_config_t* cfg_in, int32_t num_branches, int
   PlanArgs plan;
   TRY(plan_for(&cfg, g, cus, cache, ws, L, &kern, &plan));
   bool plan_done = false;
-  TRY(run_absorb(&cfg, g, q_nope, q_rope, q_pos, cache->cache_lens, w_uk, ws.q_abs, s, &plan,
+  const QView qv = ws_qview(&cfg, g, kern, ws.q_abs);
+  TRY(run_absorb(&cfg, g, q_nope, q_rope, q_pos, cache->cache_lens, w_uk, qv, s, &plan,
                  &plan_done));
   bool fast = false;
-  TRY(run_decode(&cfg, g, ws.q_abs, cache, ws, L, kern, plan, plan_done, &fast, s));
+  TRY(run_decode(&cfg, g, qv, cache, ws, L, kern, plan, plan_done, &fast, s));
   if (fast && cfg.dtype == MLRA_BF16 && proj_mfma_supported(g)) {
     // merge and out projection in one kernel: the latent stays on chip
     const __bf16* wv = static_cast<const __bf16*>(w_uv);

@@ -58,8 +58,9 @@ __global__ __launch_bounds__(256) void absorb_q_mfma(Geom g, const __bf16* __res
                                                      const int32_t* __restrict__ q_pos,
                                                      const int32_t* __restrict__ lens,
                                                      const __bf16* __restrict__ w_uk,
-                                                     __bf16* __restrict__ q_abs, float scale,
-                                                     float tau, RopeFreqs fr, PlanArgs plan) {
+                                                     __bf16* __restrict__ q_abs, int row,
+                                                     int lo_off, float scale, float tau,
+                                                     RopeFreqs fr, PlanArgs plan) {
   if (blockIdx.x == g.H) {  // the extra column of workgroups: plan (first one only)
     if (blockIdx.y == 0 && blockIdx.z == 0) plan_block(plan);
     return;
@@ -67,7 +68,6 @@ __global__ __launch_bounds__(256) void absorb_q_mfma(Geom g, const __bf16* __res
   const int h = blockIdx.x, b0 = blockIdx.y * 16 * MBLK, part = blockIdx.z, parts = gridDim.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, kg = lane >> 4;
-  const int row = g.dc + g.dr;
   const int dn = KSN * 32;
   // Every load below is unconditional (indices clamped into range, values
   // masked afterwards), so that none waits for another: the RoPE inputs of
@@ -126,7 +126,14 @@ __global__ __launch_bounds__(256) void absorb_q_mfma(Geom g, const __bf16* __res
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int b = b0 + 16 * m + 4 * kg + i;
-        if (b < g.B) q_abs[((size_t)b * g.H + h) * row + c] = (__bf16)(scale * acc[i]);
+        if (b < g.B) {
+          // q~ as bf16 and, when asked for, its rounding residue (QView)
+          const float v = scale * acc[i];
+          const __bf16 hi = (__bf16)v;
+          __bf16* qr = q_abs + ((size_t)b * g.H + h) * row;
+          qr[c] = hi;
+          if (lo_off > 0) qr[lo_off + c] = (__bf16)(v - (float)hi);
+        }
       }
     }
   }
@@ -623,8 +630,9 @@ hipError_t launch_out_t(const Geom& g, const float* lat, const __bf16* w_uv, TO*
 
 template <int KSN>
 hipError_t launch_absorb_k(const Geom& g, const __bf16* qn, const __bf16* qr, const int32_t* qp,
-                           const int32_t* lens, const __bf16* w, __bf16* qa, float scale,
-                           float tau, float theta, const PlanArgs& plan, hipStream_t s) {
+                           const int32_t* lens, const __bf16* w, __bf16* qa, int qs, int lo,
+                           float scale, float tau, float theta, const PlanArgs& plan,
+                           hipStream_t s) {
   const int gx = g.H + (plan.hdr ? 1 : 0);
   const RopeFreqs& fr = rope_freqs(theta, g.dr);
   // latent column parts per head: the most (<= 8) that split the 16-column
@@ -639,10 +647,10 @@ hipError_t launch_absorb_k(const Geom& g, const __bf16* qn, const __bf16* qr, co
     }
   if (g.B > 32) {
     hipLaunchKernelGGL((absorb_q_mfma<KSN, 4>), dim3(gx, (g.B + 63) / 64, parts), dim3(256), 0,
-                       s, g, qn, qr, qp, lens, w, qa, scale, tau, fr, plan);
+                       s, g, qn, qr, qp, lens, w, qa, qs, lo, scale, tau, fr, plan);
   } else {
     hipLaunchKernelGGL((absorb_q_mfma<KSN, 1>), dim3(gx, (g.B + 15) / 16, parts), dim3(256), 0,
-                       s, g, qn, qr, qp, lens, w, qa, scale, tau, fr, plan);
+                       s, g, qn, qr, qp, lens, w, qa, qs, lo, scale, tau, fr, plan);
   }
   return hipGetLastError();
 }
@@ -660,13 +668,19 @@ bool absorb_mfma_supported(const Geom& g) {
 
 hipError_t launch_absorb_q_mfma(const Geom& g, const __bf16* q_nope, const __bf16* q_rope,
                                 const int32_t* q_pos, const int32_t* lens, const __bf16* w_uk,
-                                __bf16* q_abs, float tau, float alpha_q, float theta,
-                                const PlanArgs& plan, hipStream_t s) {
+                                __bf16* q_abs, int q_stride, int lo_off, float tau,
+                                float alpha_q, float theta, const PlanArgs& plan, hipStream_t s) {
   const float scale = alpha_q * tau;
   switch (g.dn) {
-    case 64: return launch_absorb_k<2>(g, q_nope, q_rope, q_pos, lens, w_uk, q_abs, scale, tau, theta, plan, s);
-    case 128: return launch_absorb_k<4>(g, q_nope, q_rope, q_pos, lens, w_uk, q_abs, scale, tau, theta, plan, s);
-    case 256: return launch_absorb_k<8>(g, q_nope, q_rope, q_pos, lens, w_uk, q_abs, scale, tau, theta, plan, s);
+    case 64:
+      return launch_absorb_k<2>(g, q_nope, q_rope, q_pos, lens, w_uk, q_abs, q_stride, lo_off,
+                                scale, tau, theta, plan, s);
+    case 128:
+      return launch_absorb_k<4>(g, q_nope, q_rope, q_pos, lens, w_uk, q_abs, q_stride, lo_off,
+                                scale, tau, theta, plan, s);
+    case 256:
+      return launch_absorb_k<8>(g, q_nope, q_rope, q_pos, lens, w_uk, q_abs, q_stride, lo_off,
+                                scale, tau, theta, plan, s);
   }
   return hipErrorNotSupported;
 }

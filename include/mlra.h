@@ -93,6 +93,9 @@ typedef struct {
   mlra_dtype_t dtype;
   int32_t kv_chunk;      /* tokens per split-KV work item; 0 = chosen by the library */
   mlra_kernel_t decode_kernel;  /* MLRA_KERNEL_AUTO unless a kernel is to be forced */
+  int32_t q_residue;     /* 0 or 1 (bf16 only): the q_abs rows of mla_absorb_q and
+                            mla_decode_attn also carry q~'s rounding residue, see
+                            mla_absorb_q; mlra_decode ignores it */
 } mlra_config_t;
 
 /* Strided view of the latent cache. Element strides (not bytes). Row t of
@@ -122,9 +125,15 @@ MLRA_API mlra_status_t mlra_workspace_size(const mlra_config_t* cfg, int32_t bat
  *   q_pos  [B] int32 query positions, or NULL to use cache_lens[b] - 1
  *   cache_lens [B] int32 (read only when q_pos is NULL)
  *   w_uk   [H][d_latent][d_nope]
- *   q_abs  out [B][H][d_latent + d_rope], dtype cfg->dtype
+ *   q_abs  out [B][H][d_latent + d_rope], dtype cfg->dtype; with
+ *          cfg->q_residue = 1 (bf16), rows of d_latent + d_rope + d_latent:
+ *          q~ rounded to bf16, rho, then the residue bf16(q~ - bf16(q~)), so
+ *          that the two bf16 parts carry q~ to about 16 significant bits.
  * All branches are covered at once: branch j's absorbed query is the slice
- * S_j of q_abs. */
+ * S_j of q_abs. A query rounded to one bf16 moves a score by about 2^-9 of
+ * its spread; at MLA's scales on the pages (alpha_q = sqrt(7168 / 512)) that
+ * alone moves output rows by up to ~1.3e-2 in relative L2, which the residue
+ * removes. */
 MLRA_API mlra_status_t mla_absorb_q(const mlra_config_t* cfg, int32_t batch, const void* q_nope,
                            const void* q_rope, const int32_t* q_pos, const int32_t* cache_lens,
                            const void* w_uk, void* q_abs, void* stream);
@@ -133,7 +142,10 @@ MLRA_API mlra_status_t mla_absorb_q(const mlra_config_t* cfg, int32_t batch, con
  * softmax per branch, split over the token axis and merged
  * ("Multi-Head Low-Rank Attention", 方法步骤详情 step 2; "vllbc02MLA",
  * 苏神思路: decoding works like MQA).
- *   q_abs      [B][H][d_latent + d_rope] from mla_absorb_q
+ *   q_abs      [B][H][d_latent + d_rope] from mla_absorb_q (rows of
+ *              d_latent + d_rope + d_latent with cfg->q_residue = 1; the
+ *              residue enters the scores of the head-group and portable
+ *              kernels, the branch kernel uses the bf16 q~ alone)
  *   cache      strided cache view (16-byte aligned bases and strides for bf16)
  *   workspace  device buffer of at least mlra_workspace_size() bytes
  *   latent_out out [B][H][d_latent] fp32 = concat_j o~_j (branch-normalised) */

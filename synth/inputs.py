@@ -78,6 +78,9 @@ def _mlra4_scales():
 
 
 _AQ4, _AKV4 = _mlra4_scales()
+# MLA is one branch with d_c' = d_c = 512: alpha_q = alpha_kv = sqrt(7168 / 512)
+_A1 = math.sqrt(7168 / 512)
+MLA_SCALES = dict(alpha_q=_A1, alpha_kv=_A1)
 
 DSV3 = dict(heads=128, d_c=512, d_r=64, d_n=128, d_v=128)
 
@@ -85,15 +88,19 @@ WORKLOADS = {
     # tiny fp32 MLA, fan-in scaled, positions 0..255
     "tiny_mla_fp32": Workload("tiny_mla_fp32", 1, 4, 64, 16, 32, 32, 1, 256,
                               dtype="fp32", init="fan_in", seed=1001),
-    # MLA at the DeepSeek-V3 attention shape, B=16, L=4096
-    "mla_b16_l4k": Workload("mla_b16_l4k", 16, n=1, cache_len=4096, seed=1002, **DSV3),
+    # MLA at the DeepSeek-V3 attention shape, B=16, L=4096; the variance
+    # correction applies to MLA too (one branch: d_c' = d_c)
+    "mla_b16_l4k": Workload("mla_b16_l4k", 16, n=1, cache_len=4096, seed=1002, **MLA_SCALES,
+                            **DSV3),
     # MLRA-4 headline: B=16, L=32768
     "mlra4_b16_l32k": Workload("mlra4_b16_l32k", 16, n=4, cache_len=32768,
                                alpha_q=_AQ4, alpha_kv=_AKV4, seed=1003, **DSV3),
     # MLA at the headline shape
-    "mla_b16_l32k": Workload("mla_b16_l32k", 16, n=1, cache_len=32768, seed=1003, **DSV3),
+    "mla_b16_l32k": Workload("mla_b16_l32k", 16, n=1, cache_len=32768, seed=1003, **MLA_SCALES,
+                             **DSV3),
     # long context, B=2, L=131072
-    "mla_b2_l128k": Workload("mla_b2_l128k", 2, n=1, cache_len=131072, seed=1004, **DSV3),
+    "mla_b2_l128k": Workload("mla_b2_l128k", 2, n=1, cache_len=131072, seed=1004, **MLA_SCALES,
+                             **DSV3),
     "mlra4_b2_l128k": Workload("mlra4_b2_l128k", 2, n=4, cache_len=131072,
                                alpha_q=_AQ4, alpha_kv=_AKV4, seed=1004, **DSV3),
     # one MLRA-4 branch (one tensor-parallel shard): latent 128 + rope 64,
@@ -106,7 +113,7 @@ WORKLOADS = {
     # splits branches (one 128-wide latent slice + the RoPE key, 192-wide
     # rows, all 128 heads). B=16 at L=32768 and L=131072
     "mla_tp4_b16_l32k": Workload("mla_tp4_b16_l32k", 16, 32, 512, 64, 128, 128, 1, 32768,
-                                 seed=1006),
+                                 seed=1006, **MLA_SCALES),
     "mlra4_shard_b16_l32k": Workload("mlra4_shard_b16_l32k", 16, 128, 128, 64, 128, 128, 1,
                                      32768, alpha_q=_AQ4, alpha_kv=_AKV4,
                                      w_std=1.0 / math.sqrt(512), seed=1006),
@@ -115,7 +122,7 @@ WORKLOADS = {
     "mlra4_prefill_b4_t4k": Workload("mlra4_prefill_b4_t4k", 4, n=4, cache_len=4096,
                                      alpha_q=_AQ4, alpha_kv=_AKV4, seed=1008, **DSV3),
     "mla_tp4_b16_l128k": Workload("mla_tp4_b16_l128k", 16, 32, 512, 64, 128, 128, 1, 131072,
-                                  seed=1007),
+                                  seed=1007, **MLA_SCALES),
     "mlra4_shard_b16_l128k": Workload("mlra4_shard_b16_l128k", 16, 128, 128, 64, 128, 128, 1,
                                       131072, alpha_q=_AQ4, alpha_kv=_AKV4,
                                       w_std=1.0 / math.sqrt(512), seed=1007),

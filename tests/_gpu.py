@@ -18,17 +18,23 @@ def torch_dtype(w):
     return torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
 
-def config_for(w, n=None, kv_chunk=0, kernel="auto"):
+def config_for(w, n=None, kv_chunk=0, kernel="auto", q_residue=False):
     return br.make_config(w.heads, w.d_c, w.d_r, w.d_n, w.d_v, n=w.n if n is None else n,
                           sm_scale=w.tau, alpha_q=w.alpha_q, alpha_kv=w.alpha_kv,
-                          theta=w.theta, dtype=w.dtype, kv_chunk=kv_chunk, kernel=kernel)
+                          theta=w.theta, dtype=w.dtype, kv_chunk=kv_chunk, kernel=kernel,
+                          q_residue=q_residue)
 
 
 class Dev:
     """Device copies of one input set; the cache is one interleaved buffer of
-    [c_t || k^R_t] rows."""
+    [c_t || k^R_t] rows.
 
-    def __init__(self, w, inp, device="cuda", lens=None):
+    poison=True fills every row at or past a sequence's length (the rows in
+    [L_b, L_max)) with NaN, and the decode calls fill their workspace with
+    NaN bytes first, so that a kernel reading a row it must not read, or a
+    workspace word before it was written, puts NaN into the output."""
+
+    def __init__(self, w, inp, device="cuda", lens=None, poison=False):
         dt = torch_dtype(w)
         B, Lmax, _ = inp["ckv"].shape
         self.w = w
@@ -42,6 +48,16 @@ class Dev:
         for k in ("q_nope", "q_rope", "w_uk", "w_uv"):
             setattr(self, k, torch.from_numpy(inp[k]).to(device).to(dt))
         self.B, self.Lmax = B, Lmax
+        self.poison = poison
+        if poison:
+            for b, n in enumerate(np.asarray(L, np.int64)):
+                self.buf[b, max(int(n), 0):] = float("nan")
+
+    def workspace(self, cfg):
+        ws = br.alloc_workspace(cfg, self.B, self.Lmax)
+        if self.poison:
+            ws.fill_(0xFF)  # every fp32 word NaN
+        return ws
 
     def cache(self, cfg):
         return br.cache_view(self.ckv, self.krope, self.lens, cfg)
@@ -49,15 +65,14 @@ class Dev:
     def decode(self, cfg, n=None, out_dtype=torch.float32, q_pos=None):
         n = cfg.num_branches if n is None else n
         out = torch.empty(self.B, self.w.heads, self.w.d_v, dtype=out_dtype, device=self.buf.device)
-        ws = br.alloc_workspace(cfg, self.B, self.Lmax) if n == cfg.num_branches else \
-            br.alloc_workspace(_with_n(cfg, n), self.B, self.Lmax)
+        ws = self.workspace(cfg if n == cfg.num_branches else _with_n(cfg, n))
         br.mlra_decode(cfg, n, self.q_nope, self.q_rope, self.w_uk, self.w_uv, self.cache(cfg), ws,
                        out, q_pos=q_pos)
         torch.cuda.synchronize()
         return out
 
     def absorb(self, cfg, q_pos=None):
-        qa = torch.empty(self.B, self.w.heads, self.w.d_c + self.w.d_r, dtype=torch_dtype(self.w),
+        qa = torch.empty(self.B, self.w.heads, br.q_abs_width(cfg), dtype=torch_dtype(self.w),
                          device=self.buf.device)
         br.mla_absorb_q(cfg, self.q_nope, self.q_rope, self.w_uk, qa, q_pos=q_pos,
                         cache_lens=self.lens)
@@ -66,7 +81,7 @@ class Dev:
 
     def latent(self, cfg, q_abs):
         lo = torch.empty(self.B, self.w.heads, self.w.d_c, dtype=torch.float32, device=self.buf.device)
-        ws = br.alloc_workspace(cfg, self.B, self.Lmax)
+        ws = self.workspace(cfg)
         br.mla_decode_attn(cfg, q_abs, self.cache(cfg), ws, lo)
         torch.cuda.synchronize()
         return lo

@@ -54,8 +54,10 @@ def test_workspace_size_is_host_only_and_grows():
     # plan header + prefix + partials + intermediates, 256-byte aligned parts
     assert a % 256 == 0
     assert br.workspace_size(c, 0, 0) > 0
-    c2 = cfg(kv_chunk=64)
-    assert br.workspace_size(c2, 2, 4096) > br.workspace_size(cfg(), 2, 4096) or True
+    # a forced 16-token work item gives 512 items at 2 x 4096 tokens against the
+    # automatic 128 (64-token minimum), so more partial slots
+    c2 = cfg(kv_chunk=16)
+    assert br.workspace_size(c2, 2, 4096) > br.workspace_size(cfg(), 2, 4096)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -147,6 +149,14 @@ def test_decode_argument_validation():
     assert decode(c, cache(ckv=FAKE + 2)) == br.MLRA_ERR_INVALID_ARG    # misaligned
     assert decode(c, cache(ts=577)) == br.MLRA_ERR_INVALID_ARG          # stride not 16 B
     assert decode(c, cache(ts=0)) == br.MLRA_ERR_INVALID_ARG
+    # token strides below the row widths (16-byte multiples, so only the width
+    # check rejects them): rows would overlap, and the kernels would disagree
+    # on how much of the last row exists
+    assert decode(c, cache(ts=256)) == br.MLRA_ERR_INVALID_ARG         # < d_latent 512
+    k = cache()
+    k.krope_token_stride = 32                                           # < d_rope 64
+    assert decode(c, k) == br.MLRA_ERR_INVALID_ARG
+    assert prefill(c, k=cache(ts=256)) == br.MLRA_ERR_INVALID_ARG
     assert decode(c, cache(lens=0)) == br.MLRA_ERR_INVALID_ARG
     assert decode(c, cache(), q=0) == br.MLRA_ERR_INVALID_ARG
     assert decode(c, cache(), out=FAKE + 4) == br.MLRA_ERR_INVALID_ARG
@@ -233,3 +243,39 @@ def test_valid_arguments_without_device_report_no_device():
     assert L.mla_out_proj(ctypes.byref(c), 4, FAKE, FAKE, FAKE, 0, None) == br.MLRA_ERR_NO_DEVICE
     assert append(c) == br.MLRA_ERR_NO_DEVICE
     assert prefill(c) == br.MLRA_ERR_NO_DEVICE
+
+
+def test_read_probe_library_exports_and_validates():
+    # the benchmark's read-ceiling probe (include/mlra_probe.h): its own
+    # library; invalid arguments are refused before any HIP call
+    path = os.path.join(ROOT, "branch_rank_amd", "libmlra_probe.so")
+    L = ctypes.CDLL(path)
+    text = open(os.path.join(ROOT, "include", "mlra_probe.h")).read()
+    names = re.findall(r"MLRA_PROBE_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+    assert names == ["mlra_probe_read"]
+    f = L.mlra_probe_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    n = 1 << 20
+    assert f(None, n, 0, 256, 4, 4, FAKE, None) == -1           # null buffer
+    assert f(FAKE + 4, n, 0, 256, 4, 4, FAKE, None) == -1       # misaligned
+    assert f(FAKE, n, 0, 256, 4, 4, None, None) == -1           # null sink
+    assert f(FAKE, n + 16, 0, 256, 4, 4, FAKE, None) == -1      # not 1 KB per workgroup
+    assert f(FAKE, n, 0, 256, 17, 4, FAKE, None) == -1          # > 16 waves
+    assert f(FAKE, n, 0, 256, 4, 3, FAKE, None) == -1           # depth not offered
+    assert f(FAKE, n, 1, 256, 4, 5, FAKE, None) == -1
+    assert f(FAKE, n, 2, 256, 4, 4, FAKE, None) == -1           # unknown mode
+
+
+def test_q_residue_validation_and_row_width():
+    out = ctypes.c_size_t(0)
+    L = br.lib()
+    c = cfg(q_residue=True)
+    assert L.mlra_workspace_size(ctypes.byref(c), 4, 128, ctypes.byref(out)) == br.MLRA_OK
+    assert br.q_abs_width(c) == 512 + 64 + 512
+    assert br.q_abs_width(cfg()) == 512 + 64
+    c.q_residue = 2
+    assert L.mlra_workspace_size(ctypes.byref(c), 4, 128, ctypes.byref(out)) == br.MLRA_ERR_INVALID_ARG
+    c = cfg(q_residue=True, dtype="fp32")   # the residue is a bf16 notion
+    assert L.mlra_workspace_size(ctypes.byref(c), 4, 128, ctypes.byref(out)) == br.MLRA_ERR_INVALID_ARG

@@ -60,7 +60,8 @@ def small(w, B=3, L=(300, 1, 77), Lmax=320):
 
 # (workload, branches, decode kernel); "auto" picks the branch-per-wave kernel
 # for MLRA-4 at d_c = 512 and the head-group kernel otherwise
-KERNEL_CASES = [("mla_b16_l4k", 1, "auto"), ("mlra4_b16_l32k", 2, "auto"),
+KERNEL_CASES = [("mla_b16_l4k", 1, "auto"), ("mla_unit_scales", 1, "auto"),
+                ("mlra4_b16_l32k", 2, "auto"),
                 ("mlra4_b16_l32k", 4, "branch"), ("mlra4_b16_l32k", 4, "head_group"),
                 ("mlra4_b16_l32k", 4, "portable")]
 
@@ -69,7 +70,10 @@ KERNEL_CASES = [("mla_b16_l4k", 1, "auto"), ("mlra4_b16_l32k", 2, "auto"),
 @pytest.mark.parametrize("chunk", [0, 32, 100, 4096])
 def test_small_ragged_every_split(name, n, kernel, chunk):
     # several tiles, a ragged tail, a one-token sequence; every split size
-    base = WORKLOADS[name]
+    # "mla_unit_scales": MLA with alpha_q = alpha_kv = 1 (the other MLA cases
+    # take the pages' sqrt(7168 / 512))
+    base = WORKLOADS["mla_b16_l4k"].replace(alpha_q=1.0, alpha_kv=1.0) \
+        if name == "mla_unit_scales" else WORKLOADS[name]
     alphas = pages_alphas(base, n) if n > 1 else {}
     w, lens, Lmax = small(base.replace(n=n, **alphas))
     inp = make_inputs(w, lens=lens, max_len=Lmax)
@@ -163,13 +167,17 @@ def test_headline_b16_l32k_sampled(name, kernel):
     got = host(d.decode(config_for(w, kernel=kernel)))
     again = host(d.decode(config_for(w, kernel=kernel)))
     assert np.array_equal(got, again), "not run-to-run deterministic"
-    seqs = np.array([0, 5, 15])
+    # every sequence, all heads, against the absorbed chain; a few rows
+    # against the unabsorbed definition itself
+    seqs = np.arange(w.batch)
     say("  oracle")
     err = row_rel_err(got[seqs], absorbed_oracle(w, inp, seqs))
-    say(f"  rel err {err:.2e}")
+    say(f"  worst row rel err over {len(seqs)} sequences x {w.heads} heads: {err:.2e}")
     assert err <= TOL
-    rows = [(0, 0), (15, 127)]
-    assert row_rel_err(np.stack([got[b, h] for b, h in rows]), unabsorbed_rows(w, inp, rows)) <= TOL
+    rows = [(0, 0), (7, 64), (15, 127)]
+    err2 = row_rel_err(np.stack([got[b, h] for b, h in rows]), unabsorbed_rows(w, inp, rows))
+    say(f"  unabsorbed rows {rows}: {err2:.2e}")
+    assert err2 <= TOL
 
 
 @pytest.mark.slow
@@ -181,7 +189,7 @@ def test_long_context_b2_l128k(name):
     got = host(Dev(w, inp).decode(config_for(w)))
     say("  oracle")
     err = row_rel_err(got, absorbed_oracle(w, inp, np.arange(2)))
-    say(f"  rel err {err:.2e}")
+    say(f"  worst row rel err {err:.2e}")
     assert err <= TOL
 
 
@@ -192,10 +200,12 @@ def test_shard_b64_ragged_sampled():
     inp = make_inputs(w)
     lens = inp["lens"]
     got = host(Dev(w, inp).decode(config_for(w)))
-    seqs = np.array(sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 31, 63}))
-    say(f"  oracle on {len(seqs)} sequences, lengths {lens[seqs].tolist()}")
+    # all 64 sequences (the shortest, 1024 + a few tokens, and the longest
+    # included), all heads
+    seqs = np.arange(w.batch)
+    say(f"  oracle on {len(seqs)} sequences, lengths {int(lens.min())}..{int(lens.max())}")
     err = row_rel_err(got[seqs], absorbed_oracle(w, inp, seqs))
-    say(f"  rel err {err:.2e}")
+    say(f"  worst row rel err {err:.2e}")
     assert err <= TOL
 
 
@@ -208,10 +218,10 @@ def test_tensor_parallel_shards_sampled(name):
     say(f"{name}: inputs")
     inp = make_inputs(w)
     got = host(Dev(w, inp).decode(config_for(w)))
-    seqs = np.array([0, 9, 15])
+    seqs = np.arange(w.batch)
     say("  oracle")
     err = row_rel_err(got[seqs], absorbed_oracle(w, inp, seqs))
-    say(f"  rel err {err:.2e}")
+    say(f"  worst row rel err {err:.2e}")
     assert err <= TOL
     rows = [(3, 0), (12, w.heads - 1)]
     assert row_rel_err(np.stack([got[b, h] for b, h in rows]), unabsorbed_rows(w, inp, rows)) <= TOL
@@ -246,7 +256,8 @@ def test_fused_merge_matches_separate_calls(name, kernel, out_dtype):
     lens = rng.integers(1, 700, size=w.batch).astype(np.int32)
     lens[[3, 16]] = 0
     inp = make_inputs(w, lens=lens, max_len=700)
-    cfg = config_for(w, kernel=kernel)
+    # the separate calls carry q~'s residue as mlra_decode does internally
+    cfg = config_for(w, kernel=kernel, q_residue=True)
     d = Dev(w, inp)
     assert br.select_decode_kernel(cfg, d.cache(cfg)) == kernel
     fused = host(d.decode(cfg, out_dtype=out_dtype))
@@ -267,7 +278,7 @@ def test_fused_merge_many_slots(name, kernel):
     w = WORKLOADS[name].replace(batch=5)
     lens = np.array([5000, 2100, 64, 0, 4097], np.int32)
     inp = make_inputs(w, lens=lens, max_len=5000)
-    cfg = config_for(w, kernel=kernel, kv_chunk=64)
+    cfg = config_for(w, kernel=kernel, kv_chunk=64, q_residue=True)
     d = Dev(w, inp)
     fused = host(d.decode(cfg))
     sep = host(d.out_proj(cfg, d.latent(cfg, d.absorb(cfg))))
@@ -282,21 +293,24 @@ def test_fused_merge_many_slots(name, kernel):
 @pytest.mark.parametrize("d_c,n,heads", [(256, 2, 64), (256, 1, 128), (128, 1, 32)])
 def test_other_latent_widths(d_c, n, heads):
     # the MFMA path's d_c = 256 and d_c = 128 instantiations (absorb_q,
-    # head-group decode, fused merge + projection) against the oracle, and
-    # the fused merge against the separate calls. Unit scales: with
-    # alpha_q = sqrt(56) on 128-wide unit-RMS slices and W_UK of std 1/16,
-    # rounding q~ to bf16 alone moves these rows by up to 1.08e-2 (a numpy
-    # model of that rounding), above the bar for any bf16 query
-    w = WORKLOADS["mla_b16_l4k"].replace(d_c=d_c, n=n, heads=heads, batch=5)
+    # head-group decode, fused merge + projection) against the oracle at the
+    # pages' scales, alpha_q = sqrt(7168 / d_c') and alpha_kv = sqrt(7168 /
+    # d_c), with W of std 1/sqrt(d_c): the scores spread wider than at
+    # d_c = 512, and a query rounded to one bf16 alone would move these rows
+    # past the bar (a numpy model of that rounding gives 1.08e-2 at d_c = 256,
+    # n = 2), so the head-group kernel carries the query's rounding residue;
+    # and the fused merge against the separate calls
+    base = WORKLOADS["mla_b16_l4k"]
+    w = base.replace(d_c=d_c, n=n, heads=heads, batch=5, **pages_alphas(base.replace(d_c=d_c), n))
     lens = np.array([300, 1, 0, 77, 129], np.int32)
     inp = make_inputs(w, lens=lens, max_len=320)
-    cfg = config_for(w)
+    cfg = config_for(w, q_residue=True)
     d = Dev(w, inp)
     kernel = br.select_decode_kernel(cfg, d.cache(cfg))
     say(f"d_c={d_c} n={n} H={heads}: kernel {kernel}")
     got = host(d.decode(cfg))
     err = row_rel_err(got[[0, 1, 3, 4]], absorbed_oracle(w, inp, np.array([0, 1, 3, 4])))
-    say(f"  rel err {err:.2e}")
+    say(f"  worst row rel err {err:.2e}")
     assert err <= TOL
     assert not np.any(got[2])
     sep = host(d.out_proj(cfg, d.latent(cfg, d.absorb(cfg))))
