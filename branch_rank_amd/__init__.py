@@ -24,8 +24,8 @@ KERNELS = {"auto": MLRA_KERNEL_AUTO, "portable": MLRA_KERNEL_PORTABLE,
            "head_group": MLRA_KERNEL_HEAD_GROUP, "branch": MLRA_KERNEL_BRANCH}
 
 EXPORTS = ("mlra_workspace_size", "mla_absorb_q", "mla_decode_attn", "mla_out_proj",
-           "mlra_decode", "mlra_select_decode_kernel", "mlra_cache_append",
-           "mlra_prefill",
+           "mlra_decode", "mlra_decode_noalloc", "mlra_select_decode_kernel",
+           "mlra_cache_append", "mlra_prefill",
            "mlra_set_kernel_timing", "mlra_status_string", "mlra_last_error_detail")
 
 
@@ -71,6 +71,7 @@ def lib():
         "mla_decode_attn": [CP, I32, P, KP, P, SZ, P, P],
         "mla_out_proj": [CP, I32, P, P, P, ctypes.c_int, P],
         "mlra_decode": [CP, I32, I32, P, P, P, P, P, KP, P, SZ, P, ctypes.c_int, P],
+        "mlra_decode_noalloc": [CP, I32, I32, P, P, P, P, P, KP, P, ctypes.c_int, P],
         "mlra_select_decode_kernel": [CP, I32, KP, ctypes.POINTER(ctypes.c_int)],
         "mlra_cache_append": [CP, I32, P, P, ctypes.c_float, P, P, ctypes.c_int64,
                               ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, I32, P],
@@ -282,6 +283,28 @@ def mlra_decode(cfg, num_branches, q_nope, q_rope, w_uk, w_uv, cache, workspace,
     wp, wn = _ws(workspace, c2, B, cache.max_len)
     check(lib().mlra_decode(ctypes.byref(cfg), num_branches, B, qn, qr, qp, wk, wv,
                             ctypes.byref(cache), wp, wn, op, od, _stream(stream)))
+
+
+def mlra_decode_noalloc(cfg, num_branches, q_nope, q_rope, w_uk, w_uv, cache, out, q_pos=None,
+                        stream=None):
+    """mlra_decode with the library's own scratch instead of a workspace
+    (mlra_decode_noalloc): allocates nothing; calls that overlap on one GPU
+    race."""
+    t = _torch()
+    B = cache._batch
+    dt = _dtype(cfg)
+    H = cfg.num_heads
+    qn = _need(q_nope, "q_nope", (B, H, cfg.d_nope), dt)
+    qr = _need(q_rope, "q_rope", (B, H, cfg.d_rope), dt)
+    qp = _need(q_pos, "q_pos", (B,), t.int32) if q_pos is not None else None
+    wk = _need(w_uk, "w_uk", (H, cfg.d_latent, cfg.d_nope), dt)
+    wv = _need(w_uv, "w_uv", (H, cfg.d_latent, cfg.d_v), dt)
+    if out.dtype not in (t.float32, t.bfloat16):
+        raise ValueError("out must be float32 or bfloat16")
+    op = _need(out, "out", (B, H, cfg.d_v), out.dtype)
+    od = MLRA_BF16 if out.dtype == t.bfloat16 else MLRA_FP32
+    check(lib().mlra_decode_noalloc(ctypes.byref(cfg), num_branches, B, qn, qr, qp, wk, wv,
+                                    ctypes.byref(cache), op, od, _stream(stream)))
 
 
 def mlra_prefill(cfg, num_branches, q_nope, q_rope, w_uk, w_uv, cache, out, stream=None):

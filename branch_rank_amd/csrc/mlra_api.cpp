@@ -147,10 +147,12 @@ struct Layout {
   int64_t slots;
 };
 
-Layout layout(const mlra_config_t* c, int32_t batch, int32_t max_len) {
+// Workspace layout for up to `items` work items (default: the most any plan
+// for this batch and max_len can make).
+Layout layout(const mlra_config_t* c, int32_t batch, int32_t max_len, int64_t items = -1) {
   Layout L;
   const size_t H = c->num_heads, n = c->num_branches, dc = c->d_latent, dr = c->d_rope;
-  L.slots = items_max(c, batch, max_len) + batch;
+  L.slots = (items >= 0 ? items : items_max(c, batch, max_len)) + batch;
   size_t off = 0;
   L.hdr = off;    off = round_up(off + sizeof(PlanHeader), 256);
   L.prefix = off; off = round_up(off + 4 * (size_t)(batch + 1), 256);
@@ -315,20 +317,27 @@ mlra_status_t select_kernel(const mlra_config_t* c, const Geom& g, const mlra_ca
   return MLRA_OK;
 }
 
-// The split-KV plan for this decode: kernel choice and work-item target.
-mlra_status_t plan_for(const mlra_config_t* c, const Geom& g, int cus, const mlra_cache_t* k,
-                       const Workspace& ws, const Layout& L, mlra_kernel_t* kern, PlanArgs* a) {
-  const int64_t imax = L.slots - g.B;
-  TRY(select_kernel(c, g, k, kern));
+// Work items the automatic plan aims for with decode kernel `kern`: enough
+// workgroups for every CU.
+int target_items(const Geom& g, int cus, mlra_kernel_t kern) {
   int target;
-  if (*kern == MLRA_KERNEL_BRANCH)
+  if (kern == MLRA_KERNEL_BRANCH)
     target = cus / decode_branch_wgs_per_item(g);
-  else if (*kern == MLRA_KERNEL_HEAD_GROUP)
+  else if (kern == MLRA_KERNEL_HEAD_GROUP)
     target = decode_mfma_target_items(g, cus);
   else
     target = cus * 4 / g.H;
   if (target < 1) target = 1;
   if (target > kMaxAutoItems) target = kMaxAutoItems;
+  return target;
+}
+
+// The split-KV plan for this decode: kernel choice and work-item target.
+mlra_status_t plan_for(const mlra_config_t* c, const Geom& g, int cus, const mlra_cache_t* k,
+                       const Workspace& ws, const Layout& L, mlra_kernel_t* kern, PlanArgs* a) {
+  const int64_t imax = L.slots - g.B;
+  TRY(select_kernel(c, g, k, kern));
+  int target = target_items(g, cus, *kern);
   if (target > imax && imax > 0) target = (int)imax;
   a->lens = k->cache_lens;
   a->B = g.B;
@@ -405,6 +414,64 @@ mlra_status_t run_out_proj(const mlra_config_t* c, const Geom& g, const float* l
                                                 c->alpha_kv, s);
   }
   TRY_HIP(e, "out_proj launch");
+  return MLRA_OK;
+}
+
+// The whole decode step on a carved workspace: plan (inside absorb_q's
+// launch when the MFMA absorption runs), absorb_q, split-KV decode, then the
+// fused merge + output projection (or combine and out_proj).
+mlra_status_t run_step(const mlra_config_t* cfg, int32_t batch, int cus, const void* q_nope,
+                       const void* q_rope, const int32_t* q_pos, const void* w_uk,
+                       const void* w_uv, const mlra_cache_t* cache, const Layout& L,
+                       const Workspace& ws, void* out, mlra_dtype_t out_dtype, hipStream_t s) {
+  const Geom g = make_geom(cfg, batch, cache);
+  mlra_kernel_t kern;
+  PlanArgs plan;
+  TRY(plan_for(cfg, g, cus, cache, ws, L, &kern, &plan));
+  bool plan_done = false;
+  const QView qv = ws_qview(cfg, g, kern, ws.q_abs);
+  TRY(run_absorb(cfg, g, q_nope, q_rope, q_pos, cache->cache_lens, w_uk, qv, s, &plan,
+                 &plan_done));
+  bool fast = false;
+  TRY(run_decode(cfg, g, qv, cache, ws, L, kern, plan, plan_done, &fast, s));
+  if (fast && cfg->dtype == MLRA_BF16 && proj_mfma_supported(g)) {
+    // merge and out projection in one kernel: the latent stays on chip
+    const __bf16* wv = static_cast<const __bf16*>(w_uv);
+    TRY_HIP(out_dtype == MLRA_BF16
+                ? launch_merge_out_proj<__bf16>(g, ws, wv, static_cast<__bf16*>(out), cfg->alpha_kv, s)
+                : launch_merge_out_proj<float>(g, ws, wv, static_cast<float*>(out), cfg->alpha_kv, s),
+            "merge_out launch");
+    return MLRA_OK;
+  }
+  TRY(run_merge(g, ws, fast, ws.latent, s));
+  return run_out_proj(cfg, g, ws.latent, w_uv, out, out_dtype, s);
+}
+
+// ---- the scratch of mlra_decode_noalloc ----
+// A file-scope device array: each GPU the library runs on holds its own copy
+// (allocated when the code object loads there, kept until the process ends).
+// In host code `scratch` names a host-side stand-in, not a device address:
+// every use goes through the per-device address from hipGetSymbolAddress,
+// taken once per device with that device current. Every call on a GPU shares
+// that GPU's copy; nothing in it needs to start at zero (the plan and the
+// partials are written before they are read), and calls that overlap on one
+// GPU race.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+mlra_status_t scratch_base(int dev, void** base) {
+  std::call_once(g_scratch_once[dev], [&] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return hip_fail(g_scratch_err[dev], "hipGetSymbolAddress");
+  if (!g_scratch_ptr[dev] || (reinterpret_cast<uintptr_t>(g_scratch_ptr[dev]) & 255u))
+    return fail(MLRA_ERR_HIP, "scratch address missing or misaligned");
+  *base = g_scratch_ptr[dev];
   return MLRA_OK;
 }
 
@@ -624,29 +691,48 @@ mlra_status_t mlra_decode(const mlra_config_t* cfg_in, int32_t num_branches, int
     return fail(MLRA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   int dev, cus;
   TRY(current_device(&dev, &cus));
-  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return run_step(&cfg, batch, cus, q_nope, q_rope, q_pos, w_uk, w_uv, cache, L,
+                  carve(L, workspace), out, out_dtype, static_cast<hipStream_t>(stream));
+}
+
+mlra_status_t mlra_decode_noalloc(const mlra_config_t* cfg_in, int32_t num_branches,
+                                  int32_t batch, const void* q_nope, const void* q_rope,
+                                  const int32_t* q_pos, const void* w_uk, const void* w_uv,
+                                  const mlra_cache_t* cache, void* out, mlra_dtype_t out_dtype,
+                                  void* stream) {
+  g_detail.clear();
+  if (!cfg_in) return fail(MLRA_ERR_INVALID_ARG, "cfg is NULL");
+  mlra_config_t cfg = *cfg_in;
+  cfg.num_branches = num_branches;
+  TRY(check_cfg(&cfg));
+  TRY(check_cache(&cfg, cache, batch));
+  if (out_dtype != MLRA_BF16 && out_dtype != MLRA_FP32)
+    return fail(MLRA_ERR_INVALID_ARG, "unknown out_dtype");
+  if (batch == 0) return MLRA_OK;
+  TRY(check_ptr(q_nope, "q_nope"));
+  if (cfg.d_rope > 0) TRY(check_ptr(q_rope, "q_rope"));
+  TRY(check_ptr(w_uk, "w_uk"));
+  TRY(check_ptr(w_uv, "w_uv"));
+  TRY(check_ptr(out, "out"));
+  int dev, cus;
+  TRY(current_device(&dev, &cus));
+  void* base = nullptr;
+  TRY(scratch_base(dev, &base));
+  // Sized for the work items this call's plan can make: with kv_chunk = 0
+  // the plan makes at most target_items() items, else at most items_max().
   const Geom g = make_geom(&cfg, batch, cache);
-  const Workspace ws = carve(L, workspace);
   mlra_kernel_t kern;
-  PlanArgs plan;
-  TRY(plan_for(&cfg, g, cus, cache, ws, L, &kern, &plan));
-  bool plan_done = false;
-  const QView qv = ws_qview(&cfg, g, kern, ws.q_abs);
-  TRY(run_absorb(&cfg, g, q_nope, q_rope, q_pos, cache->cache_lens, w_uk, qv, s, &plan,
-                 &plan_done));
-  bool fast = false;
-  TRY(run_decode(&cfg, g, qv, cache, ws, L, kern, plan, plan_done, &fast, s));
-  if (fast && cfg.dtype == MLRA_BF16 && proj_mfma_supported(g)) {
-    // merge and out projection in one kernel: the latent stays on chip
-    const __bf16* wv = static_cast<const __bf16*>(w_uv);
-    TRY_HIP(out_dtype == MLRA_BF16
-                ? launch_merge_out_proj<__bf16>(g, ws, wv, static_cast<__bf16*>(out), cfg.alpha_kv, s)
-                : launch_merge_out_proj<float>(g, ws, wv, static_cast<float*>(out), cfg.alpha_kv, s),
-            "merge_out launch");
-    return MLRA_OK;
-  }
-  TRY(run_merge(g, ws, fast, ws.latent, s));
-  return run_out_proj(&cfg, g, ws.latent, w_uv, out, out_dtype, s);
+  TRY(select_kernel(&cfg, g, cache, &kern));
+  int64_t items = items_max(&cfg, batch, cache->max_len);
+  if (cfg.kv_chunk == 0 && target_items(g, cus, kern) < items) items = target_items(g, cus, kern);
+  const Layout L = layout(&cfg, batch, cache->max_len, items);
+  if (L.total > kScratchBytes)
+    return fail(MLRA_ERR_WORKSPACE,
+                "mlra_decode_noalloc needs %zu bytes of scratch for this batch and cache; the "
+                "library's scratch holds %zu (use mlra_decode with a workspace)",
+                L.total, kScratchBytes);
+  return run_step(&cfg, batch, cus, q_nope, q_rope, q_pos, w_uk, w_uv, cache, L, carve(L, base),
+                  out, out_dtype, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

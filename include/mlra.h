@@ -178,6 +178,25 @@ MLRA_API mlra_status_t mlra_decode(const mlra_config_t* cfg, int32_t num_branche
                           void* workspace, size_t ws_bytes, void* out, mlra_dtype_t out_dtype,
                           void* stream);
 
+/* mlra_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels and results, with the workspace taken from
+ * a 64 MiB device array that the library holds on each GPU it runs on
+ * (allocated when the library's code object loads there, freed when the
+ * process ends) instead of a caller's buffer. It calls no allocator.
+ * Arguments and validation as for mlra_decode. The workspace is sized for
+ * the work items this call's plan makes (about 47 MB for MLRA-4 or MLA at
+ * 128 heads, d_latent 512, B = 16, L = 32768 with kv_chunk = 0); a call that
+ * needs more returns MLRA_ERR_WORKSPACE and launches nothing. Every call on
+ * one GPU shares that GPU's array, so calls that overlap in time on one GPU
+ * (different streams or threads) race and give undefined results;
+ * serialise them. */
+MLRA_API mlra_status_t mlra_decode_noalloc(const mlra_config_t* cfg, int32_t num_branches,
+                                           int32_t batch, const void* q_nope, const void* q_rope,
+                                           const int32_t* q_pos, const void* w_uk,
+                                           const void* w_uv, const mlra_cache_t* cache, void* out,
+                                           mlra_dtype_t out_dtype, void* stream);
+
 /* The step before the decode: append one token per sequence to the latent
  * cache ("vllbc02MLA", 猛猿大佬思路: the projected row splits into the
  * compressed latent, which is RMS-normalised, and the decoupled RoPE key,

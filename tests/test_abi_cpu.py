@@ -34,7 +34,7 @@ def gpu_present():
 def test_library_exports_every_declared_symbol():
     L = br.lib()
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(br.EXPORTS)
@@ -180,6 +180,15 @@ def test_other_entry_points_validate():
                          FAKE, ws, FAKE, 0, None) == br.MLRA_ERR_INVALID_ARG
     assert L.mlra_decode(ctypes.byref(c), 4, 4, FAKE, FAKE, None, FAKE, FAKE, ctypes.byref(k),
                          FAKE, 8, FAKE, 0, None) == br.MLRA_ERR_WORKSPACE
+    # the no-allocation step validates like mlra_decode
+    assert L.mlra_decode_noalloc(ctypes.byref(c), 3, 4, FAKE, FAKE, None, FAKE, FAKE,
+                                 ctypes.byref(k), FAKE, 0, None) == br.MLRA_ERR_INVALID_ARG
+    assert L.mlra_decode_noalloc(ctypes.byref(c), 4, 4, FAKE, FAKE, None, FAKE, FAKE,
+                                 ctypes.byref(k), 0, 0, None) == br.MLRA_ERR_INVALID_ARG
+    assert L.mlra_decode_noalloc(ctypes.byref(c), 4, 4, FAKE, FAKE, None, FAKE, FAKE,
+                                 ctypes.byref(k), FAKE, 9, None) == br.MLRA_ERR_INVALID_ARG
+    assert L.mlra_decode_noalloc(ctypes.byref(c), 4, 0, FAKE, FAKE, None, FAKE, FAKE,
+                                 ctypes.byref(k), FAKE, 0, None) == br.MLRA_OK
     assert L.mlra_set_kernel_timing(FAKE, None) == br.MLRA_ERR_INVALID_ARG
     assert L.mlra_set_kernel_timing(None, None) == br.MLRA_OK
 
@@ -243,6 +252,9 @@ def test_valid_arguments_without_device_report_no_device():
     assert L.mla_out_proj(ctypes.byref(c), 4, FAKE, FAKE, FAKE, 0, None) == br.MLRA_ERR_NO_DEVICE
     assert append(c) == br.MLRA_ERR_NO_DEVICE
     assert prefill(c) == br.MLRA_ERR_NO_DEVICE
+    k = cache()
+    assert L.mlra_decode_noalloc(ctypes.byref(c), 4, 4, FAKE, FAKE, None, FAKE, FAKE,
+                                 ctypes.byref(k), FAKE, 0, None) == br.MLRA_ERR_NO_DEVICE
 
 
 def test_read_probe_library_exports_and_validates():
