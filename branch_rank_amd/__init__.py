@@ -19,9 +19,11 @@ LIB_PATH = os.environ.get("MLRA_LIB") or os.path.join(_HERE, "libmlra.so")
 MLRA_OK, MLRA_ERR_INVALID_ARG, MLRA_ERR_UNSUPPORTED, MLRA_ERR_WORKSPACE, \
     MLRA_ERR_NO_DEVICE, MLRA_ERR_HIP = range(6)
 MLRA_BF16, MLRA_FP32 = 0, 1
-MLRA_KERNEL_AUTO, MLRA_KERNEL_PORTABLE, MLRA_KERNEL_HEAD_GROUP, MLRA_KERNEL_BRANCH = 0, 1, 2, 3
+MLRA_KERNEL_AUTO, MLRA_KERNEL_PORTABLE, MLRA_KERNEL_HEAD_GROUP, MLRA_KERNEL_BRANCH, \
+    MLRA_KERNEL_WIDE = 0, 1, 2, 3, 4
 KERNELS = {"auto": MLRA_KERNEL_AUTO, "portable": MLRA_KERNEL_PORTABLE,
-           "head_group": MLRA_KERNEL_HEAD_GROUP, "branch": MLRA_KERNEL_BRANCH}
+           "head_group": MLRA_KERNEL_HEAD_GROUP, "branch": MLRA_KERNEL_BRANCH,
+           "wide": MLRA_KERNEL_WIDE}
 
 EXPORTS = ("mlra_workspace_size", "mla_absorb_q", "mla_decode_attn", "mla_out_proj",
            "mlra_decode", "mlra_decode_noalloc", "mlra_select_decode_kernel",
@@ -106,7 +108,7 @@ def check(st):
 def make_config(heads, d_latent, d_rope, d_nope, d_v, n=1, sm_scale=0.0, alpha_q=1.0,
                 alpha_kv=1.0, theta=10000.0, dtype="bf16", kv_chunk=0, kernel="auto",
                 q_residue=False):
-    """kernel: "auto", "portable", "head_group" or "branch" (mlra_kernel_t).
+    """kernel: "auto", "portable", "head_group", "branch" or "wide" (mlra_kernel_t).
     q_residue: the q_abs rows of mla_absorb_q / mla_decode_attn also carry
     the bf16 residue of q~ (bf16 only)."""
     return Config(heads, d_latent, d_rope, d_nope, d_v, n, sm_scale, alpha_q, alpha_kv, theta,
@@ -202,7 +204,7 @@ def cache_append(cfg, new_rows, ckv, krope, cache_lens, gain=None, eps=1e-6, str
 
 
 def select_decode_kernel(cfg, cache):
-    """Name of the decode kernel ("portable", "head_group" or "branch") that
+    """Name of the decode kernel ("portable", "head_group", "branch" or "wide") that
     the decode calls run for this config and cache view (host-only)."""
     k = ctypes.c_int(-1)
     check(lib().mlra_select_decode_kernel(ctypes.byref(cfg), cache._batch, ctypes.byref(cache),

@@ -134,6 +134,13 @@ hipError_t launch_decode_branch(const Geom& g, const QView& q, const void* ckv,
                                 const void* krope, const Workspace& ws, int grid_items,
                                 hipStream_t s, const KernelTiming& t);
 
+// 32 heads per wave across the whole 576-wide row (decode_wide.hip)
+bool decode_wide_supported(const Geom& g);
+bool decode_wide_reads_residue(const Geom& g);
+hipError_t launch_decode_wide(const Geom& g, const QView& q, const void* ckv, const void* krope,
+                              const Workspace& ws, int grid_items, hipStream_t s,
+                              const KernelTiming& t);
+
 bool decode_mfma_supported(const Geom& g);
 bool decode_mfma_reads_residue(const Geom& g);  // adds q~'s residue when the view has one
 int decode_mfma_target_items(const Geom& g, int cus);

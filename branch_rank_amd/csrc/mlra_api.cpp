@@ -76,7 +76,7 @@ mlra_status_t check_cfg(const mlra_config_t* c) {
   if (!std::isfinite(c->alpha_q) || !std::isfinite(c->alpha_kv) || !std::isfinite(c->sm_scale))
     return fail(MLRA_ERR_INVALID_ARG, "scales must be finite");
   if (c->kv_chunk < 0) return fail(MLRA_ERR_INVALID_ARG, "kv_chunk must be >= 0");
-  if (c->decode_kernel < MLRA_KERNEL_AUTO || c->decode_kernel > MLRA_KERNEL_BRANCH)
+  if (c->decode_kernel < MLRA_KERNEL_AUTO || c->decode_kernel > MLRA_KERNEL_WIDE)
     return fail(MLRA_ERR_INVALID_ARG, "unknown decode_kernel %d", (int)c->decode_kernel);
   if (c->q_residue != 0 && c->q_residue != 1)
     return fail(MLRA_ERR_INVALID_ARG, "q_residue must be 0 or 1");
@@ -134,7 +134,8 @@ QView ws_qview(const mlra_config_t* c, const Geom& g, mlra_kernel_t kern, const 
   const bool lo = c->dtype == MLRA_BF16 &&
                   (kern == MLRA_KERNEL_PORTABLE ||
                    (kern == MLRA_KERNEL_HEAD_GROUP && decode_mfma_reads_residue(g)) ||
-                   (kern == MLRA_KERNEL_BRANCH && decode_branch_reads_residue(g)));
+                   (kern == MLRA_KERNEL_BRANCH && decode_branch_reads_residue(g)) ||
+                   (kern == MLRA_KERNEL_WIDE && decode_wide_reads_residue(g)));
   QView v;
   v.q = q;
   v.stride = (int)q_row(c);
@@ -307,10 +308,15 @@ mlra_status_t select_kernel(const mlra_config_t* c, const Geom& g, const mlra_ca
                        (int64_t)k->max_len * k->krope_token_stride * 2 < 0x7fffffffLL;
   const bool branch_ok = mfma_ok && decode_branch_supported(g);
   const bool group_ok = mfma_ok && decode_mfma_supported(g);
+  const bool wide_ok = mfma_ok && decode_wide_supported(g);
   mlra_kernel_t kern = c->decode_kernel;
   if (kern == MLRA_KERNEL_AUTO)
-    kern = branch_ok ? MLRA_KERNEL_BRANCH : group_ok ? MLRA_KERNEL_HEAD_GROUP : MLRA_KERNEL_PORTABLE;
-  if ((kern == MLRA_KERNEL_BRANCH && !branch_ok) || (kern == MLRA_KERNEL_HEAD_GROUP && !group_ok))
+    kern = branch_ok ? MLRA_KERNEL_BRANCH
+         : wide_ok   ? MLRA_KERNEL_WIDE
+         : group_ok  ? MLRA_KERNEL_HEAD_GROUP
+                     : MLRA_KERNEL_PORTABLE;
+  if ((kern == MLRA_KERNEL_BRANCH && !branch_ok) || (kern == MLRA_KERNEL_HEAD_GROUP && !group_ok) ||
+      (kern == MLRA_KERNEL_WIDE && !wide_ok))
     return fail(MLRA_ERR_UNSUPPORTED, "decode_kernel %d does not support this configuration",
                 (int)kern);
   *out = kern;
@@ -323,6 +329,8 @@ int target_items(const Geom& g, int cus, mlra_kernel_t kern) {
   int target;
   if (kern == MLRA_KERNEL_BRANCH)
     target = cus / decode_branch_wgs_per_item(g);
+  else if (kern == MLRA_KERNEL_WIDE)
+    target = cus;  // one workgroup (all heads) per item and CU
   else if (kern == MLRA_KERNEL_HEAD_GROUP)
     target = decode_mfma_target_items(g, cus);
   else
@@ -371,6 +379,8 @@ mlra_status_t run_decode(const mlra_config_t* c, const Geom& g, const QView& q,
       e = launch_decode_branch(g, q, k->ckv, k->krope, ws, (int)imax, s, t);
     else if (kern == MLRA_KERNEL_HEAD_GROUP)
       e = launch_decode_mfma(g, q, k->ckv, k->krope, ws, (int)imax, s, t);
+    else if (kern == MLRA_KERNEL_WIDE)
+      e = launch_decode_wide(g, q, k->ckv, k->krope, ws, (int)imax, s, t);
     else if (c->dtype == MLRA_BF16)
       e = launch_decode_generic<__bf16>(g, q, (const __bf16*)k->ckv, (const __bf16*)k->krope, ws,
                                         (int)imax, s, t);
@@ -456,7 +466,7 @@ mlra_status_t run_step(const mlra_config_t* cfg, int32_t batch, int cus, const v
 // that GPU's copy; nothing in it needs to start at zero (the plan and the
 // partials are written before they are read), and calls that overlap on one
 // GPU race.
-constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr size_t kScratchBytes = size_t(128) << 20;
 __device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
 std::once_flag g_scratch_once[kMaxDevices];
 void* g_scratch_ptr[kMaxDevices];

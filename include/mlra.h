@@ -74,9 +74,13 @@ typedef enum {
                                   d_rope = 64, d_latent in {128, 256, 512},
                                   d_latent / n >= 32, n in {1, 2, 4},
                                   heads in {32, 64, 128} */
-  MLRA_KERNEL_BRANCH = 3       /* bf16 MFMA, one 128-wide branch and 32 heads per
+  MLRA_KERNEL_BRANCH = 3,      /* bf16 MFMA, one 128-wide branch and 32 heads per
                                   wave: n = 4, d_latent = 512, d_rope = 64,
-                                  heads in {64, 128} */
+                                  heads in {64, 128}; and one 128-wide branch
+                                  alone (n = 1, d_latent = 128, 128 heads) */
+  MLRA_KERNEL_WIDE = 4         /* fp16 MFMA on the cache converted in LDS, 32 heads
+                                  per wave across the whole row: n = 1 (MLA),
+                                  d_latent = 512, d_rope = 64, 128 heads */
 } mlra_kernel_t;
 
 typedef struct {
@@ -181,13 +185,14 @@ MLRA_API mlra_status_t mlra_decode(const mlra_config_t* cfg, int32_t num_branche
 /* mlra_decode for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid
  * allocation): the same kernels and results, with the workspace taken from
- * a 64 MiB device array that the library holds on each GPU it runs on
+ * a 128 MiB device array that the library holds on each GPU it runs on
  * (allocated when the library's code object loads there, freed when the
  * process ends) instead of a caller's buffer. It calls no allocator.
  * Arguments and validation as for mlra_decode. The workspace is sized for
- * the work items this call's plan makes (about 47 MB for MLRA-4 or MLA at
- * 128 heads, d_latent 512, B = 16, L = 32768 with kv_chunk = 0); a call that
- * needs more returns MLRA_ERR_WORKSPACE and launches nothing. Every call on
+ * the work items this call's plan makes (at 128 heads, d_latent 512, B = 16
+ * and kv_chunk = 0 about 47 MB for MLRA-4 and 80 MB for MLA, whatever the
+ * cache length); a call that needs more returns MLRA_ERR_WORKSPACE and
+ * launches nothing. Every call on
  * one GPU shares that GPU's array, so calls that overlap in time on one GPU
  * (different streams or threads) race and give undefined results;
  * serialise them. */

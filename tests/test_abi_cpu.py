@@ -77,7 +77,7 @@ def test_config_validation(kw, status):
     assert br.lib().mlra_last_error_detail().decode() != ""
 
 
-@pytest.mark.parametrize("value", [-1, 4, 99])
+@pytest.mark.parametrize("value", [-1, 5, 99])
 def test_unknown_decode_kernel_is_invalid(value):
     c = cfg()
     c.decode_kernel = value
@@ -98,7 +98,9 @@ def _fake_cache(c, batch, max_len, ts=None):
 @pytest.mark.parametrize("kw,max_len,kernel,expect", [
     (dict(), 32768, "auto", "branch"),                            # MLRA-4, d_c = 512, H = 128
     (dict(heads=64), 4096, "auto", "branch"),
-    (dict(n=1), 4096, "auto", "head_group"),                      # MLA
+    (dict(n=1), 4096, "auto", "wide"),                            # MLA
+    (dict(n=1, heads=64), 4096, "auto", "head_group"),
+    (dict(n=1), 4096, "head_group", "head_group"),
     (dict(n=2), 4096, "auto", "head_group"),
     (dict(n=1, d_latent=128), 4096, "auto", "branch"),            # one branch shard
     (dict(), 4096, "head_group", "head_group"),
@@ -113,6 +115,8 @@ def test_kernel_selection_host_only(kw, max_len, kernel, expect):
 
 
 @pytest.mark.parametrize("kw,kernel", [(dict(n=1), "branch"), (dict(heads=96), "branch"),
+                                       (dict(), "wide"), (dict(n=1, heads=64), "wide"),
+                                       (dict(n=1, dtype="fp32"), "wide"),
                                        (dict(heads=96), "head_group"),
                                        (dict(dtype="fp32"), "head_group")])
 def test_forced_kernel_outside_its_shapes(kw, kernel):

@@ -53,11 +53,14 @@ def test_one_wide_branches_and_single_head():
     assert err <= TOL["fp32"]
 
 
-@pytest.mark.parametrize("kernel", ["branch", "head_group", "portable"])
-def test_out_of_range_lengths_are_clamped(kernel):
+@pytest.mark.parametrize("name,kernel", [("mlra4_b16_l32k", "branch"),
+                                         ("mlra4_b16_l32k", "head_group"),
+                                         ("mlra4_b16_l32k", "portable"),
+                                         ("mla_b16_l4k", "wide")])
+def test_out_of_range_lengths_are_clamped(name, kernel):
     # lengths below 0 act as 0 and above max_len as max_len: the same output,
     # bit for bit, as the clamped lengths
-    w = WORKLOADS["mlra4_b16_l32k"].replace(batch=4)
+    w = WORKLOADS[name].replace(batch=4)
     Lmax = 96
     inp = make_inputs(w, lens=np.array([0, 96, 0, 7], np.int32), max_len=Lmax)
     cfg = config_for(w, kernel=kernel)
@@ -92,6 +95,40 @@ def test_single_long_sequence_over_all_items():
     lo = oracle.latent_attn_ref(qa, inp["ckv"], inp["krope"], inp["lens"], w.n)
     err = row_rel_err(got, oracle.out_proj_ref(lo, inp["w_uv"], w.alpha_kv))
     say(f"B=1, L=65536: rel err {err:.2e}")
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("kernel", ["wide", "head_group"])
+def test_single_long_mla_sequence_over_all_items(kernel):
+    # MLA, B = 1, L = 65536: every work item cuts the same sequence
+    w = WORKLOADS["mla_b16_l32k"].replace(batch=1, cache_len=65536)
+    inp = make_inputs(w)
+    cfg = config_for(w, kernel=kernel)
+    d = Dev(w, inp)
+    got = host(d.decode(cfg))
+    qa = oracle.absorb_q_ref(inp["q_nope"], inp["q_rope"], inp["w_uk"], inp["lens"] - 1, w.tau,
+                             w.alpha_q)
+    lo = oracle.latent_attn_ref(qa, inp["ckv"], inp["krope"], inp["lens"], w.n)
+    err = row_rel_err(got, oracle.out_proj_ref(lo, inp["w_uv"], w.alpha_kv))
+    say(f"MLA B=1, L=65536 ({kernel}): worst row rel err {err:.2e}")
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("kernel", ["wide", "head_group"])
+def test_many_short_contexts_mla(kernel):
+    # 64 sequences of 2..200 tokens at MLA's scales on the pages (8192 rows)
+    w = WORKLOADS["mla_b16_l4k"].replace(batch=64)
+    rng = np.random.default_rng(2004)
+    lens = rng.integers(2, 201, size=w.batch).astype(np.int32)
+    inp = make_inputs(w, lens=lens, max_len=int(lens.max()))
+    got = host(Dev(w, inp).decode(config_for(w, kernel=kernel)))
+    qa = oracle.absorb_q_ref(inp["q_nope"], inp["q_rope"], inp["w_uk"], lens - 1, w.tau, w.alpha_q,
+                             w.theta)
+    ref = oracle.out_proj_ref(oracle.latent_attn_ref(qa, inp["ckv"], inp["krope"], lens, w.n),
+                              inp["w_uv"], w.alpha_kv)
+    err = row_rel_err(got, ref)
+    say(f"64 short MLA contexts ({kernel}): worst row rel err {err:.2e}")
     assert err <= TOL["bf16"]
 
 

@@ -60,7 +60,8 @@ def small(w, B=3, L=(300, 1, 77), Lmax=320):
 
 # (workload, branches, decode kernel); "auto" picks the branch-per-wave kernel
 # for MLRA-4 at d_c = 512 and the head-group kernel otherwise
-KERNEL_CASES = [("mla_b16_l4k", 1, "auto"), ("mla_unit_scales", 1, "auto"),
+KERNEL_CASES = [("mla_b16_l4k", 1, "auto"), ("mla_b16_l4k", 1, "head_group"),
+                ("mla_unit_scales", 1, "auto"),
                 ("mlra4_b16_l32k", 2, "auto"),
                 ("mlra4_b16_l32k", 4, "branch"), ("mlra4_b16_l32k", 4, "head_group"),
                 ("mlra4_b16_l32k", 4, "portable")]
@@ -157,7 +158,8 @@ def test_forced_kernel_outside_its_shapes_is_unsupported():
 @pytest.mark.slow
 @pytest.mark.parametrize("name,kernel", [("mlra4_b16_l32k", "auto"),
                                          ("mlra4_b16_l32k", "head_group"),
-                                         ("mla_b16_l32k", "auto")])
+                                         ("mla_b16_l32k", "auto"),
+                                         ("mla_b16_l32k", "head_group")])
 def test_headline_b16_l32k_sampled(name, kernel):
     w = WORKLOADS[name]
     say(f"{name} ({kernel}): inputs")
@@ -244,7 +246,7 @@ def test_out_proj_step_bf16(batch):
 
 
 @pytest.mark.parametrize("name,kernel", [("mlra4_b16_l32k", "branch"), ("mla_b16_l4k", "head_group"),
-                                         ("shard_b64_ragged", "head_group")])
+                                         ("mla_b16_l4k", "wide"), ("shard_b64_ragged", "head_group")])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_fused_merge_matches_separate_calls(name, kernel, out_dtype):
     # mlra_decode merges the split-KV partials and projects them in one
@@ -269,7 +271,8 @@ def test_fused_merge_matches_separate_calls(name, kernel, out_dtype):
     assert err <= tol
 
 
-@pytest.mark.parametrize("name,kernel", [("mlra4_b16_l32k", "branch"), ("mla_b16_l4k", "head_group")])
+@pytest.mark.parametrize("name,kernel", [("mlra4_b16_l32k", "branch"), ("mla_b16_l4k", "head_group"),
+                                         ("mla_b16_l4k", "wide")])
 def test_fused_merge_many_slots(name, kernel):
     # 64-token work items give up to 79 partial slots per sequence, so the
     # fused merge runs its weight table in several 32-slot passes; a
