@@ -1,4 +1,4 @@
-// Wide-wave MFMA split-KV decode for a 512-wide latent at 128 heads, gfx950
+// Wide MFMA split-KV decode for a 512-wide latent at 128 heads, gfx950
 // (MI355X): MLA (one branch over the whole latent).
 //
 // What it computes ("Multi-Head Low-Rank Attention", 核心方法 and 方法步骤详情
@@ -10,35 +10,41 @@
 // follows.
 //
 // Mapping onto CDNA4:
-//  * One workgroup per work item, four waves (one per SIMD); wave w owns heads
-//    [32 w, 32 w + 32) across the whole 576-wide row. Every byte of a tile in
-//    LDS is then read by four waves, each MFMA A fragment (16 tokens x 32
-//    columns) feeds two MFMAs (two 16-head blocks): half the LDS reads per
-//    HBM byte of a design with 16 heads per wave, whose LDS reads would
-//    outrun the tile's HBM time. Q^T (32 heads x 576) stays in VGPRs and
-//    O^T (512 x 32 fp32) in AGPRs for the whole segment.
-//  * The RoPE score is one pair of k-steps per tile, shared by every branch
-//    (the method's flop count); each branch adds its own 512/n latent
-//    columns, runs its own softmax and its PV over those columns.
+//  * One workgroup of NW waves per work item holds all 128 heads, so every
+//    byte of a tile is streamed into LDS once per CU. The work of a tile is
+//    split two ways:
+//      - scores and softmax by heads: wave w owns heads [HPW w, HPW w + HPW)
+//        across the whole 576-wide row (Q^T stays in its registers);
+//      - P V by columns: wave w owns latent columns [CPW w, CPW w + CPW) for
+//        all 128 heads (its O^T stays in its registers), reading every head's
+//        P^T from LDS, where each wave leaves its own after the softmax.
+//    So each transposed V^T read from LDS (the slow LDS read on this chip)
+//    feeds eight MFMAs, one per 16-head block, and a wave's registers hold
+//    Q of HPW heads plus O of CPW columns: 72 + 128 with eight waves, which
+//    leaves room for a second wave on every SIMD to hide LDS latency.
+//  * The RoPE score is computed once per head and tile and shared by every
+//    branch (the method's flop count).
 //  * 32-token tiles stream HBM -> LDS by LDS-DMA (device-scope, non-temporal)
-//    into a ring of 4 stages of 36 KB; each wave issues 9 of a tile's 36
-//    1 KB instructions. One workgroup barrier per tile: after it, every wave
-//    has finished the previous tile (whose stage takes the DMA three tiles
-//    ahead) and prepared the current one.
-//  * F16 (MLA, n = 2): the MFMAs run in fp16. Right after its own DMA of the
-//    next tile lands, each lane converts the 16 bytes it loaded from bf16 to
-//    fp16 in place (exact for |x| in [2^-14, 65504]: bf16's 8 significant
-//    bits fit fp16's 11; round toward zero saturates beyond, flushes the
-//    negligible tail below). q~ (its bf16 parts summed in fp32) and P are
-//    rounded to fp16, 2^-11 relative, where a bf16 query's 2^-8 alone moves
-//    one softmax's output rows by up to ~1.3e-2 at MLA's scales. P is kept
+//    into a ring of NS stages of 36 KB; the waves share a tile's 36 1 KB
+//    instructions. Two workgroup barriers per tile: one before the scores
+//    (the tile is in LDS and converted, the previous tile's P V is done, so
+//    its stage takes the DMA NS - 1 tiles ahead and its P^T can be
+//    overwritten) and one before P V (every head's P^T is in LDS).
+//  * F16: the MFMAs run in fp16. After its own DMA of the next tile lands,
+//    each lane converts the 16 bytes it loaded from bf16 to fp16 in place
+//    (exact for |x| in [2^-14, 65504]: bf16's 8 significant bits fit fp16's
+//    11; round toward zero saturates beyond, flushes the negligible tail
+//    below). q~ (its bf16 parts summed in fp32) and P are rounded to fp16,
+//    2^-11 relative, where a bf16 query's 2^-8 alone moves one softmax's
+//    output rows by up to ~1.3e-2 at MLA's scales on the pages. P is kept
 //    <= 2^15 (the reference moves when a tile's max passes it by 15 in log2
-//    units), within fp16's range. Without F16 every MFMA runs in bf16 on the
-//    cache as stored.
+//    units), within fp16's range; the factor that rescales a head's
+//    accumulators then goes to LDS beside its P^T for the column owners.
 //  * QK: S^T[t][h] on v_mfma_f32_16x16x32_{f16,bf16}, 16 tokens as M and 16
-//    heads as N, starting from a per-row bias (0, or -inf past the segment's
-//    end). The S^T accumulators (lane = head) are P^T, the B operand of
-//    O^T[c][h] += V^T[c][t] P^T[t][h], with V^T read by ds_read_b64_tr_b16
+//    heads as N, from a per-row bias (0, or -inf past the segment's end), in
+//    two accumulator sets (even and odd k-steps) so that more MFMAs are
+//    independent. The S^T accumulators (lane = head) are P^T, the B operand
+//    of O^T[c][h] += V^T[c][t] P^T[t][h], with V^T read by ds_read_b64_tr_b16
 //    from the same LDS tile. The LDS rows are XOR-swizzled in 16-byte chunks
 //    (chunk ^ 2 (t & 15) for latent rows, ^ ((t >> 1) & 7) for RoPE rows), as
 //    in the head-group kernel, so both read patterns are free of bank
@@ -50,6 +56,10 @@
 
 #include "device_common.h"
 
+#ifndef MLRA_WIDE_WAVES
+#define MLRA_WIDE_WAVES 8
+#endif
+
 namespace mlra {
 namespace {
 
@@ -60,13 +70,11 @@ constexpr int kDC = 512;                 // latent width
 constexpr int kDR = 64;                  // RoPE width
 constexpr int kLat = kT * kDC * 2;       // latent bytes of a stage
 constexpr int kStage = kLat + kT * kDR * 2;  // 36 KB
-constexpr int kNS = 4;                   // stages (144 KB of LDS)
-constexpr int kNW = 4;                   // waves, one per SIMD
-constexpr int kHPW = 32;                 // heads per wave
-constexpr int kH = kNW * kHPW;           // heads
-constexpr int kPer = 9;                  // DMA instructions per wave and tile
+constexpr int kH = 128;                  // heads
+constexpr int kNI = kT + 4;              // DMA instructions per tile (32 latent rows + 4 RoPE)
 constexpr int kKS = kDC / 32;            // latent k-steps
-constexpr int kCB = kDC / 16;            // PV output column blocks
+constexpr int kHB = kH / 16;             // 16-head blocks
+constexpr int kNS = 4;                   // tile stages (144 KB of LDS)
 
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 
@@ -107,18 +115,39 @@ __device__ __forceinline__ i32x4 bf16_to_f16x8(i32x4 x) {
   return r;
 }
 
-template <int NB, bool F16>
-__global__ __launch_bounds__(64 * kNW, 1) void decode_wide_kernel(DecodeParams p) {
+template <int NW>
+struct WCfg {
+  static constexpr int HPW = kH / NW;         // heads per wave (scores, softmax)
+  static constexpr int NBQ = HPW / 16;        // 16-head blocks per wave
+  static constexpr int CPW = kDC / NW;        // latent columns per wave (P V)
+  static constexpr int CBW = CPW / 16;        // PV column blocks per wave
+  static constexpr int LR = kT / NW;          // latent rows each wave loads per tile
+  static_assert(HPW % 16 == 0 && CPW % 16 == 0 && kT % NW == 0 && NW >= 4, "wave shape");
+};
+
+template <int NB, bool F16, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p) {
   using O_ = Op<F16>;
   using V = typename O_::V;
   using E = typename O_::E;
+  using C = WCfg<NW>;
+  constexpr int NBQ = C::NBQ, CBW = C::CBW;
   constexpr int KPB = kKS / NB;  // latent k-steps per branch
-  constexpr int CPB = kCB / NB;  // PV column blocks per branch
   constexpr float kRescale = F16 ? 15.f : 16.f;
-  static_assert(kKS % NB == 0 && kCB % NB == 0, "branches");
+  static_assert(kKS % NB == 0, "branches");
 
-  __shared__ __attribute__((aligned(1024))) char smem_raw[kNS * kStage];
+  // LDS: the tile ring, then the P exchange (P^T fragments of NB branches x
+  // eight 16-head blocks, 1 KB each: lane l's 16 bytes at 16 l, the B-operand
+  // layout), the rescale factors per (branch, head) and one flag per (wave,
+  // branch) that says whether any of its heads' references moved
+  constexpr int kPBytes = NB * kHB * 1024;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kNS * kStage + kPBytes];
+  __shared__ float fl_raw[NB * kH];
+  __shared__ int flags_raw[NW * NB];
   char LDS_AS* smem = (char LDS_AS*)smem_raw;
+  char LDS_AS* pl = smem + kNS * kStage;
+  float LDS_AS* fl = (float LDS_AS*)fl_raw;
+  int LDS_AS* flags = (int LDS_AS*)flags_raw;
   const uint32_t sbase = (uint32_t)(uintptr_t)smem;
 
   const int k = blockIdx.x;
@@ -127,22 +156,19 @@ __global__ __launch_bounds__(64 * kNW, 1) void decode_wide_kernel(DecodeParams p
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l16 = lane & 15, kg = lane >> 4;
+  __builtin_assume(wave >= 0 && wave < NW);
+  const int jq = wave * NB / NW;  // branch of this wave's columns
 
-  // DMA: latent instruction u < 8 carries row wave + 4 u (lane l: LDS chunk
-  // l, global chunk l ^ swz(row); rows u and u + 4 share a swizzle, and the
-  // row offset rides in the scalar offset); instruction 8 carries RoPE rows
-  // 8 wave .. 8 wave + 7 (lane l: row 8 wave + l / 8, LDS chunk l % 8,
-  // global chunk (l % 8) ^ swz_r(row)).
-  uint32_t lat_c[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) lat_c[u] = (uint32_t)(16 * (lane ^ swz(wave + 4 * u)));
-  const int rope_t = 8 * wave + (lane >> 3);
-  const uint32_t rope_c = (uint32_t)(16 * ((lane & 7) ^ swz_r(rope_t)));
-  // LDS byte offset of instruction u within a stage (wave-uniform); the DMA
-  // writes lane l's 16 bytes at that offset + 16 l
-  auto row_lds = [&](int u) -> uint32_t {
-    return u < 8 ? (uint32_t)((wave + 4 * u) * 1024) : (uint32_t)(kLat + wave * 1024);
-  };
+  // DMA of a tile: wave w loads latent rows w + NW u (u < LR; lane l: LDS
+  // chunk l, global chunk l ^ swz(row), the row's offset in the scalar
+  // offset) and, for w < 4, RoPE rows 8 w .. 8 w + 7 (lane l: row 8 w + l / 8,
+  // LDS chunk l % 8, global chunk (l % 8) ^ swz_r(row)). The DMA writes lane
+  // l's 16 bytes at a wave-uniform LDS offset + 16 l.
+  const bool rope_wave = wave < 4;
+  auto lat_lds = [&](int u) { return (uint32_t)((wave + NW * u) * 1024); };
+  const uint32_t rope_lds = (uint32_t)(kLat + wave * 1024);
+  const int rope_rt = 8 * wave + (lane >> 3);
+  const uint32_t rope_c = (uint32_t)(16 * ((lane & 7) ^ swz_r(rope_rt)));
   // QK A fragments: row 16 mb + l16, logical chunk 4 ks + kg, physical chunk
   // (4 ks + kg) ^ 2 l16 = 4 ks ^ (kg ^ 2 l16); the XOR touches address bits
   // 6-9 only, which the lane base and every stage base leave zero.
@@ -174,15 +200,14 @@ __global__ __launch_bounds__(64 * kNW, 1) void decode_wide_kernel(DecodeParams p
 
     // Q^T as the B operand: lane (head, kg) holds 8 consecutive k of its
     // head; k-steps 0..15 latent, 16..17 RoPE. The fp16 query is q~'s bf16
-    // parts summed in fp32, then rounded once.
-    V q[kKS + 2][2];
-    // (without a residue in the view the residue loads re-read q~ and are
-    // weighted by 0)
+    // parts summed in fp32, then rounded once (without a residue in the view
+    // the residue loads re-read q~ and are weighted by 0).
+    V q[kKS + 2][NBQ];
     const float wlo = p.q_lo > 0 ? 1.f : 0.f;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NBQ; ++nb) {
       const __bf16* qrow =
-          p.q_abs + ((int64_t)bseq * kH + kHPW * wave + 16 * nb + l16) * p.q_stride + 8 * kg;
+          p.q_abs + ((int64_t)bseq * kH + C::HPW * wave + 16 * nb + l16) * p.q_stride + 8 * kg;
       const __bf16* lrow = qrow + p.q_lo;
 #pragma unroll
       for (int ks = 0; ks < kKS + 2; ++ks) {
@@ -208,64 +233,67 @@ __global__ __launch_bounds__(64 * kNW, 1) void decode_wide_kernel(DecodeParams p
     // count DMA only
     wait_vm<0>();
 
+    // DMA instruction u of this wave for `tile`; the segment's last tile
+    // clamps its rows to t1 - 1 (the segment's rows bound the buffer range)
     auto issue = [&](int tile) {
       const uint32_t sa = sbase + (uint32_t)((tile & (kNS - 1)) * kStage);
       const int ts0 = t0 + tile * kT;
-      if (ts0 + kT <= t1) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          dma16_stream(crs, sa + row_lds(u), lat_c[u & 3],
-                       (uint32_t)((ts0 + wave + 4 * u) * p.ckv_ts * 2));
-        dma16_stream(krs, sa + row_lds(8), (uint32_t)(rope_t * p.kr_ts * 2) + rope_c,
-                     (uint32_t)(ts0 * p.kr_ts * 2));
-      } else {  // the segment's last tile: rows clamped to t1 - 1 (wave-uniform)
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int row = min(ts0 + wave + 4 * u, t1 - 1);
-          dma16_stream(crs, sa + row_lds(u), lat_c[u & 3], (uint32_t)(row * p.ckv_ts * 2));
-        }
-        const int row = min(ts0 + rope_t, t1 - 1);
-        dma16_stream(krs, sa + row_lds(8), (uint32_t)(row * p.kr_ts * 2) + rope_c, 0u);
+      for (int u = 0; u < C::LR; ++u) {
+        const int qi = wave + NW * u;
+        const int row = min(ts0 + qi, t1 - 1);
+        dma16_stream(crs, sa + lat_lds(u), (uint32_t)(16 * (lane ^ swz(qi))),
+                     (uint32_t)(row * p.ckv_ts * 2));
+      }
+      if (rope_wave) {
+        const int row = min(ts0 + rope_rt, t1 - 1);
+        dma16_stream(krs, sa + rope_lds, (uint32_t)(row * p.kr_ts * 2) + rope_c, 0u);
       }
     };
     // wait until this wave's DMA of `tile` has landed, given the tiles
-    // issued after it that may stay in flight
+    // issued after it that may stay in flight (at most kNS - 2)
     auto wait_own = [&](int tile) {
-      const int after = min(tile + 2, ntiles - 1) - tile;  // issued tiles beyond `tile`
-      if (after >= 2) wait_vm<2 * kPer>();
-      else if (after == 1) wait_vm<kPer>();
-      else wait_vm<0>();
+      constexpr int H = C::LR + 1, L = C::LR;
+      const int after = min(tile + kNS - 2, ntiles - 1) - tile;
+      if (rope_wave) {
+        if (after >= 2) wait_vm<2 * H>();
+        else if (after == 1) wait_vm<H>();
+        else wait_vm<0>();
+      } else {
+        if (after >= 2) wait_vm<2 * L>();
+        else if (after == 1) wait_vm<L>();
+        else wait_vm<0>();
+      }
       asm volatile("" ::: "memory");
     };
-    // this lane's 16-byte chunks of `tile` from bf16 to fp16, in place, three
-    // reads in flight at a time
+    // this lane's 16-byte chunks of `tile` from bf16 to fp16, in place
     auto convert = [&](int tile) {
-      char LDS_AS* st = smem + (tile & (kNS - 1)) * kStage;
+      char LDS_AS* st = smem + (tile & (kNS - 1)) * kStage + 16 * lane;
+      i32x4 x[C::LR], r;
 #pragma unroll
-      for (int u0 = 0; u0 < kPer; u0 += 3) {
-        i32x4 x[3];
+      for (int u = 0; u < C::LR; ++u) x[u] = *(const i32x4 LDS_AS*)(st + lat_lds(u));
+      if (rope_wave) r = *(const i32x4 LDS_AS*)(st + rope_lds);
 #pragma unroll
-        for (int u = 0; u < 3; ++u) x[u] = *(const i32x4 LDS_AS*)(st + row_lds(u0 + u) + 16 * lane);
-#pragma unroll
-        for (int u = 0; u < 3; ++u)
-          *(i32x4 LDS_AS*)(st + row_lds(u0 + u) + 16 * lane) = bf16_to_f16x8(x[u]);
-      }
+      for (int u = 0; u < C::LR; ++u) *(i32x4 LDS_AS*)(st + lat_lds(u)) = bf16_to_f16x8(x[u]);
+      if (rope_wave) *(i32x4 LDS_AS*)(st + rope_lds) = bf16_to_f16x8(r);
     };
 
 #pragma unroll
     for (int s = 0; s < kNS - 1; ++s)
       if (s < ntiles) issue(s);
 
-    f32x4 o[kCB][2];
+    // O^T of this wave's columns (column blocks CBW wave + c) for every
+    // 16-head block
+    f32x4 o[CBW][kHB];
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb)
+    for (int c = 0; c < CBW; ++c)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) o[cb][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    float m_run[NB][2], l_run[NB][2];
+      for (int hb = 0; hb < kHB; ++hb) o[c][hb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    float m_run[NB][NBQ], l_run[NB][NBQ];
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < NBQ; ++nb) {
         m_run[j][nb] = -INFINITY;
         l_run[j][nb] = 0.f;
       }
@@ -274,15 +302,19 @@ __global__ __launch_bounds__(64 * kNW, 1) void decode_wide_kernel(DecodeParams p
       convert(0);
     }
 
-    for (int t = 0; t < ntiles; ++t) {
-      if constexpr (!F16) wait_own(t);
-      // this wave's LDS writes (the conversion) complete before the barrier:
-      // s_barrier does not wait for them
+    auto barrier = [&] {
+      // this wave's LDS writes complete and its reads returned: s_barrier
+      // waits for neither
       wait_lgkm0();
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
+    };
+
+    for (int t = 0; t < ntiles; ++t) {
+      if constexpr (!F16) wait_own(t);
+      barrier();  // tile t in LDS (converted); P V of tile t - 1 done
       if (t + kNS - 1 < ntiles) issue(t + kNS - 1);
       const char LDS_AS* st = smem + (t & (kNS - 1)) * kStage;
 
@@ -294,14 +326,15 @@ __global__ __launch_bounds__(64 * kNW, 1) void decode_wide_kernel(DecodeParams p
 #pragma unroll
         for (int e = 0; e < 4; ++e) bias[mb][e] = 16 * mb + 4 * kg + e < valid ? 0.f : -INFINITY;
 
-      // RoPE score, shared by the branches
-      f32x4 R[2][2];
+      // RoPE score of this wave's heads, shared by the branches
+      f32x4 R[2][NBQ];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        V a0 = *(const V LDS_AS*)(st + rp_base + mb * 2048);
-        V a1 = *(const V LDS_AS*)((const char LDS_AS*)(((uintptr_t)(st + rp_base + mb * 2048)) ^ 64));
+        const V a0 = *(const V LDS_AS*)(st + rp_base + mb * 2048);
+        const V a1 =
+            *(const V LDS_AS*)((const char LDS_AS*)(((uintptr_t)(st + rp_base + mb * 2048)) ^ 64));
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
+        for (int nb = 0; nb < NBQ; ++nb) {
           R[mb][nb] = O_::mfma(a0, q[kKS][nb], bias[mb]);
           R[mb][nb] = O_::mfma(a1, q[kKS + 1][nb], R[mb][nb]);
         }
@@ -327,27 +360,47 @@ __global__ __launch_bounds__(64 * kNW, 1) void decode_wide_kernel(DecodeParams p
 
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        f32x4 S[2][2];
+        // two accumulator sets (even and odd k-steps): more independent MFMA
+        // chains per wave
+        // with one wave per SIMD, two accumulator sets (even and odd k-steps)
+        // make more MFMA chains independent; with two, the other wave hides
+        // the chain's latency and the registers are needed for Q and O
+        constexpr bool kDual = NW < 8;
+        constexpr int kPf = kDual ? 2 : 1;  // k-steps of fragments read ahead
+        f32x4 S[2][NBQ], S2[2][NBQ];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) S[mb][nb] = R[mb][nb];
-        // software pipeline: the fragments of k-step ks + 2 are read while
+          for (int nb = 0; nb < NBQ; ++nb) {
+            S[mb][nb] = R[mb][nb];
+            if constexpr (kDual) S2[mb][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+          }
+        // software pipeline: the fragments of k-step ks + kPf are read while
         // k-step ks computes; fences keep the compiler from hoisting every
         // read of the tile (their registers would not fit beside Q and O)
-        V A[3][2];
-        qk_frag(j * KPB, A[0]);
-        if (KPB > 1) qk_frag(j * KPB + 1, A[1]);
+        V A[kPf + 1][2];
+#pragma unroll
+        for (int i = 0; i < kPf && i < KPB; ++i) qk_frag(j * KPB + i, A[i]);
 #pragma unroll
         for (int kk = 0; kk < KPB; ++kk) {
           const int ks = j * KPB + kk;
-          if (kk + 2 < KPB) qk_frag(ks + 2, A[(kk + 2) % 3]);
+          if (kk + kPf < KPB) qk_frag(ks + kPf, A[(kk + kPf) % (kPf + 1)]);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) S[mb][nb] = O_::mfma(A[kk % 3][mb], q[ks][nb], S[mb][nb]);
+            for (int nb = 0; nb < NBQ; ++nb) {
+              const V& a = A[kk % (kPf + 1)][mb];
+              if (kDual && (kk & 1)) S2[mb][nb] = O_::mfma(a, q[ks][nb], S2[mb][nb]);
+              else S[mb][nb] = O_::mfma(a, q[ks][nb], S[mb][nb]);
+            }
           __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (kDual) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NBQ; ++nb) S[mb][nb] += S2[mb][nb];
         }
         // the next tile's conversion runs while these MFMAs drain
         if constexpr (F16) {
@@ -356,23 +409,26 @@ __global__ __launch_bounds__(64 * kNW, 1) void decode_wide_kernel(DecodeParams p
             convert(t + 1);
           }
         }
-        // branch j's online softmax over the tile, per 16-head block
-        V P[2];
+        // branch j's online softmax over the tile for this wave's heads; P^T
+        // and the factor that rescales the heads' accumulators (1 unless the
+        // reference moved) go to LDS for the waves that own the columns
+        bool moved = false;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
+        for (int nb = 0; nb < NBQ; ++nb) {
           const float mx =
               fmaxf(fmaxf(fmaxf(S[0][nb][0], S[0][nb][1]), fmaxf(S[0][nb][2], S[0][nb][3])),
                     fmaxf(fmaxf(S[1][nb][0], S[1][nb][1]), fmaxf(S[1][nb][2], S[1][nb][3])));
           const float mt = max4(mx) * kLog2e;
           const bool need = mt > m_run[j][nb] + kRescale;
+          float f = 1.f;
           if (__builtin_expect(__any(need), 0)) {
             const float mn = need ? mt : m_run[j][nb];
-            const float f = __builtin_amdgcn_exp2f(m_run[j][nb] - mn);
+            f = __builtin_amdgcn_exp2f(m_run[j][nb] - mn);
             l_run[j][nb] *= f;
-#pragma unroll
-            for (int cb = j * CPB; cb < (j + 1) * CPB; ++cb) o[cb][nb] *= f;
             m_run[j][nb] = mn;
+            moved = true;
           }
+          V P;
           float ps = 0.f;
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
@@ -381,32 +437,60 @@ __global__ __launch_bounds__(64 * kNW, 1) void decode_wide_kernel(DecodeParams p
               const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(S[mb][nb][e], kLog2e,
                                                                      -m_run[j][nb]));
               ps += pe;
-              P[nb][4 * mb + e] = (E)pe;
+              P[4 * mb + e] = (E)pe;
             }
           l_run[j][nb] += ps;
+          const int hb = NBQ * wave + nb;
+          *(V LDS_AS*)(pl + ((j * kHB + hb) * 64 + lane) * 16) = P;
+          if (kg == 0) fl[j * kH + 16 * hb + l16] = f;
         }
-        // O^T += V^T P^T over branch j's columns, V^T fragments read three
-        // blocks ahead
-        V Vf[4];
+        if (lane == 0) flags[wave * NB + j] = moved ? 1 : 0;
+      }
+
+      barrier();  // every head's P^T is in LDS
+
+      // rescale this wave's accumulators of the heads whose reference moved
+      {
+        int any = 0;
 #pragma unroll
-        for (int i = 0; i < 3 && i < CPB; ++i) Vf[i] = pv_frag(j * CPB + i);
+        for (int w = 0; w < NW; ++w) any |= flags[w * NB + jq];
+        if (__builtin_expect(any != 0, 0)) {
 #pragma unroll
-        for (int c = 0; c < CPB; ++c) {
-          const int cb = j * CPB + c;
-          if (c + 3 < CPB) Vf[(c + 3) % 4] = pv_frag(cb + 3);
+          for (int hb = 0; hb < kHB; ++hb) {
+            const float f = fl[jq * kH + 16 * hb + l16];
+#pragma unroll
+            for (int c = 0; c < CBW; ++c) o[c][hb] *= f;
+          }
+        }
+      }
+      // O^T += V^T P^T over this wave's columns for all 128 heads: every V^T
+      // fragment feeds one MFMA per 16-head block; P^T fragments four at a time
+#pragma unroll
+      for (int h0 = 0; h0 < kHB; h0 += 4) {
+        V Pf[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          Pf[i] = *(const V LDS_AS*)(pl + ((jq * kHB + h0 + i) * 64 + lane) * 16);
+        V Vf[3];
+#pragma unroll
+        for (int c = 0; c < 2 && c < CBW; ++c) Vf[c] = pv_frag(CBW * wave + c);
+#pragma unroll
+        for (int c = 0; c < CBW; ++c) {
+          if (c + 2 < CBW) Vf[(c + 2) % 3] = pv_frag(CBW * wave + c + 2);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) o[cb][nb] = O_::mfma(Vf[c % 4], P[nb], o[cb][nb]);
+          for (int i = 0; i < 4; ++i) o[c][h0 + i] = O_::mfma(Vf[c % 3], Pf[i], o[c][h0 + i]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
 
-    // partial state of this segment: m, l as [slot][n][H]; acc as
-    // [slot][H][d_c], 16-byte stores of 4 consecutive latent columns
+    // partial state of this segment: m, l as [slot][n][H] (this wave's
+    // heads); acc as [slot][H][d_c] (this wave's columns, all heads), 16-byte
+    // stores of 4 consecutive latent columns
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int head = kHPW * wave + 16 * nb + l16;
+    for (int nb = 0; nb < NBQ; ++nb) {
+      const int head = C::HPW * wave + 16 * nb + l16;
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const float lt = sum4(l_run[j][nb]);
@@ -415,16 +499,19 @@ __global__ __launch_bounds__(64 * kNW, 1) void decode_wide_kernel(DecodeParams p
           p.l[((int64_t)slot * NB + j) * kH + head] = lt;
         }
       }
-      float* row = p.acc + ((int64_t)slot * kH + head) * kDC + 4 * kg;
+    }
 #pragma unroll
-      for (int cb = 0; cb < kCB; ++cb) *(f32x4*)(row + 16 * cb) = o[cb][nb];
+    for (int hb = 0; hb < kHB; ++hb) {
+      float* row = p.acc + ((int64_t)slot * kH + 16 * hb + l16) * kDC + C::CPW * wave + 4 * kg;
+#pragma unroll
+      for (int c = 0; c < CBW; ++c) *(f32x4*)(row + 16 * c) = o[c][hb];
     }
     start = seg_end;
     ++bseq;
   }
 }
 
-template <int NB, bool F16>
+template <int NB, bool F16, int NW>
 hipError_t launch_w(const Geom& g, const QView& q, const void* ckv, const void* krope,
                     const Workspace& ws, int items, hipStream_t s, const KernelTiming& t) {
   DecodeParams p;
@@ -443,7 +530,7 @@ hipError_t launch_w(const Geom& g, const QView& q, const void* ckv, const void* 
   p.l = ws.l;
   p.acc = ws.acc;
   p.B = g.B;
-  hipExtLaunchKernelGGL((decode_wide_kernel<NB, F16>), dim3(items), dim3(64 * kNW), 0, s,
+  hipExtLaunchKernelGGL((decode_wide_kernel<NB, F16, NW>), dim3(items), dim3(64 * NW), 0, s,
                         t.start, t.stop, 0, p);
   return hipGetLastError();
 }
@@ -452,10 +539,8 @@ hipError_t launch_w(const Geom& g, const QView& q, const void* ckv, const void* 
 
 // MLA: one branch over a 512-wide latent, 64-wide RoPE key, 128 heads. (The
 // kernel is written for n branches with a shared RoPE score; only n = 1 is
-// built: it needs 400 registers of Q and O per lane, which this compiler
-// fits beside the score accumulators only with the MFMAs' results in
-// VGPRs, and its pass that moves them to AGPRs fails on the four-branch
-// instantiation.)
+// built, with the MFMAs' results selected into VGPRs: this compiler's pass
+// that moves them to AGPRs fails on a four-branch instantiation.)
 bool decode_wide_supported(const Geom& g) {
   return g.dc == kDC && g.dr == kDR && g.H == kH && g.n == 1;
 }
@@ -467,7 +552,7 @@ hipError_t launch_decode_wide(const Geom& g, const QView& q, const void* ckv, co
                               const Workspace& ws, int items, hipStream_t s,
                               const KernelTiming& t) {
   if (!decode_wide_supported(g)) return hipErrorNotSupported;
-  return launch_w<1, true>(g, q, ckv, krope, ws, items, s, t);
+  return launch_w<1, true, MLRA_WIDE_WAVES>(g, q, ckv, krope, ws, items, s, t);
 }
 
 }  // namespace mlra
