@@ -35,4 +35,8 @@ from .mlra_ref import (  # noqa: F401
     variance_scales,
     rms_norm,
     cache_append_ref,
+    e4m3_decode,
+    e4m3_encode,
+    fp8_dequantize,
+    fp8_quantize,
 )

@@ -413,3 +413,77 @@ def cache_append_ref(ckv, krope, lens, new_c, new_kr, max_len, gain=None, eps=1e
         lens[b] = p + 1
     return ckv, krope, lens.astype(np.int32)
 
+
+
+# ---------------------------------------------------------------- fp8 cache --
+#
+# Quantised latent cache. The pages name INT8 for inference deployment
+# ("MLA多头潜在注意力机制", 9.2 部署注意事项) and fix no format or scale. The
+# reading taken here: 8-bit floating point E4M3 in the OCP 8-bit floating
+# point layout (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits,
+# subnormals, no infinities, exponent and mantissa all ones = NaN; largest
+# finite value 448), one float32 scale per cache tensor: a stored latent value
+# is c = ckv_scale * e4m3(code), a stored RoPE key value k = krope_scale *
+# e4m3(code). Writing a value x stores the code nearest to x / scale, ties to
+# the code with an even mantissa, saturating at +-448.
+
+
+def e4m3_decode(codes):
+    """Float64 value of each E4M3 code (uint8 array).
+
+    Normal codes (exponent field e in 1..15): (-1)^s 2^(e - 7) (1 + m / 8);
+    subnormals (e = 0): (-1)^s 2^-6 (m / 8); e = 15, m = 7: NaN.
+    Pinned by closed-form values, torch's float8_e4m3fn conversion of all 256
+    codes and the count of finite codes.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(x):
+    """E4M3 code nearest to each value of x (ties to the even mantissa),
+    saturating at +-448; NaN gives 0x7F, the sign of zero is kept.
+
+    Written from the format: in the subnormal range (|x| < 2^-6) the code is
+    |x| / 2^-9 rounded; above it x = f 2^k with f in [1, 2), the mantissa is
+    (f - 1) 8 rounded, and a mantissa that rounds up to 8 moves to the next
+    exponent. Pinned by brute-force search for the nearest of the 254 finite
+    values, round trips of every code, torch's conversion inside the finite
+    range and the saturation values.
+    """
+    x = _f64(x)
+    # infinities and magnitudes past the range saturate like any |x| > 448
+    a = np.abs(np.where(np.isnan(x), 0.0, x))
+    a = np.minimum(a, 1024.0)
+    out = np.zeros(x.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    # subnormal range: integer multiples of 2^-9 (a result of 8 is the
+    # smallest normal, code 0x08, which the same formula gives)
+    out = np.where(sub, np.rint(a / 2.0 ** -9).astype(np.int64), out)
+    f, k = np.frexp(np.where(sub, 1.0, a))  # a = f 2^k, f in [0.5, 1)
+    f, k = 2.0 * f, k - 1                  # f in [1, 2)
+    m = np.rint((f - 1.0) * 8.0).astype(np.int64)
+    k = np.where(m == 8, k + 1, k)
+    m = np.where(m == 8, 0, m)
+    e = k + 7
+    normal = ((e << 3) | m).astype(np.int64)
+    normal = np.where((e > 15) | (normal > 0x7E), 0x7E, normal)  # saturate
+    out = np.where(sub, out, normal)
+    out = np.where(np.signbit(x), out | 0x80, out)
+    out = np.where(np.isnan(x), 0x7F, out)
+    return out.astype(np.uint8)
+
+
+def fp8_dequantize(codes, scale):
+    """Stored value of an fp8 cache entry: scale * e4m3(code), float64."""
+    return float(scale) * e4m3_decode(codes)
+
+
+def fp8_quantize(x, scale):
+    """Codes that an fp8 cache with this scale stores for the values x."""
+    return e4m3_encode(_f64(x) / float(scale))

@@ -17,6 +17,7 @@ import types
 import numpy as np
 import pytest
 
+from tests.test_oracle_fp8 import _samples, brute_encode, torch_values
 from tests.test_oracle_pins import _brute, rel, tiny
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
@@ -80,7 +81,23 @@ MUTATIONS = [
     ("prefill without alpha_kv",
      "                out[b, :L, h] += alpha_kv * ((e / e.sum(axis=1, keepdims=True)) @ V)",
      "                out[b, :L, h] += ((e / e.sum(axis=1, keepdims=True)) @ V)"),
+    ("e4m3 exponent bias 8", "np.exp2(e - 7.0)", "np.exp2(e - 8.0)"),
+    ("e4m3 subnormals one binade low",
+     "mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6,", "mag = np.where(e == 0, (m / 8.0) * 2.0 ** -7,"),
+    ("e4m3 encoder rounds ties away from zero",
+     "    m = np.rint((f - 1.0) * 8.0).astype(np.int64)",
+     "    m = np.floor((f - 1.0) * 8.0 + 0.5).astype(np.int64)"),
+    ("e4m3 encoder overflows to NaN instead of saturating",
+     "    normal = np.where((e > 15) | (normal > 0x7E), 0x7E, normal)  # saturate",
+     "    normal = np.where((e > 15) | (normal > 0x7E), 0x7F, normal)"),
+    ("e4m3 subnormal step 2^-10", "np.rint(a / 2.0 ** -9)", "np.rint(a / 2.0 ** -10)"),
+    ("e4m3 mantissa carry kept in the exponent",
+     "    k = np.where(m == 8, k + 1, k)\n", "    k = k\n"),
 ]
+
+# fp8 codec inputs: sampled values, every midpoint, saturating values
+FP8_X = _samples(7, 300)
+FP8_WANT = brute_encode(FP8_X)
 
 
 def load(source):
@@ -143,6 +160,14 @@ def check_errors(m):
             want_k[b, p, 2 * i + 1] = x0 * math.sin(a) + x1 * math.cos(a)
     errs["append"] = max(rel(c2, want_c), rel(k2, want_k),
                          0.0 if l2.tolist() == [1, 3, Lmax] else np.inf)
+    # fp8 codec: every code's value against torch's float8_e4m3fn, the
+    # encoder against the brute-force nearest-value search
+    want = torch_values()
+    got = m.e4m3_decode(np.arange(256, dtype=np.uint8))
+    ok = ~np.isnan(want)
+    errs["e4m3 decode"] = (rel(got[ok], want[ok])
+                           if np.array_equal(np.isnan(got), np.isnan(want)) else np.inf)
+    errs["e4m3 encode"] = float(np.count_nonzero(m.e4m3_encode(FP8_X) != FP8_WANT))
     return {k: (v if np.isfinite(v) else np.inf) for k, v in errs.items()}
 
 
