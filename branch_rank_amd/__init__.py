@@ -27,7 +27,7 @@ KERNELS = {"auto": MLRA_KERNEL_AUTO, "portable": MLRA_KERNEL_PORTABLE,
 
 EXPORTS = ("mlra_workspace_size", "mla_absorb_q", "mla_decode_attn", "mla_out_proj",
            "mlra_decode", "mlra_decode_noalloc", "mlra_select_decode_kernel",
-           "mlra_cache_append", "mlra_prefill",
+           "mlra_cache_append", "mlra_cache_append_fp8", "mlra_prefill",
            "mlra_set_kernel_timing", "mlra_status_string", "mlra_last_error_detail")
 
 
@@ -51,7 +51,9 @@ class Cache(ctypes.Structure):
     _fields_ = [("ckv", ctypes.c_void_p), ("krope", ctypes.c_void_p),
                 ("ckv_batch_stride", ctypes.c_int64), ("ckv_token_stride", ctypes.c_int64),
                 ("krope_batch_stride", ctypes.c_int64), ("krope_token_stride", ctypes.c_int64),
-                ("cache_lens", ctypes.c_void_p), ("max_len", ctypes.c_int32)]
+                ("cache_lens", ctypes.c_void_p), ("max_len", ctypes.c_int32),
+                ("fp8", ctypes.c_int32), ("ckv_scale", ctypes.c_float),
+                ("krope_scale", ctypes.c_float)]
 
 
 _lib = None
@@ -77,6 +79,9 @@ def lib():
         "mlra_select_decode_kernel": [CP, I32, KP, ctypes.POINTER(ctypes.c_int)],
         "mlra_cache_append": [CP, I32, P, P, ctypes.c_float, P, P, ctypes.c_int64,
                               ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, I32, P],
+        "mlra_cache_append_fp8": [CP, I32, P, P, ctypes.c_float, P, P, ctypes.c_int64,
+                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, I32,
+                                  ctypes.c_float, ctypes.c_float, P],
         "mlra_prefill": [CP, I32, I32, P, P, P, P, KP, P, ctypes.c_int, P],
         "mlra_set_kernel_timing": [P, P],
         "mlra_status_string": [ctypes.c_int],
@@ -158,24 +163,29 @@ def _stream(stream):
     return getattr(stream, "cuda_stream", stream)
 
 
-def cache_view(ckv, krope, cache_lens, cfg):
+def cache_view(ckv, krope, cache_lens, cfg, fp8_scales=None):
     """Strided cache view from tensors ckv [B, L_max, d_c] and krope
     [B, L_max, d_r] (views into one interleaved buffer are fine; the last
-    dimension must be dense) and cache_lens [B] int32."""
+    dimension must be dense) and cache_lens [B] int32. With
+    fp8_scales = (ckv_scale, krope_scale) the tensors are uint8 FP8 E4M3
+    codes of a quantised cache (values scale * e4m3(code))."""
     t = _torch()
     B, Lmax, dc = ckv.shape
     if dc != cfg.d_latent or tuple(krope.shape) != (B, Lmax, cfg.d_rope):
         raise ValueError("cache shapes do not match the config")
+    want = t.uint8 if fp8_scales is not None else _dtype(cfg)
     for x, name in ((ckv, "ckv"), (krope, "krope")):
-        if x.dtype != _dtype(cfg) or not x.is_cuda:
+        if x.dtype != want or not x.is_cuda:
             raise ValueError(f"{name}: wrong dtype or device")
         if x.stride(2) != 1 and x.shape[2] > 1:
             raise ValueError(f"{name}: last dimension must be dense")
         if x.stride(0) < 0 or x.stride(1) < 1:
             raise ValueError(f"{name}: bad strides")
     _need(cache_lens, "cache_lens", (B,), t.int32)
+    fp8 = fp8_scales is not None
+    sc, sr = (float(fp8_scales[0]), float(fp8_scales[1])) if fp8 else (1.0, 1.0)
     c = Cache(ckv.data_ptr(), krope.data_ptr(), ckv.stride(0), ckv.stride(1), krope.stride(0),
-              krope.stride(1), cache_lens.data_ptr(), Lmax)
+              krope.stride(1), cache_lens.data_ptr(), Lmax, int(fp8), sc, sr)
     c._keep = (ckv, krope, cache_lens)  # keep the tensors alive with the view
     c._batch = B
     return c
@@ -201,6 +211,29 @@ def cache_append(cfg, new_rows, ckv, krope, cache_lens, gain=None, eps=1e-6, str
     check(lib().mlra_cache_append(ctypes.byref(cfg), B, rows, g, float(eps), ckv.data_ptr(),
                                   krope.data_ptr(), ckv.stride(0), ckv.stride(1),
                                   krope.stride(0), krope.stride(1), lens, Lmax, _stream(stream)))
+
+
+def cache_append_fp8(cfg, new_rows, ckv, krope, cache_lens, ckv_scale, krope_scale, gain=None,
+                     eps=1e-6, stream=None):
+    """cache_append into a quantised cache: ckv [B, L_max, d_c] and krope
+    [B, L_max, d_r] uint8 FP8 E4M3 codes; each value is stored as the code
+    nearest value / scale (mlra_cache_append_fp8)."""
+    t = _torch()
+    B, Lmax, dc = ckv.shape
+    if dc != cfg.d_latent or tuple(krope.shape) != (B, Lmax, cfg.d_rope):
+        raise ValueError("cache shapes do not match the config")
+    for x, name in ((ckv, "ckv"), (krope, "krope")):
+        if x.dtype != t.uint8 or not x.is_cuda:
+            raise ValueError(f"{name}: wrong dtype or device")
+        if x.stride(2) != 1 and x.shape[2] > 1:
+            raise ValueError(f"{name}: last dimension must be dense")
+    rows = _need(new_rows, "new_rows", (B, cfg.d_latent + cfg.d_rope), t.float32)
+    g = _need(gain, "gain", (cfg.d_latent,), t.float32) if gain is not None else None
+    lens = _need(cache_lens, "cache_lens", (B,), t.int32)
+    check(lib().mlra_cache_append_fp8(ctypes.byref(cfg), B, rows, g, float(eps), ckv.data_ptr(),
+                                      krope.data_ptr(), ckv.stride(0), ckv.stride(1),
+                                      krope.stride(0), krope.stride(1), lens, Lmax,
+                                      float(ckv_scale), float(krope_scale), _stream(stream)))
 
 
 def select_decode_kernel(cfg, cache):

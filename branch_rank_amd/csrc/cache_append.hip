@@ -9,6 +9,10 @@
 // cached): for sequence b with L_b tokens, row L_b of the cache receives
 // [RMSNorm(c) * gain || RoPE(k^R, L_b)] in the cache dtype and L_b becomes
 // L_b + 1. A sequence already holding max_len tokens is left unchanged.
+// An fp8 cache stores the E4M3 code nearest value / scale (ties to the even
+// mantissa, saturating at +-448), one scale per cache tensor
+// ("MLA多头潜在注意力机制", 9.2: an 8-bit cache for inference; the format and
+// the scale convention are this library's reading).
 //
 // One workgroup per sequence; the bytes are a few KB per step, so this is a
 // latency-bound kernel, not a streaming one.
@@ -20,8 +24,36 @@
 namespace mlra {
 namespace {
 
-__device__ __forceinline__ void store_as(float* p, float v) { *p = v; }
-__device__ __forceinline__ void store_as(__bf16* p, float v) { *p = (__bf16)v; }
+// E4M3 code of x: round to nearest, ties to the even mantissa, saturating at
+// +-448 (NaN gives 0x7F). Below 2^-6 the codes are the multiples of 2^-9;
+// above, adding 2^19 - 1 plus the lowest kept bit to the fp32 bits and
+// dropping 20 mantissa bits rounds to 3 mantissa bits, a carry moving into
+// the exponent, and the exponent's bias moves from 127 to 7.
+__device__ __forceinline__ uint8_t e4m3_code(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  if (__builtin_isnan(x)) return 0x7F;
+  const float a = fabsf(x);
+  uint32_t c;
+  if (a < 0.015625f) {
+    c = (uint32_t)rintf(a * 512.f);  // exact scaling; rintf rounds half to even
+  } else if (a >= 448.f) {
+    c = 0x7E;
+  } else {
+    const uint32_t v = u & 0x7FFFFFFFu;
+    const uint32_t r = (v + 0x7FFFFu + ((v >> 20) & 1u)) >> 20;
+    c = r - ((127u - 7u) << 3);
+    if (c > 0x7Eu) c = 0x7E;
+  }
+  return (uint8_t)(c | sign);
+}
+
+// value v of a cache entry scaled by 1 / scale (fp8 only)
+__device__ __forceinline__ void store_as(float* p, float v, float) { *p = v; }
+__device__ __forceinline__ void store_as(__bf16* p, float v, float) { *p = (__bf16)v; }
+__device__ __forceinline__ void store_as(uint8_t* p, float v, float scale) {
+  *p = e4m3_code(v / scale);
+}
 
 template <typename T>
 __global__ __launch_bounds__(256) void cache_append_kernel(AppendArgs a, RopeFreqs fr) {
@@ -60,7 +92,7 @@ __global__ __launch_bounds__(256) void cache_append_kernel(AppendArgs a, RopeFre
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int i = tid + 256 * u;
-    if (i < a.d_c) store_as(c + i, xv[u] * inv * gv[u]);
+    if (i < a.d_c) store_as(c + i, xv[u] * inv * gv[u], a.ckv_scale);
   }
   // RoPE key rotated to position p: the angle p * theta^(-2i/d_r) (frequency
   // from the host's table), its reduction to [-pi, pi] and its sine and
@@ -72,19 +104,21 @@ __global__ __launch_bounds__(256) void cache_append_kernel(AppendArgs a, RopeFre
     double sn, cs;
     sincos(r, &sn, &cs);
     const double x0 = k0, x1 = k1;
-    store_as(k + 2 * tid, (float)(x0 * cs - x1 * sn));
-    store_as(k + 2 * tid + 1, (float)(x0 * sn + x1 * cs));
+    store_as(k + 2 * tid, (float)(x0 * cs - x1 * sn), a.kr_scale);
+    store_as(k + 2 * tid + 1, (float)(x0 * sn + x1 * cs), a.kr_scale);
   }
   if (tid == 0) a.lens[b] = p + 1;
 }
 
 }  // namespace
 
-hipError_t launch_cache_append(const AppendArgs& a, bool bf16, int batch, hipStream_t s) {
+hipError_t launch_cache_append(const AppendArgs& a, CacheElt elt, int batch, hipStream_t s) {
   if (batch <= 0) return hipSuccess;
   const RopeFreqs& fr = rope_freqs(a.theta, a.d_r);
-  if (bf16)
+  if (elt == CacheElt::kBF16)
     hipLaunchKernelGGL(cache_append_kernel<__bf16>, dim3(batch), dim3(256), 0, s, a, fr);
+  else if (elt == CacheElt::kFP8)
+    hipLaunchKernelGGL(cache_append_kernel<uint8_t>, dim3(batch), dim3(256), 0, s, a, fr);
   else
     hipLaunchKernelGGL(cache_append_kernel<float>, dim3(batch), dim3(256), 0, s, a, fr);
   return hipGetLastError();

@@ -59,14 +59,22 @@ namespace {
 using namespace dev;
 using namespace bt;
 
-template <int NBR, int NSPLIT, int HPW, int NHG, int NS, bool QLO>
+template <int NBR, int NSPLIT, int HPW, int NHG, int NS, bool QLO, bool FP8>
 __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_kernel(DecodeParams p) {
   using C = BCfg<NBR, NSPLIT, HPW, NHG>;
   constexpr int H = C::H;
   constexpr int DC = C::DC;
   constexpr int D = NS - 1;  // tiles issued ahead of the one in use
   static_assert(D >= 2 && D <= 6, "tile ring");
-  __shared__ __attribute__((aligned(1024))) char smem_raw[NS * C::STAGE];
+  // fp8 codes: a stage holds the tile's codes row after row (the branch
+  // pair's 256 latent codes per row, then the 64 RoPE codes), unswizzled,
+  // 10 KB; each lane converts the 16 codes it loaded into one of two bf16
+  // tiles (the one in use and the next) laid out as the bf16 stages.
+  static_assert(!FP8 || (C::ROWB == 512 && C::NW == 8), "fp8: two branches per workgroup, 8 waves");
+  constexpr int LAT8 = kT * C::ROWB / 2;
+  constexpr int STAGE8 = LAT8 + kT * kDR;
+  constexpr int RING = FP8 ? 2 * C::STAGE + NS * STAGE8 : NS * C::STAGE;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[RING];
   char LDS_AS* smem = (char LDS_AS*)smem_raw;
   const uint32_t sbase = (uint32_t)(uintptr_t)smem;
 
@@ -128,10 +136,17 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
     const int seg_end = min(end, p.prefix[bseq + 1]);
     const int t0 = start - p.prefix[bseq], t1 = seg_end - p.prefix[bseq];
     const int ntiles = (t1 - t0 + kT - 1) / kT;
-    const i32x4 crs = seq_rsrc(p.ckv + (int64_t)bseq * p.ckv_bs, t1, p.ckv_ts);
-    const i32x4 krs = seq_rsrc(p.krope + (int64_t)bseq * p.kr_bs, t1, p.kr_ts);
+    constexpr int EB = FP8 ? 1 : 2;  // cache bytes per element
+    const i32x4 crs = seq_rsrc_bytes((const char*)p.ckv + (int64_t)bseq * p.ckv_bs * EB, t1,
+                                     p.ckv_ts * EB);
+    const i32x4 krs = seq_rsrc_bytes((const char*)p.krope + (int64_t)bseq * p.kr_bs * EB, t1,
+                                     p.kr_ts * EB);
     const int slot = k + bseq;
     const uint32_t lat_voff = (uint32_t)(lat_row * p.ckv_ts * 2 + lat_c);
+    // fp8 latent instruction `wave`: rows 4 wave .. + 3 of the tile, lane l
+    // row 4 wave + l / 16, codes hg 256 + 16 (l % 16) .. of it
+    const int lat8_c = hg * 256 + 16 * (lane & 15);
+    const uint32_t lat8_voff = (uint32_t)((lane >> 4) * p.ckv_ts + lat8_c);
 
     // earlier stores and loads of this wave done; all waves left the
     // previous segment's LDS tiles
@@ -163,9 +178,73 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
     // needed inside the tile loop (it would also drain the DMA)
     wait_vm<0>();
     // LDS byte offset of a tile's stage, advanced one tile at a time
-    auto next_stage = [](int off) { return off + C::STAGE == NS * C::STAGE ? 0 : off + C::STAGE; };
+    // (fp8: the tiles read by the phases alternate between the two bf16
+    // tiles, the loads go round the ring of code stages after them)
+    auto next_stage = [](int off) {
+      if constexpr (FP8) return off ^ C::STAGE;
+      return off + C::STAGE == NS * C::STAGE ? 0 : off + C::STAGE;
+    };
+    auto next_ring = [&](int off) {
+      if constexpr (FP8) return off + STAGE8 == NS * STAGE8 ? 0 : off + STAGE8;
+      return next_stage(off);
+    };
     int dma_off = 0;  // stage of the next tile to load
+    // fp8: DMA of a tile's codes; the latent rows of the segment's last tile
+    // are clamped per lane
+    auto issue8 = [&](int tile, bool tail) {
+      const uint32_t sa = sbase + 2 * C::STAGE + dma_off;
+      dma_off = next_ring(dma_off);
+      const int ts0 = t0 + tile * kT;
+      if (!tail) {
+        dma16_stream(crs, sa + wave * 1024, lat8_voff, (uint32_t)((ts0 + 4 * wave) * p.ckv_ts));
+      } else {
+        const int row = min(ts0 + 4 * wave + (lane >> 4), t1 - 1);
+        dma16_stream(crs, sa + wave * 1024, (uint32_t)(row * p.ckv_ts + lat8_c), 0u);
+      }
+      if (wave < 2) {
+        const int row = min(ts0 + 16 * wave + (lane >> 2), t1 - 1);
+        dma16_stream(krs, sa + LAT8 + wave * 1024, (uint32_t)(row * p.kr_ts + 16 * (lane & 3)),
+                     0u);
+      }
+    };
+    // fp8: this lane's codes of the next tile to convert, into its bf16 tile
+    // (the swizzles of the bf16 stages: latent row t's codes 16 cc .. are
+    // chunks 2 cc, 2 cc + 1, at 2 (cc ^ (t & 15)) and the next; RoPE row t's
+    // chunk c at c ^ swz_r(t)). The offsets come from an opaque copy of the
+    // lane id, so that they are recomputed instead of kept live (spilled).
+    int cv_off = 0, cv_buf = 0;
+    auto convert8 = [&]() {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const char LDS_AS* src = smem + 2 * C::STAGE + cv_off + 16 * ln;
+      char LDS_AS* dst = smem + cv_buf;
+      cv_off = next_ring(cv_off);
+      cv_buf ^= C::STAGE;
+      const i32x4 x = *(const i32x4 LDS_AS*)(src + wave * 1024);
+      i32x4 r;
+      if (wave < 2) r = *(const i32x4 LDS_AS*)(src + LAT8 + wave * 1024);
+      {
+        const int t = 4 * wave + (ln >> 4), cc = ln & 15;
+        i32x4 lo, hi;
+        fp8x16_to_bf16(x, lo, hi);
+        char LDS_AS* d = dst + t * C::ROWB + 32 * (cc ^ (t & 15));
+        *(i32x4 LDS_AS*)d = lo;
+        *(i32x4 LDS_AS*)(d + 16) = hi;
+      }
+      if (wave < 2) {
+        const int t = 16 * wave + (ln >> 2), cc = ln & 3;
+        i32x4 lo, hi;
+        fp8x16_to_bf16(r, lo, hi);
+        char LDS_AS* d = dst + C::LAT + t * 128;
+        *(i32x4 LDS_AS*)(d + 16 * ((2 * cc) ^ swz_r(t))) = lo;
+        *(i32x4 LDS_AS*)(d + 16 * ((2 * cc + 1) ^ swz_r(t))) = hi;
+      }
+    };
     auto issue = [&](int tile) {
+      if constexpr (FP8) {
+        issue8(tile, t0 + tile * kT + kT > t1);
+        return;
+      }
       const uint32_t sa = sbase + dma_off;
       dma_off = next_stage(dma_off);
       const int ts0 = t0 + tile * kT;
@@ -213,21 +292,45 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
     // exist to keep MFMA and VALU work apart), and no LDS access moves over it
     auto bar = [] {
       __builtin_amdgcn_sched_barrier(0);
+      // fp8: this wave's converted tile written (s_barrier does not wait)
+      if constexpr (FP8) wait_lgkm0();
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
     };
-    auto wait_tile = [&](int t) { wait_tiles<C, NS - 2>(min(NS - 2, ntiles - 1 - t), wave); };
+    // wait for this wave's loads of tile t (fp8: two instructions per tile on
+    // waves 0 and 1, one on the others), then (fp8) convert its codes
+    auto wait_tile = [&](int t) {
+      if constexpr (FP8) {
+        if (wave < 2) wait_tiles_per<2, NS - 2>(min(NS - 2, ntiles - 1 - t));
+        else wait_tiles_per<1, NS - 2>(min(NS - 2, ntiles - 1 - t));
+        asm volatile("" ::: "memory");
+        convert8();
+      } else {
+        wait_tiles<C, NS - 2>(min(NS - 2, ntiles - 1 - t), wave);
+      }
+    };
     auto issue_if = [&](int t) {
       if (t < ntiles) issue(t);
     };
     // steady tiles (1 <= t < ntiles - D - 1): the wait keeps NS - 2 tiles in
     // flight, the tile loaded is full and not the last, and no row is masked
     auto wait_steady = [&] {
+      if constexpr (FP8) {
+        if (wave < 2) wait_vm<(NS - 2) * 2>();
+        else wait_vm<(NS - 2) * 1>();
+        asm volatile("" ::: "memory");
+        convert8();
+        return;
+      }
       if (wave < C::NR) wait_vm<(NS - 2) * (C::NL / C::NW + 1)>();
       else wait_vm<(NS - 2) * (C::NL / C::NW)>();
     };
     auto issue_full = [&](int tile) {
+      if constexpr (FP8) {
+        issue8(tile, false);
+        return;
+      }
       const uint32_t sa = sbase + dma_off;
       dma_off = next_stage(dma_off);
       issue_tile<C, false>(sa, crs, krs, p.ckv_ts, p.kr_ts, t0 + tile * kT, t1, wave, lane, lat_voff,
@@ -429,7 +532,7 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
   }
 }
 
-template <int NBR, int NSPLIT, int HPW, int NHG, bool QLO>
+template <int NBR, int NSPLIT, int HPW, int NHG, bool QLO, bool FP8 = false>
 hipError_t launch_b(const Geom& g, const QView& q, const void* ckv, const void* krope,
                     const Workspace& ws, int items, hipStream_t s, const KernelTiming& t) {
   using C = BCfg<NBR, NSPLIT, HPW, NHG>;
@@ -454,7 +557,7 @@ hipError_t launch_b(const Geom& g, const QView& q, const void* ckv, const void* 
   p.B = g.B;
   int grid = items;
   if (NSPLIT > 1) grid = ((items + 7) / 8) * 8 * NSPLIT;  // whole XCD rounds
-  hipExtLaunchKernelGGL((decode_branch_kernel<NBR, NSPLIT, HPW, NHG, NS, QLO>), dim3(grid),
+  hipExtLaunchKernelGGL((decode_branch_kernel<NBR, NSPLIT, HPW, NHG, NS, QLO, FP8>), dim3(grid),
                         dim3(64 * C::NW), 0, s, t.start, t.stop, 0, p);
   return hipGetLastError();
 }
@@ -464,8 +567,9 @@ hipError_t launch_b(const Geom& g, const QView& q, const void* ckv, const void* 
 // MLRA-4 with 128-wide branches (two workgroups per item, one per branch
 // pair) and one such branch alone, a tensor-parallel shard (one workgroup
 // per item).
-bool decode_branch_supported(const Geom& g) {
+bool decode_branch_supported(const Geom& g, bool fp8) {
   if (g.dr != kDR) return false;
+  if (fp8) return g.dc == 4 * kBW && g.n == 4 && g.H == 128;
   if (g.dc == 4 * kBW && g.n == 4) return g.H == 64 || g.H == 128;
   return g.dc == kBW && g.n == 1 && g.H == 128;
 }
@@ -477,8 +581,8 @@ bool decode_branch_reads_residue(const Geom& g) { return g.n == 1; }
 
 hipError_t launch_decode_branch(const Geom& g, const QView& q, const void* ckv,
                                 const void* krope, const Workspace& ws, int items,
-                                hipStream_t s, const KernelTiming& t) {
-  if (!decode_branch_supported(g)) return hipErrorNotSupported;
+                                hipStream_t s, const KernelTiming& t, bool fp8) {
+  if (!decode_branch_supported(g, fp8)) return hipErrorNotSupported;
   // one branch alone (a tensor-parallel shard) is one softmax over the
   // branch: a bf16 query alone moves its output rows by up to ~1.1e-2 at the
   // pages' scales, so the shard adds q~'s residue when the view has it. With
@@ -488,6 +592,7 @@ hipError_t launch_decode_branch(const Geom& g, const QView& q, const void* ckv,
     if (q.lo > 0) return launch_b<1, 1, 16, 8, true>(g, q, ckv, krope, ws, items, s, t);
     return launch_b<1, 1, 16, 8, false>(g, q, ckv, krope, ws, items, s, t);
   }
+  if (fp8) return launch_b<4, 2, 32, 4, false, true>(g, q, ckv, krope, ws, items, s, t);
   if (g.H == 64) return launch_b<4, 2, 16, 4, false>(g, q, ckv, krope, ws, items, s, t);
   return launch_b<4, 2, 32, 4, false>(g, q, ckv, krope, ws, items, s, t);
 }

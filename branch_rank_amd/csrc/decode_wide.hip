@@ -75,6 +75,11 @@ constexpr int kNI = kT + 4;              // DMA instructions per tile (32 latent
 constexpr int kKS = kDC / 32;            // latent k-steps
 constexpr int kHB = kH / 16;             // 16-head blocks
 constexpr int kNS = 4;                   // tile stages (144 KB of LDS)
+// fp8 codes: 18 KB per stage, 16 latent DMA instructions (two rows each) and
+// two RoPE instructions (16 rows each) per tile
+constexpr int kLat8 = kT * kDC;
+constexpr int kStage8 = kLat8 + kT * kDR;
+constexpr int kLR8 = kT / 2;
 
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 
@@ -125,7 +130,7 @@ struct WCfg {
   static_assert(HPW % 16 == 0 && CPW % 16 == 0 && kT % NW == 0 && NW >= 4, "wave shape");
 };
 
-template <int NB, bool F16, int NW>
+template <int NB, bool F16, int NW, bool FP8>
 __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p) {
   using O_ = Op<F16>;
   using V = typename O_::V;
@@ -135,17 +140,21 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
   constexpr int KPB = kKS / NB;  // latent k-steps per branch
   constexpr float kRescale = F16 ? 15.f : 16.f;
   static_assert(kKS % NB == 0, "branches");
+  static_assert(!FP8 || F16, "fp8 codes are converted to fp16");
 
-  // LDS: the tile ring, then the P exchange (P^T fragments of NB branches x
+  // LDS: the tile ring (bf16: kNS stages of 36 KB, converted in place; fp8:
+  // two 36 KB fp16 tiles, the one in use and the next, then kNS stages of
+  // 18 KB of codes), then the P exchange (P^T fragments of NB branches x
   // eight 16-head blocks, 1 KB each: lane l's 16 bytes at 16 l, the B-operand
   // layout), the rescale factors per (branch, head) and one flag per (wave,
   // branch) that says whether any of its heads' references moved
   constexpr int kPBytes = NB * kHB * 1024;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[kNS * kStage + kPBytes];
+  constexpr int kRing = FP8 ? 2 * kStage + kNS * kStage8 : kNS * kStage;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kRing + kPBytes];
   __shared__ float fl_raw[NB * kH];
   __shared__ int flags_raw[NW * NB];
   char LDS_AS* smem = (char LDS_AS*)smem_raw;
-  char LDS_AS* pl = smem + kNS * kStage;
+  char LDS_AS* pl = smem + kRing;
   float LDS_AS* fl = (float LDS_AS*)fl_raw;
   int LDS_AS* flags = (int LDS_AS*)flags_raw;
   const uint32_t sbase = (uint32_t)(uintptr_t)smem;
@@ -164,11 +173,19 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
   // offset) and, for w < 4, RoPE rows 8 w .. 8 w + 7 (lane l: row 8 w + l / 8,
   // LDS chunk l % 8, global chunk (l % 8) ^ swz_r(row)). The DMA writes lane
   // l's 16 bytes at a wave-uniform LDS offset + 16 l.
-  const bool rope_wave = wave < 4;
+  //
+  // fp8: a stage holds the codes row after row (latent rows of 512 bytes,
+  // then RoPE rows of 64), unswizzled: wave w loads latent rows 2 q, 2 q + 1
+  // for q = w + NW u (u < 16 / NW; lane l: row 2 q + l / 32, bytes
+  // 16 (l % 32) of it) and, for w < 2, RoPE rows 16 w .. 16 w + 15 (lane l:
+  // row 16 w + l / 4, bytes 16 (l % 4)); rows are clamped per lane. Each lane
+  // later converts the 16 codes it loaded into the swizzled fp16 tile.
+  const bool rope_wave = FP8 ? wave < 2 : wave < 4;
   auto lat_lds = [&](int u) { return (uint32_t)((wave + NW * u) * 1024); };
-  const uint32_t rope_lds = (uint32_t)(kLat + wave * 1024);
-  const int rope_rt = 8 * wave + (lane >> 3);
-  const uint32_t rope_c = (uint32_t)(16 * ((lane & 7) ^ swz_r(rope_rt)));
+  const uint32_t rope_lds = (uint32_t)((FP8 ? kLat8 : kLat) + wave * 1024);
+  const int rope_rt = FP8 ? 16 * wave + (lane >> 2) : 8 * wave + (lane >> 3);
+  const uint32_t rope_c = FP8 ? (uint32_t)(16 * (lane & 3))
+                              : (uint32_t)(16 * ((lane & 7) ^ swz_r(rope_rt)));
   // QK A fragments: row 16 mb + l16, logical chunk 4 ks + kg, physical chunk
   // (4 ks + kg) ^ 2 l16 = 4 ks ^ (kg ^ 2 l16); the XOR touches address bits
   // 6-9 only, which the lane base and every stage base leave zero.
@@ -188,8 +205,12 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
     const int seg_end = min(end, p.prefix[bseq + 1]);
     const int t0 = start - p.prefix[bseq], t1 = seg_end - p.prefix[bseq];
     const int ntiles = (t1 - t0 + kT - 1) / kT;
-    const i32x4 crs = seq_rsrc(p.ckv + (int64_t)bseq * p.ckv_bs, t1, p.ckv_ts);
-    const i32x4 krs = seq_rsrc(p.krope + (int64_t)bseq * p.kr_bs, t1, p.kr_ts);
+    // cache bytes per element: 2 (bf16) or 1 (fp8 codes)
+    constexpr int EB = FP8 ? 1 : 2;
+    const i32x4 crs = seq_rsrc_bytes((const char*)p.ckv + (int64_t)bseq * p.ckv_bs * EB, t1,
+                                     p.ckv_ts * EB);
+    const i32x4 krs = seq_rsrc_bytes((const char*)p.krope + (int64_t)bseq * p.kr_bs * EB, t1,
+                                     p.kr_ts * EB);
     const int slot = k + bseq;
 
     // earlier stores and loads of this wave done; all waves left the
@@ -236,8 +257,21 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
     // DMA instruction u of this wave for `tile`; the segment's last tile
     // clamps its rows to t1 - 1 (the segment's rows bound the buffer range)
     auto issue = [&](int tile) {
-      const uint32_t sa = sbase + (uint32_t)((tile & (kNS - 1)) * kStage);
       const int ts0 = t0 + tile * kT;
+      if constexpr (FP8) {
+        const uint32_t sa = sbase + (uint32_t)(2 * kStage + (tile & (kNS - 1)) * kStage8);
+#pragma unroll
+        for (int u = 0; u < kLR8 / NW; ++u) {
+          const int row = min(ts0 + 2 * (wave + NW * u) + (lane >> 5), t1 - 1);
+          dma16_stream(crs, sa + lat_lds(u), (uint32_t)(row * p.ckv_ts + 16 * (lane & 31)), 0u);
+        }
+        if (rope_wave) {
+          const int row = min(ts0 + rope_rt, t1 - 1);
+          dma16_stream(krs, sa + rope_lds, (uint32_t)(row * p.kr_ts) + rope_c, 0u);
+        }
+        return;
+      }
+      const uint32_t sa = sbase + (uint32_t)((tile & (kNS - 1)) * kStage);
 #pragma unroll
       for (int u = 0; u < C::LR; ++u) {
         const int qi = wave + NW * u;
@@ -253,7 +287,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
     // wait until this wave's DMA of `tile` has landed, given the tiles
     // issued after it that may stay in flight (at most kNS - 2)
     auto wait_own = [&](int tile) {
-      constexpr int H = C::LR + 1, L = C::LR;
+      constexpr int L = FP8 ? kLR8 / NW : C::LR, H = L + 1;
       const int after = min(tile + kNS - 2, ntiles - 1) - tile;
       if (rope_wave) {
         if (after >= 2) wait_vm<2 * H>();
@@ -266,8 +300,44 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
       }
       asm volatile("" ::: "memory");
     };
-    // this lane's 16-byte chunks of `tile` from bf16 to fp16, in place
+    // this lane's 16-byte chunks of `tile` from bf16 to fp16, in place; fp8:
+    // its 16 codes per instruction into the fp16 tile (tile & 1), swizzled
+    // as the bf16 tiles: latent row t, codes 16 cc .. 16 cc + 15 are fp16
+    // chunks 2 cc, 2 cc + 1, at chunks 2 (cc ^ (t & 15)) and the next (one
+    // 32-byte store); RoPE row t's chunks 2 cc, 2 cc + 1 at (2 cc) ^ swz_r(t)
+    // and (2 cc + 1) ^ swz_r(t)
     auto convert = [&](int tile) {
+      if constexpr (FP8) {
+        // the lane's offsets are recomputed here from an opaque copy of the
+        // lane id: kept live across the loop they would be spilled, and a
+        // reload waits for every load in flight, the DMA included
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const char LDS_AS* src = smem + 2 * kStage + (tile & (kNS - 1)) * kStage8 + 16 * ln;
+        char LDS_AS* dst = smem + (tile & 1) * kStage;
+        i32x4 x[kLR8 / NW], r;
+#pragma unroll
+        for (int u = 0; u < kLR8 / NW; ++u) x[u] = *(const i32x4 LDS_AS*)(src + lat_lds(u));
+        if (rope_wave) r = *(const i32x4 LDS_AS*)(src + kLat8 + wave * 1024);
+#pragma unroll
+        for (int u = 0; u < kLR8 / NW; ++u) {
+          const int tr = 2 * (wave + NW * u) + (ln >> 5), cc = ln & 31;
+          i32x4 lo, hi;
+          fp8x16_to_f16(x[u], lo, hi);
+          char LDS_AS* d = dst + tr * 1024 + 32 * (cc ^ (tr & 15));
+          *(i32x4 LDS_AS*)d = lo;
+          *(i32x4 LDS_AS*)(d + 16) = hi;
+        }
+        if (rope_wave) {
+          const int cc = ln & 3, rt = 16 * wave + (ln >> 2);
+          i32x4 lo, hi;
+          fp8x16_to_f16(r, lo, hi);
+          char LDS_AS* d = dst + kLat + rt * 128;
+          *(i32x4 LDS_AS*)(d + 16 * ((2 * cc) ^ swz_r(rt))) = lo;
+          *(i32x4 LDS_AS*)(d + 16 * ((2 * cc + 1) ^ swz_r(rt))) = hi;
+        }
+        return;
+      }
       char LDS_AS* st = smem + (tile & (kNS - 1)) * kStage + 16 * lane;
       i32x4 x[C::LR], r;
 #pragma unroll
@@ -316,7 +386,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
       if constexpr (!F16) wait_own(t);
       barrier();  // tile t in LDS (converted); P V of tile t - 1 done
       if (t + kNS - 1 < ntiles) issue(t + kNS - 1);
-      const char LDS_AS* st = smem + (t & (kNS - 1)) * kStage;
+      const char LDS_AS* st = smem + (FP8 ? (t & 1) : (t & (kNS - 1))) * kStage;
 
       // score bias per token row: 0, or -inf past the segment's end
       f32x4 bias[2];
@@ -511,7 +581,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
   }
 }
 
-template <int NB, bool F16, int NW>
+template <int NB, bool F16, int NW, bool FP8>
 hipError_t launch_w(const Geom& g, const QView& q, const void* ckv, const void* krope,
                     const Workspace& ws, int items, hipStream_t s, const KernelTiming& t) {
   DecodeParams p;
@@ -530,7 +600,7 @@ hipError_t launch_w(const Geom& g, const QView& q, const void* ckv, const void* 
   p.l = ws.l;
   p.acc = ws.acc;
   p.B = g.B;
-  hipExtLaunchKernelGGL((decode_wide_kernel<NB, F16, NW>), dim3(items), dim3(64 * NW), 0, s,
+  hipExtLaunchKernelGGL((decode_wide_kernel<NB, F16, NW, FP8>), dim3(items), dim3(64 * NW), 0, s,
                         t.start, t.stop, 0, p);
   return hipGetLastError();
 }
@@ -541,7 +611,7 @@ hipError_t launch_w(const Geom& g, const QView& q, const void* ckv, const void* 
 // kernel is written for n branches with a shared RoPE score; only n = 1 is
 // built, with the MFMAs' results selected into VGPRs: this compiler's pass
 // that moves them to AGPRs fails on a four-branch instantiation.)
-bool decode_wide_supported(const Geom& g) {
+bool decode_wide_supported(const Geom& g, bool) {
   return g.dc == kDC && g.dr == kDR && g.H == kH && g.n == 1;
 }
 
@@ -550,9 +620,10 @@ bool decode_wide_reads_residue(const Geom&) { return true; }
 
 hipError_t launch_decode_wide(const Geom& g, const QView& q, const void* ckv, const void* krope,
                               const Workspace& ws, int items, hipStream_t s,
-                              const KernelTiming& t) {
-  if (!decode_wide_supported(g)) return hipErrorNotSupported;
-  return launch_w<1, true, MLRA_WIDE_WAVES>(g, q, ckv, krope, ws, items, s, t);
+                              const KernelTiming& t, bool fp8) {
+  if (!decode_wide_supported(g, fp8)) return hipErrorNotSupported;
+  if (fp8) return launch_w<1, true, MLRA_WIDE_WAVES, true>(g, q, ckv, krope, ws, items, s, t);
+  return launch_w<1, true, MLRA_WIDE_WAVES, false>(g, q, ckv, krope, ws, items, s, t);
 }
 
 }  // namespace mlra

@@ -48,14 +48,50 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 
 // Raw buffer descriptor (gfx9 layout: base, stride 0, byte range, word 3)
 // over one sequence's rows [0, rows).
-__device__ __forceinline__ i32x4 seq_rsrc(const __bf16* base, int rows, int ts) {
+__device__ __forceinline__ i32x4 seq_rsrc_bytes(const void* base, int rows, int ts_bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   i32x4 r;  // wave-uniform values, made explicit for the SGPR operands
   r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
   r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
-  r.z = __builtin_amdgcn_readfirstlane(rows * ts * 2);
+  r.z = __builtin_amdgcn_readfirstlane(rows * ts_bytes);
   r.w = 0x00020000;
   return r;
+}
+// the same for bf16 rows of ts elements
+__device__ __forceinline__ i32x4 seq_rsrc(const __bf16* base, int rows, int ts) {
+  return seq_rsrc_bytes(base, rows, ts * 2);
+}
+
+// 16 FP8 E4M3 codes (16 bytes, element i in byte i) to 16 exact fp16 values
+// (two 16-byte halves: elements 0-7, then 8-15): v_cvt_scalef32_pk_f16_fp8
+// with scale 1 turns two codes into two fp16 values. E4M3's range and its 3
+// mantissa bits fit fp16's normals and subnormals, so nothing rounds.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void fp8x16_to_f16(i32x4 x, i32x4& lo, i32x4& hi) {
+  int r[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const f16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)x[w], 1.0f, false);
+    const f16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)x[w], 1.0f, true);
+    r[2 * w] = __builtin_bit_cast(int, a);
+    r[2 * w + 1] = __builtin_bit_cast(int, b);
+  }
+  lo = (i32x4){r[0], r[1], r[2], r[3]};
+  hi = (i32x4){r[4], r[5], r[6], r[7]};
+}
+// the same to bf16 (E4M3 fits bf16 exactly as well)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void fp8x16_to_bf16(i32x4 x, i32x4& lo, i32x4& hi) {
+  int r[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)x[w], 1.0f, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)x[w], 1.0f, true);
+    r[2 * w] = __builtin_bit_cast(int, a);
+    r[2 * w + 1] = __builtin_bit_cast(int, b);
+  }
+  lo = (i32x4){r[0], r[1], r[2], r[3]};
+  hi = (i32x4){r[4], r[5], r[6], r[7]};
 }
 
 // One LDS-DMA instruction: 16 bytes per lane from rsrc + voff + soff into

@@ -31,9 +31,12 @@ struct AppendArgs {
   int32_t* lens;
   int max_len, d_c, d_r;
   float eps, theta;
+  float ckv_scale, kr_scale;  // fp8 cache: a value x is stored as the E4M3 code of x / scale
 };
 
-hipError_t launch_cache_append(const AppendArgs& a, bool bf16, int batch, hipStream_t s);
+// Element type of the cache the append writes.
+enum class CacheElt { kF32, kBF16, kFP8 };
+hipError_t launch_cache_append(const AppendArgs& a, CacheElt elt, int batch, hipStream_t s);
 
 // Inputs and outputs of the split-KV plan (plan_device.h).
 struct PlanArgs {
@@ -108,18 +111,30 @@ hipError_t launch_plan(const int32_t* lens, int B, int max_len, int target_items
 
 // Query absorption into rows of q_stride elements; lo_off > 0 (bf16 only)
 // also writes q~'s rounding residue at that element of each row (QView).
+// lat_scale multiplies W_UK q^N (alpha_q tau, times the cache's latent scale
+// for an fp8 cache), rope_scale the rotated q^R (tau, times the RoPE scale).
 template <typename T>
 hipError_t launch_absorb_q_generic(const Geom& g, const T* q_nope, const T* q_rope,
                                    const int32_t* q_pos, const int32_t* lens, const T* w_uk,
-                                   T* q_abs, int q_stride, int lo_off, float tau, float alpha_q,
-                                   float theta, hipStream_t s);
+                                   T* q_abs, int q_stride, int lo_off, float lat_scale,
+                                   float rope_scale, float theta, hipStream_t s);
 
-template <typename T>
-hipError_t launch_decode_generic(const Geom& g, const QView& q, const T* ckv, const T* krope,
+// Cache elements T (fp32, bf16) or fp8 E4M3 codes (uint8_t, bf16 queries).
+template <typename T, typename TC>
+hipError_t launch_decode_generic(const Geom& g, const QView& q, const TC* ckv, const TC* krope,
                                  const Workspace& ws, int grid_items, hipStream_t s,
                                  const KernelTiming& t);
 
-hipError_t launch_combine(const Geom& g, const Workspace& ws, float* latent_out, hipStream_t s);
+// latent_out = out_scale * the merged latent (out_scale: the fp8 cache's
+// latent scale, else 1).
+hipError_t launch_combine(const Geom& g, const Workspace& ws, float* latent_out, float out_scale,
+                          hipStream_t s);
+
+// Rows of `dst` = the caller's bf16 q_abs rows `src` with q~ times lat_scale
+// and rho times rope_scale (q~ taken with its residue when src has one, and
+// split again into bf16 parts when dst has one): the query for an fp8 cache.
+hipError_t launch_scale_q(const Geom& g, const QView& src, const QView& dst, float lat_scale,
+                          float rope_scale, hipStream_t s);
 
 template <typename T, typename TO>
 hipError_t launch_out_proj_generic(const Geom& g, const float* latent, const T* w_uv, TO* out,
@@ -127,19 +142,22 @@ hipError_t launch_out_proj_generic(const Geom& g, const float* latent, const T* 
 
 // Fast bf16 MFMA decode. Returns hipErrorNotSupported when the shape has no
 // specialisation (the caller then uses the generic kernel).
-bool decode_branch_supported(const Geom& g);
+// fp8: the cache holds E4M3 codes (the kernels convert them exactly after
+// LDS); the scales are folded into the query and the merge by the caller.
+bool decode_branch_supported(const Geom& g, bool fp8 = false);
 int decode_branch_wgs_per_item(const Geom& g);
 bool decode_branch_reads_residue(const Geom& g);  // adds q~'s residue when the view has one
 hipError_t launch_decode_branch(const Geom& g, const QView& q, const void* ckv,
                                 const void* krope, const Workspace& ws, int grid_items,
-                                hipStream_t s, const KernelTiming& t);
+                                hipStream_t s, const KernelTiming& t, bool fp8 = false);
 
-// 32 heads per wave across the whole 576-wide row (decode_wide.hip)
-bool decode_wide_supported(const Geom& g);
+// 16 heads per wave for the scores, 64 latent columns per wave for P V,
+// across the whole 576-wide row (decode_wide.hip)
+bool decode_wide_supported(const Geom& g, bool fp8 = false);
 bool decode_wide_reads_residue(const Geom& g);
 hipError_t launch_decode_wide(const Geom& g, const QView& q, const void* ckv, const void* krope,
                               const Workspace& ws, int grid_items, hipStream_t s,
-                              const KernelTiming& t);
+                              const KernelTiming& t, bool fp8 = false);
 
 bool decode_mfma_supported(const Geom& g);
 bool decode_mfma_reads_residue(const Geom& g);  // adds q~'s residue when the view has one
@@ -156,10 +174,11 @@ bool absorb_mfma_supported(const Geom& g);
 // split-KV plan (as launch_plan would).
 hipError_t launch_absorb_q_mfma(const Geom& g, const __bf16* q_nope, const __bf16* q_rope,
                                 const int32_t* q_pos, const int32_t* lens, const __bf16* w_uk,
-                                __bf16* q_abs, int q_stride, int lo_off, float tau, float alpha_q,
-                                float theta, const PlanArgs& plan, hipStream_t s);
+                                __bf16* q_abs, int q_stride, int lo_off, float lat_scale,
+                                float rope_scale, float theta, const PlanArgs& plan,
+                                hipStream_t s);
 hipError_t launch_combine_hc(const Geom& g, const Workspace& ws, float* latent_out,
-                             hipStream_t s);
+                             float out_scale, hipStream_t s);
 template <typename TO>
 hipError_t launch_out_proj_mfma(const Geom& g, const float* latent, const __bf16* w_uv, TO* out,
                                 float alpha_kv, hipStream_t s);

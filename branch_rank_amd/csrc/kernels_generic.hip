@@ -26,6 +26,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+// an fp8 cache entry: the E4M3 code's value (exact in fp32)
+__device__ __forceinline__ float to_f32(uint8_t x) { return __builtin_amdgcn_cvt_f32_fp8((int)x, 0); }
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
@@ -75,8 +77,8 @@ __global__ __launch_bounds__(256) void absorb_q_generic(Geom g, const T* __restr
                                                         const int32_t* __restrict__ lens,
                                                         const T* __restrict__ w_uk,
                                                         T* __restrict__ q_abs, int row,
-                                                        int lo_off, float tau, float alpha_q,
-                                                        RopeFreqs fr) {
+                                                        int lo_off, float lat_scale,
+                                                        float rope_scale, RopeFreqs fr) {
   extern __shared__ float sq[];  // [kQB][dn]
   const int h = blockIdx.x, b0 = blockIdx.y * kQB;
   const int nb = min(kQB, g.B - b0);
@@ -85,7 +87,8 @@ __global__ __launch_bounds__(256) void absorb_q_generic(Geom g, const T* __restr
     sq[bb * g.dn + e] = to_f32(q_nope[((size_t)(b0 + bb) * g.H + h) * g.dn + e]);
   }
   __syncthreads();
-  const float s = alpha_q * tau;
+  const float s = lat_scale;
+  const double tau = rope_scale;
   const T* w = w_uk + (size_t)h * g.dc * g.dn;
   for (int c = threadIdx.x; c < g.dc; c += blockDim.x) {
     float acc[kQB];
@@ -138,11 +141,11 @@ __device__ __forceinline__ int find_seq(const int32_t* prefix, int B, int pos) {
   return lo;
 }
 
-template <typename T>
+template <typename T, typename TC>
 __global__ __launch_bounds__(256) void decode_generic(Geom g, const T* __restrict__ q_abs,
                                                       int q_stride, int q_lo,
-                                                      const T* __restrict__ ckv,
-                                                      const T* __restrict__ krope,
+                                                      const TC* __restrict__ ckv,
+                                                      const TC* __restrict__ krope,
                                                       Workspace ws) {
   extern __shared__ float smem[];
   const int row = g.dc + g.dr;
@@ -168,13 +171,13 @@ __global__ __launch_bounds__(256) void decode_generic(Geom g, const T* __restric
     float m[kMaxBranches], l[kMaxBranches], acc[kMaxColsPerThr];
     for (int j = 0; j < kMaxBranches; ++j) { m[j] = -INFINITY; l[j] = 0.f; }
     for (int i = 0; i < kMaxColsPerThr; ++i) acc[i] = 0.f;
-    const T* cb = ckv + (size_t)b * g.ckv_bs;
-    const T* kb = krope + (size_t)b * g.kr_bs;
+    const TC* cb = ckv + (size_t)b * g.ckv_bs;
+    const TC* kb = krope + (size_t)b * g.kr_bs;
     for (int tc = t0; tc < t1; tc += kTok) {
       const int nt = min(kTok, t1 - tc);
       if (tid < nt) {
-        const T* crow = cb + (size_t)(tc + tid) * g.ckv_ts;
-        const T* krow = kb + (size_t)(tc + tid) * g.kr_ts;
+        const TC* crow = cb + (size_t)(tc + tid) * g.ckv_ts;
+        const TC* krow = kb + (size_t)(tc + tid) * g.kr_ts;
         float rs = 0.f;
         for (int r = 0; r < g.dr; ++r) rs += q[g.dc + r] * to_f32(krow[r]);
         for (int j = 0; j < g.n; ++j) {
@@ -232,7 +235,8 @@ constexpr int kCSlots = 8;   // slots whose weights are staged at once
 // latent_out[b][h][c] = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k,
 // one softmax per branch (the branch of column c is c / (d_c / n)).
 __global__ __launch_bounds__(256) void combine_kernel(Geom g, Workspace ws, int cb,
-                                                      float* __restrict__ latent_out) {
+                                                      float* __restrict__ latent_out,
+                                                      float out_scale) {
   extern __shared__ float sm[];
   const int H = g.H, n = g.n;
   float* Mx = sm;                       // [n][H]
@@ -295,7 +299,33 @@ __global__ __launch_bounds__(256) void combine_kernel(Geom g, Workspace ws, int 
   __syncthreads();
   for (int i = tid; i < H * nc; i += 256) {
     const int hh = i / nc, cl = i % nc;
-    latent_out[((size_t)b * H + hh) * g.dc + c0 + cl] = tile[cl * (H + 1) + hh];
+    latent_out[((size_t)b * H + hh) * g.dc + c0 + cl] = out_scale * tile[cl * (H + 1) + hh];
+  }
+}
+
+// ---------------------------------------------------------------- scale_q ----
+
+// Query rows for an fp8 cache from the caller's bf16 rows: q~ (with its
+// residue when the source has one) times lat_scale, rho times rope_scale, in
+// fp32, then bf16 (plus the new residue when the destination keeps one).
+// grid B * H rows, 256 threads.
+__global__ __launch_bounds__(256) void scale_q_kernel(Geom g, const __bf16* __restrict__ src,
+                                                      int s_stride, int s_lo,
+                                                      __bf16* __restrict__ dst, int d_stride,
+                                                      int d_lo, float lat_scale,
+                                                      float rope_scale) {
+  const int r = blockIdx.x;
+  const __bf16* a = src + (size_t)r * s_stride;
+  __bf16* o = dst + (size_t)r * d_stride;
+  for (int i = threadIdx.x; i < g.dc + g.dr; i += blockDim.x) {
+    if (i < g.dc) {
+      const float v = lat_scale * ((float)a[i] + (s_lo > 0 ? (float)a[s_lo + i] : 0.f));
+      const __bf16 hi = (__bf16)v;
+      o[i] = hi;
+      if (d_lo > 0) o[d_lo + i] = (__bf16)(v - (float)hi);
+    } else {
+      o[i] = (__bf16)(rope_scale * (float)a[i]);
+    }
   }
 }
 
@@ -367,33 +397,44 @@ hipError_t launch_plan(const int32_t* lens, int B, int max_len, int target_items
 template <typename T>
 hipError_t launch_absorb_q_generic(const Geom& g, const T* q_nope, const T* q_rope,
                                    const int32_t* q_pos, const int32_t* lens, const T* w_uk,
-                                   T* q_abs, int q_stride, int lo_off, float tau,
-                                   float alpha_q, float theta, hipStream_t s) {
+                                   T* q_abs, int q_stride, int lo_off, float lat_scale,
+                                   float rope_scale, float theta, hipStream_t s) {
   const size_t sh = sizeof(float) * kQB * g.dn;
   hipLaunchKernelGGL(absorb_q_generic<T>, dim3(g.H, (g.B + kQB - 1) / kQB), dim3(256), sh, s, g,
-                     q_nope, q_rope, q_pos, lens, w_uk, q_abs, q_stride, lo_off, tau, alpha_q,
-                     rope_freqs(theta, g.dr));
+                     q_nope, q_rope, q_pos, lens, w_uk, q_abs, q_stride, lo_off, lat_scale,
+                     rope_scale, rope_freqs(theta, g.dr));
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_decode_generic(const Geom& g, const QView& q, const T* ckv, const T* krope,
+template <typename T, typename TC>
+hipError_t launch_decode_generic(const Geom& g, const QView& q, const TC* ckv, const TC* krope,
                                  const Workspace& ws, int grid_items, hipStream_t s,
                                  const KernelTiming& t) {
   const size_t sh = sizeof(float) * (g.dc + g.dr + g.n * kTok);
-  hipExtLaunchKernelGGL(decode_generic<T>, dim3(grid_items, g.H), dim3(256), sh, s, t.start,
-                        t.stop, 0, g, static_cast<const T*>(q.q), q.stride, q.lo, ckv, krope,
-                        ws);
+  hipExtLaunchKernelGGL((decode_generic<T, TC>), dim3(grid_items, g.H), dim3(256), sh, s,
+                        t.start, t.stop, 0, g, static_cast<const T*>(q.q), q.stride, q.lo, ckv,
+                        krope, ws);
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const Geom& g, const Workspace& ws, float* latent_out, hipStream_t s) {
+hipError_t launch_scale_q(const Geom& g, const QView& src, const QView& dst, float lat_scale,
+                          float rope_scale, hipStream_t s) {
+  if (g.B * g.H == 0) return hipSuccess;
+  hipLaunchKernelGGL(scale_q_kernel, dim3(g.B * g.H), dim3(256), 0, s, g,
+                     static_cast<const __bf16*>(src.q), src.stride, src.lo,
+                     static_cast<__bf16*>(const_cast<void*>(dst.q)), dst.stride, dst.lo,
+                     lat_scale, rope_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const Geom& g, const Workspace& ws, float* latent_out, float out_scale,
+                          hipStream_t s) {
   int cb = (256 * kCPairs) / g.H;
   if (cb > g.dc) cb = g.dc;
   if (cb < 1) cb = 1;
   const size_t sh = sizeof(float) * (2 * g.n * g.H + kCSlots * g.n * g.H + cb * (g.H + 1));
   hipLaunchKernelGGL(combine_kernel, dim3(g.B, (g.dc + cb - 1) / cb), dim3(256), sh, s, g, ws,
-                     cb, latent_out);
+                     cb, latent_out, out_scale);
   return hipGetLastError();
 }
 
@@ -417,12 +458,15 @@ template hipError_t launch_absorb_q_generic<__bf16>(const Geom&, const __bf16*, 
                                                     const int32_t*, const int32_t*,
                                                     const __bf16*, __bf16*, int, int, float, float,
                                                     float, hipStream_t);
-template hipError_t launch_decode_generic<float>(const Geom&, const QView&, const float*,
+template hipError_t launch_decode_generic<float, float>(const Geom&, const QView&, const float*,
                                                  const float*, const Workspace&, int,
                                                  hipStream_t, const KernelTiming&);
-template hipError_t launch_decode_generic<__bf16>(const Geom&, const QView&, const __bf16*,
+template hipError_t launch_decode_generic<__bf16, __bf16>(const Geom&, const QView&, const __bf16*,
                                                   const __bf16*, const Workspace&, int,
                                                   hipStream_t, const KernelTiming&);
+template hipError_t launch_decode_generic<__bf16, uint8_t>(const Geom&, const QView&, const uint8_t*,
+                                                   const uint8_t*, const Workspace&, int,
+                                                   hipStream_t, const KernelTiming&);
 template hipError_t launch_out_proj_generic<float, float>(const Geom&, const float*,
                                                           const float*, float*, float,
                                                           hipStream_t);

@@ -225,6 +225,26 @@ Geom make_geom(const mlra_config_t* c, int32_t batch, const mlra_cache_t* cache)
   return g;
 }
 
+#define TRY(x)                          \
+  do {                                  \
+    mlra_status_t st_ = (x);            \
+    if (st_ != MLRA_OK) return st_;     \
+  } while (0)
+
+// fp8 cache scales: finite and within [2^-32, 2^32], so that their products
+// with the query and output scales stay far from fp32's range limits
+mlra_status_t check_fp8_scales(float sc, float sr) {
+  auto ok = [](float v) { return std::isfinite(v) && v >= 0x1p-32f && v <= 0x1p32f; };
+  if (!ok(sc) || !ok(sr))
+    return fail(MLRA_ERR_INVALID_ARG, "fp8 cache scales must be finite and in [2^-32, 2^32]");
+  return MLRA_OK;
+}
+
+// Multipliers that the decode folds into q~, rho and the merged latent: the
+// fp8 cache's scales, else 1.
+float lat_mul(const mlra_cache_t* k) { return k && k->fp8 ? k->ckv_scale : 1.f; }
+float rope_mul(const mlra_cache_t* k) { return k && k->fp8 ? k->krope_scale : 1.f; }
+
 mlra_status_t check_cache(const mlra_config_t* c, const mlra_cache_t* k, int32_t batch) {
   if (!k) return fail(MLRA_ERR_INVALID_ARG, "cache is NULL");
   mlra_status_t st = check_batch(batch, k->max_len);
@@ -236,7 +256,13 @@ mlra_status_t check_cache(const mlra_config_t* c, const mlra_cache_t* k, int32_t
     return fail(MLRA_ERR_INVALID_ARG, "cache pointers are NULL");
   if (!aligned16(k->ckv) || (c->d_rope > 0 && !aligned16(k->krope)))
     return fail(MLRA_ERR_INVALID_ARG, "cache base pointers must be 16-byte aligned");
-  const int64_t e = (int64_t)elt_size(c->dtype);
+  if (k->fp8 != 0 && k->fp8 != 1) return fail(MLRA_ERR_INVALID_ARG, "cache fp8 must be 0 or 1");
+  if (k->fp8) {
+    if (c->dtype != MLRA_BF16)
+      return fail(MLRA_ERR_INVALID_ARG, "an fp8 cache needs the bf16 dtype");
+    TRY(check_fp8_scales(k->ckv_scale, k->krope_scale));
+  }
+  const int64_t e = k->fp8 ? 1 : (int64_t)elt_size(c->dtype);
   if (k->ckv_token_stride < 1 || k->ckv_batch_stride < 0 ||
       (c->d_rope > 0 && (k->krope_token_stride < 1 || k->krope_batch_stride < 0)))
     return fail(MLRA_ERR_INVALID_ARG, "cache strides: token stride >= 1, batch stride >= 0");
@@ -257,12 +283,6 @@ mlra_status_t check_ptr(const void* p, const char* name) {
   return MLRA_OK;
 }
 
-#define TRY(x)                          \
-  do {                                  \
-    mlra_status_t st_ = (x);            \
-    if (st_ != MLRA_OK) return st_;     \
-  } while (0)
-
 #define TRY_HIP(x, what)                       \
   do {                                         \
     hipError_t e_ = (x);                       \
@@ -274,27 +294,31 @@ mlra_status_t check_ptr(const void* p, const char* name) {
 // Query absorption. When `plan` is given and the MFMA kernel runs, the split-KV
 // plan rides along in that launch and *plan_done is set.
 // Query absorption into rows described by `q` (stride, residue offset).
+// lat_m and rope_m multiply q~ and rho on top of alpha_q tau and tau (an fp8
+// cache's scales).
 mlra_status_t run_absorb(const mlra_config_t* c, const Geom& g, const void* q_nope,
                          const void* q_rope, const int32_t* q_pos, const int32_t* lens,
                          const void* w_uk, const QView& q, hipStream_t s,
-                         const PlanArgs* plan = nullptr, bool* plan_done = nullptr) {
+                         const PlanArgs* plan = nullptr, bool* plan_done = nullptr,
+                         float lat_m = 1.f, float rope_m = 1.f) {
   const float tau = tau_of(c);
+  const float lat_scale = c->alpha_q * tau * lat_m, rope_scale = tau * rope_m;
   void* q_abs = const_cast<void*>(q.q);
   hipError_t e;
   if (c->dtype == MLRA_BF16 && absorb_mfma_supported(g)) {
     PlanArgs none{};
     e = launch_absorb_q_mfma(g, (const __bf16*)q_nope, (const __bf16*)q_rope, q_pos, lens,
-                             (const __bf16*)w_uk, (__bf16*)q_abs, q.stride, q.lo, tau, c->alpha_q,
-                             c->rope_theta, plan ? *plan : none, s);
+                             (const __bf16*)w_uk, (__bf16*)q_abs, q.stride, q.lo, lat_scale,
+                             rope_scale, c->rope_theta, plan ? *plan : none, s);
     if (plan && plan_done) *plan_done = true;
   } else if (c->dtype == MLRA_BF16)
     e = launch_absorb_q_generic<__bf16>(g, (const __bf16*)q_nope, (const __bf16*)q_rope, q_pos,
                                         lens, (const __bf16*)w_uk, (__bf16*)q_abs, q.stride, q.lo,
-                                        tau, c->alpha_q, c->rope_theta, s);
+                                        lat_scale, rope_scale, c->rope_theta, s);
   else
     e = launch_absorb_q_generic<float>(g, (const float*)q_nope, (const float*)q_rope, q_pos, lens,
-                                       (const float*)w_uk, (float*)q_abs, q.stride, 0, tau,
-                                       c->alpha_q, c->rope_theta, s);
+                                       (const float*)w_uk, (float*)q_abs, q.stride, 0, lat_scale,
+                                       rope_scale, c->rope_theta, s);
   TRY_HIP(e, "absorb_q launch");
   return MLRA_OK;
 }
@@ -306,9 +330,10 @@ mlra_status_t select_kernel(const mlra_config_t* c, const Geom& g, const mlra_ca
   const bool mfma_ok = c->dtype == MLRA_BF16 &&
                        (int64_t)k->max_len * k->ckv_token_stride * 2 < 0x7fffffffLL &&
                        (int64_t)k->max_len * k->krope_token_stride * 2 < 0x7fffffffLL;
-  const bool branch_ok = mfma_ok && decode_branch_supported(g);
-  const bool group_ok = mfma_ok && decode_mfma_supported(g);
-  const bool wide_ok = mfma_ok && decode_wide_supported(g);
+  const bool fp8 = k->fp8 != 0;
+  const bool branch_ok = mfma_ok && decode_branch_supported(g, fp8);
+  const bool group_ok = mfma_ok && !fp8 && decode_mfma_supported(g);
+  const bool wide_ok = mfma_ok && decode_wide_supported(g, fp8);
   mlra_kernel_t kern = c->decode_kernel;
   if (kern == MLRA_KERNEL_AUTO)
     kern = branch_ok ? MLRA_KERNEL_BRANCH
@@ -375,18 +400,22 @@ mlra_status_t run_decode(const mlra_config_t* c, const Geom& g, const QView& q,
     t.start = g_ev_before;
     t.stop = g_ev_after;
     hipError_t e;
+    const bool fp8 = k->fp8 != 0;
     if (kern == MLRA_KERNEL_BRANCH)
-      e = launch_decode_branch(g, q, k->ckv, k->krope, ws, (int)imax, s, t);
+      e = launch_decode_branch(g, q, k->ckv, k->krope, ws, (int)imax, s, t, fp8);
     else if (kern == MLRA_KERNEL_HEAD_GROUP)
       e = launch_decode_mfma(g, q, k->ckv, k->krope, ws, (int)imax, s, t);
     else if (kern == MLRA_KERNEL_WIDE)
-      e = launch_decode_wide(g, q, k->ckv, k->krope, ws, (int)imax, s, t);
+      e = launch_decode_wide(g, q, k->ckv, k->krope, ws, (int)imax, s, t, fp8);
+    else if (fp8)
+      e = launch_decode_generic<__bf16, uint8_t>(g, q, (const uint8_t*)k->ckv,
+                                                 (const uint8_t*)k->krope, ws, (int)imax, s, t);
     else if (c->dtype == MLRA_BF16)
-      e = launch_decode_generic<__bf16>(g, q, (const __bf16*)k->ckv, (const __bf16*)k->krope, ws,
-                                        (int)imax, s, t);
+      e = launch_decode_generic<__bf16, __bf16>(g, q, (const __bf16*)k->ckv,
+                                                (const __bf16*)k->krope, ws, (int)imax, s, t);
     else
-      e = launch_decode_generic<float>(g, q, (const float*)k->ckv, (const float*)k->krope, ws,
-                                       (int)imax, s, t);
+      e = launch_decode_generic<float, float>(g, q, (const float*)k->ckv, (const float*)k->krope,
+                                              ws, (int)imax, s, t);
     TRY_HIP(e, "decode launch");
   }
   *fast_out = kern != MLRA_KERNEL_PORTABLE;
@@ -394,8 +423,9 @@ mlra_status_t run_decode(const mlra_config_t* c, const Geom& g, const QView& q,
 }
 
 mlra_status_t run_merge(const Geom& g, const Workspace& ws, bool fast, float* latent_out,
-                        hipStream_t s) {
-  TRY_HIP(fast ? launch_combine_hc(g, ws, latent_out, s) : launch_combine(g, ws, latent_out, s),
+                        float out_scale, hipStream_t s) {
+  TRY_HIP(fast ? launch_combine_hc(g, ws, latent_out, out_scale, s)
+               : launch_combine(g, ws, latent_out, out_scale, s),
           "combine launch");
   return MLRA_OK;
 }
@@ -440,20 +470,23 @@ mlra_status_t run_step(const mlra_config_t* cfg, int32_t batch, int cus, const v
   TRY(plan_for(cfg, g, cus, cache, ws, L, &kern, &plan));
   bool plan_done = false;
   const QView qv = ws_qview(cfg, g, kern, ws.q_abs);
+  // an fp8 cache's scales go into q~, rho and the merged latent
+  const float sc = lat_mul(cache), sr = rope_mul(cache);
   TRY(run_absorb(cfg, g, q_nope, q_rope, q_pos, cache->cache_lens, w_uk, qv, s, &plan,
-                 &plan_done));
+                 &plan_done, sc, sr));
   bool fast = false;
   TRY(run_decode(cfg, g, qv, cache, ws, L, kern, plan, plan_done, &fast, s));
   if (fast && cfg->dtype == MLRA_BF16 && proj_mfma_supported(g)) {
     // merge and out projection in one kernel: the latent stays on chip
     const __bf16* wv = static_cast<const __bf16*>(w_uv);
+    const float akv = cfg->alpha_kv * sc;
     TRY_HIP(out_dtype == MLRA_BF16
-                ? launch_merge_out_proj<__bf16>(g, ws, wv, static_cast<__bf16*>(out), cfg->alpha_kv, s)
-                : launch_merge_out_proj<float>(g, ws, wv, static_cast<float*>(out), cfg->alpha_kv, s),
+                ? launch_merge_out_proj<__bf16>(g, ws, wv, static_cast<__bf16*>(out), akv, s)
+                : launch_merge_out_proj<float>(g, ws, wv, static_cast<float*>(out), akv, s),
             "merge_out launch");
     return MLRA_OK;
   }
-  TRY(run_merge(g, ws, fast, ws.latent, s));
+  TRY(run_merge(g, ws, fast, ws.latent, sc, s));
   return run_out_proj(cfg, g, ws.latent, w_uv, out, out_dtype, s);
 }
 
@@ -565,19 +598,35 @@ mlra_status_t mla_decode_attn(const mlra_config_t* cfg, int32_t batch, const voi
   PlanArgs plan;
   TRY(plan_for(cfg, g, cus, cache, ws, L, &kern, &plan));
   bool fast = false;
-  const QView qv = user_qview(cfg, q_abs);
+  QView qv = user_qview(cfg, q_abs);
+  if (cache->fp8) {
+    // the cache's scales go into a copy of the query in the workspace
+    const QView scaled = ws_qview(cfg, g, kern, ws.q_abs);
+    TRY_HIP(launch_scale_q(g, qv, scaled, lat_mul(cache), rope_mul(cache), s), "scale_q launch");
+    qv = scaled;
+  }
   TRY(run_decode(cfg, g, qv, cache, ws, L, kern, plan, false, &fast, s));
-  return run_merge(g, ws, fast, latent_out, s);
+  return run_merge(g, ws, fast, latent_out, lat_mul(cache), s);
 }
 
-mlra_status_t mlra_cache_append(const mlra_config_t* cfg, int32_t batch, const float* new_rows,
-                                const float* gain, float eps, void* ckv, void* krope,
-                                int64_t ckv_batch_stride, int64_t ckv_token_stride,
-                                int64_t krope_batch_stride, int64_t krope_token_stride,
-                                int32_t* cache_lens, int32_t max_len, void* stream) {
+}  // extern "C"
+
+namespace {
+
+mlra_status_t append_impl(const mlra_config_t* cfg, int32_t batch, const float* new_rows,
+                          const float* gain, float eps, void* ckv, void* krope,
+                          int64_t ckv_batch_stride, int64_t ckv_token_stride,
+                          int64_t krope_batch_stride, int64_t krope_token_stride,
+                          int32_t* cache_lens, int32_t max_len, bool fp8, float ckv_scale,
+                          float krope_scale, void* stream) {
   g_detail.clear();
   TRY(check_cfg(cfg));
   TRY(check_batch(batch, max_len));
+  if (fp8) {
+    if (cfg->dtype != MLRA_BF16)
+      return fail(MLRA_ERR_INVALID_ARG, "an fp8 cache needs the bf16 dtype");
+    TRY(check_fp8_scales(ckv_scale, krope_scale));
+  }
   if (batch == 0 || max_len == 0) return MLRA_OK;
   if (!new_rows || !cache_lens || !ckv || (cfg->d_rope > 0 && !krope))
     return fail(MLRA_ERR_INVALID_ARG, "new_rows, cache_lens and the cache pointers must be set");
@@ -603,9 +652,39 @@ mlra_status_t mlra_cache_append(const mlra_config_t* cfg, int32_t batch, const f
   a.d_r = cfg->d_rope;
   a.eps = eps;
   a.theta = cfg->rope_theta;
-  TRY_HIP(launch_cache_append(a, cfg->dtype == MLRA_BF16, batch, static_cast<hipStream_t>(stream)),
+  a.ckv_scale = fp8 ? ckv_scale : 1.f;
+  a.kr_scale = fp8 ? krope_scale : 1.f;
+  const CacheElt elt = fp8 ? CacheElt::kFP8
+                     : cfg->dtype == MLRA_BF16 ? CacheElt::kBF16 : CacheElt::kF32;
+  TRY_HIP(launch_cache_append(a, elt, batch, static_cast<hipStream_t>(stream)),
           "cache_append launch");
   return MLRA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mlra_status_t mlra_cache_append(const mlra_config_t* cfg, int32_t batch, const float* new_rows,
+                                const float* gain, float eps, void* ckv, void* krope,
+                                int64_t ckv_batch_stride, int64_t ckv_token_stride,
+                                int64_t krope_batch_stride, int64_t krope_token_stride,
+                                int32_t* cache_lens, int32_t max_len, void* stream) {
+  return append_impl(cfg, batch, new_rows, gain, eps, ckv, krope, ckv_batch_stride,
+                     ckv_token_stride, krope_batch_stride, krope_token_stride, cache_lens,
+                     max_len, false, 1.f, 1.f, stream);
+}
+
+mlra_status_t mlra_cache_append_fp8(const mlra_config_t* cfg, int32_t batch,
+                                    const float* new_rows, const float* gain, float eps,
+                                    void* ckv, void* krope, int64_t ckv_batch_stride,
+                                    int64_t ckv_token_stride, int64_t krope_batch_stride,
+                                    int64_t krope_token_stride, int32_t* cache_lens,
+                                    int32_t max_len, float ckv_scale, float krope_scale,
+                                    void* stream) {
+  return append_impl(cfg, batch, new_rows, gain, eps, ckv, krope, ckv_batch_stride,
+                     ckv_token_stride, krope_batch_stride, krope_token_stride, cache_lens,
+                     max_len, true, ckv_scale, krope_scale, stream);
 }
 
 mlra_status_t mlra_prefill(const mlra_config_t* cfg_in, int32_t num_branches, int32_t batch,
@@ -620,6 +699,7 @@ mlra_status_t mlra_prefill(const mlra_config_t* cfg_in, int32_t num_branches, in
   TRY(check_cache(&cfg, cache, batch));
   if (out_dtype != MLRA_BF16 && out_dtype != MLRA_FP32)
     return fail(MLRA_ERR_INVALID_ARG, "unknown out_dtype");
+  if (cache->fp8) return fail(MLRA_ERR_UNSUPPORTED, "the prefill reads bf16 caches only");
   if (batch == 0 || cache->max_len == 0) return MLRA_OK;
   TRY(check_ptr(q_nope, "q_nope"));
   if (cfg.d_rope > 0) TRY(check_ptr(q_rope, "q_rope"));

@@ -178,7 +178,8 @@ constexpr int kMS = 64;   // slots per weight table
 constexpr int kMNB = 8;   // most branches
 
 __global__ __launch_bounds__(256) void combine_hc(Geom g, Workspace ws,
-                                                  float* __restrict__ latent_out) {
+                                                  float* __restrict__ latent_out,
+                                                  float out_scale) {
   __shared__ float stat[2 * kMNB * kMH];        // M, 1/L per (branch, head)
   __shared__ float wt[kMS * kMNB * kMH];        // weights of kMS slots
   const int b = blockIdx.x, h0 = blockIdx.y * kMH, tid = threadIdx.x;
@@ -242,7 +243,7 @@ __global__ __launch_bounds__(256) void combine_hc(Geom g, Workspace ws,
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int q = tid + 256 * u;
-    if (q < per) *(f32x4*)(out + 4 * q) = r[u];
+    if (q < per) *(f32x4*)(out + 4 * q) = out_scale * r[u];
   }
 }
 
@@ -668,9 +669,10 @@ bool absorb_mfma_supported(const Geom& g) {
 
 hipError_t launch_absorb_q_mfma(const Geom& g, const __bf16* q_nope, const __bf16* q_rope,
                                 const int32_t* q_pos, const int32_t* lens, const __bf16* w_uk,
-                                __bf16* q_abs, int q_stride, int lo_off, float tau,
-                                float alpha_q, float theta, const PlanArgs& plan, hipStream_t s) {
-  const float scale = alpha_q * tau;
+                                __bf16* q_abs, int q_stride, int lo_off, float lat_scale,
+                                float rope_scale, float theta, const PlanArgs& plan,
+                                hipStream_t s) {
+  const float scale = lat_scale, tau = rope_scale;
   switch (g.dn) {
     case 64:
       return launch_absorb_k<2>(g, q_nope, q_rope, q_pos, lens, w_uk, q_abs, q_stride, lo_off,
@@ -686,10 +688,10 @@ hipError_t launch_absorb_q_mfma(const Geom& g, const __bf16* q_nope, const __bf1
 }
 
 hipError_t launch_combine_hc(const Geom& g, const Workspace& ws, float* latent_out,
-                             hipStream_t s) {
+                             float out_scale, hipStream_t s) {
   if (g.n > kMNB) return hipErrorNotSupported;
   hipLaunchKernelGGL(combine_hc, dim3(g.B, (g.H + kMH - 1) / kMH), dim3(256), 0, s, g, ws,
-                     latent_out);
+                     latent_out, out_scale);
   return hipGetLastError();
 }
 

@@ -77,11 +77,17 @@ typedef enum {
   MLRA_KERNEL_BRANCH = 3,      /* bf16 MFMA, one 128-wide branch and 32 heads per
                                   wave: n = 4, d_latent = 512, d_rope = 64,
                                   heads in {64, 128}; and one 128-wide branch
-                                  alone (n = 1, d_latent = 128, 128 heads) */
-  MLRA_KERNEL_WIDE = 4         /* fp16 MFMA on the cache converted in LDS, 32 heads
-                                  per wave across the whole row: n = 1 (MLA),
-                                  d_latent = 512, d_rope = 64, 128 heads */
+                                  alone (n = 1, d_latent = 128, 128 heads).
+                                  fp8 caches: n = 4 at 128 heads */
+  MLRA_KERNEL_WIDE = 4         /* fp16 MFMA on the cache converted in LDS, 16 heads
+                                  per wave for the scores and 64 latent columns
+                                  per wave for P V, across the whole row: n = 1
+                                  (MLA), d_latent = 512, d_rope = 64, 128 heads;
+                                  bf16 and fp8 caches */
 } mlra_kernel_t;
+/* The head-group kernel reads bf16 caches only; with an fp8 cache the
+ * automatic choice is the branch or wide kernel where they fit, else the
+ * portable kernel. */
 
 typedef struct {
   int32_t num_heads;     /* H >= 1 */
@@ -107,7 +113,18 @@ typedef struct {
  * contiguous elements) and krope + b*krope_batch_stride + t*krope_token_stride
  * (d_rope contiguous elements, stored already rotated at position t). One
  * interleaved buffer of [c_t || k^R_t] rows, two separate buffers, or a branch
- * shard all fit this view. */
+ * shard all fit this view.
+ *
+ * Quantised cache ("MLA多头潜在注意力机制", 9.2 部署注意事项: an 8-bit cache for
+ * inference; the pages fix no format, this is the library's reading): with
+ * fp8 = 1 the elements are one-byte FP8 E4M3 codes in the OCP 8-bit floating
+ * point layout (bias 7, largest finite 448, no infinities) and the values
+ * they stand for are c = ckv_scale * e4m3(code) and k^R = krope_scale *
+ * e4m3(code): one fp32 scale per cache tensor. Strides are then bytes. Only
+ * with cfg->dtype = MLRA_BF16 (queries, weights and outputs stay bf16). The
+ * decode calls (mla_decode_attn, mlra_decode, mlra_decode_noalloc) accept it;
+ * mlra_prefill returns MLRA_ERR_UNSUPPORTED. With fp8 = 0 the scales are
+ * ignored and the elements have cfg->dtype. */
 typedef struct {
   const void* ckv;
   const void* krope;
@@ -115,6 +132,9 @@ typedef struct {
   int64_t krope_batch_stride, krope_token_stride;
   const int32_t* cache_lens;  /* device [B] */
   int32_t max_len;            /* rows allocated per sequence */
+  int32_t fp8;                /* 0: elements of cfg->dtype; 1: FP8 E4M3 codes */
+  float ckv_scale;            /* fp8: finite, in [2^-32, 2^32] */
+  float krope_scale;          /* fp8: finite, in [2^-32, 2^32] */
 } mlra_cache_t;
 
 /* Bytes of workspace that mla_decode_attn and mlra_decode need for this
@@ -148,9 +168,13 @@ MLRA_API mlra_status_t mla_absorb_q(const mlra_config_t* cfg, int32_t batch, con
  * 苏神思路: decoding works like MQA).
  *   q_abs      [B][H][d_latent + d_rope] from mla_absorb_q (rows of
  *              d_latent + d_rope + d_latent with cfg->q_residue = 1; the
- *              residue enters the scores of the head-group and portable
- *              kernels, the branch kernel uses the bf16 q~ alone)
- *   cache      strided cache view (16-byte aligned bases and strides for bf16)
+ *              residue enters the scores of every kernel except the
+ *              four-branch branch kernel, which uses the bf16 q~ alone)
+ *   cache      strided cache view (16-byte aligned bases and byte strides
+ *              that are multiples of 16). With an fp8 cache the call first
+ *              writes q~ * ckv_scale and rho * krope_scale into the workspace
+ *              (the caller's q_abs is not changed) and latent_out is the
+ *              latent of the dequantised cache (times ckv_scale).
  *   workspace  device buffer of at least mlra_workspace_size() bytes
  *   latent_out out [B][H][d_latent] fp32 = concat_j o~_j (branch-normalised) */
 MLRA_API mlra_status_t mla_decode_attn(const mlra_config_t* cfg, int32_t batch, const void* q_abs,
@@ -175,7 +199,10 @@ MLRA_API mlra_status_t mla_out_proj(const mlra_config_t* cfg, int32_t batch, con
 
 /* The whole decode step (steps 1-3) for MLRA with `num_branches` branches
  * (overrides cfg->num_branches; 1 = MLA). Intermediates live in the workspace.
- * Arguments as for the three calls above. */
+ * Arguments as for the three calls above. With an fp8 cache the scales are
+ * folded into the absorbed query (q~ * ckv_scale, rho * krope_scale) and the
+ * output scale (alpha_kv * ckv_scale): the result is the decode of the
+ * dequantised cache. */
 MLRA_API mlra_status_t mlra_decode(const mlra_config_t* cfg, int32_t num_branches, int32_t batch,
                           const void* q_nope, const void* q_rope, const int32_t* q_pos,
                           const void* w_uk, const void* w_uv, const mlra_cache_t* cache,
@@ -234,6 +261,21 @@ MLRA_API mlra_status_t mlra_cache_append(const mlra_config_t* cfg, int32_t batch
                                          int64_t ckv_token_stride, int64_t krope_batch_stride,
                                          int64_t krope_token_stride, int32_t* cache_lens,
                                          int32_t max_len, void* stream);
+
+/* mlra_cache_append into an fp8 cache (see mlra_cache_t): the same row values
+ * as mlra_cache_append, each stored as the FP8 E4M3 code nearest value /
+ * scale (fp32 division, round to nearest with ties to the even mantissa,
+ * saturating at +-448; ckv_scale for the latent, krope_scale for the RoPE
+ * key). ckv and krope are byte buffers, strides in bytes (= elements).
+ * Needs cfg->dtype = MLRA_BF16; scales finite and in [2^-32, 2^32]. */
+MLRA_API mlra_status_t mlra_cache_append_fp8(const mlra_config_t* cfg, int32_t batch,
+                                             const float* new_rows, const float* gain, float eps,
+                                             void* ckv, void* krope, int64_t ckv_batch_stride,
+                                             int64_t ckv_token_stride,
+                                             int64_t krope_batch_stride,
+                                             int64_t krope_token_stride, int32_t* cache_lens,
+                                             int32_t max_len, float ckv_scale, float krope_scale,
+                                             void* stream);
 
 /* Causal prefill over the cache ("MLA多头潜在注意力机制" 3.3: a key after the
  * query's position is masked; "Multi-Head Low-Rank Attention", 核心方法 and

@@ -13,4 +13,8 @@ from .inputs import (  # noqa: F401
     round_bf16,
     bf16_bits,
     ragged_lens,
+    fp8_codes,
+    fp8_scale,
+    fp8_inputs,
+    fp8_device,
 )

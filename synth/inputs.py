@@ -222,3 +222,47 @@ def make_cache_device(w: Workload, seed: int, lens=None, device="cuda"):
             k *= 1.0 / math.sqrt(w.d_r)
         buf[b, :, w.d_c:] = k.to(dt)
     return buf, np.asarray(lens, np.int32)
+
+
+def fp8_codes(x, scale):
+    """FP8 E4M3 codes (uint8) of the values x / scale, by torch's
+    float8_e4m3fn cast (round to nearest even). With scale = fp8_scale(x) no
+    value passes 448, so no code is NaN."""
+    import torch
+
+    t = torch.as_tensor(np.asarray(x, np.float32)) / float(scale)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def fp8_scale(x):
+    """Per-tensor scale that maps the largest magnitude of x to 448, the
+    largest finite E4M3 value (a plain max calibration)."""
+    a = float(np.max(np.abs(x))) if np.size(x) else 0.0
+    return a / 448.0 if a > 0 else 1.0
+
+
+def fp8_inputs(inp):
+    """Adds the quantised cache of a drawn input set: ckv8, krope8 (uint8
+    codes) and their per-tensor scales sc, sr."""
+    out = dict(inp)
+    out["sc"], out["sr"] = fp8_scale(inp["ckv"]), fp8_scale(inp["krope"])
+    out["ckv8"] = fp8_codes(inp["ckv"], out["sc"])
+    out["krope8"] = fp8_codes(inp["krope"], out["sr"])
+    return out
+
+
+def fp8_device(buf, d_c):
+    """The device version for an interleaved cache buffer [B, L_max, d_c + d_r]
+    (bf16 or fp32): returns (codes [B, L_max, d_c + d_r] uint8, sc, sr), one
+    scale per part. Converts one sequence at a time to bound the fp32
+    scratch."""
+    import torch
+
+    sc = float(buf[..., :d_c].abs().amax()) / 448.0
+    sr = float(buf[..., d_c:].abs().amax()) / 448.0
+    sc, sr = sc if sc > 0 else 1.0, sr if sr > 0 else 1.0
+    out = torch.empty(buf.shape, dtype=torch.uint8, device=buf.device)
+    for b in range(buf.shape[0]):
+        out[b, :, :d_c] = (buf[b, :, :d_c].float() / sc).to(torch.float8_e4m3fn).view(torch.uint8)
+        out[b, :, d_c:] = (buf[b, :, d_c:].float() / sr).to(torch.float8_e4m3fn).view(torch.uint8)
+    return out, sc, sr

@@ -34,13 +34,21 @@ class Dev:
     NaN bytes first, so that a kernel reading a row it must not read, or a
     workspace word before it was written, puts NaN into the output."""
 
-    def __init__(self, w, inp, device="cuda", lens=None, poison=False):
+    def __init__(self, w, inp, device="cuda", lens=None, poison=False, fp8=False):
         dt = torch_dtype(w)
         B, Lmax, _ = inp["ckv"].shape
         self.w = w
-        self.buf = torch.empty(B, Lmax, w.d_c + w.d_r, dtype=dt, device=device)
-        self.buf[..., :w.d_c] = torch.from_numpy(inp["ckv"]).to(device).to(dt)
-        self.buf[..., w.d_c:] = torch.from_numpy(inp["krope"]).to(device).to(dt)
+        # fp8: the cache holds the E4M3 codes inp["ckv8"], inp["krope8"] with
+        # the scales inp["sc"], inp["sr"] (synth.fp8_inputs)
+        self.fp8 = (inp["sc"], inp["sr"]) if fp8 else None
+        if fp8:
+            self.buf = torch.empty(B, Lmax, w.d_c + w.d_r, dtype=torch.uint8, device=device)
+            self.buf[..., :w.d_c] = torch.from_numpy(inp["ckv8"]).to(device)
+            self.buf[..., w.d_c:] = torch.from_numpy(inp["krope8"]).to(device)
+        else:
+            self.buf = torch.empty(B, Lmax, w.d_c + w.d_r, dtype=dt, device=device)
+            self.buf[..., :w.d_c] = torch.from_numpy(inp["ckv"]).to(device).to(dt)
+            self.buf[..., w.d_c:] = torch.from_numpy(inp["krope"]).to(device).to(dt)
         self.ckv = self.buf[..., :w.d_c]
         self.krope = self.buf[..., w.d_c:]
         L = inp["lens"] if lens is None else lens
@@ -51,7 +59,8 @@ class Dev:
         self.poison = poison
         if poison:
             for b, n in enumerate(np.asarray(L, np.int64)):
-                self.buf[b, max(int(n), 0):] = float("nan")
+                # NaN (E4M3: code 0x7F)
+                self.buf[b, max(int(n), 0):] = 0x7F if fp8 else float("nan")
 
     def workspace(self, cfg):
         ws = br.alloc_workspace(cfg, self.B, self.Lmax)
@@ -60,7 +69,7 @@ class Dev:
         return ws
 
     def cache(self, cfg):
-        return br.cache_view(self.ckv, self.krope, self.lens, cfg)
+        return br.cache_view(self.ckv, self.krope, self.lens, cfg, fp8_scales=self.fp8)
 
     def decode(self, cfg, n=None, out_dtype=torch.float32, q_pos=None):
         n = cfg.num_branches if n is None else n

@@ -34,7 +34,7 @@ def gpu_present():
 def test_library_exports_every_declared_symbol():
     L = br.lib()
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(br.EXPORTS)
@@ -295,3 +295,74 @@ def test_q_residue_validation_and_row_width():
     assert L.mlra_workspace_size(ctypes.byref(c), 4, 128, ctypes.byref(out)) == br.MLRA_ERR_INVALID_ARG
     c = cfg(q_residue=True, dtype="fp32")   # the residue is a bf16 notion
     assert L.mlra_workspace_size(ctypes.byref(c), 4, 128, ctypes.byref(out)) == br.MLRA_ERR_INVALID_ARG
+
+
+# ---- fp8 (E4M3) caches: validation and kernel choice, host only ----
+
+def _fp8_cache(c, batch, max_len, sc=0.01, sr=0.02, fp8=1, ts=None):
+    ts = c.d_latent + c.d_rope if ts is None else ts  # bytes
+    k = br.Cache(0x100000, 0x100000 + c.d_latent, max_len * ts, ts, max_len * ts, ts,
+                 0x200000, max_len, fp8, sc, sr)
+    k._batch = batch
+    return k
+
+
+@pytest.mark.parametrize("kw,kernel,expect", [
+    (dict(), "auto", "branch"),                    # MLRA-4, 128 heads
+    (dict(n=1), "auto", "wide"),                   # MLA
+    (dict(heads=64), "auto", "portable"),          # MLRA-4 at 64 heads: no fp8 MFMA kernel
+    (dict(n=2), "auto", "portable"),
+    (dict(n=1, d_latent=128), "auto", "portable"),  # one branch shard
+    (dict(), "portable", "portable"),
+])
+def test_fp8_kernel_selection(kw, kernel, expect):
+    c = cfg(kernel=kernel, **kw)
+    assert br.select_decode_kernel(c, _fp8_cache(c, 2, 4096)) == expect
+
+
+def test_fp8_head_group_is_unsupported():
+    c = cfg(kernel="head_group", n=2)
+    with pytest.raises(br.MlraError) as e:
+        br.select_decode_kernel(c, _fp8_cache(c, 2, 4096))
+    assert e.value.status == br.MLRA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,cache_kw", [
+    (dict(dtype="fp32"), dict()),                  # fp8 needs bf16 queries and weights
+    (dict(), dict(sc=0.0)),
+    (dict(), dict(sr=-1.0)),
+    (dict(), dict(sc=float("inf"))),
+    (dict(), dict(sc=float("nan"))),
+    (dict(), dict(sr=2.0 ** 40)),
+    (dict(), dict(fp8=2)),
+    (dict(), dict(ts=584)),                        # byte stride not a multiple of 16
+])
+def test_fp8_cache_validation(kw, cache_kw):
+    c = cfg(**kw)
+    k = _fp8_cache(c, 4, 128, **cache_kw)
+    assert decode(c, k) == br.MLRA_ERR_INVALID_ARG
+
+
+def test_fp8_byte_strides_accepted():
+    c = cfg()
+    k = _fp8_cache(c, 4, 128)  # 576-byte rows: a multiple of 16 bytes
+    out = ctypes.c_int(-1)
+    assert br.lib().mlra_select_decode_kernel(ctypes.byref(c), 4, ctypes.byref(k),
+                                              ctypes.byref(out)) == br.MLRA_OK
+
+
+def test_fp8_prefill_is_unsupported():
+    c = cfg()
+    k = _fp8_cache(c, 2, 128)
+    assert br.lib().mlra_prefill(ctypes.byref(c), 4, 2, FAKE, FAKE, FAKE, FAKE, ctypes.byref(k),
+                                 FAKE, br.MLRA_FP32, None) == br.MLRA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,sc,sr", [(dict(dtype="fp32"), 0.1, 0.1), (dict(), 0.0, 0.1),
+                                      (dict(), 0.1, float("inf")), (dict(), 2.0 ** -40, 0.1)])
+def test_fp8_append_validation(kw, sc, sr):
+    c = cfg(**kw)
+    L = br.lib()
+    assert L.mlra_cache_append_fp8(ctypes.byref(c), 2, FAKE, None, 1e-6, FAKE, FAKE, 576 * 8,
+                                   576, 576 * 8, 576, FAKE, 8, sc, sr, None) == \
+        br.MLRA_ERR_INVALID_ARG
