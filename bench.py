@@ -77,11 +77,15 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the causal prefill leg (MLRA-4, 4 prompts of 4096 tokens)")
     ap.add_argument("--prefill-workload", default="mlra4_prefill_b4_t4k")
+    ap.add_argument("--mla-prefill-workload", default="mla_prefill_b4_t4k",
+                    help="MLA prefill (unabsorbed form) also timed ('' = none)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the prefill leg: print its JSON object and stop")
     ap.add_argument("--time-every", type=int, default=4,
                     help="stamp the decode dispatch's start/end events on every N-th timed step")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--fp8", default="mlra4_b16_l32k,mla_b16_l32k",
+                    help="workloads also timed on an fp8 (E4M3) copy of their cache ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe-copy", action="store_true",
                     help="only run a 1 GiB device copy (scale factor for HBM counters)")
@@ -92,14 +96,14 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_flops_bytes(w, lens):
+def kernel_flops_bytes(w, lens, fp8=False):
     """Algorithmic work of the split-KV decode kernel: every cached element is
     read once (the branches share the RoPE key and partition the latent), and
     per token each head does 2*(d_c + d_r) flop for the scores and 2*d_c for
-    the value accumulation."""
+    the value accumulation. fp8 caches hold one byte per element."""
     tokens = int(sum(int(x) for x in lens))
     row = w.d_c + w.d_r
-    esz = 2 if w.dtype == "bf16" else 4
+    esz = 1 if fp8 else (2 if w.dtype == "bf16" else 4)
     return tokens * row * esz, tokens * w.heads * 2 * (row + w.d_c), tokens
 
 
@@ -160,13 +164,13 @@ def sample_clock(step, torch, limit_s=30.0):
 
 
 def run_workload(name, steps, warmup, cache_gib, torch, br, synth, kernel="auto", every=4,
-                 clock=False):
+                 clock=False, fp8=False):
     w = synth.WORKLOADS[name]
     inp = synth.make_inputs(w, parts=("q_nope", "q_rope", "w_uk", "w_uv"))
     lens = inp["lens"]
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = {k: torch.from_numpy(inp[k]).cuda().to(dt) for k in ("q_nope", "q_rope", "w_uk", "w_uv")}
-    kv_bytes, flops, tokens = kernel_flops_bytes(w, lens)
+    kv_bytes, flops, tokens = kernel_flops_bytes(w, lens, fp8)
     copies = max(2, min(16, math.ceil(cache_gib * 2**30 / max(kv_bytes, 1))))
     log(f"[bench] {name}: B={w.batch} tokens={tokens} cache={kv_bytes / 1e6:.1f} MB x {copies} copies")
     lens_dev = torch.from_numpy(lens).cuda()
@@ -176,8 +180,13 @@ def run_workload(name, steps, warmup, cache_gib, torch, br, synth, kernel="auto"
     views, bufs = [], []
     for i in range(copies):
         buf, _ = synth.make_cache_device(w, seed=w.seed + 7919 * (i + 1), lens=lens)
+        scales = None
+        if fp8:  # E4M3 codes of the same cache, one scale per part
+            buf, sc, sr = synth.fp8_device(buf, w.d_c)
+            scales = (sc, sr)
         bufs.append(buf)
-        views.append(br.cache_view(buf[..., :w.d_c], buf[..., w.d_c:], lens_dev, cfg))
+        views.append(br.cache_view(buf[..., :w.d_c], buf[..., w.d_c:], lens_dev, cfg,
+                                   fp8_scales=scales))
     ws = br.alloc_workspace(cfg, w.batch, bufs[0].shape[1])
     kname = br.select_decode_kernel(cfg, views[0])
     out = torch.empty(w.batch, w.heads, w.d_v, dtype=torch.float32, device="cuda")
@@ -268,9 +277,23 @@ def prefill_flops(w, lens):
     return attn, attn + proj, pairs, attn_rep
 
 
+def mha_prefill_flops(w, lens):
+    """Algorithmic work of MLA's prefill in the unabsorbed (multi-head) form:
+    each (query, key) pair costs, per head, 2 (d_n + d_r) flop for the score
+    and 2 d_v for the value (640 at the DeepSeek-V3 shape); each cached row and
+    head adds the up-projection 2 d_c (d_n + d_v). Returns (attention part,
+    up-projection part, pairs)."""
+    pairs = sum(int(L) * (int(L) + 1) // 2 for L in lens)
+    attn = pairs * w.heads * 2 * (w.d_n + w.d_r + w.d_v)
+    rows = int(sum(int(L) for L in lens))
+    return attn, rows * w.heads * 2 * w.d_c * (w.d_n + w.d_v), pairs
+
+
 def time_prefill(name, steps, warmup, torch, br, synth):
-    """One mlra_prefill call per step over B full prompts (one kernel); its
-    dispatch stamps a pair of HIP events every step."""
+    """One prefill call per step over B full prompts: mlra_prefill (one
+    kernel) for several branches, mla_prefill (the up-projection, then the
+    attention kernel) for one. The attention dispatch stamps a pair of HIP
+    events every step."""
     w = synth.WORKLOADS[name]
     T = w.cache_len
     inp = synth.make_inputs(w, parts=("w_uk", "w_uv"))
@@ -288,9 +311,15 @@ def time_prefill(name, steps, warmup, torch, br, synth):
     cache = br.cache_view(buf[..., :w.d_c], buf[..., w.d_c:], lens_dev, cfg)
     out = torch.empty(w.batch, T, w.heads, w.d_v, dtype=torch.bfloat16, device="cuda")
     log(f"[bench] prefill {name}: B={w.batch} T={T}")
+    mha = w.n == 1
+    ws = (torch.empty(br.mla_prefill_workspace_size(cfg, w.batch, T), dtype=torch.uint8,
+                      device="cuda") if mha else None)
 
     def call():
-        br.mlra_prefill(cfg, w.n, qn, qr, wk, wv, cache, out)
+        if mha:
+            br.mla_prefill(cfg, qn, qr, wk, wv, cache, out, workspace=ws)
+        else:
+            br.mlra_prefill(cfg, w.n, qn, qr, wk, wv, cache, out)
 
     for _ in range(warmup):
         call()
@@ -311,6 +340,23 @@ def time_prefill(name, steps, warmup, torch, br, synth):
     assert torch.isfinite(out.float()).all().item(), "non-finite prefill output"
     ms = g0.elapsed_time(g1) / steps
     k_ms = sum(x.elapsed_time(y) for x, y in kev) / steps
+    if mha:
+        attn, proj, pairs = mha_prefill_flops(w, lens)
+        tf = attn / (k_ms / 1e3) / 1e12
+        return {"workload": name, "batch": w.batch, "prompt_len": T, "heads": w.heads,
+                "branches": w.n, "form": "unabsorbed (multi-head): up-projection + attention",
+                "steps": steps, "ms_per_call": ms,
+                "prompt_tokens_per_s": int(sum(int(L) for L in lens)) / (ms / 1e3),
+                "attention_kernel_ms": k_ms, "up_projection_ms": ms - k_ms,
+                "attention_flops": attn, "up_projection_flops": proj,
+                "flop_count": "2 (d_n + d_r + d_v) flop per (query, key) pair and head; "
+                              "2 d_c (d_n + d_v) per cached row and head",
+                "tflops_whole_call": (attn + proj) / (ms / 1e3) / 1e12,
+                "attn_pairs": pairs,
+                "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
+                             "note": "attention kernel, fp16 MFMA (same peak as bf16)",
+                             "traffic": None}}
     attn, total, pairs, attn_rep = prefill_flops(w, lens)
     tf = total / (k_ms / 1e3) / 1e12
     return {"workload": name, "batch": w.batch, "prompt_len": T, "heads": w.heads,
@@ -465,10 +511,32 @@ def main():
             "kv_cache_gbs_kernel": r["kv_bytes"] / (r["kernel_ms"] / 1e3) / 1e9,
             "kv_cache_gbs_step": r["kv_bytes"] / (r["ms_step"] / 1e3) / 1e9,
         }
+    # quantised cache: the same workloads on E4M3 codes (half the bytes),
+    # beside the bf16 decode kernel of the same run
+    bf16_us = {a.workload: main_r["kernel_ms"] * 1e3,
+               **{k: v["decode_kernel_us"] for k, v in extras.items()}}
+    fp8 = {}
+    for name in [x for x in a.fp8.split(",") if x]:
+        r = run_workload(name, a.steps, a.warmup, a.cache_bytes_min, torch, br, synth, "auto",
+                         a.time_every, fp8=True)
+        k_us = r["kernel_ms"] * 1e3
+        fp8[name] = {
+            "tokens_per_s": r["w"].batch / (r["ms_step"] / 1e3),
+            "ms_per_step": r["ms_step"],
+            "decode_kernel": r["kernel"],
+            "decode_kernel_us": k_us,
+            "kv_bytes": r["kv_bytes"],
+            "kv_cache_gbs_kernel": r["kv_bytes"] / (k_us / 1e6) / 1e9,
+            "bf16_decode_kernel_us": bf16_us.get(name),
+            "speedup_vs_bf16_kernel": bf16_us[name] / k_us if name in bf16_us else None,
+        }
     append_us = time_cache_append(main_r["w"], a.steps, a.warmup, torch, br)
-    prefill = None
+    prefill = prefill_mla = None
     if not a.no_prefill:
         prefill = time_prefill(a.prefill_workload, max(2, min(a.steps, 10)), 2, torch, br, synth)
+        if a.mla_prefill_workload:
+            prefill_mla = time_prefill(a.mla_prefill_workload, max(2, min(a.steps, 10)), 2, torch,
+                                       br, synth)
     shards = None
     if not a.no_shards:
         shards = {}
@@ -533,7 +601,9 @@ def main():
         "cache_append_us": append_us,
         "also": extras,
         "shard_compare": shards,
+        "fp8_cache": fp8,
         "prefill": prefill,
+        "prefill_mla": prefill_mla,
     }
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)

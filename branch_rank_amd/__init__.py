@@ -28,6 +28,7 @@ KERNELS = {"auto": MLRA_KERNEL_AUTO, "portable": MLRA_KERNEL_PORTABLE,
 EXPORTS = ("mlra_workspace_size", "mla_absorb_q", "mla_decode_attn", "mla_out_proj",
            "mlra_decode", "mlra_decode_noalloc", "mlra_select_decode_kernel",
            "mlra_cache_append", "mlra_cache_append_fp8", "mlra_prefill",
+           "mla_prefill_workspace_size", "mla_prefill",
            "mlra_set_kernel_timing", "mlra_status_string", "mlra_last_error_detail")
 
 
@@ -83,6 +84,8 @@ def lib():
                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, I32,
                                   ctypes.c_float, ctypes.c_float, P],
         "mlra_prefill": [CP, I32, I32, P, P, P, P, KP, P, ctypes.c_int, P],
+        "mla_prefill_workspace_size": [CP, I32, I32, ctypes.POINTER(SZ)],
+        "mla_prefill": [CP, I32, P, P, P, P, KP, P, SZ, P, ctypes.c_int, P],
         "mlra_set_kernel_timing": [P, P],
         "mlra_status_string": [ctypes.c_int],
         "mlra_last_error_detail": [],
@@ -360,6 +363,38 @@ def mlra_prefill(cfg, num_branches, q_nope, q_rope, w_uk, w_uv, cache, out, stre
     od = MLRA_BF16 if out.dtype == t.bfloat16 else MLRA_FP32
     check(lib().mlra_prefill(ctypes.byref(cfg), num_branches, B, qn, qr, wk, wv,
                              ctypes.byref(cache), op, od, _stream(stream)))
+
+
+def mla_prefill_workspace_size(cfg, batch, max_len):
+    """Bytes of workspace mla_prefill needs (host only)."""
+    n = ctypes.c_size_t(0)
+    check(lib().mla_prefill_workspace_size(ctypes.byref(cfg), batch, max_len, ctypes.byref(n)))
+    return n.value
+
+
+def mla_prefill(cfg, q_nope, q_rope, w_uk, w_uv, cache, out, workspace=None, stream=None):
+    """Causal prefill of MLA in the unabsorbed (multi-head) form (mla_prefill):
+    arguments as for mlra_prefill; the up-projected keys and values live in
+    `workspace` (a uint8 device tensor of mla_prefill_workspace_size bytes,
+    allocated here when not given)."""
+    t = _torch()
+    B, T = cache._batch, cache.max_len
+    dt = _dtype(cfg)
+    H = cfg.num_heads
+    qn = _need(q_nope, "q_nope", (B, T, H, cfg.d_nope), dt)
+    qr = _need(q_rope, "q_rope", (B, T, H, cfg.d_rope), dt)
+    wk = _need(w_uk, "w_uk", (H, cfg.d_latent, cfg.d_nope), dt)
+    wv = _need(w_uv, "w_uv", (H, cfg.d_latent, cfg.d_v), dt)
+    if out.dtype not in (t.float32, t.bfloat16):
+        raise ValueError("out must be float32 or bfloat16")
+    op = _need(out, "out", (B, T, H, cfg.d_v), out.dtype)
+    od = MLRA_BF16 if out.dtype == t.bfloat16 else MLRA_FP32
+    need = mla_prefill_workspace_size(cfg, B, T)
+    if workspace is None:
+        workspace = t.empty(max(need, 256), dtype=t.uint8, device=out.device)
+    check(lib().mla_prefill(ctypes.byref(cfg), B, qn, qr, wk, wv, ctypes.byref(cache),
+                            workspace.data_ptr(), workspace.numel(), op, od, _stream(stream)))
+    return workspace
 
 
 def set_kernel_timing(before=None, after=None):

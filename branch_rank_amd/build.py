@@ -19,17 +19,18 @@ PROBE_SRC = "probe_read.hip"
 PROBE_LIB = os.path.join(PKG, "libmlra_probe.so")
 
 SOURCES = ["mlra_api.cpp", "kernels_generic.hip", "decode_mfma.hip", "decode_branch.hip",
-           "decode_wide.hip", "proj_mfma.hip", "cache_append.hip", "prefill_branch.hip"]
+           "decode_wide.hip", "proj_mfma.hip", "cache_append.hip", "prefill_branch.hip",
+           "prefill_mha.hip"]
 # The split-KV decode kernels hold no NaN by construction (finite scores, -inf
 # for masked tokens): without NaN semantics their max reductions need no
 # canonicalising moves.
 EXTRA = {"decode_mfma.hip": ["-fno-honor-nans"], "decode_branch.hip": ["-fno-honor-nans"],
          "decode_wide.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "prefill_branch.hip": ["-fno-honor-nans"]}
-# decode_wide.hip holds 400 registers of query and output per lane: with the
-# MFMA results selected into VGPRs the register allocator splits them between
-# the VGPR and AGPR files without spilling (the default, every MFMA result in
-# AGPRs, spills about 1 KB per lane)
+         "prefill_branch.hip": ["-fno-honor-nans"], "prefill_mha.hip": ["-fno-honor-nans"]}
+# decode_wide.hip holds 200 registers of query and output per lane beside a
+# second wave on its SIMD: with the MFMA results selected into VGPRs the
+# register allocator keeps the loop free of spills (the default, every MFMA
+# result in AGPRs, spills)
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -93,6 +93,18 @@ hipError_t launch_prefill_branch(const Geom& g, int T, const void* q_nope, const
                                  float tau, float alpha_q, float alpha_kv, float theta,
                                  hipStream_t s, const KernelTiming& t);
 
+// Causal prefill of MLA in the unabsorbed (MHA) form (prefill_mha.hip): the
+// up-projected keys and values of every head go to `workspace`
+// (prefill_mha_workspace bytes), then causal attention writes out
+// [B][T][H][d_v].
+bool prefill_mha_supported(const Geom& g);
+size_t prefill_mha_workspace(const Geom& g, int T);
+hipError_t launch_prefill_mha(const Geom& g, int T, const void* q_nope, const void* q_rope,
+                              const void* w_uk, const void* w_uv, const void* ckv,
+                              const void* krope, const int32_t* lens, void* workspace, void* out,
+                              bool out_bf16, float tau, float alpha_q, float alpha_kv,
+                              float theta, hipStream_t s, const KernelTiming& t);
+
 // Rotary frequencies omega_k = theta^(-2k / d_r), k < d_r / 2, in double,
 // computed on the host once per (theta, d_r) and passed to the kernels by
 // value, so that no kernel evaluates pow() per element.

@@ -729,6 +729,66 @@ mlra_status_t mlra_prefill(const mlra_config_t* cfg_in, int32_t num_branches, in
   return MLRA_OK;
 }
 
+mlra_status_t mla_prefill_workspace_size(const mlra_config_t* cfg, int32_t batch,
+                                         int32_t max_len, size_t* bytes) {
+  g_detail.clear();
+  TRY(check_cfg(cfg));
+  TRY(check_batch(batch, max_len));
+  if (!bytes) return fail(MLRA_ERR_INVALID_ARG, "bytes is NULL");
+  mlra_config_t c = *cfg;
+  c.num_branches = 1;
+  *bytes = round_up(prefill_mha_workspace(make_geom(&c, batch, nullptr), max_len), 256);
+  return MLRA_OK;
+}
+
+mlra_status_t mla_prefill(const mlra_config_t* cfg_in, int32_t batch, const void* q_nope,
+                          const void* q_rope, const void* w_uk, const void* w_uv,
+                          const mlra_cache_t* cache, void* workspace, size_t ws_bytes, void* out,
+                          mlra_dtype_t out_dtype, void* stream) {
+  g_detail.clear();
+  if (!cfg_in) return fail(MLRA_ERR_INVALID_ARG, "cfg is NULL");
+  mlra_config_t cfg = *cfg_in;
+  cfg.num_branches = 1;
+  TRY(check_cfg(&cfg));
+  TRY(check_cache(&cfg, cache, batch));
+  if (out_dtype != MLRA_BF16 && out_dtype != MLRA_FP32)
+    return fail(MLRA_ERR_INVALID_ARG, "unknown out_dtype");
+  if (cache->fp8) return fail(MLRA_ERR_UNSUPPORTED, "the prefill reads bf16 caches only");
+  const Geom g = make_geom(&cfg, batch, cache);
+  const bool ranges_ok = (int64_t)cache->max_len * cache->ckv_token_stride * 2 < 0x7fffffffLL &&
+                         (int64_t)cache->max_len * cache->krope_token_stride * 2 < 0x7fffffffLL &&
+                         (int64_t)cache->max_len * 256 < 0x7fffffffLL;
+  if (cfg.dtype != MLRA_BF16 || !prefill_mha_supported(g) || !ranges_ok)
+    return fail(MLRA_ERR_UNSUPPORTED,
+                "mla_prefill supports bf16 MLA at d_latent 512, d_rope 64, d_nope 128, d_v 128 "
+                "and per-sequence byte ranges below 2^31");
+  if ((int64_t)batch * cache->max_len > kMaxPrefillRows)
+    return fail(MLRA_ERR_UNSUPPORTED, "batch * max_len must stay at or below %d prompt rows",
+                kMaxPrefillRows);
+  if (batch == 0 || cache->max_len == 0) return MLRA_OK;
+  TRY(check_ptr(q_nope, "q_nope"));
+  TRY(check_ptr(q_rope, "q_rope"));
+  TRY(check_ptr(w_uk, "w_uk"));
+  TRY(check_ptr(w_uv, "w_uv"));
+  TRY(check_ptr(out, "out"));
+  const size_t need = round_up(prefill_mha_workspace(g, cache->max_len), 256);
+  if (!workspace || ws_bytes < need)
+    return fail(MLRA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(MLRA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  int dev, cus;
+  TRY(current_device(&dev, &cus));
+  KernelTiming timing;
+  timing.start = g_ev_before;
+  timing.stop = g_ev_after;
+  TRY_HIP(launch_prefill_mha(g, cache->max_len, q_nope, q_rope, w_uk, w_uv, cache->ckv,
+                             cache->krope, cache->cache_lens, workspace, out,
+                             out_dtype == MLRA_BF16, tau_of(&cfg), cfg.alpha_q, cfg.alpha_kv,
+                             cfg.rope_theta, static_cast<hipStream_t>(stream), timing),
+          "mla_prefill launch");
+  return MLRA_OK;
+}
+
 mlra_status_t mlra_select_decode_kernel(const mlra_config_t* cfg, int32_t batch,
                                         const mlra_cache_t* cache, mlra_kernel_t* kernel) {
   g_detail.clear();

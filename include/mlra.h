@@ -292,7 +292,8 @@ MLRA_API mlra_status_t mlra_cache_append_fp8(const mlra_config_t* cfg, int32_t b
  *   out     device [batch][max_len][H][d_v], out_dtype; rows t >= L_b get 0.
  *
  * One kernel: absorption, attention and the W_UV projection stay on chip, so
- * no workspace is needed. Supported: bf16 MLRA-4 at d_latent 512, d_rope 64,
+ * no workspace is needed. For MLA (num_branches = 1) use mla_prefill, the
+ * unabsorbed form. Supported: bf16 MLRA-4 at d_latent 512, d_rope 64,
  * d_nope 128, d_v 128, per-sequence byte ranges below 2^31 and
  * batch * max_len <= 2^22 rows, else UNSUPPORTED; argument checks as for
  * mlra_decode. With d_c' = d_nope = d_v this absorbed form costs the same
@@ -302,6 +303,35 @@ MLRA_API mlra_status_t mlra_prefill(const mlra_config_t* cfg, int32_t num_branch
                                     const void* q_nope, const void* q_rope, const void* w_uk,
                                     const void* w_uv, const mlra_cache_t* cache, void* out,
                                     mlra_dtype_t out_dtype, void* stream);
+
+/* Causal prefill of MLA (one branch) in the unabsorbed, multi-head form
+ * ("vllbc02MLA", 苏神思路: the prefill is compute-bound and runs as ordinary
+ * multi-head attention over keys and values up-projected from the latent;
+ * the decode uses the absorbed form; "MLA多头潜在注意力机制" 3.2-3.3: K^N =
+ * C W_UK and V = C W_UV per head, the RoPE key shared by all heads, a key
+ * after the query's position masked). For every position t < L_b of every
+ * sequence b, out[b][t][h] is what mlra_decode with num_branches = 1 returns
+ * for sequence b when its cache holds the rows 0..t and its query sits at
+ * position t; rows t >= L_b get 0. cfg->num_branches is ignored (1).
+ *
+ *   q_nope, q_rope, w_uk, w_uv, cache, out   as for mlra_prefill
+ *   workspace  device buffer of at least mla_prefill_workspace_size() bytes
+ *              (256-byte aligned): K^N (pre-scaled by alpha_q tau log2 e),
+ *              V [B][H][T][128] and k^R [B][T][64] as fp16, T = max_len;
+ *              2 * B * T * (256 H + 64) bytes.
+ *
+ * Two kernels: the up-projection (a bf16 MFMA GEMM per head) and causal
+ * flash attention on fp16 MFMA. Supported: bf16, d_latent 512, d_rope 64,
+ * d_nope 128, d_v 128, any head count, per-sequence byte ranges below 2^31
+ * and batch * max_len <= 2^22 rows, else UNSUPPORTED; an fp8 cache is
+ * UNSUPPORTED. Enqueued on `stream`; nothing is allocated. The timing events
+ * of mlra_set_kernel_timing bracket the attention kernel. */
+MLRA_API mlra_status_t mla_prefill_workspace_size(const mlra_config_t* cfg, int32_t batch,
+                                                  int32_t max_len, size_t* bytes);
+MLRA_API mlra_status_t mla_prefill(const mlra_config_t* cfg, int32_t batch, const void* q_nope,
+                                   const void* q_rope, const void* w_uk, const void* w_uv,
+                                   const mlra_cache_t* cache, void* workspace, size_t ws_bytes,
+                                   void* out, mlra_dtype_t out_dtype, void* stream);
 
 /* Instrumentation: when both are non-NULL hipEvent_t handles (created by the
  * caller, owned by the caller, valid until timing is stopped), every later

@@ -121,6 +121,9 @@ WORKLOADS = {
     # 4096 tokens, one query per position (q_rows = 4096)
     "mlra4_prefill_b4_t4k": Workload("mlra4_prefill_b4_t4k", 4, n=4, cache_len=4096,
                                      alpha_q=_AQ4, alpha_kv=_AKV4, seed=1008, **DSV3),
+    # causal prefill of MLA (one branch) in the same shape
+    "mla_prefill_b4_t4k": Workload("mla_prefill_b4_t4k", 4, n=1, cache_len=4096, seed=1009,
+                                   **MLA_SCALES, **DSV3),
     "mla_tp4_b16_l128k": Workload("mla_tp4_b16_l128k", 16, 32, 512, 64, 128, 128, 1, 131072,
                                   seed=1007, **MLA_SCALES),
     "mlra4_shard_b16_l128k": Workload("mlra4_shard_b16_l128k", 16, 128, 128, 64, 128, 128, 1,

@@ -34,7 +34,7 @@ def gpu_present():
 def test_library_exports_every_declared_symbol():
     L = br.lib()
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(br.EXPORTS)
@@ -366,3 +366,32 @@ def test_fp8_append_validation(kw, sc, sr):
     assert L.mlra_cache_append_fp8(ctypes.byref(c), 2, FAKE, None, 1e-6, FAKE, FAKE, 576 * 8,
                                    576, 576 * 8, 576, FAKE, 8, sc, sr, None) == \
         br.MLRA_ERR_INVALID_ARG
+
+
+# ---- mla_prefill (MLA in the unabsorbed form), host only ----
+
+def test_mla_prefill_workspace_size():
+    c = cfg(n=1)
+    n = br.mla_prefill_workspace_size(c, 4, 4096)
+    assert n >= 2 * 4 * 4096 * (256 * 128 + 64)
+    assert br.mla_prefill_workspace_size(c, 0, 4096) == 0
+
+
+@pytest.mark.parametrize("kw,expect", [(dict(n=1, dtype="fp32"), br.MLRA_ERR_UNSUPPORTED),
+                                       (dict(n=1, d_latent=256), br.MLRA_ERR_UNSUPPORTED),
+                                       (dict(n=1, d_v=64), br.MLRA_ERR_UNSUPPORTED)])
+def test_mla_prefill_unsupported_shapes(kw, expect):
+    c = cfg(**kw)
+    k = br.Cache(FAKE, FAKE + 1024, 576 * 128, 576, 576 * 128, 576, FAKE, 128)
+    assert br.lib().mla_prefill(ctypes.byref(c), 2, FAKE, FAKE, FAKE, FAKE, ctypes.byref(k),
+                                FAKE, 1 << 40, FAKE, br.MLRA_FP32, None) == expect
+
+
+def test_mla_prefill_workspace_checked():
+    c = cfg(n=1)
+    k = br.Cache(FAKE, FAKE + 1024, 576 * 128, 576, 576 * 128, 576, FAKE, 128)
+    L = br.lib()
+    assert L.mla_prefill(ctypes.byref(c), 2, FAKE, FAKE, FAKE, FAKE, ctypes.byref(k), FAKE, 1024,
+                         FAKE, br.MLRA_FP32, None) == br.MLRA_ERR_WORKSPACE
+    assert L.mla_prefill(ctypes.byref(c), 2, FAKE, FAKE, FAKE, FAKE, ctypes.byref(k), FAKE + 16,
+                         1 << 40, FAKE, br.MLRA_FP32, None) == br.MLRA_ERR_INVALID_ARG

@@ -87,3 +87,31 @@ def test_prefill_with_nan_guard_rows():
             worst = max(worst, row_rel_err(got[b, :L], ref[b, :L]))
     say(f"prefill with poisoned rows: worst row rel err {worst:.2e}")
     assert worst <= TOL
+
+
+def test_mla_prefill_with_nan_guard_rows():
+    # the up-projection and the attention read cache rows 0..t for position t;
+    # rows past L_b are NaN
+    w = WORKLOADS["mla_prefill_b4_t4k"].replace(batch=3, heads=8)
+    T = 200
+    lens = np.array([161, 33, 0], np.int32)
+    inp = make_inputs(w, lens=lens, max_len=T, q_rows=T)
+    d = Dev(w, inp, poison=True)
+    cfg = config_for(w)
+    out = torch.empty(3, T, w.heads, w.d_v, dtype=torch.float32, device="cuda")
+    ws = torch.full((br.mla_prefill_workspace_size(cfg, 3, T),), 0xFF, dtype=torch.uint8,
+                    device="cuda")  # every fp16 word NaN
+    br.mla_prefill(cfg, d.q_nope, d.q_rope, d.w_uk, d.w_uv, d.cache(cfg), out, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item(), "NaN reached the prefill output"
+    got = host(out)
+    ref = oracle.mlra_prefill_ref(inp["q_nope"], inp["q_rope"], inp["w_uk"], inp["w_uv"],
+                                  inp["ckv"], inp["krope"], lens, 1, tau=w.tau,
+                                  alpha_q=w.alpha_q, alpha_kv=w.alpha_kv, theta=w.theta)
+    worst = 0.0
+    for b, L in enumerate(lens):
+        assert not np.any(got[b, L:])
+        if L:
+            worst = max(worst, row_rel_err(got[b, :L], ref[b, :L]))
+    say(f"mla_prefill with poisoned rows and workspace: worst row rel err {worst:.2e}")
+    assert worst <= TOL

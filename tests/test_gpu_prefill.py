@@ -101,3 +101,89 @@ def test_prefill_full_size_sampled_rows():
         assert err <= TOL
     for b, L in enumerate(lens):
         assert not np.any(got[b, L:])
+
+
+# ---- MLA (one branch) in the unabsorbed, multi-head form: mla_prefill ----
+
+def run_mla_prefill(w, inp, d=None, out_dtype=torch.float32):
+    d = Dev(w, inp) if d is None else d
+    cfg = config_for(w)
+    out = torch.empty(d.B, d.Lmax, w.heads, w.d_v, dtype=out_dtype, device="cuda")
+    br.mla_prefill(cfg, d.q_nope, d.q_rope, d.w_uk, d.w_uv, d.cache(cfg), out)
+    torch.cuda.synchronize()
+    return out, d
+
+
+@pytest.mark.parametrize("lens,T", [([300, 1, 129, 0], 300), ([128, 127, 33], 160),
+                                    ([64, 65, 255], 256)])
+def test_mla_prefill_all_rows_small(lens, T):
+    # several 128-position blocks and 64-position projection blocks, ragged
+    # ends, a one-token prompt and an empty one; MLA at the pages' scales
+    # (alpha_q = alpha_kv = sqrt(7168 / 512)) against the unabsorbed oracle
+    w = WORKLOADS["mla_prefill_b4_t4k"].replace(batch=len(lens), heads=8)
+    inp = make_inputs(w, lens=np.array(lens, np.int32), max_len=T, q_rows=T)
+    say(f"mla_prefill lens {lens} T={T}")
+    got, _ = run_mla_prefill(w, inp)
+    err = check_rows(host(got), oracle_prefill(w, inp), lens)
+    say(f"  worst row rel err {err:.2e}")
+    assert err <= TOL
+
+
+def test_mla_prefill_bf16_output_and_clamped_lengths():
+    w = WORKLOADS["mla_prefill_b4_t4k"].replace(batch=3, heads=4)
+    T = 96
+    inp = make_inputs(w, lens=np.array([96, 40, 0], np.int32), max_len=T, q_rows=T)
+    want, d = run_mla_prefill(w, inp)
+    got16, _ = run_mla_prefill(w, inp, d=d, out_dtype=torch.bfloat16)
+    assert torch.equal(got16, want.to(torch.bfloat16))
+    d.lens.copy_(torch.tensor([96 + 7, 40, -5], dtype=torch.int32))
+    got, _ = run_mla_prefill(w, inp, d=d)
+    assert torch.equal(got, want)
+    assert check_rows(host(want), oracle_prefill(w, inp), [96, 40, 0]) <= TOL
+
+
+def test_mla_prefill_row_equals_decode_of_cut_cache():
+    # row t of the prefill is the decode (num_branches = 1) of the cache cut
+    # after row t: both through the library, on the same inputs
+    w = WORKLOADS["mla_prefill_b4_t4k"].replace(batch=2, heads=128)
+    T = 200
+    lens = np.array([200, 77], np.int32)
+    inp = make_inputs(w, lens=lens, max_len=T, q_rows=T)
+    got, d = run_mla_prefill(w, inp)
+    got = host(got)
+    cfg = config_for(w, q_residue=True)
+    for b, t in [(0, 0), (0, 31), (0, 127), (0, 128), (0, 199), (1, 76)]:
+        dec = Dev(w.replace(batch=1), dict(ckv=inp["ckv"][b:b + 1], krope=inp["krope"][b:b + 1],
+                                           q_nope=inp["q_nope"][b:b + 1, t],
+                                           q_rope=inp["q_rope"][b:b + 1, t], w_uk=inp["w_uk"],
+                                           w_uv=inp["w_uv"], lens=np.array([t + 1], np.int32)))
+        row = host(dec.decode(cfg))[0]
+        err = row_rel_err(got[b, t], row)
+        say(f"  row ({b}, {t}) vs decode: rel err {err:.2e}")
+        assert err <= 2 * TOL
+
+
+@pytest.mark.slow
+def test_mla_prefill_full_size_sampled_rows():
+    w = WORKLOADS["mla_prefill_b4_t4k"]
+    T = w.cache_len
+    lens = np.array([T, T - 1, 2049, 1], np.int32)
+    inp = make_inputs(w, lens=lens, q_rows=T)
+    say(f"mla_prefill B={w.batch} T={T} H={w.heads}")
+    got, _ = run_mla_prefill(w, inp)
+    got = host(got)
+    rng = np.random.default_rng(6)
+    picks = [(0, 0), (0, 31), (0, 127), (0, 128), (0, T - 1), (1, T - 2), (2, 2048), (2, 1000),
+             (3, 0)] + [(int(b), int(rng.integers(0, lens[b]))) for b in rng.integers(0, 3, 6)]
+    for b, t in picks:
+        # the unabsorbed decode of the cache cut after row t, one query
+        ref = oracle.mlra_decode_ref(inp["q_nope"][b:b + 1, t], inp["q_rope"][b:b + 1, t],
+                                     inp["w_uk"], inp["w_uv"], inp["ckv"][b:b + 1, :t + 1],
+                                     inp["krope"][b:b + 1, :t + 1], np.array([t + 1], np.int32), 1,
+                                     tau=w.tau, alpha_q=w.alpha_q, alpha_kv=w.alpha_kv,
+                                     theta=w.theta)[0]
+        err = row_rel_err(got[b, t], ref)
+        say(f"  row ({b}, {t}): rel err {err:.2e}")
+        assert err <= TOL
+    for b, L in enumerate(lens):
+        assert not np.any(got[b, L:])
