@@ -33,12 +33,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "latent_decode_traffic.json")
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
 KERNEL_SRC = {"prefill": "branch_rank_amd/csrc/prefill_branch.hip",
               "branch": "branch_rank_amd/csrc/decode_branch.hip",
+              "wide": "branch_rank_amd/csrc/decode_wide.hip",
               "head_group": "branch_rank_amd/csrc/decode_mfma.hip",
               "portable": "branch_rank_amd/csrc/kernels_generic.hip"}
 # headers each kernel's source includes (their text is part of the kernel)
 _CSRC = "branch_rank_amd/csrc/"
 KERNEL_DEPS = {"prefill": ["device_common.h", "internal.h"],
                "branch": ["branch_tiles.h", "device_common.h", "internal.h"],
+               "wide": ["device_common.h", "internal.h"],
                "head_group": ["device_common.h", "internal.h"],
                "portable": ["internal.h", "plan_device.h"]}
 
@@ -108,17 +110,19 @@ def kernel_flops_bytes(w, lens, fp8=False):
 
 
 def traffic_for(workload, kernel, path=TRAFFIC_FILE):
-    """HBM bytes per launch from a committed counter summary, if it was taken
-    on this workload, this kernel and the kernel's current source; else None."""
+    """HBM bytes per launch from a committed counter summary (one record or a
+    list of them), if one was taken on this workload, this kernel and the
+    kernel's current source; else None."""
     try:
         with open(path) as f:
-            t = json.load(f)
+            recs = json.load(f)
         src = KERNEL_SRC[kernel]
         sha = source_sha(kernel)
-        if (t.get("kernel_source") != src or t.get("kernel_sha256") != sha
-                or t.get("workload") != workload):
-            return None
-        return int(t["hbm_bytes_per_launch"])
+        for t in recs if isinstance(recs, list) else [recs]:
+            if (t.get("kernel_source") == src and t.get("kernel_sha256") == sha
+                    and t.get("workload") == workload):
+                return int(t["hbm_bytes_per_launch"])
+        return None
     except (OSError, ValueError, KeyError):
         return None
 
