@@ -300,14 +300,19 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
     };
     // wait for this wave's loads of tile t (fp8: two instructions per tile on
     // waves 0 and 1, one on the others), then (fp8) convert its codes
+    // (fp8: nothing to wait for here; conv(u) below waits for tile u's codes
+    // and converts them in the phase before the barrier that opens M(u))
     auto wait_tile = [&](int t) {
+      if constexpr (!FP8) wait_tiles<C, NS - 2>(min(NS - 2, ntiles - 1 - t), wave);
+    };
+    // fp8: this wave's codes of tile u have landed (the tiles issued after it,
+    // up to u + D - 1, may be in flight), then its lanes convert them
+    auto conv = [&](int u) {
       if constexpr (FP8) {
-        if (wave < 2) wait_tiles_per<2, NS - 2>(min(NS - 2, ntiles - 1 - t));
-        else wait_tiles_per<1, NS - 2>(min(NS - 2, ntiles - 1 - t));
+        if (wave < 2) wait_tiles_per<2, D - 1>(min(D - 1, ntiles - 1 - u));
+        else wait_tiles_per<1, D - 1>(min(D - 1, ntiles - 1 - u));
         asm volatile("" ::: "memory");
         convert8();
-      } else {
-        wait_tiles<C, NS - 2>(min(NS - 2, ntiles - 1 - t), wave);
       }
     };
     auto issue_if = [&](int t) {
@@ -316,13 +321,7 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
     // steady tiles (1 <= t < ntiles - D - 1): the wait keeps NS - 2 tiles in
     // flight, the tile loaded is full and not the last, and no row is masked
     auto wait_steady = [&] {
-      if constexpr (FP8) {
-        if (wave < 2) wait_vm<(NS - 2) * 2>();
-        else wait_vm<(NS - 2) * 1>();
-        asm volatile("" ::: "memory");
-        convert8();
-        return;
-      }
+      if constexpr (FP8) return;
       if (wave < C::NR) wait_vm<(NS - 2) * (C::NL / C::NW + 1)>();
       else wait_vm<(NS - 2) * (C::NL / C::NW)>();
     };
@@ -456,12 +455,18 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
     // u + NS - 1 is issued right after b(2u + 2), at the start of V(u) in the
     // first group and of M(u) in the second. Both groups pass 2 ntiles + 2
     // barriers per segment.
+    // fp8: tile u is converted in the phase before b(2u + 1): the first group
+    // at the start of V(u - 1), the second at the start of M(u - 1); the bf16
+    // tile it overwrites (u - 2) was last read in the second group's V(u - 2),
+    // which ends at b(2u)
     if (!lag) {
+      conv(0);
       wait_tile(0);
       bar();
       mphase(0, F_{}, T_{}, F_{});
       bar();
       issue_if(D);
+      if (1 < ntiles) conv(1);
       vphase();
       int t = 1;
       for (; t < steady_end; ++t) {
@@ -470,6 +475,7 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
         mphase(t, T_{}, T_{}, T_{});
         bar();
         issue_full(t + D);
+        conv(t + 1);
         vphase();
       }
       for (; t < ntiles; ++t) {
@@ -478,16 +484,19 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
         mphase(t, T_{}, T_{}, F_{});
         bar();
         issue_if(t + D);
+        if (t + 1 < ntiles) conv(t + 1);
         vphase();
       }
       bar();
       mphase(ntiles, T_{}, F_{}, F_{});
       bar();
     } else {
+      conv(0);
       wait_tile(0);
       bar();
       bar();
       issue_if(D);
+      if (1 < ntiles) conv(1);
       mphase(0, F_{}, T_{}, F_{});
       if (1 < ntiles) wait_tile(1);
       bar();
@@ -496,6 +505,7 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
       int t = 1;
       for (; t < steady_end; ++t) {
         issue_full(t + D);
+        conv(t + 1);
         mphase(t, T_{}, T_{}, T_{});
         wait_steady();
         bar();
@@ -504,6 +514,7 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
       }
       for (; t < ntiles; ++t) {
         issue_if(t + D);
+        if (t + 1 < ntiles) conv(t + 1);
         mphase(t, T_{}, T_{}, F_{});
         if (t + 1 < ntiles) wait_tile(t + 1);
         bar();
