@@ -11,8 +11,10 @@
 // Mapping onto CDNA4:
 //  * A workgroup owns one work item and 16*NW heads (16 per wave); when that
 //    is less than all heads, the workgroups of one item's head groups are
-//    placed on the same XCD back to back so that the second read of every KV
-//    tile hits that XCD's L2.
+//    placed on the same XCD back to back, reading each tile at about the same
+//    time. The tiles use device-scope non-temporal loads even then: in paired
+//    runs on one box plain loads were no faster for two workgroups per item
+//    (MLA at 16 x 32K: 280.7 / 281.5 us against 275.4 / 279.6 us).
 //  * KV tiles (32 tokens) stream HBM -> LDS with buffer_load_dwordx4 ... lds
 //    (no VGPR staging) through an NS-stage ring shared by all waves; vmcnt
 //    waits are placed by hand because the compiler does not order LDS-DMA
@@ -531,7 +533,11 @@ hipError_t launch_nb(const Geom& g, const QView& q, const void* c, const void* k
 
 }  // namespace
 
-bool decode_mfma_reads_residue(const Geom&) { return true; }
+// q~'s residue for one or two branches: a softmax over one or two branch
+// slices on a bf16 query alone moves output rows by up to ~1.1e-2 at the
+// pages' scales; four branches average their errors (<= 8.6e-3 measured), as
+// in the branch kernel, and the residue would double the latent k-steps.
+bool decode_mfma_reads_residue(const Geom& g) { return g.n < 4; }
 
 bool decode_mfma_supported(const Geom& g) {
   if (g.dr != kDR) return false;
