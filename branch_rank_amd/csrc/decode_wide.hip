@@ -70,10 +70,9 @@ constexpr int kDC = 512;                 // latent width
 constexpr int kDR = 64;                  // RoPE width
 constexpr int kLat = kT * kDC * 2;       // latent bytes of a stage
 constexpr int kStage = kLat + kT * kDR * 2;  // 36 KB
-constexpr int kH = 128;                  // heads
+constexpr int kHMax = 128;               // most heads
 constexpr int kNI = kT + 4;              // DMA instructions per tile (32 latent rows + 4 RoPE)
 constexpr int kKS = kDC / 32;            // latent k-steps
-constexpr int kHB = kH / 16;             // 16-head blocks
 constexpr int kNS = 4;                   // tile stages (144 KB of LDS)
 // fp8 codes: 18 KB per stage, 16 latent DMA instructions (two rows each) and
 // two RoPE instructions (16 rows each) per tile
@@ -120,23 +119,32 @@ __device__ __forceinline__ i32x4 bf16_to_f16x8(i32x4 x) {
   return r;
 }
 
-template <int NW>
+// Wave shape for H heads: the score waves (the first QW; with fewer than 16
+// heads per wave the others only load, convert and accumulate) own
+// HPW = 16 NBQ heads each; every wave accumulates CPW latent columns of all H
+// heads.
+template <int NW, int H>
 struct WCfg {
-  static constexpr int HPW = kH / NW;         // heads per wave (scores, softmax)
-  static constexpr int NBQ = HPW / 16;        // 16-head blocks per wave
-  static constexpr int CPW = kDC / NW;        // latent columns per wave (P V)
-  static constexpr int CBW = CPW / 16;        // PV column blocks per wave
-  static constexpr int LR = kT / NW;          // latent rows each wave loads per tile
-  static_assert(HPW % 16 == 0 && CPW % 16 == 0 && kT % NW == 0 && NW >= 4, "wave shape");
+  static constexpr int HB = H / 16;                  // 16-head blocks
+  static constexpr int QW = HB < NW ? HB : NW;       // score waves
+  static constexpr int HPW = H / QW;                 // heads per score wave
+  static constexpr int NBQ = HPW / 16;               // 16-head blocks per score wave
+  static constexpr int CPW = kDC / NW;               // latent columns per wave (P V)
+  static constexpr int CBW = CPW / 16;               // PV column blocks per wave
+  static constexpr int LR = kT / NW;                 // latent rows each wave loads per tile
+  static constexpr int PB = HB < 4 ? HB : 4;         // P^T fragments read at a time
+  static_assert(H % 16 == 0 && H <= kHMax && HPW % 16 == 0 && CPW % 16 == 0 && kT % NW == 0 &&
+                    NW >= 4 && HB % PB == 0,
+                "wave shape");
 };
 
-template <int NB, bool F16, int NW, bool FP8>
+template <int NB, bool F16, int NW, bool FP8, int H>
 __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p) {
   using O_ = Op<F16>;
   using V = typename O_::V;
   using E = typename O_::E;
-  using C = WCfg<NW>;
-  constexpr int NBQ = C::NBQ, CBW = C::CBW;
+  using C = WCfg<NW, H>;
+  constexpr int NBQ = C::NBQ, CBW = C::CBW, kHB = C::HB, QW = C::QW, PB = C::PB;
   constexpr int KPB = kKS / NB;  // latent k-steps per branch
   constexpr float kRescale = F16 ? 15.f : 16.f;
   static_assert(kKS % NB == 0, "branches");
@@ -145,13 +153,13 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
   // LDS: the tile ring (bf16: kNS stages of 36 KB, converted in place; fp8:
   // two 36 KB fp16 tiles, the one in use and the next, then kNS stages of
   // 18 KB of codes), then the P exchange (P^T fragments of NB branches x
-  // eight 16-head blocks, 1 KB each: lane l's 16 bytes at 16 l, the B-operand
-  // layout), the rescale factors per (branch, head) and one flag per (wave,
-  // branch) that says whether any of its heads' references moved
+  // H / 16 16-head blocks, 1 KB each: lane l's 16 bytes at 16 l, the B-operand
+  // layout), the rescale factors per (branch, head) and one flag per (score
+  // wave, branch) that says whether any of its heads' references moved
   constexpr int kPBytes = NB * kHB * 1024;
   constexpr int kRing = FP8 ? 2 * kStage + kNS * kStage8 : kNS * kStage;
   __shared__ __attribute__((aligned(1024))) char smem_raw[kRing + kPBytes];
-  __shared__ float fl_raw[NB * kH];
+  __shared__ float fl_raw[NB * H];
   __shared__ int flags_raw[NW * NB];
   char LDS_AS* smem = (char LDS_AS*)smem_raw;
   char LDS_AS* pl = smem + kRing;
@@ -228,7 +236,9 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
 #pragma unroll
     for (int nb = 0; nb < NBQ; ++nb) {
       const __bf16* qrow =
-          p.q_abs + ((int64_t)bseq * kH + C::HPW * wave + 16 * nb + l16) * p.q_stride + 8 * kg;
+          p.q_abs + ((int64_t)bseq * H + C::HPW * (wave < QW ? wave : 0) + 16 * nb + l16) *
+                        p.q_stride +
+          8 * kg;
       const __bf16* lrow = qrow + p.q_lo;
 #pragma unroll
       for (int ks = 0; ks < kKS + 2; ++ks) {
@@ -287,11 +297,11 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
     // wait until this wave's DMA of `tile` has landed, given the tiles
     // issued after it that may stay in flight (at most kNS - 2)
     auto wait_own = [&](int tile) {
-      constexpr int L = FP8 ? kLR8 / NW : C::LR, H = L + 1;
+      constexpr int L = FP8 ? kLR8 / NW : C::LR, LH = L + 1;
       const int after = min(tile + kNS - 2, ntiles - 1) - tile;
       if (rope_wave) {
-        if (after >= 2) wait_vm<2 * H>();
-        else if (after == 1) wait_vm<H>();
+        if (after >= 2) wait_vm<2 * LH>();
+        else if (after == 1) wait_vm<LH>();
         else wait_vm<0>();
       } else {
         if (after >= 2) wait_vm<2 * L>();
@@ -387,7 +397,26 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
       barrier();  // tile t in LDS (converted); P V of tile t - 1 done
       if (t + kNS - 1 < ntiles) issue(t + kNS - 1);
       const char LDS_AS* st = smem + (FP8 ? (t & 1) : (t & (kNS - 1))) * kStage;
+      // V^T fragment of column block cb
+      auto pv_frag = [&](int cb) -> V {
+        const int coff = 512 * (cb >> 4) + 16 * ((2 * (cb & 15)) ^ pv_w);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(st + pv_lo + coff));
+        const i16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(st + pv_lo + 16 * 1024 + coff));
+        const i16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(V, vv);
+      };
 
+      // scores and softmax (score waves); the others convert their share of
+      // the next tile
+      if (wave >= QW) {
+        if constexpr (F16) {
+          if (t + 1 < ntiles) {
+            wait_own(t + 1);
+            convert(t + 1);
+          }
+        }
+      } else {
       // score bias per token row: 0, or -inf past the segment's end
       f32x4 bias[2];
       const int valid = t1 - (t0 + t * kT);
@@ -418,15 +447,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
                                                                        mb * 16 * 1024)) ^
                                                           (64 * ks)));
       };
-      // V^T fragment of column block cb
-      auto pv_frag = [&](int cb) -> V {
-        const int coff = 512 * (cb >> 4) + 16 * ((2 * (cb & 15)) ^ pv_w);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(st + pv_lo + coff));
-        const i16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(st + pv_lo + 16 * 1024 + coff));
-        const i16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        return __builtin_bit_cast(V, vv);
-      };
+
 
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
@@ -512,9 +533,10 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
           l_run[j][nb] += ps;
           const int hb = NBQ * wave + nb;
           *(V LDS_AS*)(pl + ((j * kHB + hb) * 64 + lane) * 16) = P;
-          if (kg == 0) fl[j * kH + 16 * hb + l16] = f;
+          if (kg == 0) fl[j * H + 16 * hb + l16] = f;
         }
         if (lane == 0) flags[wave * NB + j] = moved ? 1 : 0;
+      }
       }
 
       barrier();  // every head's P^T is in LDS
@@ -523,23 +545,23 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
       {
         int any = 0;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) any |= flags[w * NB + jq];
+        for (int w = 0; w < QW; ++w) any |= flags[w * NB + jq];
         if (__builtin_expect(any != 0, 0)) {
 #pragma unroll
           for (int hb = 0; hb < kHB; ++hb) {
-            const float f = fl[jq * kH + 16 * hb + l16];
+            const float f = fl[jq * H + 16 * hb + l16];
 #pragma unroll
             for (int c = 0; c < CBW; ++c) o[c][hb] *= f;
           }
         }
       }
-      // O^T += V^T P^T over this wave's columns for all 128 heads: every V^T
-      // fragment feeds one MFMA per 16-head block; P^T fragments four at a time
+      // O^T += V^T P^T over this wave's columns for all heads: every V^T
+      // fragment feeds one MFMA per 16-head block; P^T fragments PB at a time
 #pragma unroll
-      for (int h0 = 0; h0 < kHB; h0 += 4) {
-        V Pf[4];
+      for (int h0 = 0; h0 < kHB; h0 += PB) {
+        V Pf[PB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < PB; ++i)
           Pf[i] = *(const V LDS_AS*)(pl + ((jq * kHB + h0 + i) * 64 + lane) * 16);
         V Vf[3];
 #pragma unroll
@@ -549,13 +571,13 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
           if (c + 2 < CBW) Vf[(c + 2) % 3] = pv_frag(CBW * wave + c + 2);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) o[c][h0 + i] = O_::mfma(Vf[c % 3], Pf[i], o[c][h0 + i]);
+          for (int i = 0; i < PB; ++i) o[c][h0 + i] = O_::mfma(Vf[c % 3], Pf[i], o[c][h0 + i]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
 
-    // partial state of this segment: m, l as [slot][n][H] (this wave's
+    // partial state of this segment: m, l as [slot][n][H] (a score wave's
     // heads); acc as [slot][H][d_c] (this wave's columns, all heads), 16-byte
     // stores of 4 consecutive latent columns
 #pragma unroll
@@ -564,15 +586,15 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const float lt = sum4(l_run[j][nb]);
-        if (kg == 0) {
-          p.m[((int64_t)slot * NB + j) * kH + head] = m_run[j][nb];
-          p.l[((int64_t)slot * NB + j) * kH + head] = lt;
+        if (kg == 0 && wave < QW) {
+          p.m[((int64_t)slot * NB + j) * H + head] = m_run[j][nb];
+          p.l[((int64_t)slot * NB + j) * H + head] = lt;
         }
       }
     }
 #pragma unroll
     for (int hb = 0; hb < kHB; ++hb) {
-      float* row = p.acc + ((int64_t)slot * kH + 16 * hb + l16) * kDC + C::CPW * wave + 4 * kg;
+      float* row = p.acc + ((int64_t)slot * H + 16 * hb + l16) * kDC + C::CPW * wave + 4 * kg;
 #pragma unroll
       for (int c = 0; c < CBW; ++c) *(f32x4*)(row + 16 * c) = o[c][hb];
     }
@@ -581,7 +603,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
   }
 }
 
-template <int NB, bool F16, int NW, bool FP8>
+template <int NB, bool F16, int NW, bool FP8, int H>
 hipError_t launch_w(const Geom& g, const QView& q, const void* ckv, const void* krope,
                     const Workspace& ws, int items, hipStream_t s, const KernelTiming& t) {
   DecodeParams p;
@@ -600,30 +622,43 @@ hipError_t launch_w(const Geom& g, const QView& q, const void* ckv, const void* 
   p.l = ws.l;
   p.acc = ws.acc;
   p.B = g.B;
-  hipExtLaunchKernelGGL((decode_wide_kernel<NB, F16, NW, FP8>), dim3(items), dim3(64 * NW), 0, s,
+  hipExtLaunchKernelGGL((decode_wide_kernel<NB, F16, NW, FP8, H>), dim3(items), dim3(64 * NW), 0, s,
                         t.start, t.stop, 0, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// MLA: one branch over a 512-wide latent, 64-wide RoPE key, 128 heads. (The
-// kernel is written for n branches with a shared RoPE score; only n = 1 is
-// built, with the MFMAs' results selected into VGPRs: this compiler's pass
-// that moves them to AGPRs fails on a four-branch instantiation.)
+// MLA: one branch over a 512-wide latent, 64-wide RoPE key, 32, 64 or 128
+// heads (all of MLA's heads, or one device's share of them under 2- or 4-way
+// tensor parallelism). (The kernel is written for n branches with a shared
+// RoPE score; only n = 1 is built, with the MFMAs' results selected into
+// VGPRs: this compiler's pass that moves them to AGPRs fails on a four-branch
+// instantiation.)
 bool decode_wide_supported(const Geom& g, bool) {
-  return g.dc == kDC && g.dr == kDR && g.H == kH && g.n == 1;
+  return g.dc == kDC && g.dr == kDR && (g.H == 32 || g.H == 64 || g.H == 128) && g.n == 1;
 }
 
 // fp16 MFMAs on q~ with its residue
 bool decode_wide_reads_residue(const Geom&) { return true; }
 
+template <bool FP8>
+hipError_t launch_wh(const Geom& g, const QView& q, const void* ckv, const void* krope,
+                     const Workspace& ws, int items, hipStream_t s, const KernelTiming& t) {
+  switch (g.H) {
+    case 32: return launch_w<1, true, MLRA_WIDE_WAVES, FP8, 32>(g, q, ckv, krope, ws, items, s, t);
+    case 64: return launch_w<1, true, MLRA_WIDE_WAVES, FP8, 64>(g, q, ckv, krope, ws, items, s, t);
+    case 128: return launch_w<1, true, MLRA_WIDE_WAVES, FP8, 128>(g, q, ckv, krope, ws, items, s, t);
+  }
+  return hipErrorNotSupported;
+}
+
 hipError_t launch_decode_wide(const Geom& g, const QView& q, const void* ckv, const void* krope,
                               const Workspace& ws, int items, hipStream_t s,
                               const KernelTiming& t, bool fp8) {
   if (!decode_wide_supported(g, fp8)) return hipErrorNotSupported;
-  if (fp8) return launch_w<1, true, MLRA_WIDE_WAVES, true>(g, q, ckv, krope, ws, items, s, t);
-  return launch_w<1, true, MLRA_WIDE_WAVES, false>(g, q, ckv, krope, ws, items, s, t);
+  return fp8 ? launch_wh<true>(g, q, ckv, krope, ws, items, s, t)
+             : launch_wh<false>(g, q, ckv, krope, ws, items, s, t);
 }
 
 }  // namespace mlra

@@ -99,7 +99,9 @@ def _fake_cache(c, batch, max_len, ts=None):
     (dict(), 32768, "auto", "branch"),                            # MLRA-4, d_c = 512, H = 128
     (dict(heads=64), 4096, "auto", "branch"),
     (dict(n=1), 4096, "auto", "wide"),                            # MLA
-    (dict(n=1, heads=64), 4096, "auto", "head_group"),
+    (dict(n=1, heads=64), 4096, "auto", "wide"),                 # MLA, 2-way TP share
+    (dict(n=1, heads=32), 4096, "auto", "wide"),                 # MLA, 4-way TP share
+    (dict(n=1, heads=32), 4096, "head_group", "head_group"),
     (dict(n=1), 4096, "head_group", "head_group"),
     (dict(n=2), 4096, "auto", "head_group"),
     (dict(n=1, d_latent=128), 4096, "auto", "branch"),            # one branch shard
@@ -115,7 +117,7 @@ def test_kernel_selection_host_only(kw, max_len, kernel, expect):
 
 
 @pytest.mark.parametrize("kw,kernel", [(dict(n=1), "branch"), (dict(heads=96), "branch"),
-                                       (dict(), "wide"), (dict(n=1, heads=64), "wide"),
+                                       (dict(), "wide"), (dict(n=1, heads=96), "wide"),
                                        (dict(n=1, dtype="fp32"), "wide"),
                                        (dict(heads=96), "head_group"),
                                        (dict(dtype="fp32"), "head_group")])

@@ -36,6 +36,8 @@ def absorbed_oracle(w, inp, n=None):
                                          ("mlra4_b16_l32k", "portable"),
                                          ("mla_b16_l4k", "head_group"),
                                          ("mla_b16_l4k", "wide"),
+                                         ("mla_tp4_b16_l32k", "wide"),
+                                         ("mla_tp4_b16_l32k", "head_group"),
                                          ("shard_b64_ragged", "branch")])
 @pytest.mark.parametrize("chunk", [0, 96])
 def test_decode_with_nan_guard_rows_and_workspace(name, kernel, chunk):
