@@ -13,11 +13,13 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# MLRA_LIB points at another build of the same library (kernel tuning)
+# MLRA_LIB points at another build of the same library: libmlra_debug.so (the
+# device bounds checks), or a tuning build
 LIB_PATH = os.environ.get("MLRA_LIB") or os.path.join(_HERE, "libmlra.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libmlra_debug.so")
 
 MLRA_OK, MLRA_ERR_INVALID_ARG, MLRA_ERR_UNSUPPORTED, MLRA_ERR_WORKSPACE, \
-    MLRA_ERR_NO_DEVICE, MLRA_ERR_HIP = range(6)
+    MLRA_ERR_NO_DEVICE, MLRA_ERR_HIP, MLRA_ERR_BOUNDS = range(7)
 MLRA_BF16, MLRA_FP32 = 0, 1
 MLRA_KERNEL_AUTO, MLRA_KERNEL_PORTABLE, MLRA_KERNEL_HEAD_GROUP, MLRA_KERNEL_BRANCH, \
     MLRA_KERNEL_WIDE = 0, 1, 2, 3, 4
@@ -29,7 +31,8 @@ EXPORTS = ("mlra_workspace_size", "mla_absorb_q", "mla_decode_attn", "mla_out_pr
            "mlra_decode", "mlra_decode_noalloc", "mlra_select_decode_kernel",
            "mlra_cache_append", "mlra_cache_append_fp8", "mlra_prefill",
            "mla_prefill_workspace_size", "mla_prefill",
-           "mlra_set_kernel_timing", "mlra_status_string", "mlra_last_error_detail")
+           "mlra_set_kernel_timing", "mlra_status_string", "mlra_last_error_detail",
+           "mlra_bounds_checks")
 
 
 class MlraError(RuntimeError):
@@ -89,6 +92,7 @@ def lib():
         "mlra_set_kernel_timing": [P, P],
         "mlra_status_string": [ctypes.c_int],
         "mlra_last_error_detail": [],
+        "mlra_bounds_checks": [],
     }
     for name, args in sigs.items():
         f = getattr(L, name)
@@ -109,6 +113,11 @@ def _status_name(st):
 def check(st):
     if st != MLRA_OK:
         raise MlraError(st, lib().mlra_last_error_detail().decode())
+
+
+def bounds_checks():
+    """True when the loaded library is the debug build (device bounds checks)."""
+    return bool(lib().mlra_bounds_checks())
 
 
 # ------------------------------------------------------------ config ----

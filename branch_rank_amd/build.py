@@ -1,6 +1,9 @@
 """Build libmlra.so for gfx950 with hipcc (in-tree, no JIT cache).
 
-python -m branch_rank_amd.build [--jobs N]
+python -m branch_rank_amd.build [--jobs N] [--no-debug]
+
+Builds libmlra.so and, from the same sources with MLRA_DEBUG_BOUNDS (device
+bounds checks, see mlra_bounds_checks in include/mlra.h), libmlra_debug.so.
 """
 
 import argparse
@@ -14,6 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmlra.so")
+DEBUG_LIB = os.path.join(PKG, "libmlra_debug.so")
+OBJ_DEBUG = os.path.join(PKG, "_build_debug")
 # the benchmark's HBM read-ceiling probe (include/mlra_probe.h), a library of its own
 PROBE_SRC = "probe_read.hip"
 PROBE_LIB = os.path.join(PKG, "libmlra_probe.so")
@@ -42,10 +47,10 @@ FLAGS = [
 ]
 
 
-def _compile(src):
-    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src),
-           "-o", obj]
+def _compile(src, debug=False):
+    obj = os.path.join(OBJ_DEBUG if debug else OBJ, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *(["-DMLRA_DEBUG_BOUNDS"] if debug else []), *EXTRA.get(src, []),
+           "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     return src, obj, r.returncode, r.stdout + r.stderr, cmd
 
@@ -61,21 +66,26 @@ def _link(objs, lib):
     os.replace(tmp, lib)
 
 
-def build(jobs=None, verbose=False):
+def build(jobs=None, verbose=False, debug=True):
     os.makedirs(OBJ, exist_ok=True)
-    srcs = SOURCES + [PROBE_SRC]
-    jobs = jobs or min(len(srcs), os.cpu_count() or 1)
+    os.makedirs(OBJ_DEBUG, exist_ok=True)
+    work = [(s, False) for s in SOURCES + [PROBE_SRC]]
+    if debug:
+        work += [(s, True) for s in SOURCES]
+    jobs = jobs or min(len(work), os.cpu_count() or 1)
     objs = {}
     with cf.ThreadPoolExecutor(jobs) as ex:
-        for src, obj, rc, out, cmd in ex.map(_compile, srcs):
+        for (src, dbg), (_, obj, rc, out, cmd) in zip(work, ex.map(lambda a: _compile(*a), work)):
             if verbose or rc:
                 print(" ".join(cmd))
                 print(out)
             if rc:
-                raise RuntimeError(f"hipcc failed on {src}")
-            objs[src] = obj
-    _link([objs[s] for s in SOURCES], LIB)
-    _link([objs[PROBE_SRC]], PROBE_LIB)
+                raise RuntimeError(f"hipcc failed on {src}{' (debug)' if dbg else ''}")
+            objs[(src, dbg)] = obj
+    _link([objs[(s, False)] for s in SOURCES], LIB)
+    _link([objs[(PROBE_SRC, False)]], PROBE_LIB)
+    if debug:
+        _link([objs[(s, True)] for s in SOURCES], DEBUG_LIB)
     return LIB
 
 
@@ -83,6 +93,7 @@ if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--no-debug", action="store_true", help="skip libmlra_debug.so")
     a = ap.parse_args()
-    print(build(a.jobs, a.verbose))
+    print(build(a.jobs, a.verbose, debug=not a.no_debug))
     sys.exit(0)

@@ -128,6 +128,7 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
   const int rope_c = 16 * ((lane & 7) ^ swz_r(rope_t));
 
   int start = k * hd.chunk;
+  MLRA_DCHECK(p.hdr, start >= 0 && start < hd.total, 4);
   const int end = min(start + hd.chunk, hd.total);
   int bseq = find_seq(p.prefix, p.B, start);
 
@@ -142,6 +143,9 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
     const i32x4 krs = seq_rsrc_bytes((const char*)p.krope + (int64_t)bseq * p.kr_bs * EB, t1,
                                      p.kr_ts * EB);
     const int slot = k + bseq;
+    MLRA_DCHECK(p.hdr, bseq >= 0 && bseq < p.B, 1);
+    MLRA_DCHECK(p.hdr, t0 >= 0 && t1 > t0 && t1 <= p.prefix[bseq + 1] - p.prefix[bseq], 2);
+    MLRA_DCHECK(p.hdr, slot >= 0 && slot < hd.n_items + p.B, 3);
     const uint32_t lat_voff = (uint32_t)(lat_row * p.ckv_ts * 2 + lat_c);
     // fp8 latent instruction `wave`: rows 4 wave .. + 3 of the tile, lane l
     // row 4 wave + l / 16, codes hg 256 + 16 (l % 16) .. of it

@@ -220,6 +220,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(DecodeParams p)
   const int pv_row_hi = pv_row_lo + 16 * DC * 2;
 
   int start = k * hd.chunk;
+  MLRA_DCHECK(p.hdr, start >= 0 && start < hd.total, 4);
   const int end = min(start + hd.chunk, hd.total);
   int b = find_seq(p.prefix, p.B, start);
 
@@ -231,6 +232,9 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(DecodeParams p)
     const i32x4 crs = seq_rsrc(p.ckv + (int64_t)b * p.ckv_bs, t1, p.ckv_ts);
     const i32x4 krs = seq_rsrc(p.krope + (int64_t)b * p.kr_bs, t1, p.kr_ts);
     const int slot = k + b;
+    MLRA_DCHECK(p.hdr, b >= 0 && b < p.B, 1);
+    MLRA_DCHECK(p.hdr, t0 >= 0 && t1 > t0 && t1 <= p.prefix[b + 1] - p.prefix[b], 2);
+    MLRA_DCHECK(p.hdr, slot >= 0 && slot < hd.n_items + p.B, 3);
     float* acc_row = p.acc + ((int64_t)slot * H + head) * DC + 4 * kg;
 
     // earlier stores and loads of this wave done; all waves left the

@@ -205,6 +205,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
   const int pv_lo = (4 * kg + pv_r) * 1024 + 8 * (pv_q & 1);
 
   int start = k * hd.chunk;
+  MLRA_DCHECK(p.hdr, start >= 0 && start < hd.total, 4);
   const int end = min(start + hd.chunk, hd.total);
   int bseq = find_seq(p.prefix, p.B, start);
 
@@ -220,6 +221,9 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
     const i32x4 krs = seq_rsrc_bytes((const char*)p.krope + (int64_t)bseq * p.kr_bs * EB, t1,
                                      p.kr_ts * EB);
     const int slot = k + bseq;
+    MLRA_DCHECK(p.hdr, bseq >= 0 && bseq < p.B, 1);
+    MLRA_DCHECK(p.hdr, t0 >= 0 && t1 > t0 && t1 <= p.prefix[bseq + 1] - p.prefix[bseq], 2);
+    MLRA_DCHECK(p.hdr, slot >= 0 && slot < hd.n_items + p.B, 3);
 
     // earlier stores and loads of this wave done; all waves left the
     // previous segment's LDS tiles

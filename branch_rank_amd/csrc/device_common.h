@@ -21,6 +21,24 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Device bounds checks of the debug build (-DMLRA_DEBUG_BOUNDS): a failed
+// check records its site in the plan header (the first failure wins, by a
+// vector compare-and-swap) and the kernel goes on with the values it has,
+// which every access clamps; the debug library's host side reads the word
+// after the call and fails the call. Without the define the checks compile
+// to nothing. Sites: 1 sequence index, 2 token range of a segment, 3 slot of
+// the partial state, 4 work item past the plan, 5 merge slot range.
+#ifdef MLRA_DEBUG_BOUNDS
+#define MLRA_DCHECK(hdr, cond, site)                                                     \
+  do {                                                                                   \
+    if (!(cond)) atomicCAS(const_cast<int*>(&(hdr)->bounds_fail), 0, (site));           \
+  } while (0)
+#else
+#define MLRA_DCHECK(hdr, cond, site) \
+  do {                               \
+  } while (0)
+#endif
+
 // Arguments of the split-KV decode kernels (one struct, passed by value).
 struct DecodeParams {
   const __bf16* q_abs;  // row (b, h) at q_abs + (b * H + h) * q_stride: q~ (d_c), rho (d_r)

@@ -17,7 +17,7 @@ struct PlanHeader {
   int32_t chunk;
   int32_t n_items;
   int32_t total;
-  int32_t pad;
+  int32_t bounds_fail;  // debug build: site of the first failed device bounds check, else 0
 };
 
 // Arguments of the cache append (cache_append.hip): rows [B][d_c + d_r] fp32

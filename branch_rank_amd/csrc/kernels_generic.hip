@@ -15,6 +15,7 @@
 #include <hip/hip_ext.h>
 #include <math.h>
 
+#include "device_common.h"  // MLRA_DCHECK
 #include "internal.h"
 #include "plan_device.h"
 
@@ -156,6 +157,7 @@ __global__ __launch_bounds__(256) void decode_generic(Geom g, const T* __restric
   const PlanHeader hd = *ws.hdr;
   if (k >= hd.n_items) return;
   int start = k * hd.chunk;
+  MLRA_DCHECK(ws.hdr, start >= 0 && start < hd.total, 4);
   const int end = min(start + hd.chunk, hd.total);
   int b = find_seq(ws.prefix, g.B, start);
   const int dcp = g.dc / g.n;
@@ -212,6 +214,9 @@ __global__ __launch_bounds__(256) void decode_generic(Geom g, const T* __restric
       __syncthreads();
     }
     const int slot = k + b;
+    MLRA_DCHECK(ws.hdr, b >= 0 && b < g.B, 1);
+    MLRA_DCHECK(ws.hdr, t0 >= 0 && t1 > t0 && t1 <= ws.prefix[b + 1] - ws.prefix[b], 2);
+    MLRA_DCHECK(ws.hdr, slot >= 0 && slot < hd.n_items + g.B, 3);
     if (tid < g.n) {
       ws.m[((size_t)slot * g.n + tid) * g.H + h] = m[tid];
       ws.l[((size_t)slot * g.n + tid) * g.H + h] = l[tid];
@@ -256,6 +261,7 @@ __global__ __launch_bounds__(256) void combine_kernel(Geom g, Workspace ws, int 
     return;
   }
   const int kf = p0 / hd.chunk, kl = (p1 - 1) / hd.chunk;
+  MLRA_DCHECK(ws.hdr, kf >= 0 && kf <= kl && kl < hd.n_items, 5);
   for (int i = tid; i < n * H; i += 256) {
     float M = -INFINITY;
     for (int k = kf; k <= kl; ++k) M = fmaxf(M, ws.m[(size_t)(k + b) * n * H + i]);

@@ -457,10 +457,27 @@ mlra_status_t run_out_proj(const mlra_config_t* c, const Geom& g, const float* l
   return MLRA_OK;
 }
 
+// Debug build (MLRA_DEBUG_BOUNDS): the plan header's bounds word after the
+// call, where every device bounds check that failed left its site; the
+// release build checks nothing and waits for nothing.
+mlra_status_t debug_bounds(const Workspace& ws, hipStream_t s) {
+#ifdef MLRA_DEBUG_BOUNDS
+  PlanHeader h;
+  TRY_HIP(hipMemcpyAsync(&h, ws.hdr, sizeof h, hipMemcpyDeviceToHost, s), "bounds word copy");
+  TRY_HIP(hipStreamSynchronize(s), "bounds word sync");
+  if (h.bounds_fail != 0)
+    return fail(MLRA_ERR_BOUNDS, "device bounds check failed (site %d)", h.bounds_fail);
+#else
+  (void)ws;
+  (void)s;
+#endif
+  return MLRA_OK;
+}
+
 // The whole decode step on a carved workspace: plan (inside absorb_q's
 // launch when the MFMA absorption runs), absorb_q, split-KV decode, then the
 // fused merge + output projection (or combine and out_proj).
-mlra_status_t run_step(const mlra_config_t* cfg, int32_t batch, int cus, const void* q_nope,
+mlra_status_t run_step_body(const mlra_config_t* cfg, int32_t batch, int cus, const void* q_nope,
                        const void* q_rope, const int32_t* q_pos, const void* w_uk,
                        const void* w_uv, const mlra_cache_t* cache, const Layout& L,
                        const Workspace& ws, void* out, mlra_dtype_t out_dtype, hipStream_t s) {
@@ -488,6 +505,15 @@ mlra_status_t run_step(const mlra_config_t* cfg, int32_t batch, int cus, const v
   }
   TRY(run_merge(g, ws, fast, ws.latent, sc, s));
   return run_out_proj(cfg, g, ws.latent, w_uv, out, out_dtype, s);
+}
+
+mlra_status_t run_step(const mlra_config_t* cfg, int32_t batch, int cus, const void* q_nope,
+                       const void* q_rope, const int32_t* q_pos, const void* w_uk,
+                       const void* w_uv, const mlra_cache_t* cache, const Layout& L,
+                       const Workspace& ws, void* out, mlra_dtype_t out_dtype, hipStream_t s) {
+  TRY(run_step_body(cfg, batch, cus, q_nope, q_rope, q_pos, w_uk, w_uv, cache, L, ws, out,
+                    out_dtype, s));
+  return debug_bounds(ws, s);
 }
 
 // ---- the scratch of mlra_decode_noalloc ----
@@ -530,11 +556,20 @@ const char* mlra_status_string(mlra_status_t s) {
     case MLRA_ERR_WORKSPACE: return "MLRA_ERR_WORKSPACE";
     case MLRA_ERR_NO_DEVICE: return "MLRA_ERR_NO_DEVICE";
     case MLRA_ERR_HIP: return "MLRA_ERR_HIP";
+    case MLRA_ERR_BOUNDS: return "MLRA_ERR_BOUNDS";
   }
   return "MLRA_ERR_UNKNOWN";
 }
 
 const char* mlra_last_error_detail(void) { return g_detail.c_str(); }
+
+int mlra_bounds_checks(void) {
+#ifdef MLRA_DEBUG_BOUNDS
+  return 1;
+#else
+  return 0;
+#endif
+}
 
 mlra_status_t mlra_set_kernel_timing(void* before, void* after) {
   if ((before == nullptr) != (after == nullptr))
@@ -606,7 +641,8 @@ mlra_status_t mla_decode_attn(const mlra_config_t* cfg, int32_t batch, const voi
     qv = scaled;
   }
   TRY(run_decode(cfg, g, qv, cache, ws, L, kern, plan, false, &fast, s));
-  return run_merge(g, ws, fast, latent_out, lat_mul(cache), s);
+  TRY(run_merge(g, ws, fast, latent_out, lat_mul(cache), s));
+  return debug_bounds(ws, s);
 }
 
 }  // extern "C"

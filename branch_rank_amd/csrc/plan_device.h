@@ -52,7 +52,7 @@ __device__ inline void plan_block(const PlanArgs& a) {
     h.chunk = chunk;
     h.n_items = total > 0 ? (total + chunk - 1) / chunk : 0;
     h.total = total;
-    h.pad = 0;
+    h.bounds_fail = 0;
     *a.hdr = h;
   }
 }

@@ -193,6 +193,7 @@ __global__ __launch_bounds__(256) void combine_hc(Geom g, Workspace ws,
     return;
   }
   const int kf = p0 / hd.chunk, kl = (p1 - 1) / hd.chunk;
+  MLRA_DCHECK(ws.hdr, kf >= 0 && kf <= kl && kl < hd.n_items, 5);
   // per (branch, head): the max M and 1/L over the sequence's slots
   for (int q = tid; q < NP; q += 256) {
     const int j = q / kMH, hh = q % kMH;
@@ -435,6 +436,7 @@ __global__ __launch_bounds__(512) void merge_out(Geom g, Workspace ws,
       const int p0 = ws.prefix[b0 + bb], p1 = ws.prefix[b0 + bb + 1];
       kf = p0 / chunk;
       kl = p1 > p0 ? (p1 - 1) / chunk : kf - 1;
+      MLRA_DCHECK(ws.hdr, kf >= 0 && kl < ws.hdr->n_items, 5);
     }
     rng[2 * bb] = kf;
     rng[2 * bb + 1] = kl;

@@ -59,7 +59,8 @@ typedef enum {
   MLRA_ERR_UNSUPPORTED = 2,  /* valid but unsupported combination of sizes/dtypes */
   MLRA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than mlra_workspace_size */
   MLRA_ERR_NO_DEVICE = 4,    /* no usable HIP device */
-  MLRA_ERR_HIP = 5           /* a HIP runtime call or kernel launch failed */
+  MLRA_ERR_HIP = 5,          /* a HIP runtime call or kernel launch failed */
+  MLRA_ERR_BOUNDS = 6        /* debug build only: a device bounds check failed during the call */
 } mlra_status_t;
 
 typedef enum { MLRA_BF16 = 0, MLRA_FP32 = 1 } mlra_dtype_t;
@@ -347,6 +348,16 @@ MLRA_API const char* mlra_status_string(mlra_status_t status);
 
 /* Detail of the last error on the calling thread ("" if none). */
 MLRA_API const char* mlra_last_error_detail(void);
+
+/* 1 in the debug build (libmlra_debug.so, built with MLRA_DEBUG_BOUNDS), 0 in
+ * the release build. The debug build checks, on the device, the indices the
+ * split-KV plan hands the decode and merge kernels (sequence, token range,
+ * partial-state slot, work item, the merge's slot range); a failed check is
+ * recorded without stopping the kernel, and mlra_decode,
+ * mlra_decode_noalloc and mla_decode_attn then wait for their stream and
+ * return MLRA_ERR_BOUNDS (the detail names the check). Takes no arguments and
+ * has no failure mode. */
+MLRA_API int mlra_bounds_checks(void);
 
 #ifdef __cplusplus
 }

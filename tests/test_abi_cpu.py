@@ -34,10 +34,26 @@ def gpu_present():
 def test_library_exports_every_declared_symbol():
     L = br.lib()
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(br.EXPORTS)
+
+
+def test_debug_build_exports_the_same_symbols_and_says_so():
+    # libmlra_debug.so: the same sources built with the device bounds checks
+    # (the build makes both); only its mlra_bounds_checks() differs
+    import ctypes
+    assert os.path.exists(br.DEBUG_LIB_PATH), "libmlra_debug.so is not built"
+    D = ctypes.CDLL(br.DEBUG_LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(D, n), n
+    D.mlra_bounds_checks.restype = ctypes.c_int
+    assert D.mlra_bounds_checks() == 1
+    if os.path.realpath(br.LIB_PATH) != os.path.realpath(br.DEBUG_LIB_PATH):
+        assert not br.bounds_checks()
+    D.mlra_status_string.restype = ctypes.c_char_p
+    assert D.mlra_status_string(br.MLRA_ERR_BOUNDS) == b"MLRA_ERR_BOUNDS"
 
 
 def cfg(**kw):
