@@ -59,9 +59,39 @@ namespace {
 using namespace dev;
 using namespace bt;
 
-template <int NBR, int NSPLIT, int HPW, int NHG, int NS, bool QLO, bool FP8>
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+
+// Operand type of the MFMAs: bf16 (the cache as stored), or fp16 (F16: each
+// tile converted in LDS, q~ from its two bf16 parts, P in fp16, 2^-11 where
+// bf16 gives 2^-9).
+template <bool F16>
+struct BOp {
+  using V = bf16x8;
+  using E = __bf16;
+  static constexpr float kRes = kRescale, kSum = kSumLimit;
+  static __device__ __forceinline__ f32x4 mfma(V a, V b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct BOp<true> {
+  using V = f16x8;
+  using E = _Float16;
+  // P stays below fp16's 65504: a per-lane sum of 8 values above 2^15 moves
+  // the reference, to 12 below the tile max (so 8 p <= 2^15 after a move)
+  static constexpr float kRes = 12.f, kSum = 32768.f;
+  static __device__ __forceinline__ f32x4 mfma(V a, V b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <int NBR, int NSPLIT, int HPW, int NHG, int NS, bool QLO, bool FP8, bool F16>
 __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_kernel(DecodeParams p) {
   using C = BCfg<NBR, NSPLIT, HPW, NHG>;
+  using O_ = BOp<F16>;
+  using VT = typename O_::V;
+  using ET = typename O_::E;
+  static_assert(!(F16 && QLO), "fp16: q~'s two parts are summed, not multiplied apart");
   constexpr int H = C::H;
   constexpr int DC = C::DC;
   constexpr int D = NS - 1;  // tiles issued ahead of the one in use
@@ -161,14 +191,30 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
     // Q^T as the B operand: lane (head, kg) holds 8 consecutive k of its head;
     // with QLO also q~'s bf16 residue over the branch's latent k-steps, whose
     // products with the same K fragments go into the same scores
-    bf16x8 q[C::KS][C::NBLK];
+    VT q[C::KS][C::NBLK];
     bf16x8 ql[QLO ? C::KL : 1][C::NBLK];
+    // fp16: q~ is its two bf16 parts summed in fp32, rounded once (a view
+    // without the residue re-reads q~ and weights it by 0)
+    auto to_q = [&](const __bf16* hi, const __bf16* lo, float wlo) -> VT {
+      const bf16x8 h = *(const bf16x8*)hi;
+      if constexpr (F16) {
+        const bf16x8 l = *(const bf16x8*)lo;
+        VT v;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (_Float16)__builtin_fmaf(wlo, (float)l[i], (float)h[i]);
+        return v;
+      } else {
+        return h;
+      }
+    };
+    const float wlo = p.q_lo > 0 ? 1.f : 0.f;
 #pragma unroll
     for (int nb = 0; nb < C::NBLK; ++nb) {
       const __bf16* qrow = p.q_abs + ((int64_t)bseq * H + head0 + 16 * nb + l16) * p.q_stride;
 #pragma unroll
       for (int ks = 0; ks < C::KL; ++ks)
-        q[ks][nb] = *(const bf16x8*)(qrow + kBW * j + 32 * ks + 8 * kg);
+        q[ks][nb] = to_q(qrow + kBW * j + 32 * ks + 8 * kg,
+                         qrow + p.q_lo + kBW * j + 32 * ks + 8 * kg, wlo);
       if constexpr (QLO) {
 #pragma unroll
         for (int ks = 0; ks < C::KL; ++ks)
@@ -176,7 +222,8 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
       }
 #pragma unroll
       for (int ks = C::KL; ks < C::KS; ++ks)
-        q[ks][nb] = *(const bf16x8*)(qrow + DC + 32 * (ks - C::KL) + 8 * kg);
+        q[ks][nb] = to_q(qrow + DC + 32 * (ks - C::KL) + 8 * kg,
+                         qrow + DC + 32 * (ks - C::KL) + 8 * kg, 0.f);
     }
     // Q complete before any DMA is in flight: no vmcnt wait for Q is then
     // needed inside the tile loop (it would also drain the DMA)
@@ -230,7 +277,8 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
       {
         const int t = 4 * wave + (ln >> 4), cc = ln & 15;
         i32x4 lo, hi;
-        fp8x16_to_bf16(x, lo, hi);
+        if constexpr (F16) fp8x16_to_f16(x, lo, hi);
+        else fp8x16_to_bf16(x, lo, hi);
         char LDS_AS* d = dst + t * C::ROWB + 32 * (cc ^ (t & 15));
         *(i32x4 LDS_AS*)d = lo;
         *(i32x4 LDS_AS*)(d + 16) = hi;
@@ -238,7 +286,8 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
       if (wave < 2) {
         const int t = 16 * wave + (ln >> 2), cc = ln & 3;
         i32x4 lo, hi;
-        fp8x16_to_bf16(r, lo, hi);
+        if constexpr (F16) fp8x16_to_f16(r, lo, hi);
+        else fp8x16_to_bf16(r, lo, hi);
         char LDS_AS* d = dst + C::LAT + t * 128;
         *(i32x4 LDS_AS*)(d + 16 * ((2 * cc) ^ swz_r(t))) = lo;
         *(i32x4 LDS_AS*)(d + 16 * ((2 * cc + 1) ^ swz_r(t))) = hi;
@@ -288,8 +337,8 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
     // behind the first, so on every SIMD one wave's MFMAs run beside the
     // other wave's softmax.
     f32x4 S[2][C::NBLK];   // scores of the tile between M(t) and V(t)
-    bf16x8 P[C::NBLK];     // P^T of tile t, from V(t) to M(t + 1)
-    bf16x8 V[C::CB];       // V^T of tile t, from V(t) to M(t + 1)
+    VT P[C::NBLK];         // P^T of tile t, from V(t) to M(t + 1)
+    VT V[C::CB];           // V^T of tile t, from V(t) to M(t + 1)
     int m_off = 0, v_off = 0;  // stages of the tiles the next M and V phases read
 
     // a phase boundary: no instruction is scheduled across it (the phases
@@ -297,7 +346,7 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
     auto bar = [] {
       __builtin_amdgcn_sched_barrier(0);
       // fp8: this wave's converted tile written (s_barrier does not wait)
-      if constexpr (FP8) wait_lgkm0();
+      if constexpr (FP8 || F16) wait_lgkm0();
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
@@ -306,8 +355,31 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
     // waves 0 and 1, one on the others), then (fp8) convert its codes
     // (fp8: nothing to wait for here; conv(u) below waits for tile u's codes
     // and converts them in the phase before the barrier that opens M(u))
+    // fp16 from the bf16 cache: once this wave's loads of the tile at stage
+    // `off` have landed, its lanes convert the 16 bytes each loaded, in
+    // place (its latent instructions wave + NW u and, on waves < NR, its
+    // RoPE one), before the barrier that opens the tile's first matrix
+    // phase. The lane offsets come from an opaque copy of the lane id, so
+    // that they are recomputed instead of kept live (spilled).
+    auto convert16 = [&](int off) {
+      if constexpr (F16 && !FP8) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        char LDS_AS* st = smem + off + 16 * ln;
+        i32x4 x[C::NL / C::NW], r;
+#pragma unroll
+        for (int u = 0; u < C::NL / C::NW; ++u)
+          x[u] = *(const i32x4 LDS_AS*)(st + (wave + C::NW * u) * 1024);
+        if (wave < C::NR) r = *(const i32x4 LDS_AS*)(st + C::LAT + wave * 1024);
+#pragma unroll
+        for (int u = 0; u < C::NL / C::NW; ++u)
+          *(i32x4 LDS_AS*)(st + (wave + C::NW * u) * 1024) = bf16_to_f16x8(x[u]);
+        if (wave < C::NR) *(i32x4 LDS_AS*)(st + C::LAT + wave * 1024) = bf16_to_f16x8(r);
+      }
+    };
     auto wait_tile = [&](int t) {
       if constexpr (!FP8) wait_tiles<C, NS - 2>(min(NS - 2, ntiles - 1 - t), wave);
+      convert16(m_off);  // fp16: the tile the next matrix phase reads
     };
     // fp8: this wave's codes of tile u have landed (the tiles issued after it,
     // up to u + D - 1, may be in flight), then its lanes convert them
@@ -328,6 +400,7 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
       if constexpr (FP8) return;
       if (wave < C::NR) wait_vm<(NS - 2) * (C::NL / C::NW + 1)>();
       else wait_vm<(NS - 2) * (C::NL / C::NW)>();
+      convert16(m_off);
     };
     auto issue_full = [&](int tile) {
       if constexpr (FP8) {
@@ -344,7 +417,7 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
     auto mphase = [&](int t, auto pv_tag, auto qk_tag, auto steady_tag) {
       constexpr bool PV = decltype(pv_tag)::value, QK = decltype(qk_tag)::value;
       constexpr bool STEADY = decltype(steady_tag)::value;
-      bf16x8 A[2][C::KS];
+      VT A[2][C::KS];
       if constexpr (QK) {
         const char LDS_AS* st = smem + __builtin_amdgcn_readfirstlane(m_off);
         m_off = next_stage(m_off);
@@ -359,11 +432,11 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
         for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
           for (int ks = 0; ks < C::KL; ++ks)
-            A[mb][ks] = *(const bf16x8 LDS_AS*)((const char LDS_AS*)(((uintptr_t)(st + qk_lat)) ^ (64 * ks)) +
+            A[mb][ks] = *(const VT LDS_AS*)((const char LDS_AS*)(((uintptr_t)(st + qk_lat)) ^ (64 * ks)) +
                                                 mb * 16 * C::ROWB);
-          A[mb][C::KL] = *(const bf16x8 LDS_AS*)(st + qk_rp + mb * 2048);
+          A[mb][C::KL] = *(const VT LDS_AS*)(st + qk_rp + mb * 2048);
           A[mb][C::KL + 1] =
-              *(const bf16x8 LDS_AS*)((const char LDS_AS*)(((uintptr_t)(st + qk_rp)) ^ 64) + mb * 2048);
+              *(const VT LDS_AS*)((const char LDS_AS*)(((uintptr_t)(st + qk_rp)) ^ 64) + mb * 2048);
         }
       }
       if constexpr (PV) {
@@ -371,18 +444,17 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
         for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
           for (int nb = 0; nb < C::NBLK; ++nb)
-            o[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(V[cb], P[nb], o[cb][nb], 0, 0, 0);
+            o[cb][nb] = O_::mfma(V[cb], P[nb], o[cb][nb]);
       }
       if constexpr (QK) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int nb = 0; nb < C::NBLK; ++nb) {
-            S[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][0], q[0][nb], bias[mb], 0, 0, 0);
+            S[mb][nb] = O_::mfma(A[mb][0], q[0][nb], bias[mb]);
 #pragma unroll
             for (int ks = 1; ks < C::KS; ++ks)
-              S[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][ks], q[ks][nb], S[mb][nb],
-                                                                  0, 0, 0);
+              S[mb][nb] = O_::mfma(A[mb][ks], q[ks][nb], S[mb][nb]);
             if constexpr (QLO) {
 #pragma unroll
               for (int ks = 0; ks < C::KL; ++ks)
@@ -409,7 +481,7 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)a);
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(a + 16 * C::ROWB));
         const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        V[cb] = __builtin_bit_cast(bf16x8, v);
+        V[cb] = __builtin_bit_cast(VT, v);
       }
       float ps[C::NBLK];
       bool need = false;
@@ -421,13 +493,13 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
           for (int e = 0; e < 4; ++e) {
             const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(S[mb][nb][e], kLog2e, -m_run[nb]));
             ps[nb] += pe;
-            P[nb][4 * mb + e] = (__bf16)pe;
+            P[nb][4 * mb + e] = (ET)pe;
           }
       };
 #pragma unroll
       for (int nb = 0; nb < C::NBLK; ++nb) {
         probs(nb);
-        need |= !(ps[nb] <= kSumLimit);
+        need |= !(ps[nb] <= O_::kSum);
       }
       if (__builtin_expect(__any(need), 0)) {
 #pragma unroll
@@ -436,7 +508,7 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
                                  fmaxf(fmaxf(S[1][nb][0], S[1][nb][1]), fmaxf(S[1][nb][2], S[1][nb][3])));
           const float mt = max4(mx) * kLog2e;
           const float mr = m_run[nb] == kNoRef ? mt : m_run[nb];  // first tile sets it
-          const float mn = fmaxf(mr, mt - kRescale);
+          const float mn = fmaxf(mr, mt - O_::kRes);
           const float f = __builtin_amdgcn_exp2f(mr - mn);
           l_run[nb] *= f;
 #pragma unroll
@@ -547,7 +619,7 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
   }
 }
 
-template <int NBR, int NSPLIT, int HPW, int NHG, bool QLO, bool FP8 = false>
+template <int NBR, int NSPLIT, int HPW, int NHG, bool QLO, bool FP8 = false, bool F16 = false>
 hipError_t launch_b(const Geom& g, const QView& q, const void* ckv, const void* krope,
                     const Workspace& ws, int items, hipStream_t s, const KernelTiming& t) {
   using C = BCfg<NBR, NSPLIT, HPW, NHG>;
@@ -557,7 +629,7 @@ hipError_t launch_b(const Geom& g, const QView& q, const void* ckv, const void* 
   DecodeParams p;
   p.q_abs = (const __bf16*)q.q;
   p.q_stride = q.stride;
-  p.q_lo = QLO ? q.lo : 0;
+  p.q_lo = QLO || F16 ? q.lo : 0;
   p.ckv = (const __bf16*)ckv;
   p.krope = (const __bf16*)krope;
   p.ckv_bs = g.ckv_bs;
@@ -572,7 +644,7 @@ hipError_t launch_b(const Geom& g, const QView& q, const void* ckv, const void* 
   p.B = g.B;
   int grid = items;
   if (NSPLIT > 1) grid = ((items + 7) / 8) * 8 * NSPLIT;  // whole XCD rounds
-  hipExtLaunchKernelGGL((decode_branch_kernel<NBR, NSPLIT, HPW, NHG, NS, QLO, FP8>), dim3(grid),
+  hipExtLaunchKernelGGL((decode_branch_kernel<NBR, NSPLIT, HPW, NHG, NS, QLO, FP8, F16>), dim3(grid),
                         dim3(64 * C::NW), 0, s, t.start, t.stop, 0, p);
   return hipGetLastError();
 }
@@ -592,7 +664,14 @@ bool decode_branch_supported(const Geom& g, bool fp8) {
 // Workgroups per work item; one workgroup per CU.
 int decode_branch_wgs_per_item(const Geom& g) { return g.n == 1 ? 1 : 2; }
 
-bool decode_branch_reads_residue(const Geom& g) { return g.n == 1; }
+// The one-branch shard always adds q~'s residue to its bf16 scores. The
+// four-branch kernel at 128 heads reads it, and then runs in fp16 (q~ from
+// both parts, the tiles converted in LDS, P in fp16), with an fp8 cache (whose
+// tiles are converted anyway, so the fp16 form costs about 3%) or when the
+// caller asks for it (cfg->q_residue; about 19% more time on a bf16 cache).
+bool decode_branch_reads_residue(const Geom& g, bool fp8, bool want) {
+  return g.n == 1 || (g.n == 4 && g.H == 128 && (fp8 || want));
+}
 
 hipError_t launch_decode_branch(const Geom& g, const QView& q, const void* ckv,
                                 const void* krope, const Workspace& ws, int items,
@@ -601,14 +680,17 @@ hipError_t launch_decode_branch(const Geom& g, const QView& q, const void* ckv,
   // one branch alone (a tensor-parallel shard) is one softmax over the
   // branch: a bf16 query alone moves its output rows by up to ~1.1e-2 at the
   // pages' scales, so the shard adds q~'s residue when the view has it. With
-  // four branches the summed output averages the branches' errors (<= 8.6e-3
-  // measured) and the residue's registers would cost the second wave per SIMD.
+  // four branches the summed output averages the branches' errors (<= 9.8e-3
+  // measured) and a residue in the scores would need registers that cost the
+  // second wave per SIMD; with the residue in the view the kernel runs in
+  // fp16 instead (<= 2.0e-3 measured).
   if (g.n == 1) {
     if (q.lo > 0) return launch_b<1, 1, 16, 8, true>(g, q, ckv, krope, ws, items, s, t);
     return launch_b<1, 1, 16, 8, false>(g, q, ckv, krope, ws, items, s, t);
   }
-  if (fp8) return launch_b<4, 2, 32, 4, false, true>(g, q, ckv, krope, ws, items, s, t);
+  if (fp8) return launch_b<4, 2, 32, 4, false, true, true>(g, q, ckv, krope, ws, items, s, t);
   if (g.H == 64) return launch_b<4, 2, 16, 4, false>(g, q, ckv, krope, ws, items, s, t);
+  if (q.lo > 0) return launch_b<4, 2, 32, 4, false, false, true>(g, q, ckv, krope, ws, items, s, t);
   return launch_b<4, 2, 32, 4, false>(g, q, ckv, krope, ws, items, s, t);
 }
 

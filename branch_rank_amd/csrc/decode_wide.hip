@@ -105,19 +105,6 @@ struct Op<false> {
 __device__ __forceinline__ int swz(int t) { return 2 * (t & 15); }
 __device__ __forceinline__ int swz_r(int t) { return (t >> 1) & 7; }
 
-// bf16 -> fp16 of 8 values in one 16-byte chunk, round toward zero (exact in
-// fp16's normal range).
-__device__ __forceinline__ i32x4 bf16_to_f16x8(i32x4 x) {
-  i32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t v = (uint32_t)x[i];
-    const auto h = __builtin_amdgcn_cvt_pkrtz(__builtin_bit_cast(float, v << 16),
-                                              __builtin_bit_cast(float, v & 0xFFFF0000u));
-    r[i] = __builtin_bit_cast(int, h);
-  }
-  return r;
-}
 
 // Wave shape for H heads: the score waves (the first QW; with fewer than 16
 // heads per wave the others only load, convert and accumulate) own

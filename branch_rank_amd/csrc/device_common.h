@@ -83,6 +83,22 @@ __device__ __forceinline__ i32x4 seq_rsrc(const __bf16* base, int rows, int ts) 
 // 16 FP8 E4M3 codes (16 bytes, element i in byte i) to 16 exact fp16 values
 // (two 16-byte halves: elements 0-7, then 8-15): v_cvt_scalef32_pk_f16_fp8
 // with scale 1 turns two codes into two fp16 values. E4M3's range and its 3
+// bf16 -> fp16 of the 8 values in a 16-byte chunk, rounded toward zero:
+// exact for |x| in fp16's normal range [2^-14, 65504] (bf16's 8 significant
+// bits fit fp16's 11); larger magnitudes saturate to 65504 and the tail below
+// 2^-14 keeps fp16's subnormal precision.
+__device__ __forceinline__ i32x4 bf16_to_f16x8(i32x4 x) {
+  i32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t v = (uint32_t)x[i];
+    const auto h = __builtin_amdgcn_cvt_pkrtz(__builtin_bit_cast(float, v << 16),
+                                              __builtin_bit_cast(float, v & 0xFFFF0000u));
+    r[i] = __builtin_bit_cast(int, h);
+  }
+  return r;
+}
+
 // mantissa bits fit fp16's normals and subnormals, so nothing rounds.
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void fp8x16_to_f16(i32x4 x, i32x4& lo, i32x4& hi) {

@@ -158,7 +158,9 @@ hipError_t launch_out_proj_generic(const Geom& g, const float* latent, const T* 
 // LDS); the scales are folded into the query and the merge by the caller.
 bool decode_branch_supported(const Geom& g, bool fp8 = false);
 int decode_branch_wgs_per_item(const Geom& g);
-bool decode_branch_reads_residue(const Geom& g);  // adds q~'s residue when the view has one
+// whether the branch kernel reads q~'s residue for this geometry, cache type
+// and the caller's wish (cfg->q_residue)
+bool decode_branch_reads_residue(const Geom& g, bool fp8, bool want);
 hipError_t launch_decode_branch(const Geom& g, const QView& q, const void* ckv,
                                 const void* krope, const Workspace& ws, int grid_items,
                                 hipStream_t s, const KernelTiming& t, bool fp8 = false);

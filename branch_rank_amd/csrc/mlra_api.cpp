@@ -130,11 +130,13 @@ QView user_qview(const mlra_config_t* c, const void* q) {
   return v;
 }
 
-QView ws_qview(const mlra_config_t* c, const Geom& g, mlra_kernel_t kern, const void* q) {
+QView ws_qview(const mlra_config_t* c, const Geom& g, mlra_kernel_t kern, const void* q,
+               bool fp8) {
   const bool lo = c->dtype == MLRA_BF16 &&
                   (kern == MLRA_KERNEL_PORTABLE ||
                    (kern == MLRA_KERNEL_HEAD_GROUP && decode_mfma_reads_residue(g)) ||
-                   (kern == MLRA_KERNEL_BRANCH && decode_branch_reads_residue(g)) ||
+                   (kern == MLRA_KERNEL_BRANCH &&
+                    decode_branch_reads_residue(g, fp8, c->q_residue != 0)) ||
                    (kern == MLRA_KERNEL_WIDE && decode_wide_reads_residue(g)));
   QView v;
   v.q = q;
@@ -486,7 +488,7 @@ mlra_status_t run_step_body(const mlra_config_t* cfg, int32_t batch, int cus, co
   PlanArgs plan;
   TRY(plan_for(cfg, g, cus, cache, ws, L, &kern, &plan));
   bool plan_done = false;
-  const QView qv = ws_qview(cfg, g, kern, ws.q_abs);
+  const QView qv = ws_qview(cfg, g, kern, ws.q_abs, cache->fp8 != 0);
   // an fp8 cache's scales go into q~, rho and the merged latent
   const float sc = lat_mul(cache), sr = rope_mul(cache);
   TRY(run_absorb(cfg, g, q_nope, q_rope, q_pos, cache->cache_lens, w_uk, qv, s, &plan,
@@ -636,7 +638,7 @@ mlra_status_t mla_decode_attn(const mlra_config_t* cfg, int32_t batch, const voi
   QView qv = user_qview(cfg, q_abs);
   if (cache->fp8) {
     // the cache's scales go into a copy of the query in the workspace
-    const QView scaled = ws_qview(cfg, g, kern, ws.q_abs);
+    const QView scaled = ws_qview(cfg, g, kern, ws.q_abs, true);
     TRY_HIP(launch_scale_q(g, qv, scaled, lat_mul(cache), rope_mul(cache), s), "scale_q launch");
     qv = scaled;
   }

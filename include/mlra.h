@@ -106,7 +106,9 @@ typedef struct {
   mlra_kernel_t decode_kernel;  /* MLRA_KERNEL_AUTO unless a kernel is to be forced */
   int32_t q_residue;     /* 0 or 1 (bf16 only): the q_abs rows of mla_absorb_q and
                             mla_decode_attn also carry q~'s rounding residue, see
-                            mla_absorb_q; mlra_decode ignores it */
+                            mla_absorb_q; mlra_decode writes it wherever the chosen
+                            kernel reads it, and q_residue = 1 also makes the
+                            four-branch branch kernel read it (see mla_decode_attn) */
 } mlra_config_t;
 
 /* Strided view of the latent cache. Element strides (not bytes). Row t of
@@ -169,8 +171,11 @@ MLRA_API mlra_status_t mla_absorb_q(const mlra_config_t* cfg, int32_t batch, con
  * 苏神思路: decoding works like MQA).
  *   q_abs      [B][H][d_latent + d_rope] from mla_absorb_q (rows of
  *              d_latent + d_rope + d_latent with cfg->q_residue = 1; the
- *              residue enters the scores of every kernel except the
- *              four-branch branch kernel, which uses the bf16 q~ alone)
+ *              residue enters the scores of every kernel. The four-branch
+ *              branch kernel (MLRA-4 at 128 heads) then runs in fp16: q~
+ *              from both parts, the tiles converted in LDS, P in fp16, about
+ *              19% more time on a bf16 cache and ~1.4e-3 instead of
+ *              ~7.4e-3 worst-row error; it always does with an fp8 cache)
  *   cache      strided cache view (16-byte aligned bases and byte strides
  *              that are multiples of 16). With an fp8 cache the call first
  *              writes q~ * ckv_scale and rho * krope_scale into the workspace
