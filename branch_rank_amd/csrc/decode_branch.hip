@@ -600,8 +600,9 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
       mphase(ntiles, T_{}, F_{}, F_{});
     }
 
-    // partial state of this segment: m, l as [slot][n][H]; acc as
-    // [slot][H][d_c] with this branch's 128 columns, 16-byte stores
+    // partial state of this segment: m, l as [slot][n][H]; the accumulator
+    // normalised by l (a weighted mean of cache rows) as fp16 [slot][H][d_c],
+    // this branch's 128 columns, 8-byte stores
 #pragma unroll
     for (int nb = 0; nb < C::NBLK; ++nb) {
       const int head = head0 + 16 * nb + l16;
@@ -610,9 +611,11 @@ __global__ __launch_bounds__(64 * (NBR / NSPLIT) * NHG, 1) void decode_branch_ke
         p.m[((int64_t)slot * NBR + j) * H + head] = m_run[nb];
         p.l[((int64_t)slot * NBR + j) * H + head] = lt;
       }
-      float* row = p.acc + ((int64_t)slot * H + head) * DC + kBW * j + 4 * kg;
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      _Float16* row = reinterpret_cast<_Float16*>(p.acc) + ((int64_t)slot * H + head) * DC +
+                      kBW * j + 4 * kg;
 #pragma unroll
-      for (int cb = 0; cb < C::CB; ++cb) *(f32x4*)(row + 16 * cb) = o[cb][nb];
+      for (int cb = 0; cb < C::CB; ++cb) store_f16x4_sat(row + 16 * cb, o[cb][nb] * inv);
     }
     start = seg_end;
     ++bseq;

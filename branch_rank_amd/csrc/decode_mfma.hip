@@ -235,7 +235,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(DecodeParams p)
     MLRA_DCHECK(p.hdr, b >= 0 && b < p.B, 1);
     MLRA_DCHECK(p.hdr, t0 >= 0 && t1 > t0 && t1 <= p.prefix[b + 1] - p.prefix[b], 2);
     MLRA_DCHECK(p.hdr, slot >= 0 && slot < hd.n_items + p.B, 3);
-    float* acc_row = p.acc + ((int64_t)slot * H + head) * DC + 4 * kg;
+    _Float16* acc_row = reinterpret_cast<_Float16*>(p.acc) + ((int64_t)slot * H + head) * DC + 4 * kg;
 
     // earlier stores and loads of this wave done; all waves left the
     // previous segment's LDS tiles
@@ -439,8 +439,10 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(DecodeParams p)
       tile(smem + (it % NS) * C::STAGE, min(kT, t1 - (t0 + it * kT)), MaskOn{});
     }
 
-    // partial state of this segment: m, l as [slot][n][H]; acc as
-    // [slot][H][d_c], 16-byte stores of 4 consecutive latent columns
+    // partial state of this segment: m, l as [slot][n][H]; the accumulator
+    // normalised by its branch's l (a weighted mean of cache rows) as fp16
+    // [slot][H][d_c], 8-byte stores of 4 consecutive latent columns
+    float inv[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const float lt = sum4(l_run[j]);
@@ -448,9 +450,11 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mfma_kernel(DecodeParams p)
         p.m[((int64_t)slot * NB + j) * H + head] = m_run[j];
         p.l[((int64_t)slot * NB + j) * H + head] = lt;
       }
+      inv[j] = lt > 0.f ? 1.f / lt : 0.f;
     }
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb) *(f32x4*)(acc_row + 16 * mb) = o[mb];
+    for (int mb = 0; mb < C::MB; ++mb)
+      store_f16x4_sat(acc_row + 16 * mb, o[mb] * inv[(16 * mb) / (DC / NB)]);
     start = seg_end;
     ++b;
   }

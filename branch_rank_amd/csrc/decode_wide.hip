@@ -569,8 +569,12 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
     }
 
     // partial state of this segment: m, l as [slot][n][H] (a score wave's
-    // heads); acc as [slot][H][d_c] (this wave's columns, all heads), 16-byte
-    // stores of 4 consecutive latent columns
+    // heads); the accumulator normalised by l (a weighted mean of cache rows)
+    // as fp16 [slot][H][d_c] (this wave's columns, all heads), 8-byte stores
+    // of 4 consecutive latent columns. The score waves pass 1/l to the column
+    // owners through the rescale table, once every wave has left the last
+    // P V (which read it).
+    barrier();
 #pragma unroll
     for (int nb = 0; nb < NBQ; ++nb) {
       const int head = C::HPW * wave + 16 * nb + l16;
@@ -580,14 +584,18 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_wide_kernel(DecodeParams p)
         if (kg == 0 && wave < QW) {
           p.m[((int64_t)slot * NB + j) * H + head] = m_run[j][nb];
           p.l[((int64_t)slot * NB + j) * H + head] = lt;
+          fl[j * H + head] = lt > 0.f ? 1.f / lt : 0.f;
         }
       }
     }
+    barrier();
 #pragma unroll
     for (int hb = 0; hb < kHB; ++hb) {
-      float* row = p.acc + ((int64_t)slot * H + 16 * hb + l16) * kDC + C::CPW * wave + 4 * kg;
+      const float inv = fl[jq * H + 16 * hb + l16];
+      _Float16* row = reinterpret_cast<_Float16*>(p.acc) + ((int64_t)slot * H + 16 * hb + l16) * kDC +
+                      C::CPW * wave + 4 * kg;
 #pragma unroll
-      for (int c = 0; c < CBW; ++c) *(f32x4*)(row + 16 * c) = o[c][hb];
+      for (int c = 0; c < CBW; ++c) store_f16x4_sat(row + 16 * c, o[c][hb] * inv);
     }
     start = seg_end;
     ++bseq;

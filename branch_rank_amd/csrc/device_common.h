@@ -80,9 +80,6 @@ __device__ __forceinline__ i32x4 seq_rsrc(const __bf16* base, int rows, int ts) 
   return seq_rsrc_bytes(base, rows, ts * 2);
 }
 
-// 16 FP8 E4M3 codes (16 bytes, element i in byte i) to 16 exact fp16 values
-// (two 16-byte halves: elements 0-7, then 8-15): v_cvt_scalef32_pk_f16_fp8
-// with scale 1 turns two codes into two fp16 values. E4M3's range and its 3
 // bf16 -> fp16 of the 8 values in a 16-byte chunk, rounded toward zero:
 // exact for |x| in fp16's normal range [2^-14, 65504] (bf16's 8 significant
 // bits fit fp16's 11); larger magnitudes saturate to 65504 and the tail below
@@ -99,6 +96,24 @@ __device__ __forceinline__ i32x4 bf16_to_f16x8(i32x4 x) {
   return r;
 }
 
+// Four fp32 values as fp16 (round to nearest even) in one 8-byte store; a
+// value beyond fp16's range saturates at +-65504 instead of becoming inf (a
+// NaN stays NaN).
+__device__ __forceinline__ void store_f16x4_sat(_Float16* dst, f32x4 v) {
+  typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+  u16x4 b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    unsigned short x = __builtin_bit_cast(unsigned short, (_Float16)v[i]);
+    if ((x & 0x7fff) == 0x7c00) x = (unsigned short)((x & 0x8000) | 0x7bff);
+    b[i] = x;
+  }
+  *(u16x4*)dst = b;
+}
+
+// 16 FP8 E4M3 codes (16 bytes, element i in byte i) to 16 exact fp16 values
+// (two 16-byte halves: elements 0-7, then 8-15): v_cvt_scalef32_pk_f16_fp8
+// with scale 1 turns two codes into two fp16 values. E4M3's range and its 3
 // mantissa bits fit fp16's normals and subnormals, so nothing rounds.
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void fp8x16_to_f16(i32x4 x, i32x4& lo, i32x4& hi) {

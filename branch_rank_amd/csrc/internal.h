@@ -49,13 +49,15 @@ struct PlanArgs {
 };
 
 // Partial softmax state per slot: m and l as [slot][n][H] fp32 (m in log2
-// units, i.e. max of score*log2(e)), acc as [slot][d_c][H] fp32 (unnormalised).
+// units, i.e. max of score*log2(e)). The accumulator region holds, after the
+// portable decode, acc as [slot][d_c][H] fp32 (unnormalised); after the MFMA
+// decodes, acc / l as fp16 [slot][H][d_c] (half of the region).
 struct Workspace {
   PlanHeader* hdr;
   int32_t* prefix;  // [B + 1]
   float* m;         // [slots][n][H]
   float* l;         // [slots][n][H]
-  float* acc;       // [slots][d_c][H]
+  float* acc;       // [slots][d_c][H] fp32, or fp16 [slots][H][d_c] (see above)
   void* q_abs;      // [B][H][d_c + d_r (+ d_c, bf16: q~'s residue)] (mlra_decode only)
   float* latent;    // [B][H][d_c]       (mlra_decode only)
 };

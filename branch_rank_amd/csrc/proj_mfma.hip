@@ -14,9 +14,12 @@
 //    keeps fp32 accuracy; W_UV[h] is staged in LDS once and read transposed
 //    with ds_read_b64_tr_b16.
 //
-// Partials come from decode_mfma_kernel: m, l as [slot][n][H] (m in log2
-// units), acc as [slot][H][d_c]; sequence b's slots are k + b for the work
-// items k that overlap it (see PlanHeader).
+// Partials come from the MFMA decodes: m, l as [slot][n][H] (m in log2
+// units) and the accumulator normalised by l, acc / l (a weighted mean of
+// cache rows), as fp16 [slot][H][d_c]; sequence b's slots are k + b for the
+// work items k that overlap it (see PlanHeader). Slot k's weight in the merge
+// of a (branch, head) is 2^(m_k - M) l_k / L with M the largest m_k and
+// L = sum_k 2^(m_k - M) l_k.
 
 #include <math.h>
 
@@ -32,6 +35,20 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
 #define LDS_AS __attribute__((address_space(3)))
+
+// r[0], r[1] (8 consecutive latent columns) += w times the 8 fp16 values of
+// a 16-byte chunk of a partial row
+__device__ __forceinline__ void fma_f16x8(f32x4* r, float w, dev::i32x4 x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // the element goes through a scalar first: this compiler's bit_cast of a
+    // vector element x[i] reads element 0 whatever i is
+    const int xi = x[i];
+    const dev::f16x2_t h = __builtin_bit_cast(dev::f16x2_t, xi);
+    r[i >> 1][2 * (i & 1)] += w * (float)h[0];
+    r[i >> 1][2 * (i & 1) + 1] += w * (float)h[1];
+  }
+}
 
 __device__ __forceinline__ int clamp_len(int v, int max_len) {
   return v < 0 ? 0 : (v > max_len ? max_len : v);
@@ -168,11 +185,12 @@ __global__ __launch_bounds__(256) void absorb_q_mfma(Geom g, const __bf16* __res
 // ----------------------------------------------------------- combine_hc ----
 
 // Merge of the split-KV partials of sequence b into its branch-normalised
-// latent, o~_j[h] = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k over the
-// slots k of the sequence (textbook online-softmax merge; one softmax per
-// branch, "Multi-Head Low-Rank Attention", 核心方法). grid (B, H / kMH);
-// the weights 2^(m_k - M) / L of (slot, branch, head) are computed once into
-// LDS, kMS slots at a time, then each thread sums 16-byte partial rows.
+// latent, o~_j[h] = sum_k 2^(m_k - M) l_k (acc_k / l_k) / sum_k 2^(m_k - M) l_k
+// over the slots k of the sequence (textbook online-softmax merge; one
+// softmax per branch, "Multi-Head Low-Rank Attention", 核心方法). grid
+// (B, H / kMH); the weights 2^(m_k - M) l_k / L of (slot, branch, head) are
+// computed once into LDS, kMS slots at a time, then each thread sums the
+// 16-byte fp16 chunks (8 columns) of its partial rows.
 constexpr int kMH = 4;    // heads per workgroup
 constexpr int kMS = 64;   // slots per weight table
 constexpr int kMNB = 8;   // most branches
@@ -183,13 +201,13 @@ __global__ __launch_bounds__(256) void combine_hc(Geom g, Workspace ws,
   __shared__ float stat[2 * kMNB * kMH];        // M, 1/L per (branch, head)
   __shared__ float wt[kMS * kMNB * kMH];        // weights of kMS slots
   const int b = blockIdx.x, h0 = blockIdx.y * kMH, tid = threadIdx.x;
-  const int H = g.H, DC = g.dc, NB = g.n, C4 = g.dc / 4, NP = NB * kMH;
+  const int H = g.H, DC = g.dc, NB = g.n, C8 = g.dc / 8, NP = NB * kMH;
   const int hn = min(kMH, H - h0);
   const PlanHeader hd = *ws.hdr;
   const int p0 = ws.prefix[b], p1 = ws.prefix[b + 1];
   float* out = latent_out + ((size_t)b * H + h0) * DC;
   if (p1 <= p0) {  // empty sequence: o = 0
-    for (int q = tid; q < hn * C4; q += 256) *(f32x4*)(out + 4 * q) = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int q = tid; q < hn * DC / 4; q += 256) *(f32x4*)(out + 4 * q) = (f32x4){0.f, 0.f, 0.f, 0.f};
     return;
   }
   const int kf = p0 / hd.chunk, kl = (p1 - 1) / hd.chunk;
@@ -212,39 +230,35 @@ __global__ __launch_bounds__(256) void combine_hc(Geom g, Workspace ws,
       stat[2 * q + 1] = 1.f / L;
     }
   }
-  // thread -> (head hh, 4 latent columns 4 c4 of branch j)
-  const int per = hn * C4;
-  f32x4 r[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) r[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // thread -> (head hh, 8 latent columns 8 c8 of branch j); d_c <= 512, so
+  // kMH heads take at most 256 threads
+  const int per = hn * C8;
+  const _Float16* acc16 = reinterpret_cast<const _Float16*>(ws.acc);
+  f32x4 r[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   for (int k0 = kf; k0 <= kl; k0 += kMS) {
     const int nk = min(kMS, kl - k0 + 1);
     __syncthreads();  // stats ready / previous table consumed
     for (int q = tid; q < nk * NP; q += 256) {
       const int kk = q / NP, pr = q % NP, j = pr / kMH, hh = pr % kMH;
       float w = 0.f;
-      if (hh < hn)
-        w = exp2f(ws.m[((size_t)(k0 + kk + b) * NB + j) * H + h0 + hh] - stat[2 * pr]) *
-            stat[2 * pr + 1];
+      if (hh < hn) {
+        const size_t i = ((size_t)(k0 + kk + b) * NB + j) * H + h0 + hh;
+        w = exp2f(ws.m[i] - stat[2 * pr]) * ws.l[i] * stat[2 * pr + 1];
+      }
       wt[q] = w;
     }
     __syncthreads();
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = tid + 256 * u;
-      if (q < per) {
-        const int hh = q / C4, c4 = q % C4, j = (4 * c4) / (DC / NB);
-        const float* src = ws.acc + ((size_t)(k0 + b) * H + h0 + hh) * DC + 4 * c4;
+    if (tid < per) {
+      const int hh = tid / C8, c8 = tid % C8, j = (8 * c8) / (DC / NB);
+      const _Float16* src = acc16 + ((size_t)(k0 + b) * H + h0 + hh) * DC + 8 * c8;
 #pragma unroll 8
-        for (int kk = 0; kk < nk; ++kk)
-          r[u] += wt[kk * NP + j * kMH + hh] * *(const f32x4*)(src + (size_t)kk * H * DC);
-      }
+      for (int kk = 0; kk < nk; ++kk)
+        fma_f16x8(r, wt[kk * NP + j * kMH + hh], *(const dev::i32x4*)(src + (size_t)kk * H * DC));
     }
   }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int q = tid + 256 * u;
-    if (q < per) *(f32x4*)(out + 4 * q) = out_scale * r[u];
+  if (tid < per) {
+    *(f32x4*)(out + 8 * tid) = out_scale * r[0];
+    *(f32x4*)(out + 8 * tid + 4) = out_scale * r[1];
   }
 }
 
@@ -358,15 +372,15 @@ __global__ __launch_bounds__(256) void out_proj(Geom g, const float* __restrict_
 // XOR-swizzled by kWSwz, so the transposed reads of the projection hit 64
 // distinct banks. Meanwhile waves 4-7 merge: a 16-lane group per (sequence,
 // branch) reads the slots' (m, l), reduces them to (M, 1/L) with lane
-// shuffles and writes the weights 2^(m_k - M) / L to an LDS table (kMOS
-// slots per pass); every thread's first kMKU partial rows are already in
-// flight by then. The latent rows go to LDS as bf16 hi + lo (rows 8..15 of
+// shuffles and writes the weights 2^(m_k - M) l_k / L to an LDS table (kMOS
+// slots per pass); every thread's first kMKU partial rows (16-byte fp16
+// chunks, 8 columns) are already in flight by then. The latent rows go to LDS as bf16 hi + lo (rows 8..15 of
 // the MFMA's A operand are zero) and all 8 waves project 16 output columns
 // each. The workgroups of a head run on one XCD (8 apart in launch order),
 // so W_UV[h] comes from L2 after the first.
 constexpr int kMOS = 32;  // slots per weight table pass
 constexpr int kMSQ = 8;   // sequences per block
-constexpr int kMKU = 8;   // partial rows per (thread, column quad) in flight
+constexpr int kMKU = 8;   // partial rows per (thread, column oct) in flight
 
 __device__ __forceinline__ int kWSwz(int row) { return 2 * ((row & 3) | (((row >> 3) & 1) << 2)); }
 
@@ -408,8 +422,8 @@ __global__ __launch_bounds__(512) void merge_out(Geom g, Workspace ws,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, kg = lane >> 4;
   const int NB = g.n, H = g.H, bw = DC / NB;
-  constexpr int C4 = DC / 4;
-  constexpr int NQ = (kMSQ * C4 + 511) / 512;  // column quads per thread
+  constexpr int C8 = DC / 8;
+  constexpr int NQ = (kMSQ * C8 + 511) / 512;  // column octs (16-byte fp16 chunks) per thread
   const int nbq = min(kMSQ, g.B - b0);
 
   if (wave < 4) {
@@ -447,12 +461,14 @@ __global__ __launch_bounds__(512) void merge_out(Geom g, Workspace ws,
   for (int bb = 0; bb < kMSQ; ++bb) maxs = max(maxs, rng[2 * bb + 1] - rng[2 * bb] + 1);
 
   // waves 4-7 reduce (m, l): group grp = (tid / 16) % 16 takes (sequence,
-  // branch) pairs grp, grp + 16, ...; every thread sums quads q = tid + 512 u
+  // branch) pairs grp, grp + 16, ...; every thread sums octs q = tid + 512 u
   const int grp = (tid >> 4) & 15;
   constexpr int PPG = kMSQ * kMNB / 16;  // most pairs per group
   float Mp[PPG], Ip[PPG], mk[PPG][2], lk[PPG][2];
-  f32x4 r[NQ], v[kMKU][NQ];
-  const float* src[NQ];
+  f32x4 r[NQ][2];
+  dev::i32x4 v[kMKU][NQ];
+  const _Float16* acc16 = reinterpret_cast<const _Float16*>(ws.acc);
+  const _Float16* src[NQ];
   int nsq[NQ], wi[NQ];
   // (m, l) of the first 32 slots of each pair: loads on every wave without a
   // branch (slot clamped into the sequence's range, or slot 0 when it has
@@ -471,16 +487,16 @@ __global__ __launch_bounds__(512) void merge_out(Geom g, Workspace ws,
       lk[pj][e] = ws.l[idx];
     }
   }
-  // the first kMKU partial rows of every quad: in flight with the (m, l)
+  // the first kMKU partial rows of every oct: in flight with the (m, l)
   // loads (and, on waves 0-3, behind the W_UV DMA)
 #pragma unroll
   for (int u = 0; u < NQ; ++u) {
-    const int q = min(tid + 512 * u, kMSQ * C4 - 1), bb = q / C4, c4 = q % C4;
+    const int q = min(tid + 512 * u, kMSQ * C8 - 1), bb = q / C8, c8 = q % C8;
     const int kf = rng[2 * bb];
-    nsq[u] = tid + 512 * u < kMSQ * C4 ? rng[2 * bb + 1] - kf + 1 : 0;
-    src[u] = ws.acc + ((size_t)(kf + b0 + bb) * H + h) * DC + 4 * c4;
-    wi[u] = bb * kMOS * NB + (4 * c4) / bw;
-    r[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    nsq[u] = tid + 512 * u < kMSQ * C8 ? rng[2 * bb + 1] - kf + 1 : 0;
+    src[u] = acc16 + ((size_t)(kf + b0 + bb) * H + h) * DC + 8 * c8;
+    wi[u] = bb * kMOS * NB + (8 * c8) / bw;
+    r[u][0] = r[u][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int k = 0; k < kMKU; ++k)
@@ -488,9 +504,9 @@ __global__ __launch_bounds__(512) void merge_out(Geom g, Workspace ws,
     for (int u = 0; u < NQ; ++u) {
       // no branch: a slot past the sequence re-reads its last one (or slot
       // 0 of the workspace) and is zeroed
-      const float* a = nsq[u] > 0 ? src[u] + (size_t)min(k, nsq[u] - 1) * H * DC : ws.acc;
-      const f32x4 x = *(const f32x4*)a;
-      v[k][u] = k < nsq[u] ? x : (f32x4){0.f, 0.f, 0.f, 0.f};
+      const _Float16* a = nsq[u] > 0 ? src[u] + (size_t)min(k, nsq[u] - 1) * H * DC : acc16;
+      const dev::i32x4 x = *(const dev::i32x4*)a;
+      v[k][u] = k < nsq[u] ? x : (dev::i32x4){0, 0, 0, 0};
     }
   if (wave >= 4) {
     // (M, 1/L) per pair: online over this lane's slots, then over the 16 lanes
@@ -529,10 +545,14 @@ __global__ __launch_bounds__(512) void merge_out(Geom g, Workspace ws,
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int s = s0 + l16 + 16 * e;
-          float m = mk[pj][e];
-          if (s0 > 0 && s < ns) m = ws.m[((size_t)(kf + s + b0 + bb) * NB + j) * H + h];
+          float m = mk[pj][e], l = lk[pj][e];
+          if (s0 > 0 && s < ns) {
+            const size_t i = ((size_t)(kf + s + b0 + bb) * NB + j) * H + h;
+            m = ws.m[i];
+            l = ws.l[i];
+          }
           wt[(bb * kMOS + l16 + 16 * e) * NB + j] =
-              s < ns && m > -INFINITY ? exp2f(m - Mp[pj]) * Ip[pj] : 0.f;
+              s < ns && m > -INFINITY ? exp2f(m - Mp[pj]) * l * Ip[pj] : 0.f;
         }
       }
     }
@@ -548,15 +568,15 @@ __global__ __launch_bounds__(512) void merge_out(Geom g, Workspace ws,
 #pragma unroll
             for (int u = 0; u < NQ; ++u)
               v[k][u] = s0 + k0 + k < nsq[u] && k0 + k < kMOS
-                            ? *(const f32x4*)(src[u] + (size_t)(s0 + k0 + k) * H * DC)
-                            : (f32x4){0.f, 0.f, 0.f, 0.f};
+                            ? *(const dev::i32x4*)(src[u] + (size_t)(s0 + k0 + k) * H * DC)
+                            : (dev::i32x4){0, 0, 0, 0};
         }
 #pragma unroll
         for (int k = 0; k < kMKU; ++k)
 #pragma unroll
           for (int u = 0; u < NQ; ++u)
             if (s0 + k0 + k < nsq[u] && k0 + k < kMOS)
-              r[u] += wt[wi[u] + (k0 + k) * NB] * v[k][u];
+              fma_f16x8(r[u], wt[wi[u] + (k0 + k) * NB], v[k][u]);
       }
     }
   }
@@ -564,18 +584,17 @@ __global__ __launch_bounds__(512) void merge_out(Geom g, Workspace ws,
     // the block's latent rows as bf16 hi + lo
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
-      const int q = tid + 512 * u, bb = q / C4, c4 = q % C4;
-      if (q >= kMSQ * C4) break;
-      __bf16 hi[4], lo[4];
+      const int q = tid + 512 * u, bb = q / C8, c8 = q % C8;
+      if (q >= kMSQ * C8) break;
+      bf16x8 hi, lo;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hi[e] = (__bf16)r[u][e];
-        lo[e] = (__bf16)(r[u][e] - (float)hi[e]);
+      for (int e = 0; e < 8; ++e) {
+        const float x = r[u][e >> 2][e & 3];
+        hi[e] = (__bf16)x;
+        lo[e] = (__bf16)(x - (float)hi[e]);
       }
-      __bf16 LDS_AS* ph = (__bf16 LDS_AS*)(lhi + bb * MD::LROW) + 4 * c4;
-      __bf16 LDS_AS* pl = (__bf16 LDS_AS*)(llo + bb * MD::LROW) + 4 * c4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { ph[e] = hi[e]; pl[e] = lo[e]; }
+      *(bf16x8 LDS_AS*)((__bf16 LDS_AS*)(lhi + bb * MD::LROW) + 8 * c8) = hi;
+      *(bf16x8 LDS_AS*)((__bf16 LDS_AS*)(llo + bb * MD::LROW) + 8 * c8) = lo;
     }
   }
   if (wave < 4) dev::wait_vm<0>();  // this wave's share of W_UV[h] is in LDS

@@ -127,7 +127,13 @@ typedef struct {
  * with cfg->dtype = MLRA_BF16 (queries, weights and outputs stay bf16). The
  * decode calls (mla_decode_attn, mlra_decode, mlra_decode_noalloc) accept it;
  * mlra_prefill returns MLRA_ERR_UNSUPPORTED. With fp8 = 0 the scales are
- * ignored and the elements have cfg->dtype. */
+ * ignored and the elements have cfg->dtype.
+ *
+ * Value range: the MFMA decode kernels (head-group, branch, wide) keep each
+ * work item's partial latent output, a weighted mean of cache rows, in fp16
+ * between the decode and the merge, and the wide kernel and the fp16 modes
+ * convert the cache itself to fp16; latent values beyond fp16's range
+ * (|c| > 65504) saturate there. The portable kernel has no such limit. */
 typedef struct {
   const void* ckv;
   const void* krope;
