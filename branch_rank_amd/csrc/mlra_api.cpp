@@ -386,8 +386,8 @@ mlra_status_t plan_for(const mlra_config_t* c, const Geom& g, int cus, const mlr
 
 // Split-KV decode into the workspace partials, after the plan (launched here
 // unless plan_done). *fast tells which kind of decode ran: an MFMA kernel
-// (partial acc as [slot][H][d_c]) or the portable one ([slot][d_c][H]); the
-// merge must match.
+// (partials acc / l as fp16 [slot][H][d_c]) or the portable one (acc as fp32
+// [slot][d_c][H]); the merge must match.
 mlra_status_t run_decode(const mlra_config_t* c, const Geom& g, const QView& q,
                          const mlra_cache_t* k, const Workspace& ws, const Layout& L,
                          mlra_kernel_t kern, const PlanArgs& plan, bool plan_done, bool* fast_out,
