@@ -710,7 +710,8 @@ hipError_t launch_absorb_q_mfma(const Geom& g, const __bf16* q_nope, const __bf1
 
 hipError_t launch_combine_hc(const Geom& g, const Workspace& ws, float* latent_out,
                              float out_scale, hipStream_t s) {
-  if (g.n > kMNB) return hipErrorNotSupported;
+  // one thread per 8-column chunk of kMH heads: d_c <= 512 (every MFMA decode's)
+  if (g.n > kMNB || g.dc > 512 || g.dc % 8) return hipErrorNotSupported;
   hipLaunchKernelGGL(combine_hc, dim3(g.B, (g.H + kMH - 1) / kMH), dim3(256), 0, s, g, ws,
                      latent_out, out_scale);
   return hipGetLastError();
